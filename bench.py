@@ -1,0 +1,265 @@
+"""Benchmark of the owner-side Muon step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--precision P]
+
+A step is one full muon_step over every batch of the workload (momentum,
+normalisation, transpose-first, K Newton-Schulz steps, decay and update), with
+all inputs resident in device memory.  Prints ONE JSON line with:
+
+* value: Newton-Schulz TFLOP/s, counting 4 m^2 n + 2 m^3 flops per
+  Newton-Schulz step per matrix (m <= n), divided by the full step time;
+* ms_per_step: batched step latency;
+* roofline: the dominant kernel (largest share of traced time), its
+  algorithmic bytes (or flops) per launch over its average launch time,
+  measured with HIP events recorded by the library on the launch stream;
+* cpu_baseline: the float64 CPU oracle timed on a bounded sample of the same
+  workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 (vector / MFMA)
+SKINNY_MAX_ROWS = 32
+
+
+def dsize(dtype: str) -> int:
+    return 2 if dtype == "bf16" else 4
+
+
+def kernel_model(name, count, M, N, prec, pdt, gdt, with_ns_out=False):
+    """(bound, algorithmic quantity per launch, unit) of one kernel launch.
+
+    Bytes are what the kernel's function needs to move once (inputs read once,
+    outputs written once); flops are the products the algorithm needs (the
+    symmetric products counted on one triangle, diagonal included)."""
+    m, n = min(M, N), max(M, N)
+    E = count * m * n
+    xs = 2 if prec == "bf16" else 4
+    gs, ps = dsize(gdt), dsize(pdt)
+    if m <= SKINNY_MAX_ROWS:
+        L = 512 if prec == "f32" else 1024
+        S = math.ceil(n / L)
+        T = m * (m + 1) // 2
+        part = count * S * T * 4
+        if name == "sk_momentum_norm_gram":
+            return "hbm", E * (gs + 4 + 4 + xs) + part + count * S * 4, "B"
+        if name == "sk_ns_step":
+            return "hbm", E * 2 * xs + 2 * part, "B"
+        if name == "sk_ns_step_update":
+            return "hbm", E * (xs + 2 * ps + (4 if with_ns_out else 0)) + part, "B"
+    else:
+        if name == "tl_momentum_norm":
+            return "hbm", E * (gs + 8), "B"
+        if name == "tl_layout":
+            return "hbm", E * (gs + 4) + E * (2 * xs + (4 if prec == "bf16_x32" else 0)), "B"
+        if name == "tl_gram":
+            return "mfma", count * m * (m + 1) * n, "flop"
+        if name == "tl_poly":
+            return "mfma", count * m * m * (m + 1), "flop"
+        if name in ("tl_apply", "tl_apply_update"):
+            return "mfma", count * 2 * m * m * n, "flop"
+        if name == "tl_norm_finalize":
+            return "hbm", count * 4 * 1024, "B"
+    return "hbm", 0, "B"
+
+
+def make_device_batches(wl, plan, dtype, reuse_shapes: bool):
+    """Per-batch device buffers from the seeded generator.  With reuse_shapes,
+    batches of identical [count, M, N] get copies of the first one's data."""
+    import torch
+    from tests import harness as H
+    cache = {}
+    out = []
+    for b in plan.batches:
+        key = (b.count, b.M, b.N)
+        if reuse_shapes and key in cache:
+            src = cache[key]
+            out.append({k: v.clone() for k, v in src.items()})
+            continue
+        arrays = H.batch_arrays(wl, b)
+        dev = {"param": H.to_device(arrays["param"], dtype), "grad": H.to_device(arrays["grad"], dtype),
+               "momentum": H.to_device(arrays["momentum"], "f32")}
+        del arrays
+        if reuse_shapes:
+            cache[key] = dev
+        out.append(dev)
+    return out
+
+
+def cpu_baseline(wl, plan, dtype, hp, budget_s=12.0, max_matrices=None):
+    """Time the float64 oracle on this host on a bounded sample of the workload."""
+    from oracle import muon_oracle as ORC
+    from tests import harness as H
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    kw = None
+    flops = 0.0
+    t0 = time.perf_counter()
+    done = 0
+    reps = 0
+    samples = []
+    for b in plan.batches:
+        ids = H.matrix_ids(b)
+        take = ids if max_matrices is None else ids[:max_matrices]
+        for (pi, mi) in take:
+            samples.append((b, pi, mi))
+    # decode the sample once, then run the oracle until the budget is used
+    data = []
+    for (b, pi, mi) in samples:
+        W = H.decode(wl.matrix(pi, mi, "param"))
+        G = H.decode(wl.matrix(pi, mi, "grad"))
+        Mo = wl.matrix(pi, mi, "momentum").astype(np.float64)
+        data.append((b, W, G, Mo))
+        if max_matrices is not None and len(data) >= max_matrices:
+            break
+    t0 = time.perf_counter()
+    while True:
+        for (b, W, G, Mo) in data:
+            kw = H.oracle_kwargs(hp, b.M, b.N)
+            ORC.muon_step_matrix(W, G, Mo, **kw)
+            m, n = min(b.M, b.N), max(b.M, b.N)
+            flops += hp.ns_steps * (4.0 * m * m * n + 2.0 * m ** 3)
+            done += 1
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(data)} matrices of the workload x {reps} repetitions ({done} oracle steps, "
+                      f"{el:.1f} s, float64 NumPy)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="fused_74x24x10240")
+    ap.add_argument("--precision", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--reuse-shapes", action="store_true",
+                    help="batches of identical shape share generated input values (copied per batch)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the step shards by whole matrices; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from matrix_optimizer_amd import binding as B
+    from matrix_optimizer_amd import workloads as WL
+    from tests import harness as H
+
+    wl = WL.WORKLOADS[args.workload]
+    prec = args.precision or wl.hp.precision
+    dtype = wl.params[0].dtype
+    hp = H.c_hparams(wl.hp, precision=prec)
+    torch.cuda.set_device(0)
+    plan = B.Plan([p.shape for p in wl.params])
+    bufs = make_device_batches(wl, plan, dtype, args.reuse_shapes)
+    ws_bytes = max(plan.workspace_bytes(b.index, prec) for b in plan.batches)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for b in plan.batches:
+            d = bufs[b.index]
+            B.muon_step(plan, b.index, d["param"], d["grad"], d["momentum"], hp, ws, stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel times: a second pass of the same K steps with library launch tracing
+    launches = 0
+    for b in plan.batches:
+        launches += 64
+    B.muon_trace_start(args.steps * launches + 16)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    traced_ms = t0.elapsed_time(t1) / args.steps
+    recs = B.muon_trace_stop()
+    per = {}
+    for name, t in recs:
+        per.setdefault(name, []).append(t)
+    kernels = {k: {"launches_per_step": len(v) / args.steps, "avg_ms": float(np.mean(v)),
+                   "total_ms_per_step": float(np.sum(v)) / args.steps} for k, v in per.items()}
+    dom = max(kernels, key=lambda k: kernels[k]["total_ms_per_step"])
+    # algorithmic quantity of one launch of the dominant kernel (averaged over batches)
+    qty = 0.0
+    nlaunch = 0
+    bound, unit = "hbm", "B"
+    for b in plan.batches:
+        bd, q, u = kernel_model(dom, b.count, b.M, b.N, prec, dtype, dtype)
+        per_batch = {"sk_ns_step": hp.ns_steps - 1, "tl_gram": hp.ns_steps, "tl_poly": hp.ns_steps,
+                     "tl_apply": hp.ns_steps - 1}.get(dom, 1)
+        qty += q * per_batch
+        nlaunch += per_batch
+        bound, unit = bd, u
+    qty_per_launch = qty / max(nlaunch, 1)
+    avg_s = kernels[dom]["avg_ms"] / 1e3
+    if bound == "hbm":
+        achieved = qty_per_launch / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": None}
+    else:
+        achieved = qty_per_launch / avg_s / 1e12
+        peak = FP32_PEAK_TFLOPS if prec == "f32" else BF16_PEAK_TFLOPS
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": None}
+    roof["kernel"] = dom
+    roof["avg_launch_ms"] = kernels[dom]["avg_ms"]
+    roof["algorithmic_per_launch"] = qty_per_launch
+    roof["algorithmic_unit"] = "bytes" if unit == "B" else "flops"
+
+    flops = wl.nominal_ns_flops()
+    if hp.ns_steps != wl.hp.ns_steps:
+        flops = flops / wl.hp.ns_steps * hp.ns_steps
+    value = flops / (ms / 1e3) / 1e12
+    cfg = {"workload": wl.name, "matrices": int(sum(b.count for b in plan.batches)),
+           "batches": [[b.count, b.M, b.N] for b in plan.batches], "param_dtype": dtype,
+           "precision": prec, "ns_steps": hp.ns_steps, "coeffs": list(hp.coeffs),
+           "inputs": "seeded synthetic" + (", same-shape batches share values" if args.reuse_shapes else "")}
+    out = {"metric": "Muon-step NS TFLOP/s (bf16 MFMA)", "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if prec != "f32" else "f32",
+           "data": "synthetic", "config": cfg, "roofline": roof,
+           "detail": {"ns_frac_of_bf16_peak": value / BF16_PEAK_TFLOPS, "traced_ms_per_step": traced_ms,
+                      "kernels": kernels, "device": torch.cuda.get_device_name(0)}}
+    if not args.no_cpu_baseline:
+        maxm = None if min(wl.params[0].matrix_shape) <= SKINNY_MAX_ROWS else 1
+        out["cpu_baseline"] = cpu_baseline(wl, plan, dtype, hp, args.cpu_budget, maxm)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,183 @@
+/*
+ * muon.h -- C ABI of libmuon, the owner-side Muon optimizer step on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One step on one matrix W (m x n) with gradient G and fp32 momentum M:
+ *
+ *   M' = mu M + G                      DMuon-2 §2.1 (momentum recurrence);
+ *   U  = G + mu M'  (Nesterov)         the Nesterov variant that page uses;
+ *   X0 = U / (||U||_F + eps)           HyperParallel-FSDP §2.3;
+ *   if rows > cols iterate on X0^T     HyperParallel-FSDP §6.6 (transpose-first);
+ *   X_{k+1} = a_k X + b_k (X X^T) X + c_k (X X^T)^2 X,  k = 0..K-1
+ *                                      HyperParallel-FSDP §2.3, Eq. (1);
+ *   O  = X_K (back in W's orientation)
+ *   W' = W - lr (wd W + s O)           decoupled decay (HyperParallel-FSDP §6.3,
+ *                                      §6.4 step 4; HyperParallel RFC item 6),
+ *   s  = 0.2 sqrt(max(m, n))           RMS-matched scale, HyperParallel-FSDP §2.3.
+ *
+ * Parameters of the same core shape are batched ("shape fusion",
+ * HyperParallel-FSDP §6.6 / Figure 10(a); HyperParallel RFC item 3): [A,B],
+ * [A,1,B] and [E,A,B] all contribute (A,B) matrices, an expert tensor being E
+ * independent matrices (HyperParallel-FSDP §6.3).  muon_plan_create does that
+ * bucketing on the host; muon_step runs one batch on the caller's stream.
+ *
+ * Memory and ownership.  Every device pointer is owned by the caller.  Per
+ * batch, param, grad, momentum and ns_out are contiguous row-major
+ * [count, M, N] regions (a parameter's matrices sit at the segment offsets
+ * that muon_plan_segments reports).  The library never allocates, frees or
+ * synchronises device memory or streams; its only state is the host-side plan.
+ * All kernels are enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ * and the call returns without waiting for them.
+ *
+ * Errors.  Every argument is checked before anything is enqueued; on an error
+ * nothing is launched and no buffer is touched.  A launch failure returns
+ * MUON_ERR_HIP; a fault inside a kernel surfaces at the caller's next stream
+ * synchronisation.
+ *
+ * Threading.  A plan is immutable after creation and may be used from several
+ * threads.  Concurrent muon_step calls on different streams need separate
+ * workspaces (and separate buffers).
+ */
+#ifndef LIBMUON_MUON_H
+#define LIBMUON_MUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MUON_ABI_VERSION 1
+
+typedef enum {
+  MUON_OK = 0,
+  MUON_ERR_INVALID_ARG = 1,        /* null pointer, bad index, non-finite or out-of-range value, aliasing */
+  MUON_ERR_UNSUPPORTED = 2,        /* a shape or combination the library does not handle (1-D, 4-D, ...) */
+  MUON_ERR_WORKSPACE_TOO_SMALL = 3,
+  MUON_ERR_NO_MEMORY = 4,          /* host allocation of the plan failed */
+  MUON_ERR_HIP = 5,                /* the HIP runtime refused a launch */
+  MUON_ERR_INTERNAL = 6
+} muon_status;
+
+typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
+
+/* Where Newton-Schulz keeps X and what the matrix products take as operands.
+ *  MUON_PREC_BF16     X stored in bf16; bf16 MFMA operands, fp32 accumulation.
+ *  MUON_PREC_BF16_X32 fp32 master copy of X (the a X term in fp32), bf16 MFMA
+ *                     operands; for ill-conditioned inputs.
+ *  MUON_PREC_F32      every product and every stored intermediate in fp32
+ *                     (the check path). */
+typedef enum { MUON_PREC_BF16 = 0, MUON_PREC_BF16_X32 = 1, MUON_PREC_F32 = 2 } muon_precision;
+
+/* MUON_SCALE_RMS: s = 0.2 sqrt(max(M, N)); MUON_SCALE_NONE: s = 1. */
+typedef enum { MUON_SCALE_NONE = 0, MUON_SCALE_RMS = 1 } muon_scale;
+
+/* A parameter shape: [M,N] (ndim 2), [M,1,N] or [E,M,N] (ndim 3).  A 3-D
+ * shape whose middle dimension is 1 is read as [M,1,N]. */
+typedef struct { int32_t ndim; int64_t dims[3]; } muon_shape;
+
+typedef struct {
+  int64_t max_batch_elems;  /* cap on elements per batch; 0 -> 2^29 ("memory-safe batching",
+                               HyperParallel-FSDP §6.6).  A single matrix above the cap
+                               still forms a batch of its own. */
+  int32_t order;            /* 0: batches in descending element count (HyperParallel-FSDP
+                               Figure 10(b)), ties in creation order; 1: creation order */
+} muon_plan_options;
+
+typedef struct muon_plan muon_plan;   /* opaque, host-only, immutable */
+
+typedef struct {
+  int64_t M, N;             /* stored matrix shape */
+  int64_t count;            /* matrices in the batch */
+  int32_t transposed;       /* 1 if M > N: Newton-Schulz runs on the transpose */
+  int32_t num_segments;
+} muon_batch_info;
+
+/* A run of consecutive matrices of one parameter inside a batch. */
+typedef struct {
+  int32_t param_index;      /* index into the shapes given to muon_plan_create */
+  int32_t reserved;
+  int64_t first_matrix;     /* first expert index (0 for 2-D parameters) */
+  int64_t num_matrices;
+  int64_t elem_offset;      /* element offset of the run inside the batch buffers */
+} muon_segment;
+
+typedef struct {
+  float lr;                 /* eta */
+  float momentum;           /* mu, in [0, 1] */
+  float weight_decay;       /* lambda, >= 0 */
+  float eps;                /* >= 0; a zero denominator gives a zero direction */
+  int32_t nesterov;         /* 1: U = G + mu M'; 0: U = M' */
+  int32_t ns_steps;         /* K, 1..64 */
+  const float* coeffs;      /* host array: 3 floats (a,b,c) used for every step, or 3*K floats */
+  int32_t num_coeff_sets;   /* 1 or ns_steps */
+  muon_scale scale;
+  muon_precision precision;
+} muon_hparams;
+
+typedef struct {
+  void* param;              /* [count,M,N] of param_dtype, updated in place */
+  muon_dtype param_dtype;
+  const void* grad;         /* [count,M,N] of grad_dtype */
+  muon_dtype grad_dtype;
+  float* momentum;          /* [count,M,N] fp32, updated in place */
+  float* ns_out;            /* optional [count,M,N] fp32: receives O (the orthogonalised
+                               direction, in W's orientation, before the scale s); NULL to skip */
+} muon_batch_buffers;
+
+int32_t muon_abi_version(void);
+const char* muon_status_str(muon_status s);
+
+/* Build the batch plan of n parameter shapes (HyperParallel-FSDP §6.6).
+ * opt may be NULL (defaults).  On success *out owns a plan to be released
+ * with muon_plan_destroy.  Errors: INVALID_ARG (null, n < 1, a zero or
+ * negative dimension, element count overflow), UNSUPPORTED (ndim not 2 or 3). */
+muon_status muon_plan_create(const muon_shape* shapes, int32_t n, const muon_plan_options* opt,
+                             muon_plan** out);
+void muon_plan_destroy(muon_plan* plan);
+int32_t muon_plan_num_batches(const muon_plan* plan);
+muon_status muon_plan_batch_info(const muon_plan* plan, int32_t batch, muon_batch_info* out);
+/* Copies up to `capacity` segments of a batch into out. */
+muon_status muon_plan_segments(const muon_plan* plan, int32_t batch, muon_segment* out, int32_t capacity);
+
+/* Device workspace (bytes, a multiple of 256) that muon_step / muon_stage_ns
+ * need for this batch at this precision.  Pure host computation. */
+muon_status muon_workspace_bytes(const muon_plan* plan, int32_t batch, muon_precision precision,
+                                 size_t* out);
+
+/* One full Muon step on one batch: momentum, normalisation, transpose-first,
+ * K Newton-Schulz steps, decay and update.  workspace: device memory of at
+ * least muon_workspace_bytes, 256-byte aligned, owned by the caller and not
+ * shared with a concurrent call.  Buffers must not overlap one another or the
+ * workspace; device pointers must be 16-byte aligned. */
+muon_status muon_step(const muon_plan* plan, int32_t batch, const muon_batch_buffers* bufs,
+                      const muon_hparams* hp, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage entry points, same validation.  They run the stages of muon_step one
+ * at a time so each can be checked on its own.
+ *  momentum: M' = mu M + G (in place) and u_out = U (fp32 [count,M,N]).
+ *  ns:       o_out = O from u_in (both fp32 [count,M,N], W's orientation).
+ *  update:   W' = W - lr (wd W + s O) from o_in (fp32 [count,M,N]). */
+muon_status muon_stage_momentum(const muon_plan* plan, int32_t batch, const void* grad, muon_dtype grad_dtype,
+                                float* momentum, float* u_out, const muon_hparams* hp, void* stream);
+muon_status muon_stage_ns(const muon_plan* plan, int32_t batch, const float* u_in, float* o_out,
+                          const muon_hparams* hp, void* workspace, size_t workspace_bytes, void* stream);
+muon_status muon_stage_update(const muon_plan* plan, int32_t batch, void* param, muon_dtype param_dtype,
+                              const float* o_in, const muon_hparams* hp, void* stream);
+
+/* Launch tracing, for measurement.  muon_trace_start(n) makes the next (at
+ * most n) kernel launches of muon_step and the stage calls record a HIP event
+ * before and after themselves on their stream.  muon_trace_stop waits for
+ * those events, writes up to `capacity` durations (ms) and kernel names
+ * (static strings) in launch order, releases the events and returns the
+ * number of launches traced (-1 if tracing was not started).  Tracing state
+ * is process-wide; start returns INVALID_ARG if it is already on. */
+muon_status muon_trace_start(int32_t max_launches);
+int32_t muon_trace_stop(float* ms, const char** names, int32_t capacity);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMUON_MUON_H */

@@ -1,0 +1,301 @@
+"""ctypes binding of libmuon's C ABI (include/muon.h).
+
+Argument marshalling only: every step of the optimizer runs in the library's
+HIP kernels.  PyTorch supplies device memory and the stream (``data_ptr()``
+and ``torch.cuda.current_stream().cuda_stream``).  If the built library is
+missing, loading fails with an error; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence, Tuple
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libmuon.so")
+_lib = None
+
+# enums (muon.h)
+MUON_OK, MUON_ERR_INVALID_ARG, MUON_ERR_UNSUPPORTED, MUON_ERR_WORKSPACE_TOO_SMALL, \
+    MUON_ERR_NO_MEMORY, MUON_ERR_HIP, MUON_ERR_INTERNAL = range(7)
+MUON_F32, MUON_BF16 = 0, 1
+MUON_PREC_BF16, MUON_PREC_BF16_X32, MUON_PREC_F32 = 0, 1, 2
+MUON_SCALE_NONE, MUON_SCALE_RMS = 0, 1
+
+PRECISIONS = {"bf16": MUON_PREC_BF16, "bf16_x32": MUON_PREC_BF16_X32, "f32": MUON_PREC_F32}
+SCALES = {"none": MUON_SCALE_NONE, "rms": MUON_SCALE_RMS}
+
+EXPORTED = ["muon_abi_version", "muon_status_str", "muon_plan_create", "muon_plan_destroy",
+            "muon_plan_num_batches", "muon_plan_batch_info", "muon_plan_segments",
+            "muon_workspace_bytes", "muon_step", "muon_stage_momentum", "muon_stage_ns",
+            "muon_stage_update", "muon_trace_start", "muon_trace_stop"]
+
+
+class muon_shape(C.Structure):
+    _fields_ = [("ndim", C.c_int32), ("dims", C.c_int64 * 3)]
+
+
+class muon_plan_options(C.Structure):
+    _fields_ = [("max_batch_elems", C.c_int64), ("order", C.c_int32)]
+
+
+class muon_batch_info(C.Structure):
+    _fields_ = [("M", C.c_int64), ("N", C.c_int64), ("count", C.c_int64),
+                ("transposed", C.c_int32), ("num_segments", C.c_int32)]
+
+
+class muon_segment(C.Structure):
+    _fields_ = [("param_index", C.c_int32), ("reserved", C.c_int32), ("first_matrix", C.c_int64),
+                ("num_matrices", C.c_int64), ("elem_offset", C.c_int64)]
+
+
+class muon_hparams(C.Structure):
+    _fields_ = [("lr", C.c_float), ("momentum", C.c_float), ("weight_decay", C.c_float),
+                ("eps", C.c_float), ("nesterov", C.c_int32), ("ns_steps", C.c_int32),
+                ("coeffs", C.POINTER(C.c_float)), ("num_coeff_sets", C.c_int32),
+                ("scale", C.c_int32), ("precision", C.c_int32)]
+
+
+class muon_batch_buffers(C.Structure):
+    _fields_ = [("param", C.c_void_p), ("param_dtype", C.c_int32), ("grad", C.c_void_p),
+                ("grad_dtype", C.c_int32), ("momentum", C.c_void_p), ("ns_out", C.c_void_p)]
+
+
+class MuonError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libmuon.so (built by matrix_optimizer_amd.build); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"libmuon is not built ({_LIB_PATH} missing); run "
+                          "`python -m matrix_optimizer_amd.build` or __graft_entry__.build()")
+    L = C.CDLL(_LIB_PATH)
+    L.muon_abi_version.restype = C.c_int32
+    L.muon_status_str.restype = C.c_char_p
+    L.muon_status_str.argtypes = [C.c_int32]
+    L.muon_plan_create.restype = C.c_int32
+    L.muon_plan_create.argtypes = [C.POINTER(muon_shape), C.c_int32, C.POINTER(muon_plan_options),
+                                   C.POINTER(C.c_void_p)]
+    L.muon_plan_destroy.restype = None
+    L.muon_plan_destroy.argtypes = [C.c_void_p]
+    L.muon_plan_num_batches.restype = C.c_int32
+    L.muon_plan_num_batches.argtypes = [C.c_void_p]
+    L.muon_plan_batch_info.restype = C.c_int32
+    L.muon_plan_batch_info.argtypes = [C.c_void_p, C.c_int32, C.POINTER(muon_batch_info)]
+    L.muon_plan_segments.restype = C.c_int32
+    L.muon_plan_segments.argtypes = [C.c_void_p, C.c_int32, C.POINTER(muon_segment), C.c_int32]
+    L.muon_workspace_bytes.restype = C.c_int32
+    L.muon_workspace_bytes.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.POINTER(C.c_size_t)]
+    L.muon_step.restype = C.c_int32
+    L.muon_step.argtypes = [C.c_void_p, C.c_int32, C.POINTER(muon_batch_buffers), C.POINTER(muon_hparams),
+                            C.c_void_p, C.c_size_t, C.c_void_p]
+    L.muon_stage_momentum.restype = C.c_int32
+    L.muon_stage_momentum.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
+                                      C.POINTER(muon_hparams), C.c_void_p]
+    L.muon_stage_ns.restype = C.c_int32
+    L.muon_stage_ns.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.POINTER(muon_hparams),
+                                C.c_void_p, C.c_size_t, C.c_void_p]
+    L.muon_stage_update.restype = C.c_int32
+    L.muon_stage_update.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p,
+                                    C.POINTER(muon_hparams), C.c_void_p]
+    L.muon_trace_start.restype = C.c_int32
+    L.muon_trace_start.argtypes = [C.c_int32]
+    L.muon_trace_stop.restype = C.c_int32
+    L.muon_trace_stop.argtypes = [C.POINTER(C.c_float), C.POINTER(C.c_char_p), C.c_int32]
+    _lib = L
+    return L
+
+
+def status_str(s: int) -> str:
+    try:
+        return lib().muon_status_str(s).decode()
+    except ImportError:
+        return str(s)
+
+
+def _check(status: int, where: str):
+    if status != MUON_OK:
+        raise MuonError(status, where)
+
+
+def muon_abi_version() -> int:
+    return lib().muon_abi_version()
+
+
+@dataclass
+class BatchInfo:
+    index: int
+    M: int
+    N: int
+    count: int
+    transposed: bool
+    segments: List[Tuple[int, int, int, int]]   # (param_index, first_matrix, num_matrices, elem_offset)
+
+    @property
+    def elems(self) -> int:
+        return self.count * self.M * self.N
+
+
+class Plan:
+    """muon_plan_create / muon_plan_* on a list of parameter shapes."""
+
+    def __init__(self, shapes: Sequence[Sequence[int]], max_batch_elems: int = 0, order: int = 0):
+        L = lib()
+        arr = (muon_shape * len(shapes))()
+        for i, s in enumerate(shapes):
+            arr[i].ndim = len(s)
+            for d in range(min(len(s), 3)):
+                arr[i].dims[d] = int(s[d])
+        opt = muon_plan_options(int(max_batch_elems), int(order))
+        h = C.c_void_p()
+        _check(L.muon_plan_create(arr, len(shapes), C.byref(opt), C.byref(h)), "muon_plan_create")
+        self._h = h
+        self.shapes = [tuple(int(x) for x in s) for s in shapes]
+        self.batches: List[BatchInfo] = []
+        for b in range(L.muon_plan_num_batches(h)):
+            info = muon_batch_info()
+            _check(L.muon_plan_batch_info(h, b, C.byref(info)), "muon_plan_batch_info")
+            segs = (muon_segment * max(1, info.num_segments))()
+            _check(L.muon_plan_segments(h, b, segs, info.num_segments), "muon_plan_segments")
+            self.batches.append(BatchInfo(b, info.M, info.N, info.count, bool(info.transposed),
+                                          [(s.param_index, s.first_matrix, s.num_matrices, s.elem_offset)
+                                           for s in segs[:info.num_segments]]))
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.muon_plan_destroy(h)
+            self._h = None
+
+    def workspace_bytes(self, batch: int, precision: str = "bf16") -> int:
+        out = C.c_size_t()
+        _check(lib().muon_workspace_bytes(self._h, batch, PRECISIONS[precision], C.byref(out)),
+               "muon_workspace_bytes")
+        return out.value
+
+
+@dataclass
+class HParams:
+    lr: float = 0.02
+    momentum: float = 0.95
+    weight_decay: float = 0.1
+    eps: float = 1e-7
+    nesterov: bool = True
+    ns_steps: int = 5
+    coeffs: Tuple[float, ...] = (3.4445, -4.7750, 2.0315)
+    scale: str = "rms"
+    precision: str = "bf16"
+
+    def to_c(self):
+        """(struct, keep-alive coefficient array)."""
+        arr = (C.c_float * len(self.coeffs))(*self.coeffs)
+        hp = muon_hparams(self.lr, self.momentum, self.weight_decay, self.eps, int(bool(self.nesterov)),
+                          int(self.ns_steps), C.cast(arr, C.POINTER(C.c_float)), len(self.coeffs) // 3,
+                          SCALES[self.scale], PRECISIONS[self.precision])
+        return hp, arr
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return MUON_BF16
+    if t.dtype == torch.float32:
+        return MUON_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return int(stream)
+
+
+def muon_step(plan: Plan, batch: int, param, grad, momentum, hp: HParams, workspace,
+              ns_out=None, stream=None) -> None:
+    """One full step on one batch (muon_step).  Tensors are device tensors;
+    param/grad bf16 or fp32, momentum fp32, workspace a uint8 tensor."""
+    hpc, keep = hp.to_c()
+    bufs = muon_batch_buffers(_ptr(param), _dtype_code(param), _ptr(grad), _dtype_code(grad),
+                              _ptr(momentum), _ptr(ns_out))
+    st = lib().muon_step(plan.handle, batch, C.byref(bufs), C.byref(hpc), _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "muon_step")
+
+
+def muon_stage_momentum(plan: Plan, batch: int, grad, momentum, u_out, hp: HParams, stream=None) -> None:
+    hpc, keep = hp.to_c()
+    _check(lib().muon_stage_momentum(plan.handle, batch, _ptr(grad), _dtype_code(grad), _ptr(momentum),
+                                     _ptr(u_out), C.byref(hpc), _stream(stream)), "muon_stage_momentum")
+
+
+def muon_stage_ns(plan: Plan, batch: int, u_in, o_out, hp: HParams, workspace, stream=None) -> None:
+    hpc, keep = hp.to_c()
+    _check(lib().muon_stage_ns(plan.handle, batch, _ptr(u_in), _ptr(o_out), C.byref(hpc), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream)), "muon_stage_ns")
+
+
+def muon_stage_update(plan: Plan, batch: int, param, o_in, hp: HParams, stream=None) -> None:
+    hpc, keep = hp.to_c()
+    _check(lib().muon_stage_update(plan.handle, batch, _ptr(param), _dtype_code(param), _ptr(o_in),
+                                   C.byref(hpc), _stream(stream)), "muon_stage_update")
+
+
+def muon_trace_start(max_launches: int) -> None:
+    _check(lib().muon_trace_start(int(max_launches)), "muon_trace_start")
+
+
+def muon_trace_stop() -> List[Tuple[str, float]]:
+    """(kernel name, milliseconds) of every traced launch, in launch order."""
+    L = lib()
+    cap = 1 << 16
+    ms = (C.c_float * cap)()
+    names = (C.c_char_p * cap)()
+    n = L.muon_trace_stop(ms, names, cap)
+    if n < 0:
+        raise RuntimeError("muon_trace_stop: tracing was not started")
+    return [(names[i].decode(), float(ms[i])) for i in range(min(n, cap))]
+
+
+class BatchedMuon:
+    """All batches of a plan with per-batch contiguous [count, M, N] buffers
+    (parameters of a batch are views into its buffer, as in HyperParallel-FSDP
+    §6.6's merged tensor) and one workspace sized for the largest batch."""
+
+    def __init__(self, shapes, dtype, hp: HParams, device="cuda", max_batch_elems=0, order=0):
+        import torch
+        self.plan = Plan(shapes, max_batch_elems, order)
+        self.hp = hp
+        self.dtype = dtype
+        self.device = device
+        self.params, self.grads, self.moms = [], [], []
+        for b in self.plan.batches:
+            shp = (b.count, b.M, b.N)
+            self.params.append(torch.empty(shp, dtype=dtype, device=device))
+            self.grads.append(torch.empty(shp, dtype=dtype, device=device))
+            self.moms.append(torch.zeros(shp, dtype=torch.float32, device=device))
+        ws = max(self.plan.workspace_bytes(b.index, hp.precision) for b in self.plan.batches)
+        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+
+    def step(self, ns_outs=None, stream=None):
+        for b in self.plan.batches:
+            muon_step(self.plan, b.index, self.params[b.index], self.grads[b.index], self.moms[b.index],
+                      self.hp, self.workspace, None if ns_outs is None else ns_outs[b.index], stream)

@@ -1,0 +1,382 @@
+// C ABI of libmuon: the host-side batch plan, argument validation, workspace
+// layout and dispatch to the kernel launchers.  Declared in include/muon.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/muon.h"
+#include "internal.h"
+
+using namespace muon;
+
+struct muon_plan {
+  struct Batch {
+    int64_t M, N, count;
+    bool transposed;
+    std::vector<muon_segment> segs;
+  };
+  std::vector<Batch> batches;
+};
+
+namespace {
+
+constexpr int64_t kDefaultCap = int64_t(1) << 29;
+constexpr int64_t kMaxMatrixElems = int64_t(1) << 31;   // per padded matrix (32-bit safe tiles)
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+BatchShape shape_of(const muon_plan::Batch& b) {
+  BatchShape s;
+  s.count = b.count;
+  s.M = b.M;
+  s.N = b.N;
+  s.m = std::min(b.M, b.N);
+  s.n = std::max(b.M, b.N);
+  s.transposed = b.M > b.N;
+  return s;
+}
+
+}  // namespace
+
+namespace muon {
+
+WsLayout workspace_layout(const BatchShape& b, int prec) {
+  WsLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  if (b.m <= kSkinnyMaxRows) {
+    L.skinny = true;
+    const int64_t Lc = skinny_chunk(prec);
+    L.ldx = round_up(b.n, Lc);
+    L.S = L.ldx / Lc;
+    L.T = b.m * (b.m + 1) / 2;
+    const size_t xs = prec == PREC_BF16 ? 2 : 4;
+    L.x = take(size_t(b.count) * b.m * L.ldx * xs);
+    L.gp0 = take(size_t(b.count) * L.S * L.T * 4);
+    L.gp1 = take(size_t(b.count) * L.S * L.T * 4);
+    L.sp = take(size_t(b.count) * L.S * 4);
+  } else {
+    L.skinny = false;
+    L.mp = round_up(b.m, kTilePad);
+    L.np = round_up(b.n, kTilePad);
+    L.nparts = norm_parts(b.M * b.N);
+    const size_t op = prec == PREC_F32 ? 4 : 2;
+    const size_t xe = size_t(b.count) * L.mp * L.np;
+    const size_t ae = size_t(b.count) * L.mp * L.mp;
+    L.x = take(xe * op);
+    L.xt0 = take(xe * op);
+    L.xt1 = take(xe * op);
+    if (prec == PREC_BF16_X32) L.x32 = take(xe * 4);
+    L.a32 = take(ae * 4);
+    if (prec != PREC_F32) L.a16 = take(ae * 2);
+    L.pb = take(ae * op);
+    L.ssp = take(size_t(b.count) * L.nparts * 4);
+    L.inv = take(size_t(b.count) * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+}  // namespace muon
+
+namespace {
+
+bool finite(float x) { return std::isfinite(x); }
+
+muon_status check_hparams(const muon_hparams* hp, bool need_ns, bool need_update, bool need_mom) {
+  if (!hp) return MUON_ERR_INVALID_ARG;
+  if (need_mom) {
+    if (!finite(hp->momentum) || hp->momentum < 0.f || hp->momentum > 1.f) return MUON_ERR_INVALID_ARG;
+    if (hp->nesterov != 0 && hp->nesterov != 1) return MUON_ERR_INVALID_ARG;
+  }
+  if (need_ns) {
+    if (hp->ns_steps < 1 || hp->ns_steps > 64) return MUON_ERR_INVALID_ARG;
+    if (hp->num_coeff_sets != 1 && hp->num_coeff_sets != hp->ns_steps) return MUON_ERR_INVALID_ARG;
+    if (!hp->coeffs) return MUON_ERR_INVALID_ARG;
+    for (int i = 0; i < 3 * hp->num_coeff_sets; ++i)
+      if (!finite(hp->coeffs[i])) return MUON_ERR_INVALID_ARG;
+    if (!finite(hp->eps) || hp->eps < 0.f) return MUON_ERR_INVALID_ARG;
+    if (hp->precision != MUON_PREC_BF16 && hp->precision != MUON_PREC_BF16_X32 && hp->precision != MUON_PREC_F32)
+      return MUON_ERR_INVALID_ARG;
+  }
+  if (need_update) {
+    if (!finite(hp->lr) || hp->lr < 0.f) return MUON_ERR_INVALID_ARG;
+    if (!finite(hp->weight_decay) || hp->weight_decay < 0.f) return MUON_ERR_INVALID_ARG;
+    if (hp->scale != MUON_SCALE_NONE && hp->scale != MUON_SCALE_RMS) return MUON_ERR_INVALID_ARG;
+  }
+  return MUON_OK;
+}
+
+bool valid_dtype(muon_dtype d) { return d == MUON_F32 || d == MUON_BF16; }
+size_t dsize(muon_dtype d) { return d == MUON_BF16 ? 2 : 4; }
+
+struct Region {
+  uintptr_t lo, hi;
+};
+
+// null -> invalid; 16-byte alignment; pairwise disjoint.
+bool regions_ok(std::vector<Region> rs) {
+  for (const Region& r : rs)
+    if (r.lo == 0 || (r.lo & 15u)) return false;
+  for (size_t i = 0; i < rs.size(); ++i)
+    for (size_t j = i + 1; j < rs.size(); ++j)
+      if (rs[i].lo < rs[j].hi && rs[j].lo < rs[i].hi) return false;
+  return true;
+}
+
+Region region(const void* p, size_t bytes) {
+  uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Region{a, a + bytes};
+}
+
+void fill_common(StepArgs& a, const muon_plan::Batch& b, const muon_hparams* hp, void* stream) {
+  a.shape = shape_of(b);
+  a.stream = reinterpret_cast<hipStream_t>(stream);
+  a.param = nullptr; a.grad = nullptr; a.mom = nullptr; a.u_in = nullptr; a.u_out = nullptr;
+  a.ns_out = nullptr; a.o_in = nullptr; a.ws = nullptr;
+  a.param_dtype = DT_F32; a.grad_dtype = DT_F32;
+  a.lr = hp->lr; a.mu = hp->momentum; a.wd = hp->weight_decay; a.eps = hp->eps;
+  a.nesterov = hp->nesterov;
+  a.s = hp->scale == MUON_SCALE_RMS ? float(0.2 * std::sqrt(double(std::max(b.M, b.N)))) : 1.0f;
+  a.steps = hp->ns_steps;
+  a.prec = hp->precision;
+  a.coeffs.clear();
+  if (hp->coeffs) {
+    for (int k = 0; k < hp->ns_steps; ++k) {
+      const float* c = hp->coeffs + 3 * (hp->num_coeff_sets == 1 ? 0 : k);
+      a.coeffs.push_back(c[0]); a.coeffs.push_back(c[1]); a.coeffs.push_back(c[2]);
+    }
+  }
+}
+
+const muon_plan::Batch* get_batch(const muon_plan* plan, int32_t batch) {
+  if (!plan || batch < 0 || batch >= (int32_t)plan->batches.size()) return nullptr;
+  return &plan->batches[batch];
+}
+
+muon_status hip_status(hipError_t e) { return e == hipSuccess ? MUON_OK : MUON_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t muon_abi_version(void) { return MUON_ABI_VERSION; }
+
+const char* muon_status_str(muon_status s) {
+  switch (s) {
+    case MUON_OK: return "ok";
+    case MUON_ERR_INVALID_ARG: return "invalid argument";
+    case MUON_ERR_UNSUPPORTED: return "unsupported shape or combination";
+    case MUON_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MUON_ERR_NO_MEMORY: return "host out of memory";
+    case MUON_ERR_HIP: return "HIP launch error";
+    case MUON_ERR_INTERNAL: return "internal error";
+  }
+  return "unknown status";
+}
+
+muon_status muon_plan_create(const muon_shape* shapes, int32_t n, const muon_plan_options* opt, muon_plan** out) {
+  if (!out) return MUON_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!shapes || n < 1) return MUON_ERR_INVALID_ARG;
+  int64_t cap = kDefaultCap;
+  int32_t order = 0;
+  if (opt) {
+    if (opt->max_batch_elems < 0 || (opt->order != 0 && opt->order != 1)) return MUON_ERR_INVALID_ARG;
+    if (opt->max_batch_elems > 0) cap = opt->max_batch_elems;
+    order = opt->order;
+  }
+  // core shape of every parameter (HyperParallel-FSDP §6.6: [A,B], [A,1,B], [N,A,B] -> (A,B))
+  struct Core { int64_t nm, M, N; };
+  std::vector<Core> cores;
+  for (int32_t i = 0; i < n; ++i) {
+    const muon_shape& s = shapes[i];
+    if (s.ndim != 2 && s.ndim != 3) return MUON_ERR_UNSUPPORTED;
+    for (int d = 0; d < s.ndim; ++d)
+      if (s.dims[d] <= 0) return MUON_ERR_INVALID_ARG;
+    Core c;
+    if (s.ndim == 2) c = {1, s.dims[0], s.dims[1]};
+    else if (s.dims[1] == 1) c = {1, s.dims[0], s.dims[2]};
+    else c = {s.dims[0], s.dims[1], s.dims[2]};
+    int64_t per, tot;
+    if (!mul_ok(c.M, c.N, &per) || !mul_ok(per, c.nm, &tot)) return MUON_ERR_INVALID_ARG;
+    // padded matrix must stay addressable with the kernels' tile arithmetic
+    int64_t mp = round_up(std::min(c.M, c.N), kTilePad), np = round_up(std::max(c.M, c.N), kTilePad), pe;
+    if (!mul_ok(mp, np, &pe) || pe > kMaxMatrixElems) return MUON_ERR_UNSUPPORTED;
+    cores.push_back(c);
+  }
+  muon_plan* p = new (std::nothrow) muon_plan;
+  if (!p) return MUON_ERR_NO_MEMORY;
+  try {
+    // buckets in first-seen order of (M, N)
+    std::vector<std::pair<std::pair<int64_t, int64_t>, std::vector<std::pair<int32_t, int64_t>>>> buckets;
+    for (int32_t i = 0; i < n; ++i) {
+      auto key = std::make_pair(cores[i].M, cores[i].N);
+      auto it = std::find_if(buckets.begin(), buckets.end(), [&](const auto& b) { return b.first == key; });
+      if (it == buckets.end()) {
+        buckets.push_back({key, {}});
+        it = buckets.end() - 1;
+      }
+      for (int64_t e = 0; e < cores[i].nm; ++e) it->second.push_back({i, e});
+    }
+    for (auto& bk : buckets) {
+      const int64_t M = bk.first.first, N = bk.first.second, per = M * N;
+      const int64_t max_count = std::max<int64_t>(1, cap / per);
+      const auto& mats = bk.second;
+      for (size_t start = 0; start < mats.size(); start += (size_t)max_count) {
+        const size_t end = std::min(mats.size(), start + (size_t)max_count);
+        muon_plan::Batch b;
+        b.M = M; b.N = N; b.count = (int64_t)(end - start); b.transposed = M > N;
+        for (size_t k = start; k < end; ++k) {
+          const int32_t pi = mats[k].first;
+          const int64_t mi = mats[k].second;
+          if (!b.segs.empty() && b.segs.back().param_index == pi &&
+              b.segs.back().first_matrix + b.segs.back().num_matrices == mi) {
+            b.segs.back().num_matrices += 1;
+          } else {
+            muon_segment sg;
+            sg.param_index = pi; sg.reserved = 0; sg.first_matrix = mi; sg.num_matrices = 1;
+            sg.elem_offset = (int64_t)(k - start) * per;
+            b.segs.push_back(sg);
+          }
+        }
+        p->batches.push_back(std::move(b));
+      }
+    }
+    if (order == 0)
+      std::stable_sort(p->batches.begin(), p->batches.end(), [](const muon_plan::Batch& x, const muon_plan::Batch& y) {
+        return x.count * x.M * x.N > y.count * y.M * y.N;
+      });
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return MUON_ERR_NO_MEMORY;
+  }
+  *out = p;
+  return MUON_OK;
+}
+
+void muon_plan_destroy(muon_plan* plan) { delete plan; }
+
+int32_t muon_plan_num_batches(const muon_plan* plan) { return plan ? (int32_t)plan->batches.size() : -1; }
+
+muon_status muon_plan_batch_info(const muon_plan* plan, int32_t batch, muon_batch_info* out) {
+  const muon_plan::Batch* b = get_batch(plan, batch);
+  if (!b || !out) return MUON_ERR_INVALID_ARG;
+  out->M = b->M; out->N = b->N; out->count = b->count; out->transposed = b->transposed ? 1 : 0;
+  out->num_segments = (int32_t)b->segs.size();
+  return MUON_OK;
+}
+
+muon_status muon_plan_segments(const muon_plan* plan, int32_t batch, muon_segment* out, int32_t capacity) {
+  const muon_plan::Batch* b = get_batch(plan, batch);
+  if (!b || !out || capacity < 0) return MUON_ERR_INVALID_ARG;
+  const int32_t k = std::min<int32_t>(capacity, (int32_t)b->segs.size());
+  for (int32_t i = 0; i < k; ++i) out[i] = b->segs[i];
+  return MUON_OK;
+}
+
+muon_status muon_workspace_bytes(const muon_plan* plan, int32_t batch, muon_precision precision, size_t* out) {
+  const muon_plan::Batch* b = get_batch(plan, batch);
+  if (!b || !out) return MUON_ERR_INVALID_ARG;
+  if (precision != MUON_PREC_BF16 && precision != MUON_PREC_BF16_X32 && precision != MUON_PREC_F32)
+    return MUON_ERR_INVALID_ARG;
+  *out = workspace_layout(shape_of(*b), precision).total;
+  return MUON_OK;
+}
+
+muon_status muon_step(const muon_plan* plan, int32_t batch, const muon_batch_buffers* bufs, const muon_hparams* hp,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  const muon_plan::Batch* b = get_batch(plan, batch);
+  if (!b || !bufs) return MUON_ERR_INVALID_ARG;
+  muon_status st = check_hparams(hp, true, true, true);
+  if (st != MUON_OK) return st;
+  if (!valid_dtype(bufs->param_dtype) || !valid_dtype(bufs->grad_dtype)) return MUON_ERR_INVALID_ARG;
+  const size_t elems = size_t(b->count) * b->M * b->N;
+  const WsLayout L = workspace_layout(shape_of(*b), hp->precision);
+  if (workspace_bytes < L.total) return MUON_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return MUON_ERR_INVALID_ARG;
+  std::vector<Region> rs = {region(bufs->param, elems * dsize(bufs->param_dtype)),
+                            region(bufs->grad, elems * dsize(bufs->grad_dtype)),
+                            region(bufs->momentum, elems * 4), region(workspace, L.total)};
+  if (bufs->ns_out) rs.push_back(region(bufs->ns_out, elems * 4));
+  if (!regions_ok(rs)) return MUON_ERR_INVALID_ARG;
+
+  StepArgs a;
+  fill_common(a, *b, hp, stream);
+  a.phase = PH_FULL;
+  a.param = bufs->param; a.param_dtype = bufs->param_dtype == MUON_BF16 ? DT_BF16 : DT_F32;
+  a.grad = bufs->grad; a.grad_dtype = bufs->grad_dtype == MUON_BF16 ? DT_BF16 : DT_F32;
+  a.mom = bufs->momentum; a.ns_out = bufs->ns_out;
+  a.ws = static_cast<char*>(workspace);
+  return hip_status(L.skinny ? run_skinny(a, L) : run_tiled(a, L));
+}
+
+muon_status muon_stage_momentum(const muon_plan* plan, int32_t batch, const void* grad, muon_dtype grad_dtype,
+                                float* momentum, float* u_out, const muon_hparams* hp, void* stream) {
+  const muon_plan::Batch* b = get_batch(plan, batch);
+  if (!b) return MUON_ERR_INVALID_ARG;
+  muon_status st = check_hparams(hp, false, false, true);
+  if (st != MUON_OK) return st;
+  if (!valid_dtype(grad_dtype)) return MUON_ERR_INVALID_ARG;
+  const size_t elems = size_t(b->count) * b->M * b->N;
+  if (!regions_ok({region(grad, elems * dsize(grad_dtype)), region(momentum, elems * 4), region(u_out, elems * 4)}))
+    return MUON_ERR_INVALID_ARG;
+  StepArgs a;
+  fill_common(a, *b, hp, stream);
+  a.phase = PH_MOMENTUM;
+  a.grad = grad; a.grad_dtype = grad_dtype == MUON_BF16 ? DT_BF16 : DT_F32;
+  a.mom = momentum; a.u_out = u_out;
+  return hip_status(run_momentum_only(a));
+}
+
+muon_status muon_stage_ns(const muon_plan* plan, int32_t batch, const float* u_in, float* o_out, const muon_hparams* hp,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  const muon_plan::Batch* b = get_batch(plan, batch);
+  if (!b) return MUON_ERR_INVALID_ARG;
+  muon_status st = check_hparams(hp, true, false, false);
+  if (st != MUON_OK) return st;
+  const size_t elems = size_t(b->count) * b->M * b->N;
+  const WsLayout L = workspace_layout(shape_of(*b), hp->precision);
+  if (workspace_bytes < L.total) return MUON_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return MUON_ERR_INVALID_ARG;
+  if (!regions_ok({region(u_in, elems * 4), region(o_out, elems * 4), region(workspace, L.total)}))
+    return MUON_ERR_INVALID_ARG;
+  StepArgs a;
+  fill_common(a, *b, hp, stream);
+  a.phase = PH_NS;
+  a.u_in = u_in; a.ns_out = o_out;
+  a.ws = static_cast<char*>(workspace);
+  return hip_status(L.skinny ? run_skinny(a, L) : run_tiled(a, L));
+}
+
+muon_status muon_stage_update(const muon_plan* plan, int32_t batch, void* param, muon_dtype param_dtype,
+                              const float* o_in, const muon_hparams* hp, void* stream) {
+  const muon_plan::Batch* b = get_batch(plan, batch);
+  if (!b) return MUON_ERR_INVALID_ARG;
+  muon_status st = check_hparams(hp, false, true, false);
+  if (st != MUON_OK) return st;
+  if (!valid_dtype(param_dtype)) return MUON_ERR_INVALID_ARG;
+  const size_t elems = size_t(b->count) * b->M * b->N;
+  if (!regions_ok({region(param, elems * dsize(param_dtype)), region(o_in, elems * 4)})) return MUON_ERR_INVALID_ARG;
+  StepArgs a;
+  fill_common(a, *b, hp, stream);
+  a.phase = PH_UPDATE;
+  a.param = param; a.param_dtype = param_dtype == MUON_BF16 ? DT_BF16 : DT_F32;
+  a.o_in = o_in;
+  return hip_status(run_update_only(a));
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Device helpers shared by the libmuon kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_t;   // bf16 stored as raw bits
+
+constexpr int WAVE = 64;
+
+__device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// Load / store one element of a tensor whose dtype is a template parameter.
+template <typename T> __device__ __forceinline__ float ld_as_f32(const T* p, int64_t i);
+template <> __device__ __forceinline__ float ld_as_f32<float>(const float* p, int64_t i) { return p[i]; }
+template <> __device__ __forceinline__ float ld_as_f32<bf16_t>(const bf16_t* p, int64_t i) { return bf2f(p[i]); }
+
+template <typename T> __device__ __forceinline__ void st_from_f32(T* p, int64_t i, float v);
+template <> __device__ __forceinline__ void st_from_f32<float>(float* p, int64_t i, float v) { p[i] = v; }
+template <> __device__ __forceinline__ void st_from_f32<bf16_t>(bf16_t* p, int64_t i, float v) { p[i] = f2bf(v); }
+
+// Value a stored element takes after rounding to T (identity for fp32).
+template <typename T> __device__ __forceinline__ float round_to(float v);
+template <> __device__ __forceinline__ float round_to<float>(float v) { return v; }
+template <> __device__ __forceinline__ float round_to<bf16_t>(float v) { return bf2f(f2bf(v)); }
+
+// Wave-wide sum with a fixed butterfly order (deterministic).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+// Row/column of accumulator register r of lane l in a 32x32 MFMA output block.
+__device__ __forceinline__ int mfma32_row(int lane, int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+__device__ __forceinline__ int mfma32_col(int lane) { return lane & 31; }
+
+// Decoupled decay plus the orthogonal update on one element, fp32.
+__device__ __forceinline__ float apply_update(float w, float o, float lr, float wd, float s) {
+  return w - lr * (wd * w + s * o);
+}
+
+}  // namespace muon

@@ -1,0 +1,92 @@
+// Internal host-side interface between the C ABI (abi.cpp) and the kernel
+// launchers (skinny.hip, tiled.hip).  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+namespace muon {
+
+enum Dtype { DT_F32 = 0, DT_BF16 = 1 };
+enum Prec { PREC_BF16 = 0, PREC_BF16_X32 = 1, PREC_F32 = 2 };
+
+// Which part of the step a call runs.
+enum Phase { PH_FULL = 0, PH_MOMENTUM = 1, PH_NS = 2, PH_UPDATE = 3 };
+
+// Matrices with m = min(M, N) up to this many rows take the skinny path.
+constexpr int64_t kSkinnyMaxRows = 32;
+
+// Skinny path: columns of X handled by one workgroup.
+inline int64_t skinny_chunk(int prec) { return prec == PREC_F32 ? 512 : 1024; }
+
+// Tiled path: rows and columns of X are padded to this multiple.
+constexpr int64_t kTilePad = 128;
+// Tiled path: workgroups per matrix that reduce ||U||_F^2.
+inline int64_t norm_parts(int64_t elems) {
+  int64_t p = (elems + 16383) / 16384;
+  return p < 1 ? 1 : (p > 1024 ? 1024 : p);
+}
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct BatchShape {
+  int64_t count, M, N;   // stored [count, M, N]
+  int64_t m, n;          // Newton-Schulz orientation: m = min(M,N) rows, n = max(M,N) columns
+  bool transposed;       // M > N
+};
+
+// Device workspace carve-up of one batch (offsets in bytes from the base).
+struct WsLayout {
+  bool skinny = false;
+  size_t total = 0;
+  // skinny path
+  int64_t ldx = 0, S = 0, T = 0;
+  size_t x = 0, gp0 = 0, gp1 = 0, sp = 0;
+  // tiled path
+  int64_t mp = 0, np = 0, nparts = 0;
+  size_t xt0 = 0, xt1 = 0, x32 = 0, a32 = 0, a16 = 0, pb = 0, ssp = 0, inv = 0;
+};
+
+WsLayout workspace_layout(const BatchShape& b, int prec);
+
+struct StepArgs {
+  BatchShape shape;
+  int phase;
+  void* param; int param_dtype;
+  const void* grad; int grad_dtype;
+  float* mom;
+  const float* u_in;     // PH_NS input
+  float* u_out;          // PH_MOMENTUM output
+  float* ns_out;         // O output (PH_FULL optional, PH_NS required)
+  const float* o_in;     // PH_UPDATE input
+  float lr, mu, wd, eps, s;
+  int nesterov;
+  int steps;
+  std::vector<float> coeffs;   // 3 * steps (expanded)
+  int prec;
+  char* ws;
+  hipStream_t stream;
+};
+
+// Launch tracing (trace.cpp): no-ops unless muon_trace_start is active.
+void trace_begin(const char* name, hipStream_t s);
+void trace_end(hipStream_t s);
+
+// Launch a kernel, bracketed by trace events when tracing is on.
+#define MUON_LAUNCH(NAME, KERNEL, GRID, BLOCK, STREAM, ...)             \
+  do {                                                                  \
+    ::muon::trace_begin(NAME, STREAM);                                  \
+    hipLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, STREAM, __VA_ARGS__);    \
+    ::muon::trace_end(STREAM);                                          \
+  } while (0)
+
+// Each returns hipSuccess or the first launch error.
+hipError_t run_skinny(const StepArgs& a, const WsLayout& L);
+hipError_t run_tiled(const StepArgs& a, const WsLayout& L);
+hipError_t run_momentum_only(const StepArgs& a);
+hipError_t run_update_only(const StepArgs& a);
+
+}  // namespace muon

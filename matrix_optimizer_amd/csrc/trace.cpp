@@ -1,0 +1,86 @@
+// Launch tracing: when enabled, every kernel launch of muon_step and the stage
+// calls is bracketed by two HIP events on the launch stream, so a caller can
+// read per-kernel durations without an external profiler.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/muon.h"
+#include "internal.h"
+
+namespace {
+
+struct Rec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+
+std::mutex g_mu;
+bool g_on = false;
+std::vector<hipEvent_t> g_pool;
+std::vector<Rec> g_recs;
+size_t g_next = 0;
+
+}  // namespace
+
+namespace muon {
+
+void trace_begin(const char* name, hipStream_t s) {
+  if (!g_on) return;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_on || g_next + 2 > g_pool.size()) return;
+  Rec r{name, g_pool[g_next], g_pool[g_next + 1]};
+  g_next += 2;
+  (void)hipEventRecord(r.start, s);
+  g_recs.push_back(r);
+}
+
+void trace_end(hipStream_t s) {
+  if (!g_on) return;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_on || g_recs.empty()) return;
+  (void)hipEventRecord(g_recs.back().stop, s);
+}
+
+}  // namespace muon
+
+extern "C" {
+
+muon_status muon_trace_start(int32_t max_launches) {
+  if (max_launches < 1) return MUON_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_on) return MUON_ERR_INVALID_ARG;
+  for (hipEvent_t e : g_pool) (void)hipEventDestroy(e);
+  g_pool.assign(size_t(max_launches) * 2, nullptr);
+  for (auto& e : g_pool)
+    if (hipEventCreate(&e) != hipSuccess) return MUON_ERR_HIP;
+  g_recs.clear();
+  g_recs.reserve(max_launches);
+  g_next = 0;
+  g_on = true;
+  return MUON_OK;
+}
+
+int32_t muon_trace_stop(float* ms, const char** names, int32_t capacity) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_on) return -1;
+  g_on = false;
+  int32_t n = 0;
+  for (const Rec& r : g_recs) {
+    if (n < capacity) {
+      float t = -1.f;
+      if (hipEventSynchronize(r.stop) == hipSuccess) (void)hipEventElapsedTime(&t, r.start, r.stop);
+      if (ms) ms[n] = t;
+      if (names) names[n] = r.name;
+    }
+    ++n;
+  }
+  for (hipEvent_t e : g_pool) (void)hipEventDestroy(e);
+  g_pool.clear();
+  g_recs.clear();
+  g_next = 0;
+  return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,256 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle.
+
+Bars (per matrix):
+* O (the orthogonalised direction): relative Frobenius error <= 3e-2 for the
+  bf16 MFMA modes, <= 1e-5 for the fp32 check path;
+* M' (momentum): elementwise |gpu - ref| <= 1e-6 (|mu M| + |G|);
+* W' given the GPU's own O: elementwise <= 1e-6 (|W| + lr|wd W| + lr|s O|)
+  for fp32 W, within one bf16 ulp for bf16 W (round-to-nearest-even store);
+* W' - W end to end against the oracle: the O bound plus the bf16 rounding
+  of the stored W' (derived per matrix from half an ulp of every element).
+Hyperparameters are handed to the oracle as the fp32 values the kernels see.
+"""
+import numpy as np
+import pytest
+
+from matrix_optimizer_amd import binding as B
+from matrix_optimizer_amd import workloads as WL
+from oracle import muon_oracle as ORC
+from tests import harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+
+
+def check_batch(wl, h: B.HParams, dtype: str, select=None, plan=None, batches=None):
+    """Run every (or the chosen) batch of wl's plan and compare the selected
+    matrices with the oracle.  Returns the list of O errors."""
+    plan = plan or B.Plan([p.shape for p in wl.params])
+    errs = []
+    for binfo in plan.batches:
+        if batches is not None and binfo.index not in batches:
+            continue
+        arrays = H.batch_arrays(wl, binfo)
+        Wp, Mp, O = H.run_gpu_step(plan, binfo, arrays, dtype, h)
+        M, N = binfo.M, binfo.N
+        kw = H.oracle_kwargs(h, M, N)
+        s = H.oracle_scale(h, M, N)
+        sel = range(binfo.count) if select is None else select(binfo)
+        for q in sel:
+            W0 = H.decode(arrays["param"][q])
+            G = H.decode(arrays["grad"][q])
+            M0 = arrays["momentum"][q].astype(np.float64)
+            ref = ORC.muon_step_matrix(W0, G, M0, **kw)
+            H.check_momentum(Mp[q], M0, G, kw["momentum"])
+            e = H.rel_fro(O[q].astype(np.float64), ref["O"])
+            errs.append(e)
+            assert np.all(np.isfinite(O[q]))
+            assert e <= H.o_tolerance(h.precision), f"batch {binfo.index} matrix {q}: O error {e:.3g}"
+            Oq = O[q].astype(np.float64)
+            H.check_update(Wp[q], W0, Oq, kw["lr"], kw["weight_decay"], s)
+            dW_ref = ref["W"] - W0
+            dW = H.decode(Wp[q]) - W0
+            if np.linalg.norm(dW_ref) > 0:
+                slack = 0.0
+                if Wp[q].dtype == np.uint16:
+                    half_ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref["W"]), 1e-38))) - 8)
+                    slack = np.linalg.norm(half_ulp) / np.linalg.norm(dW_ref)
+                assert H.rel_fro(dW, dW_ref) <= H.o_tolerance(h.precision) + slack + 1e-6
+    return errs
+
+
+PRECS = ["bf16", "bf16_x32", "f32"]
+
+
+# --------------------------------------------------------------------------
+# the single 128x256 fp32 matrix (seed 0)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("prec", PRECS)
+def test_single_128x256(prec):
+    wl = WL.WORKLOADS["single_128x256_f32"]
+    errs = check_batch(wl, H.c_hparams(wl.hp, precision=prec), WL.F32)
+    print(f"single_128x256 {prec}: O error {errs}")
+
+
+# --------------------------------------------------------------------------
+# ragged and degenerate shapes, both paths, all precisions and dtypes
+# --------------------------------------------------------------------------
+SHAPE_SETS = {
+    "skinny_ragged": [(24, 333), (24, 333)],
+    "skinny_tall": [(333, 24)],
+    "skinny_mixed_forms": [(7, 1000), (7, 1, 1000), (3, 7, 1000)],
+    "skinny_32": [(32, 2049)],
+    "row_vector": [(1, 50)],
+    "col_vector": [(50, 1)],
+    "tiny": [(2, 3), (3, 2)],
+    "square_33": [(33, 33)],
+    "tiled_wide": [(100, 300)],
+    "tiled_tall": [(300, 100)],
+    "tiled_square": [(130, 130)],
+    "tiled_multi_tile": [(129, 400), (2, 129, 400)],
+    "tiled_experts_tall": [(2, 300, 40)],
+}
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("dtype", [WL.BF16, WL.F32])
+@pytest.mark.parametrize("name", sorted(SHAPE_SETS))
+def test_small_shapes(name, dtype, prec):
+    wl = WL.small_workload(name, SHAPE_SETS[name], dtype=dtype, momentum_recipe="normal",
+                           wid=200 + sorted(SHAPE_SETS).index(name))
+    check_batch(wl, H.c_hparams(wl.hp, precision=prec), dtype)
+
+
+# --------------------------------------------------------------------------
+# hyperparameter variants
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("shapes", [[(24, 500)], [(160, 200)]], ids=["skinny", "tiled"])
+@pytest.mark.parametrize("variant", ["one_step", "schedule", "no_nesterov", "no_scale", "eps_zero", "seven_steps"])
+def test_hparam_variants(shapes, variant):
+    wl = WL.small_workload("v", shapes, momentum_recipe="normal", wid=300)
+    over = {
+        "one_step": dict(ns_steps=1),
+        "schedule": dict(ns_steps=3, coeffs=(3.0, -3.2, 1.2, 3.4445, -4.7750, 2.0315, 2.0, -1.5, 0.5)),
+        "no_nesterov": dict(nesterov=False),
+        "no_scale": dict(scale="none"),
+        "eps_zero": dict(eps=0.0),
+        "seven_steps": dict(ns_steps=7),
+    }[variant]
+    for prec in ("bf16", "f32"):
+        check_batch(wl, H.c_hparams(wl.hp, precision=prec, **over), WL.BF16)
+
+
+# --------------------------------------------------------------------------
+# special cases
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("shapes", [[(24, 700)], [(200, 72)]], ids=["skinny", "tiled"])
+def test_zero_gradient_and_zero_lr(shapes):
+    import torch
+    plan = B.Plan(shapes)
+    b = plan.batches[0]
+    wl = WL.small_workload("z", shapes, dtype=WL.F32, momentum_recipe="zeros", wid=301)
+    arrays = H.batch_arrays(wl, b)
+    arrays["grad"] = np.zeros_like(arrays["grad"])
+    for prec in PRECS:
+        h = H.c_hparams(wl.hp, precision=prec)
+        Wp, Mp, O = H.run_gpu_step(plan, b, arrays, WL.F32, h)
+        assert np.all(O == 0) and np.all(Mp == 0)
+        W0 = arrays["param"].astype(np.float32)
+        lr, wd = np.float32(h.lr), np.float32(h.weight_decay)
+        ref = W0 - lr * (wd * W0 + np.float32(0) * np.float32(0))
+        assert np.max(np.abs(Wp - ref)) <= 1e-7 * np.max(np.abs(W0))
+        # lr = 0 leaves W bitwise unchanged
+        h0 = H.c_hparams(wl.hp, precision=prec, lr=0.0)
+        arrays2 = H.batch_arrays(wl, b)
+        Wp0, _, _ = H.run_gpu_step(plan, b, arrays2, WL.F32, h0)
+        assert np.array_equal(Wp0, arrays2["param"])
+
+
+# --------------------------------------------------------------------------
+# determinism, batch independence, transpose symmetry
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("shapes", [[(24, 3000)] * 3, [(300, 500)] * 3], ids=["skinny", "tiled"])
+@pytest.mark.parametrize("prec", PRECS)
+def test_deterministic_and_batch_independent(shapes, prec):
+    wl = WL.small_workload("d", shapes, momentum_recipe="normal", wid=302)
+    h = H.c_hparams(wl.hp, precision=prec)
+    plan = B.Plan(shapes)
+    b = plan.batches[0]
+    arrays = H.batch_arrays(wl, b)
+    r1 = H.run_gpu_step(plan, b, arrays, WL.BF16, h)
+    r2 = H.run_gpu_step(plan, b, arrays, WL.BF16, h)
+    for x, y in zip(r1, r2):
+        assert np.array_equal(x, y), "run-to-run results differ"
+    # each matrix alone gives bitwise the batched result
+    single = B.Plan([shapes[0]])
+    for q in range(len(shapes)):
+        one = {k: v[q:q + 1].copy() for k, v in arrays.items()}
+        Wq, Mq, Oq = H.run_gpu_step(single, single.batches[0], one, WL.BF16, h)
+        assert np.array_equal(Oq[0], r1[2][q]) and np.array_equal(Wq[0], r1[0][q])
+
+
+@pytest.mark.parametrize("shape", [(24, 900), (96, 260)], ids=["skinny", "tiled"])
+def test_transpose_symmetry(shape):
+    """NS(G^T) = NS(G)^T: the tall matrix runs on the transpose."""
+    wl = WL.small_workload("t", [shape], dtype=WL.F32, momentum_recipe="normal", wid=303)
+    plan = B.Plan([shape])
+    planT = B.Plan([shape[::-1]])
+    arrays = H.batch_arrays(wl, plan.batches[0])
+    arraysT = {k: np.ascontiguousarray(np.swapaxes(v, 1, 2)) for k, v in arrays.items()}
+    for prec in ("bf16", "f32"):
+        h = H.c_hparams(wl.hp, precision=prec)
+        _, _, O = H.run_gpu_step(plan, plan.batches[0], arrays, WL.F32, h)
+        _, _, OT = H.run_gpu_step(planT, planT.batches[0], arraysT, WL.F32, h)
+        assert H.rel_fro(OT[0].T.astype(np.float64), O[0].astype(np.float64)) <= (1e-6 if prec == "f32" else 2e-2)
+
+
+# --------------------------------------------------------------------------
+# stage entry points
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("shapes", [[(24, 1500), (24, 1500)], [(150, 260)], [(260, 150)]],
+                         ids=["skinny", "tiled", "tiled_tall"])
+def test_stage_entry_points(shapes):
+    import torch
+    wl = WL.small_workload("s", shapes, dtype=WL.BF16, momentum_recipe="normal", wid=304)
+    plan = B.Plan(shapes)
+    b = plan.batches[0]
+    arrays = H.batch_arrays(wl, b)
+    for prec in PRECS:
+        h = H.c_hparams(wl.hp, precision=prec)
+        kw = H.oracle_kwargs(h, b.M, b.N)
+        g = H.to_device(arrays["grad"], WL.BF16)
+        m = H.to_device(arrays["momentum"], WL.F32)
+        u = torch.empty((b.count, b.M, b.N), dtype=torch.float32, device="cuda")
+        B.muon_stage_momentum(plan, b.index, g, m, u, h)
+        o = torch.empty_like(u)
+        ws = torch.empty(plan.workspace_bytes(b.index, prec), dtype=torch.uint8, device="cuda")
+        B.muon_stage_ns(plan, b.index, u, o, h, ws)
+        p = H.to_device(arrays["param"], WL.BF16)
+        B.muon_stage_update(plan, b.index, p, o, h)
+        torch.cuda.synchronize()
+        U, Mn, O, Wn = H.to_host(u), H.to_host(m), H.to_host(o), H.to_host(p)
+        for q in range(b.count):
+            G = H.decode(arrays["grad"][q])
+            M0 = arrays["momentum"][q].astype(np.float64)
+            H.check_momentum(Mn[q], M0, G, kw["momentum"])
+            mu = kw["momentum"]
+            Uref = G + mu * Mn[q].astype(np.float64)
+            assert np.all(np.abs(U[q] - Uref) <= 1e-6 * (np.abs(G) + np.abs(mu * Mn[q])) + 1e-30)
+            Oref = ORC.orthogonalize(U[q].astype(np.float64), kw["coeffs"], h.ns_steps, kw["eps"])
+            assert H.rel_fro(O[q].astype(np.float64), Oref) <= H.o_tolerance(prec)
+            H.check_update(Wn[q], H.decode(arrays["param"][q]), O[q].astype(np.float64), kw["lr"],
+                           kw["weight_decay"], H.oracle_scale(h, b.M, b.N))
+
+
+# --------------------------------------------------------------------------
+# the workloads at full size
+# --------------------------------------------------------------------------
+def test_fused_74x24x10240_full():
+    wl = WL.WORKLOADS["fused_74x24x10240"]
+    errs = check_batch(wl, H.c_hparams(wl.hp), WL.BF16)
+    print(f"fused_74x24x10240: max O error {max(errs):.3g} over {len(errs)} matrices")
+
+
+def test_moe_experts_skinny_full():
+    wl = WL.WORKLOADS["moe_experts"]
+    plan = B.Plan([p.shape for p in wl.params])
+    idx = [b.index for b in plan.batches if b.M == 24]
+    errs = check_batch(wl, H.c_hparams(wl.hp), WL.BF16, plan=plan, batches=idx)
+    print(f"moe [32,24,10240]: max O error {max(errs):.3g}")
+
+
+def test_moe_experts_2048x7168_sampled():
+    wl = WL.WORKLOADS["moe_experts"]
+    plan = B.Plan([p.shape for p in wl.params])
+    idx = [b.index for b in plan.batches if b.M == 2048]
+    rng = np.random.default_rng(7)
+    errs = check_batch(wl, H.c_hparams(wl.hp), WL.BF16, plan=plan, batches=idx,
+                       select=lambda b: sorted({0, b.count - 1, int(rng.integers(1, b.count - 1))}))
+    print(f"moe [64,2048,7168] sampled: O errors {errs}")
