@@ -67,7 +67,11 @@ typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
  *  MUON_PREC_BF16_X32 fp32 master copy of X (the a X term in fp32), bf16 MFMA
  *                     operands; for ill-conditioned inputs.
  *  MUON_PREC_F32      every product and every stored intermediate in fp32
- *                     (the check path). */
+ *                     (the check path).
+ * Matrices whose short side is at most 32 keep the Gram matrix, the polynomial
+ * and the B X product in fp32 in every mode (the products are tiny); those
+ * with a short side from 33 to 127 run every product on fp32 operands in every
+ * mode, because bf16 rounding of A and B costs too much accuracy there. */
 typedef enum { MUON_PREC_BF16 = 0, MUON_PREC_BF16_X32 = 1, MUON_PREC_F32 = 2 } muon_precision;
 
 /* MUON_SCALE_RMS: s = 0.2 sqrt(max(M, N)); MUON_SCALE_NONE: s = 1. */

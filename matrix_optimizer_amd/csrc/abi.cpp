@@ -50,6 +50,7 @@ BatchShape shape_of(const muon_plan::Batch& b) {
 namespace muon {
 
 WsLayout workspace_layout(const BatchShape& b, int prec) {
+  prec = effective_prec(b.m, prec);
   WsLayout L;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -152,7 +153,7 @@ void fill_common(StepArgs& a, const muon_plan::Batch& b, const muon_hparams* hp,
   a.nesterov = hp->nesterov;
   a.s = hp->scale == MUON_SCALE_RMS ? float(0.2 * std::sqrt(double(std::max(b.M, b.N)))) : 1.0f;
   a.steps = hp->ns_steps;
-  a.prec = hp->precision;
+  a.prec = effective_prec(std::min(b.M, b.N), hp->precision);
   a.coeffs.clear();
   if (hp->coeffs) {
     for (int k = 0; k < hp->ns_steps; ++k) {

@@ -23,6 +23,15 @@ inline int64_t skinny_chunk(int prec) { return prec == PREC_F32 ? 512 : 1024; }
 
 // Tiled path: rows and columns of X are padded to this multiple.
 constexpr int64_t kTilePad = 128;
+// Tiled path: below this short side the bf16 placements (A and B rounded to
+// bf16 as MFMA operands) lose too much accuracy, so products run on fp32
+// operands whatever precision was asked for; the flops there are small.
+constexpr int64_t kTiledBf16MinRows = 128;
+
+// Precision the kernels actually run for a matrix with short side m.
+inline int effective_prec(int64_t m, int prec) {
+  return (m > kSkinnyMaxRows && m < kTiledBf16MinRows) ? PREC_F32 : prec;
+}
 // Tiled path: workgroups per matrix that reduce ||U||_F^2.
 inline int64_t norm_parts(int64_t elems) {
   int64_t p = (elems + 16383) / 16384;

@@ -91,12 +91,12 @@ def test_plan_errors():
 
 
 def test_workspace_bytes():
-    p = B.Plan([(24, 10240)] * 3 + [(300, 100)] * 2)
+    p = B.Plan([(24, 10240)] * 3 + [(300, 200)] * 2)
     for b in p.batches:
         for prec in ("bf16", "bf16_x32", "f32"):
             w = p.workspace_bytes(b.index, prec)
             assert w > 0 and w % 256 == 0
-    tiled = [b for b in p.batches if b.M == 300][0]
+    tiled = [b for b in p.batches if b.M == 300][0]   # short side 200: bf16 placements apply
     assert p.workspace_bytes(tiled.index, "bf16_x32") > p.workspace_bytes(tiled.index, "bf16")
     with pytest.raises(B.MuonError):
         p.workspace_bytes(99, "bf16")
