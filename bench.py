@@ -50,7 +50,7 @@ def kernel_model(name, count, M, N, prec, pdt, gdt, with_ns_out=False):
     xs = 2 if prec == "bf16" else 4
     gs, ps = dsize(gdt), dsize(pdt)
     if m <= SKINNY_MAX_ROWS:
-        L = 512 if prec == "f32" else 1024
+        L = 512 if prec == "bf16" else 256      # chunk widths of the skinny kernels
         S = math.ceil(n / L)
         T = m * (m + 1) // 2
         part = count * S * T * 4
@@ -58,6 +58,8 @@ def kernel_model(name, count, M, N, prec, pdt, gdt, with_ns_out=False):
             return "hbm", E * (gs + 4 + 4 + xs) + part + count * S * 4, "B"
         if name == "sk_ns_step":
             return "hbm", E * 2 * xs + 2 * part, "B"
+        if name == "sk_bprime":
+            return "hbm", part + count * 4096, "B"
         if name == "sk_ns_step_update":
             return "hbm", E * (xs + 2 * ps + (4 if with_ns_out else 0)) + part, "B"
     else:
@@ -154,6 +156,8 @@ def main():
     ap.add_argument("--precision", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 512 MiB device copy (the reference for HBM byte counters)")
     ap.add_argument("--reuse-shapes", action="store_true",
                     help="batches of identical shape share generated input values (copied per batch)")
     args = ap.parse_args()
@@ -220,7 +224,8 @@ def main():
     bound, unit = "hbm", "B"
     for b in plan.batches:
         bd, q, u = kernel_model(dom, b.count, b.M, b.N, prec, dtype, dtype)
-        per_batch = {"sk_ns_step": hp.ns_steps - 1, "tl_gram": hp.ns_steps, "tl_poly": hp.ns_steps,
+        per_batch = {"sk_ns_step": hp.ns_steps - 1, "sk_bprime": hp.ns_steps, "tl_gram": hp.ns_steps,
+                     "tl_poly": hp.ns_steps,
                      "tl_apply": hp.ns_steps - 1}.get(dom, 1)
         qty += q * per_batch
         nlaunch += per_batch
@@ -255,6 +260,21 @@ def main():
            "data": "synthetic", "config": cfg, "roofline": roof,
            "detail": {"ns_frac_of_bf16_peak": value / BF16_PEAK_TFLOPS, "traced_ms_per_step": traced_ms,
                       "kernels": kernels, "device": torch.cuda.get_device_name(0)}}
+    if args.calibrate_copy:
+        # plain copy kernel of known size: 512 MiB read + 512 MiB written per launch
+        src = torch.empty(1 << 29, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(2):
+            dst.copy_(src)
+        c0.record(stream)
+        for _ in range(5):
+            dst.copy_(src)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        ms_copy = c0.elapsed_time(c1) / 5
+        out["detail"]["copy_calibration"] = {"bytes_read": 1 << 29, "bytes_written": 1 << 29, "avg_ms": ms_copy,
+                                             "GBps": 2 * (1 << 29) / (ms_copy / 1e3) / 1e9}
     if not args.no_cpu_baseline:
         maxm = None if min(wl.params[0].matrix_shape) <= SKINNY_MAX_ROWS else 1
         out["cpu_baseline"] = cpu_baseline(wl, plan, dtype, hp, args.cpu_budget, maxm)

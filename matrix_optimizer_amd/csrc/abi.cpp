@@ -69,6 +69,7 @@ WsLayout workspace_layout(const BatchShape& b, int prec) {
     L.gp0 = take(size_t(b.count) * L.S * L.T * 4);
     L.gp1 = take(size_t(b.count) * L.S * L.T * 4);
     L.sp = take(size_t(b.count) * L.S * 4);
+    L.bfrag = take(size_t(b.count) * 64 * 64);   // B' as MFMA fragments: 64 lanes x 64 bytes
   } else {
     L.skinny = false;
     L.mp = round_up(b.m, kTilePad);

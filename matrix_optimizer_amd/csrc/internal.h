@@ -18,8 +18,15 @@ enum Phase { PH_FULL = 0, PH_MOMENTUM = 1, PH_NS = 2, PH_UPDATE = 3 };
 // Matrices with m = min(M, N) up to this many rows take the skinny path.
 constexpr int64_t kSkinnyMaxRows = 32;
 
-// Skinny path: columns of X handled by one workgroup.
-inline int64_t skinny_chunk(int prec) { return prec == PREC_F32 ? 512 : 1024; }
+// Skinny path: columns of X handled by one workgroup (bf16-stored X, and
+// fp32-stored X).  Both must be multiples of 64.
+#ifndef MUON_SK_CHUNK_BF16
+#define MUON_SK_CHUNK_BF16 512
+#endif
+#ifndef MUON_SK_CHUNK_F32
+#define MUON_SK_CHUNK_F32 256
+#endif
+inline int64_t skinny_chunk(int prec) { return prec == PREC_BF16 ? MUON_SK_CHUNK_BF16 : MUON_SK_CHUNK_F32; }
 
 // Tiled path: rows and columns of X are padded to this multiple.
 constexpr int64_t kTilePad = 128;
@@ -53,7 +60,7 @@ struct WsLayout {
   size_t total = 0;
   // skinny path
   int64_t ldx = 0, S = 0, T = 0;
-  size_t x = 0, gp0 = 0, gp1 = 0, sp = 0;
+  size_t x = 0, gp0 = 0, gp1 = 0, sp = 0, bfrag = 0;
   // tiled path
   int64_t mp = 0, np = 0, nparts = 0;
   size_t xt0 = 0, xt1 = 0, x32 = 0, a32 = 0, a16 = 0, pb = 0, ssp = 0, inv = 0;

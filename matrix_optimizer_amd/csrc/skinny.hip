@@ -2,21 +2,26 @@
 // (e.g. the 74 fused [24, 10240] parameters of the HyperParallel RFC, item 3).
 //
 // The m x m Gram matrix is tiny and the long side n is long, so the work is
-// memory-bound.  Each workgroup owns a chunk of L columns of X (m x n in the
-// Newton-Schulz orientation) and one Newton-Schulz step is one kernel:
+// memory-bound.  X (m x n in the Newton-Schulz orientation, rows padded to 32)
+// is cut into chunks of L columns, one workgroup per chunk.  One
+// Newton-Schulz step (HyperParallel-FSDP Eq. (1)) is two launches:
 //
-//   1. sum the split-K Gram partials of the previous step in a fixed order
-//      -> A = X X^T (fp32, m x m), identical in every workgroup of a matrix;
-//   2. B = b A + c A A in fp32 (the polynomial of HyperParallel-FSDP Eq. (1));
-//   3. X' = a X + B X on the chunk, fp32 arithmetic, written back in place;
-//   4. the chunk's Gram partial X'_c X'_c^T on MFMA (bf16 operands, or fp32
-//      operands on the check path) for the next step; the last step instead
-//      applies decay and update to W.
+//   sk_bprime  one workgroup per matrix: A = X X^T from the chunks' split-K
+//              Gram partials (summed in chunk order), A A on fp32 MFMA, and
+//              B' = a I + b A + c A A, so that X' = a X + b A X + c A^2 X is
+//              the single product B' X.  B' is written as the per-lane MFMA
+//              operand fragments the chunk kernel loads straight into
+//              registers: a bf16 hi + lo pair (the product keeps about 16
+//              bits of B'), or fp32 on the check path.
+//   sk_iter    one workgroup per chunk: stage the chunk in LDS, X' = B' X on
+//              MFMA in place, write X' back with 16-byte stores and form its
+//              Gram partial X'_c X'_c^T on MFMA for the next step; the last
+//              step applies decay and update to W instead.
 //
-// The first kernel fuses momentum, the Nesterov direction, the Frobenius-norm
-// partials and the Gram partial of U, so a whole K-step update is K+1 launches
-// and X never leaves the L2 / Infinity Cache between steps.  All reductions
-// are fixed-order: results are bitwise reproducible run to run.
+// sk_first fuses momentum, the Nesterov direction, the Frobenius-norm partials
+// and the Gram partial of U; the norm enters the first step as a scale on A
+// and B'.  X stays in the L2 / Infinity Cache between launches.  Every
+// reduction has a fixed order, so results are bitwise reproducible.
 #include "common.h"
 #include "internal.h"
 
@@ -27,19 +32,19 @@ constexpr int SK_THREADS = 256;
 constexpr int SK_WAVES = SK_THREADS / WAVE;
 constexpr int SK_MP = 32;  // rows padded to one 32x32 MFMA block
 
-template <bool F32OP> struct SkCfg;
-template <> struct SkCfg<false> {  // bf16 Gram operands
-  static constexpr int L = 1024, CPT = L / SK_THREADS, LDX = L + 8;
-  typedef bf16_t Op;
-};
-template <> struct SkCfg<true> {   // fp32 Gram operands (check path)
-  static constexpr int L = 512, CPT = L / SK_THREADS, LDX = L + 4;
-  typedef float Op;
-};
+// MODE 0: X stored bf16 (bf16 operands).  MODE 1: X stored fp32, bf16 hi+lo
+// operands for B' X, bf16 operands for the Gram.  MODE 2: fp32 everywhere.
+template <int MODE> struct SkCfg;
+template <> struct SkCfg<0> { typedef bf16_t XS; static constexpr int L = MUON_SK_CHUNK_BF16, LDX = L + 8; };
+template <> struct SkCfg<1> { typedef float XS; static constexpr int L = MUON_SK_CHUNK_F32, LDX = L + 4; };
+template <> struct SkCfg<2> { typedef float XS; static constexpr int L = MUON_SK_CHUNK_F32, LDX = L + 4; };
 
-constexpr int kLdsXBytes = SK_MP * (1024 + 8) * 2;  // == SK_MP * (512 + 4) * 4
-static_assert(kLdsXBytes == SK_MP * (512 + 4) * 4, "LDS staging sizes differ");
-static_assert(SK_WAVES * SK_MP * (SK_MP + 1) * 4 <= kLdsXBytes, "reduction buffer must fit");
+template <int MODE> struct SkLds {
+  static constexpr int TILE = SK_MP * SkCfg<MODE>::LDX * (int)sizeof(typename SkCfg<MODE>::XS);
+  static constexpr int RED = SK_WAVES * SK_MP * (SK_MP + 1) * 4;   // Gram partial reduction buffer
+  static constexpr int BYTES = TILE > RED ? TILE : RED;
+};
+static_assert(MUON_SK_CHUNK_BF16 % 64 == 0 && MUON_SK_CHUNK_F32 % 64 == 0, "chunk must be a multiple of 64");
 
 __device__ __forceinline__ void tri_rc(int idx, int& r, int& s) {
   int rr = (int)((sqrtf(8.0f * idx + 1.0f) - 1.0f) * 0.5f);
@@ -49,30 +54,58 @@ __device__ __forceinline__ void tri_rc(int idx, int& r, int& s) {
   s = idx - rr * (rr + 1) / 2;
 }
 
+// Element (row r, column j) of a stored [M,N] matrix in the Newton-Schulz
+// orientation (m x n): row-major if not transposed, else the transpose.
+__device__ __forceinline__ int64_t stored_index(bool transposed, int r, int64_t j, int m, int64_t n) {
+  return transposed ? j * m + r : (int64_t)r * n + j;
+}
+
+// 16-byte vectors of the staged chunk.
+template <int MODE> struct Vec {
+  typedef typename SkCfg<MODE>::XS XS;
+  static constexpr int EPV = 16 / (int)sizeof(XS);
+  static constexpr int PER_ROW = SkCfg<MODE>::L / EPV;
+};
+
 // Gram partial of the staged chunk: out[idx(r,s)] = sum_k X[r][k] X[s][k] over
 // the L staged columns, lower triangle packed (idx = r(r+1)/2 + s).  Wave w
 // takes columns [w L/4, (w+1) L/4); the four wave sums are added in order.
-template <bool F32OP>
+template <int MODE>
 __device__ void gram_partial(unsigned char* lds_raw, float* __restrict__ out, int T) {
-  typedef SkCfg<F32OP> C;
+  typedef SkCfg<MODE> C;
   const int lane = threadIdx.x & (WAVE - 1);
   const int w = threadIdx.x / WAVE;
+  const int row = lane & 31;
   f32x16 acc = {};
-  if constexpr (!F32OP) {
+  constexpr int KW = C::L / SK_WAVES;
+  if constexpr (MODE == 0) {
     const bf16_t* lx = reinterpret_cast<const bf16_t*>(lds_raw);
-    const int row = lane & 31;
     const int koff = (lane >> 5) * 8;
 #pragma unroll 4
-    for (int k0 = w * (C::L / SK_WAVES); k0 < (w + 1) * (C::L / SK_WAVES); k0 += 16) {
+    for (int k0 = w * KW; k0 < (w + 1) * KW; k0 += 16) {
       bf16x8 v = *reinterpret_cast<const bf16x8*>(lx + row * C::LDX + k0 + koff);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, v, acc, 0, 0, 0);
+    }
+  } else if constexpr (MODE == 1) {
+    const float* lx = reinterpret_cast<const float*>(lds_raw);
+    const int koff = (lane >> 5) * 8;
+#pragma unroll 2
+    for (int k0 = w * KW; k0 < (w + 1) * KW; k0 += 16) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(lx + row * C::LDX + k0 + koff);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(lx + row * C::LDX + k0 + koff + 4);
+      bf16x8 v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[q] = __builtin_bit_cast(__bf16, f2bf(a[q]));
+        v[q + 4] = __builtin_bit_cast(__bf16, f2bf(b[q]));
+      }
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, v, acc, 0, 0, 0);
     }
   } else {
     const float* lx = reinterpret_cast<const float*>(lds_raw);
-    const int row = lane & 31;
     const int koff = lane >> 5;
 #pragma unroll 8
-    for (int k0 = w * (C::L / SK_WAVES); k0 < (w + 1) * (C::L / SK_WAVES); k0 += 2) {
+    for (int k0 = w * KW; k0 < (w + 1) * KW; k0 += 2) {
       float v = lx[row * C::LDX + k0 + koff];
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(v, v, acc, 0, 0, 0);
     }
@@ -93,10 +126,230 @@ __device__ void gram_partial(unsigned char* lds_raw, float* __restrict__ out, in
   }
 }
 
-// Element (row r, column j) of a stored [M,N] matrix seen in the Newton-Schulz
-// orientation (m x n): row-major if not transposed, else the transpose.
-__device__ __forceinline__ int64_t stored_index(bool transposed, int r, int64_t j, int m, int64_t n) {
-  return transposed ? j * m + r : (int64_t)r * n + j;
+// Sum of a per-thread value over the workgroup, fixed order.
+__device__ float block_sum(float v, float* wsum) {
+  v = wave_sum(v);
+  if ((threadIdx.x & (WAVE - 1)) == 0) wsum[threadIdx.x / WAVE] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int q = 0; q < SK_WAVES; ++q) s += wsum[q];
+  return s;
+}
+
+// Staged chunk <-> workspace, 16-byte vectors; rows >= m of the LDS tile zeroed.
+template <int MODE>
+__device__ void chunk_load(const typename SkCfg<MODE>::XS* __restrict__ src, unsigned char* lds_raw, int m,
+                           int64_t ldx) {
+  typedef SkCfg<MODE> C;
+  typedef Vec<MODE> V;
+  typename C::XS* lx = reinterpret_cast<typename C::XS*>(lds_raw);
+  constexpr int N = SK_MP * V::PER_ROW / SK_THREADS;
+  uint4 d[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int v = threadIdx.x + SK_THREADS * i;
+    const int r = v / V::PER_ROW, cv = (v % V::PER_ROW) * V::EPV;
+    d[i] = make_uint4(0, 0, 0, 0);
+    if (r < m) d[i] = *reinterpret_cast<const uint4*>(src + r * ldx + cv);
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int v = threadIdx.x + SK_THREADS * i;
+    const int r = v / V::PER_ROW, cv = (v % V::PER_ROW) * V::EPV;
+    *reinterpret_cast<uint4*>(lx + r * C::LDX + cv) = d[i];
+  }
+}
+
+template <int MODE>
+__device__ void chunk_store(typename SkCfg<MODE>::XS* __restrict__ dst, const unsigned char* lds_raw, int m,
+                            int64_t ldx) {
+  typedef SkCfg<MODE> C;
+  typedef Vec<MODE> V;
+  const typename C::XS* lx = reinterpret_cast<const typename C::XS*>(lds_raw);
+  for (int v = threadIdx.x; v < m * V::PER_ROW; v += SK_THREADS) {
+    const int r = v / V::PER_ROW, cv = (v % V::PER_ROW) * V::EPV;
+    *reinterpret_cast<uint4*>(dst + r * ldx + cv) = *reinterpret_cast<const uint4*>(lx + r * C::LDX + cv);
+  }
+}
+
+// B' fragments of one lane, as written by sk_bprime and read by sk_iter:
+// 64 bytes per lane, 4 KB per matrix.
+//   bf16 modes: hi[kb][t], lo[kb][t] = B'[lane%32][kb*16 + (lane/32)*8 + t]  (kb < 2, t < 8)
+//   fp32 mode:  f[kb] = B'[lane%32][kb*2 + lane/32]                          (kb < 16)
+struct BFrag {
+  uint4 q[4];
+};
+
+// X' = B' X for the staged chunk, in place in LDS.  Wave w handles 32-column
+// blocks w, w+4, ...
+template <int MODE>
+__device__ void apply_bx(unsigned char* lds_raw, const BFrag& fr) {
+  typedef SkCfg<MODE> C;
+  typedef typename C::XS XS;
+  XS* lx = reinterpret_cast<XS*>(lds_raw);
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int w = threadIdx.x / WAVE;
+  const int row = lane & 31, hi8 = (lane >> 5) * 8;
+  constexpr int NB = C::L / 32;
+  if constexpr (MODE == 2) {
+    float bf[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf[4 * i] = __uint_as_float(fr.q[i].x);
+      bf[4 * i + 1] = __uint_as_float(fr.q[i].y);
+      bf[4 * i + 2] = __uint_as_float(fr.q[i].z);
+      bf[4 * i + 3] = __uint_as_float(fr.q[i].w);
+    }
+    for (int jb = w; jb < NB; jb += SK_WAVES) {
+      const int col = jb * 32 + row;
+      f32x16 acc = {};
+#pragma unroll
+      for (int kb = 0; kb < 16; ++kb) {
+        const float xv = lx[(kb * 2 + (lane >> 5)) * C::LDX + col];
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(bf[kb], xv, acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) lx[mfma32_row(lane, r) * C::LDX + col] = acc[r];
+    }
+  } else {
+    const bf16x8 bh[2] = {__builtin_bit_cast(bf16x8, fr.q[0]), __builtin_bit_cast(bf16x8, fr.q[1])};
+    const bf16x8 bl[2] = {__builtin_bit_cast(bf16x8, fr.q[2]), __builtin_bit_cast(bf16x8, fr.q[3])};
+    for (int jb = w; jb < NB; jb += SK_WAVES) {
+      const int col = jb * 32 + row;
+      f32x16 acc = {};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if constexpr (MODE == 0) {
+          bf16x8 xv;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) xv[t] = __builtin_bit_cast(__bf16, lx[(kb * 16 + hi8 + t) * C::LDX + col]);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[kb], xv, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bl[kb], xv, acc, 0, 0, 0);
+        } else {
+          bf16x8 xh, xl;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const float v = lx[(kb * 16 + hi8 + t) * C::LDX + col];
+            const bf16_t h = f2bf(v);
+            xh[t] = __builtin_bit_cast(__bf16, h);
+            xl[t] = __builtin_bit_cast(__bf16, f2bf(v - bf2f(h)));
+          }
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[kb], xh, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[kb], xl, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bl[kb], xh, acc, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if constexpr (MODE == 0) lx[mfma32_row(lane, r) * C::LDX + col] = f2bf(acc[r]);
+        else lx[mfma32_row(lane, r) * C::LDX + col] = acc[r];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// B' of one Newton-Schulz step, one workgroup per matrix.
+//   first: A and B' are scaled by inv^2 and inv, inv = 1/(||U||_F + eps)
+//          from the norm partials (the first step works on U = X0 / inv).
+// ---------------------------------------------------------------------------
+template <int MODE>
+__global__ void __launch_bounds__(SK_THREADS)
+sk_bprime(const float* __restrict__ gp, const float* __restrict__ sp, int first, float eps, int m, int S, int T,
+          float ca, float cb, float cc, BFrag* __restrict__ bfrag) {
+  __shared__ float As[SK_MP][SK_MP + 1];
+  __shared__ float Bp[SK_MP][SK_MP + 1];
+  __shared__ float inv_s;
+  const int64_t b = blockIdx.x;
+  const int t = threadIdx.x;
+  const int lane = t & (WAVE - 1);
+  for (int e = t; e < SK_MP * (SK_MP + 1); e += SK_THREADS) (&As[0][0])[e] = 0.f;
+  if (t < WAVE) {
+    // inv from the norm partials: lane-strided sums, then a fixed butterfly
+    float inv = 1.f;
+    if (first) {
+      float v = 0.f;
+      for (int q = lane; q < S; q += WAVE) v += sp[b * S + q];
+      v = wave_sum(v);
+      const float den = sqrtf(v) + eps;
+      inv = den > 0.f ? 1.f / den : 0.f;
+    }
+    if (lane == 0) inv_s = inv;
+  }
+  __syncthreads();
+  const float inv = inv_s;
+  const float scaleA = inv * inv;
+  const float* g = gp + b * S * (int64_t)T;
+  for (int idx = t; idx < T; idx += SK_THREADS) {
+    // all chunk partials of one entry: 16 loads in flight, added in chunk order
+    float v = 0.f;
+    for (int q0 = 0; q0 < S; q0 += 16) {
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = (q0 + i < S) ? g[(int64_t)(q0 + i) * T + idx] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v += x[i];
+    }
+    int r, s;
+    tri_rc(idx, r, s);
+    v *= scaleA;
+    As[r][s] = v;
+    As[s][r] = v;
+  }
+  __syncthreads();
+  if (t < WAVE) {
+    // A A on fp32 MFMA: A operand A[lane%32][2kb + lane/32], B operand A[2kb + lane/32][lane%32]
+    f32x16 acc = {};
+#pragma unroll
+    for (int kb = 0; kb < 16; ++kb)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[lane & 31][2 * kb + (lane >> 5)],
+                                                 As[2 * kb + (lane >> 5)][lane & 31], acc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = mfma32_row(lane, r), j = mfma32_col(lane);
+      const float v = (i < m && j < m) ? cb * As[i][j] + cc * acc[r] + (i == j ? ca : 0.f) : 0.f;
+      Bp[i][j] = v * inv;
+    }
+  }
+  __syncthreads();
+  if (t < WAVE) {
+    const int row = lane & 31;
+    BFrag f;
+    if constexpr (MODE == 2) {
+      float v[16];
+#pragma unroll
+      for (int kb = 0; kb < 16; ++kb) v[kb] = Bp[row][2 * kb + (lane >> 5)];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        f.q[i] = make_uint4(__float_as_uint(v[4 * i]), __float_as_uint(v[4 * i + 1]), __float_as_uint(v[4 * i + 2]),
+                            __float_as_uint(v[4 * i + 3]));
+    } else {
+      uint32_t hw[8], lw[8];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          uint32_t h2 = 0, l2 = 0;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const float v = Bp[row][kb * 16 + (lane >> 5) * 8 + 2 * p + e];
+            const bf16_t h = f2bf(v);
+            const bf16_t l = f2bf(v - bf2f(h));
+            h2 |= (uint32_t)h << (16 * e);
+            l2 |= (uint32_t)l << (16 * e);
+          }
+          hw[kb * 4 + p] = h2;
+          lw[kb * 4 + p] = l2;
+        }
+      }
+      f.q[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      f.q[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+      f.q[2] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      f.q[3] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+    }
+    bfrag[b * WAVE + lane] = f;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -104,32 +357,93 @@ __device__ __forceinline__ int64_t stored_index(bool transposed, int r, int64_t 
 // U into the workspace, and the Gram partial of U.
 //   mode 0: M' = mu M + G (in place), U = G + mu M' (or M' without Nesterov)
 //   mode 1: U read from u_in
+// vec: stored rows are X rows and n % 8 == 0 (16-byte vectors along rows).
 // ---------------------------------------------------------------------------
-template <bool F32OP, typename XS, typename GT>
+template <int MODE, typename GT>
 __global__ void __launch_bounds__(SK_THREADS)
 sk_first(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const float* __restrict__ u_in,
-         XS* __restrict__ xws, float* __restrict__ gp_out, float* __restrict__ sp,
-         int m, int64_t n, int64_t ldx, int S, int T, int transposed, float mu, int nesterov) {
-  typedef SkCfg<F32OP> C;
-  typedef typename C::Op Op;
-  __shared__ __attribute__((aligned(16))) unsigned char lds_raw[kLdsXBytes];
+         typename SkCfg<MODE>::XS* __restrict__ xws, float* __restrict__ gp_out, float* __restrict__ sp,
+         int m, int64_t n, int64_t ldx, int S, int T, int transposed, int vec, float mu, int nesterov) {
+  typedef SkCfg<MODE> C;
+  typedef typename C::XS XS;
+  __shared__ __attribute__((aligned(16))) unsigned char lds_raw[SkLds<MODE>::BYTES];
   __shared__ float wsum[SK_WAVES];
-  Op* lx = reinterpret_cast<Op*>(lds_raw);
+  XS* lx = reinterpret_cast<XS*>(lds_raw);
 
   const int64_t blk = blockIdx.x;
   const int64_t b = blk / S;
   const int c = (int)(blk % S);
-  const int t = threadIdx.x;
+  const int64_t j0 = (int64_t)c * C::L;
   const int64_t mat = b * (int64_t)m * n;
   float ss = 0.f;
 
-  for (int r = 0; r < SK_MP; ++r) {
+  // zero the padding rows of the tile
+  for (int e = threadIdx.x; e < (SK_MP - m) * C::LDX; e += SK_THREADS) lx[m * C::LDX + e] = (XS)0;
+
+  if (vec) {
+    // 8 consecutive columns of one row per item
+    constexpr int PR = C::L / 8;
+    for (int v = threadIdx.x; v < m * PR; v += SK_THREADS) {
+      const int r = v / PR, jl = (v % PR) * 8;
+      const int64_t j = j0 + jl;
+      float u[8];
+      if (j < n) {   // n % 8 == 0: the 8 columns are all in range or all out
+        const int64_t si = mat + (int64_t)r * n + j;
+        if (mode == 0) {
+          float g[8];
+          if constexpr (sizeof(GT) == 2) {
+            const uint4 gv = *reinterpret_cast<const uint4*>(grad + si);
+            const uint32_t w4[4] = {gv.x, gv.y, gv.z, gv.w};
 #pragma unroll
-    for (int q = 0; q < C::CPT; ++q) {
-      const int jl = t * C::CPT + q;
-      const int64_t j = (int64_t)c * C::L + jl;
+            for (int q = 0; q < 4; ++q) {
+              g[2 * q] = __uint_as_float(w4[q] << 16);
+              g[2 * q + 1] = __uint_as_float(w4[q] & 0xffff0000u);
+            }
+          } else {
+            const f32x4 g0 = *reinterpret_cast<const f32x4*>(grad + si);
+            const f32x4 g1 = *reinterpret_cast<const f32x4*>(grad + si + 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) { g[q] = g0[q]; g[q + 4] = g1[q]; }
+          }
+          f32x4 m0 = *reinterpret_cast<const f32x4*>(mom + si);
+          f32x4 m1 = *reinterpret_cast<const f32x4*>(mom + si + 4);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float a0 = mu * m0[q] + g[q];
+            const float a1 = mu * m1[q] + g[q + 4];
+            m0[q] = a0;
+            m1[q] = a1;
+            u[q] = nesterov ? g[q] + mu * a0 : a0;
+            u[q + 4] = nesterov ? g[q + 4] + mu * a1 : a1;
+          }
+          *reinterpret_cast<f32x4*>(mom + si) = m0;
+          *reinterpret_cast<f32x4*>(mom + si + 4) = m1;
+        } else {
+          const f32x4 u0 = *reinterpret_cast<const f32x4*>(u_in + si);
+          const f32x4 u1 = *reinterpret_cast<const f32x4*>(u_in + si + 4);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) { u[q] = u0[q]; u[q + 4] = u1[q]; }
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) u[q] = 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        ss += u[q] * u[q];
+        if constexpr (MODE == 0) lx[r * C::LDX + jl + q] = f2bf(u[q]);
+        else lx[r * C::LDX + jl + q] = u[q];
+      }
+    }
+  } else {
+    // element by element, walking the stored layout of the chunk
+    for (int e = threadIdx.x; e < m * C::L; e += SK_THREADS) {
+      int r, jl;
+      if (transposed) { jl = e / m; r = e % m; }
+      else { r = e / C::L; jl = e % C::L; }
+      const int64_t j = j0 + jl;
       float u = 0.f;
-      if (r < m && j < n) {
+      if (j < n) {
         const int64_t si = mat + stored_index(transposed, r, j, m, n);
         if (mode == 0) {
           const float g = ld_as_f32(grad, si);
@@ -140,203 +454,189 @@ sk_first(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const f
           u = u_in[si];
         }
       }
-      float us = 0.f;
-      if (r < m) {
-        us = round_to<XS>(u);
-        st_from_f32(xws, (b * m + r) * ldx + j, u);
-      }
       ss += u * u;
-      if constexpr (F32OP) lx[r * C::LDX + jl] = us;
-      else lx[r * C::LDX + jl] = f2bf(us);
+      if constexpr (MODE == 0) lx[r * C::LDX + jl] = f2bf(u);
+      else lx[r * C::LDX + jl] = u;
     }
   }
-  ss = wave_sum(ss);
-  if ((t & (WAVE - 1)) == 0) wsum[t / WAVE] = ss;
-  __syncthreads();
-  if (t == 0) {
-    float v = 0.f;
-    for (int q = 0; q < SK_WAVES; ++q) v += wsum[q];
-    sp[blk] = v;
-  }
-  gram_partial<F32OP>(lds_raw, gp_out + blk * T, T);
+  const float tot = block_sum(ss, wsum);   // includes a barrier: the tile is complete
+  if (threadIdx.x == 0) sp[blk] = tot;
+  chunk_store<MODE>(xws + b * m * ldx + j0, lds_raw, m, ldx);
+  gram_partial<MODE>(lds_raw, gp_out + blk * T, T);
 }
 
 // ---------------------------------------------------------------------------
-// One Newton-Schulz step on a chunk.  LAST: apply the update (or write O).
+// One Newton-Schulz step on a chunk: X' = B' X.  LAST: apply the update (or
+// write O) instead of storing X' and its Gram partial.
 // ---------------------------------------------------------------------------
-template <int MAXM, bool F32OP, typename XS, typename PT, bool LAST>
+template <int MODE, typename PT, bool LAST>
 __global__ void __launch_bounds__(SK_THREADS)
-sk_iter(XS* __restrict__ xws, const float* __restrict__ gp_in, float* __restrict__ gp_out,
-        const float* __restrict__ sp, int first, float eps,
-        int m, int64_t n, int64_t ldx, int S, int T, int transposed,
-        float ca, float cb, float cc,
+sk_iter(typename SkCfg<MODE>::XS* __restrict__ xws, const BFrag* __restrict__ bfrag, float* __restrict__ gp_out,
+        int m, int64_t n, int64_t ldx, int S, int T, int transposed, int vec,
         PT* __restrict__ param, float* __restrict__ ns_out, float lr, float wd, float s_scale) {
-  typedef SkCfg<F32OP> C;
-  typedef typename C::Op Op;
-  __shared__ __attribute__((aligned(16))) unsigned char lds_raw[kLdsXBytes];
-  __shared__ float As[SK_MP][SK_MP + 1];
-  __shared__ float Bs[SK_MP][SK_MP + 1];
-  __shared__ float inv_s;
-  Op* lx = reinterpret_cast<Op*>(lds_raw);
+  typedef SkCfg<MODE> C;
+  typedef typename C::XS XS;
+  __shared__ __attribute__((aligned(16))) unsigned char lds_raw[SkLds<MODE>::BYTES];
+  XS* lx = reinterpret_cast<XS*>(lds_raw);
 
   const int64_t blk = blockIdx.x;
   const int64_t b = blk / S;
   const int c = (int)(blk % S);
+  const int64_t j0 = (int64_t)c * C::L;
   const int t = threadIdx.x;
+  const int64_t mat = b * (int64_t)m * n;
+  constexpr int PR8 = C::L / 8;                      // 8-column items per row
+  constexpr int NI = SK_MP * PR8 / SK_THREADS;       // items per thread (upper bound)
 
-  // 1. A from the partials (fixed order over chunks)
-  for (int e = t; e < SK_MP * (SK_MP + 1); e += SK_THREADS) (&As[0][0])[e] = 0.f;
-  if (t == 0) {
-    float inv = 1.f;
-    if (first) {
-      float v = 0.f;
-      for (int q = 0; q < S; ++q) v += sp[b * S + q];
-      const float den = sqrtf(v) + eps;
-      inv = den > 0.f ? 1.f / den : 0.f;
-    }
-    inv_s = inv;
-  }
-  __syncthreads();
-  const float inv = inv_s;
-  const float scaleA = inv * inv;
-  for (int idx = t; idx < T; idx += SK_THREADS) {
-    float v = 0.f;
-    const float* p = gp_in + b * S * (int64_t)T + idx;
-    for (int q = 0; q < S; ++q) v += p[(int64_t)q * T];
-    int r, s;
-    tri_rc(idx, r, s);
-    v *= scaleA;
-    As[r][s] = v;
-    As[s][r] = v;
-  }
-  __syncthreads();
-  // 2. B = b A + c A A  (fp32)
-  for (int e = t; e < MAXM * MAXM; e += SK_THREADS) {
-    const int r = e / MAXM, s = e % MAXM;
-    float acc = 0.f;
-#pragma unroll 8
-    for (int k = 0; k < MAXM; ++k) acc += As[r][k] * As[k][s];
-    Bs[r][s] = cb * As[r][s] + cc * acc;
-  }
-  __syncthreads();
+  const BFrag fr = bfrag[b * WAVE + (t & (WAVE - 1))];
 
-  // 3. X' = a X + B X on this thread's CPT columns
-  float x[C::CPT][MAXM];
+  // last step, bf16 W: start reading W now, it is needed only at the end
+  uint4 wpre[LAST && sizeof(PT) == 2 ? NI : 1];
+  if constexpr (LAST && sizeof(PT) == 2) {
+    if (vec && param) {
 #pragma unroll
-  for (int r = 0; r < MAXM; ++r) {
-#pragma unroll
-    for (int q = 0; q < C::CPT; ++q) {
-      const int64_t j = (int64_t)c * C::L + t * C::CPT + q;
-      x[q][r] = (r < m) ? ld_as_f32(xws, (b * m + r) * ldx + j) * inv : 0.f;
-    }
-  }
-  if constexpr (!LAST) {
-    for (int r = m; r < SK_MP; ++r) {
-#pragma unroll
-      for (int q = 0; q < C::CPT; ++q) lx[r * C::LDX + t * C::CPT + q] = (Op)0;
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < MAXM; ++r) {
-    float y[C::CPT];
-#pragma unroll
-    for (int q = 0; q < C::CPT; ++q) y[q] = ca * x[q][r];
-#pragma unroll
-    for (int s = 0; s < MAXM; ++s) {
-      const float bv = Bs[r][s];
-#pragma unroll
-      for (int q = 0; q < C::CPT; ++q) y[q] += bv * x[q][s];
-    }
-    if (r < m) {
-#pragma unroll
-      for (int q = 0; q < C::CPT; ++q) {
-        const int jl = t * C::CPT + q;
-        const int64_t j = (int64_t)c * C::L + jl;
-        if constexpr (!LAST) {
-          st_from_f32(xws, (b * m + r) * ldx + j, y[q]);
-          const float ys = round_to<XS>(y[q]);
-          if constexpr (F32OP) lx[r * C::LDX + jl] = ys;
-          else lx[r * C::LDX + jl] = f2bf(ys);
-        } else if (j < n) {
-          const int64_t si = b * (int64_t)m * n + stored_index(transposed, r, j, m, n);
-          if (ns_out) ns_out[si] = y[q];
-          if (param) {
-            const float w = ld_as_f32(param, si);
-            st_from_f32(param, si, apply_update(w, y[q], lr, wd, s_scale));
-          }
-        }
+      for (int i = 0; i < NI; ++i) {
+        const int v = t + SK_THREADS * i;
+        const int r = v / PR8, jl = (v % PR8) * 8;
+        if (r < m && j0 + jl < n) wpre[i] = *reinterpret_cast<const uint4*>(param + mat + (int64_t)r * n + j0 + jl);
       }
     }
   }
+
+  chunk_load<MODE>(xws + b * m * ldx + j0, lds_raw, m, ldx);
+  __syncthreads();
+  apply_bx<MODE>(lds_raw, fr);
+  __syncthreads();
+
   if constexpr (!LAST) {
-    __syncthreads();
-    gram_partial<F32OP>(lds_raw, gp_out + blk * T, T);
+    chunk_store<MODE>(xws + b * m * ldx + j0, lds_raw, m, ldx);
+    gram_partial<MODE>(lds_raw, gp_out + blk * T, T);
+  } else {
+    if (vec) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int v = t + SK_THREADS * i;
+        const int r = v / PR8, jl = (v % PR8) * 8;
+        const int64_t j = j0 + jl;
+        if (r >= m || j >= n) continue;
+        const int64_t si = mat + (int64_t)r * n + j;
+        float o[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if constexpr (MODE == 0) o[q] = bf2f(lx[r * C::LDX + jl + q]);
+          else o[q] = lx[r * C::LDX + jl + q];
+        }
+        if (ns_out) {
+          *reinterpret_cast<f32x4*>(ns_out + si) = f32x4{o[0], o[1], o[2], o[3]};
+          *reinterpret_cast<f32x4*>(ns_out + si + 4) = f32x4{o[4], o[5], o[6], o[7]};
+        }
+        if (param) {
+          if constexpr (sizeof(PT) == 2) {
+            const uint4 wv = wpre[i];
+            uint32_t w4[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float w0 = __uint_as_float(w4[q] << 16);
+              const float w1 = __uint_as_float(w4[q] & 0xffff0000u);
+              const uint32_t n0 = f2bf(apply_update(w0, o[2 * q], lr, wd, s_scale));
+              const uint32_t n1 = f2bf(apply_update(w1, o[2 * q + 1], lr, wd, s_scale));
+              w4[q] = n0 | (n1 << 16);
+            }
+            *reinterpret_cast<uint4*>(param + si) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+          } else {
+            f32x4 w0 = *reinterpret_cast<const f32x4*>(param + si);
+            f32x4 w1 = *reinterpret_cast<const f32x4*>(param + si + 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              w0[q] = apply_update(w0[q], o[q], lr, wd, s_scale);
+              w1[q] = apply_update(w1[q], o[q + 4], lr, wd, s_scale);
+            }
+            *reinterpret_cast<f32x4*>(param + si) = w0;
+            *reinterpret_cast<f32x4*>(param + si + 4) = w1;
+          }
+        }
+      }
+    } else {
+      for (int e = t; e < m * C::L; e += SK_THREADS) {
+        int r, jl;
+        if (transposed) { jl = e / m; r = e % m; }
+        else { r = e / C::L; jl = e % C::L; }
+        const int64_t j = j0 + jl;
+        if (j >= n) continue;
+        float o;
+        if constexpr (MODE == 0) o = bf2f(lx[r * C::LDX + jl]);
+        else o = lx[r * C::LDX + jl];
+        const int64_t si = mat + stored_index(transposed, r, j, m, n);
+        if (ns_out) ns_out[si] = o;
+        if (param) st_from_f32(param, si, apply_update(ld_as_f32(param, si), o, lr, wd, s_scale));
+      }
+    }
   }
 }
 
-template <bool F32OP, typename XS, typename GT>
-hipError_t launch_first(const StepArgs& a, const WsLayout& L, int mode) {
+template <int MODE, typename GT>
+hipError_t launch_first(const StepArgs& a, const WsLayout& L, int mode, int vec) {
+  typedef typename SkCfg<MODE>::XS XS;
   const BatchShape& sh = a.shape;
   dim3 grid((unsigned)(sh.count * L.S)), block(SK_THREADS);
-  MUON_LAUNCH(mode == 0 ? "sk_momentum_norm_gram" : "sk_norm_gram", (sk_first<F32OP, XS, GT>), grid, block,
-              a.stream, mode,
-                     (const GT*)a.grad, a.mom, a.u_in, (XS*)(a.ws + L.x), (float*)(a.ws + L.gp0),
-                     (float*)(a.ws + L.sp), (int)sh.m, sh.n, L.ldx, (int)L.S, (int)L.T,
-                     (int)sh.transposed, a.mu, a.nesterov);
+  MUON_LAUNCH(mode == 0 ? "sk_momentum_norm_gram" : "sk_norm_gram", (sk_first<MODE, GT>), grid, block,
+              a.stream, mode, (const GT*)a.grad, a.mom, a.u_in, (XS*)(a.ws + L.x), (float*)(a.ws + L.gp0),
+              (float*)(a.ws + L.sp), (int)sh.m, sh.n, L.ldx, (int)L.S, (int)L.T, (int)sh.transposed, vec, a.mu,
+              a.nesterov);
   return hipGetLastError();
 }
 
-template <int MAXM, bool F32OP, typename XS, typename PT>
-hipError_t launch_iters(const StepArgs& a, const WsLayout& L) {
+template <int MODE, typename PT>
+hipError_t launch_iters(const StepArgs& a, const WsLayout& L, int vec) {
+  typedef typename SkCfg<MODE>::XS XS;
   const BatchShape& sh = a.shape;
   dim3 grid((unsigned)(sh.count * L.S)), block(SK_THREADS);
   float* gp[2] = {(float*)(a.ws + L.gp0), (float*)(a.ws + L.gp1)};
+  BFrag* bfrag = (BFrag*)(a.ws + L.bfrag);
   PT* param = a.phase == PH_FULL ? (PT*)a.param : nullptr;
   for (int k = 0; k < a.steps; ++k) {
     const float ca = a.coeffs[3 * k], cb = a.coeffs[3 * k + 1], cc = a.coeffs[3 * k + 2];
-    const bool last = (k == a.steps - 1);
-    if (!last)
-      MUON_LAUNCH("sk_ns_step", (sk_iter<MAXM, F32OP, XS, PT, false>), grid, block, a.stream,
-                         (XS*)(a.ws + L.x), gp[k & 1], gp[(k + 1) & 1], (const float*)(a.ws + L.sp),
-                         (int)(k == 0), a.eps, (int)sh.m, sh.n, L.ldx, (int)L.S, (int)L.T,
-                         (int)sh.transposed, ca, cb, cc, param, a.ns_out, a.lr, a.wd, a.s);
-    else
-      MUON_LAUNCH("sk_ns_step_update", (sk_iter<MAXM, F32OP, XS, PT, true>), grid, block, a.stream,
-                         (XS*)(a.ws + L.x), gp[k & 1], gp[(k + 1) & 1], (const float*)(a.ws + L.sp),
-                         (int)(k == 0), a.eps, (int)sh.m, sh.n, L.ldx, (int)L.S, (int)L.T,
-                         (int)sh.transposed, ca, cb, cc, param, a.ns_out, a.lr, a.wd, a.s);
+    // step k reads the Gram partials in gp[k & 1] and writes its own into gp[(k + 1) & 1]
+    MUON_LAUNCH("sk_bprime", (sk_bprime<MODE>), dim3((unsigned)sh.count), block, a.stream, gp[k & 1],
+                (const float*)(a.ws + L.sp), (int)(k == 0), a.eps, (int)sh.m, (int)L.S, (int)L.T, ca, cb, cc,
+                bfrag);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (k < a.steps - 1)
+      MUON_LAUNCH("sk_ns_step", (sk_iter<MODE, PT, false>), grid, block, a.stream, (XS*)(a.ws + L.x),
+                  (const BFrag*)bfrag, gp[(k + 1) & 1], (int)sh.m, sh.n, L.ldx, (int)L.S, (int)L.T,
+                  (int)sh.transposed, vec, param, a.ns_out, a.lr, a.wd, a.s);
+    else
+      MUON_LAUNCH("sk_ns_step_update", (sk_iter<MODE, PT, true>), grid, block, a.stream, (XS*)(a.ws + L.x),
+                  (const BFrag*)bfrag, gp[(k + 1) & 1], (int)sh.m, sh.n, L.ldx, (int)L.S, (int)L.T,
+                  (int)sh.transposed, vec, param, a.ns_out, a.lr, a.wd, a.s);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
-template <bool F32OP, typename XS>
+template <int MODE>
 hipError_t run_mode(const StepArgs& a, const WsLayout& L) {
-  hipError_t e;
+  // the workspace carve-up and the kernels must agree on the chunk width
+  if (L.S * SkCfg<MODE>::L != L.ldx || L.ldx < a.shape.n) return hipErrorInvalidValue;
   const int mode = a.phase == PH_FULL ? 0 : 1;
-  if (a.grad_dtype == DT_BF16) e = launch_first<F32OP, XS, bf16_t>(a, L, mode);
-  else e = launch_first<F32OP, XS, float>(a, L, mode);
+  // 16-byte vectors along stored rows need rows = X rows and 8 | n
+  const int vec = (!a.shape.transposed && a.shape.n % 8 == 0) ? 1 : 0;
+  hipError_t e = a.grad_dtype == DT_BF16 ? launch_first<MODE, bf16_t>(a, L, mode, vec)
+                                         : launch_first<MODE, float>(a, L, mode, vec);
   if (e != hipSuccess) return e;
-  const int64_t m = a.shape.m;
   const bool pbf = (a.phase == PH_FULL && a.param_dtype == DT_BF16);
-#define MUON_SK_ITERS(MM)                                                   \
-  return pbf ? launch_iters<MM, F32OP, XS, bf16_t>(a, L)                    \
-             : launch_iters<MM, F32OP, XS, float>(a, L);
-  if (m <= 8) { MUON_SK_ITERS(8) }
-  if (m <= 16) { MUON_SK_ITERS(16) }
-  if (m <= 24) { MUON_SK_ITERS(24) }
-  MUON_SK_ITERS(32)
-#undef MUON_SK_ITERS
+  return pbf ? launch_iters<MODE, bf16_t>(a, L, vec) : launch_iters<MODE, float>(a, L, vec);
 }
 
 }  // namespace
 
 hipError_t run_skinny(const StepArgs& a, const WsLayout& L) {
   switch (a.prec) {
-    case PREC_BF16: return run_mode<false, bf16_t>(a, L);
-    case PREC_BF16_X32: return run_mode<false, float>(a, L);
-    default: return run_mode<true, float>(a, L);
+    case PREC_BF16: return run_mode<0>(a, L);
+    case PREC_BF16_X32: return run_mode<1>(a, L);
+    default: return run_mode<2>(a, L);
   }
 }
 
