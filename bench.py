@@ -101,6 +101,38 @@ def make_device_batches(wl, plan, dtype, reuse_shapes: bool):
     return out
 
 
+def make_device_batches_gpu(wl, plan, dtype, seed=0):
+    """Per-batch device buffers drawn on the GPU with seeded torch generators,
+    following the workload's recipes (for large workloads, where drawing on
+    the host would take minutes).  Not the generator the parity tests use."""
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = []
+    for b in plan.batches:
+        g = torch.Generator(device="cuda").manual_seed(seed * 100003 + b.index)
+        shp = (b.count, b.M, b.N)
+        p = (torch.randn(shp, generator=g, device="cuda") * 0.02).to(tdt)
+        if wl.grad_recipe == "normal":
+            gr = torch.randn(shp, generator=g, device="cuda") * wl.grad_scale
+        elif wl.grad_recipe == "row_scaled":
+            r = torch.exp(torch.empty((b.count, b.M, 1), device="cuda").uniform_(
+                math.log(0.1), math.log(10.0), generator=g))
+            gr = torch.randn(shp, generator=g, device="cuda") * wl.grad_scale * r
+        else:
+            U = torch.randn((b.count, b.M, 64), generator=g, device="cuda")
+            V = torch.randn((b.count, b.N, 64), generator=g, device="cuda")
+            gr = torch.bmm(U, V.transpose(1, 2).contiguous()) + 0.1 * torch.randn(shp, generator=g, device="cuda")
+            del U, V
+        gr = gr.to(tdt)
+        if wl.momentum_recipe == "zeros":
+            mom = torch.zeros(shp, dtype=torch.float32, device="cuda")
+        else:
+            mom = torch.randn(shp, generator=g, device="cuda")
+        out.append({"param": p, "grad": gr, "momentum": mom})
+        torch.cuda.synchronize()
+    return out
+
+
 def cpu_baseline(wl, plan, dtype, hp, budget_s=12.0, max_matrices=None):
     """Time the float64 oracle on this host on a bounded sample of the workload."""
     from oracle import muon_oracle as ORC
@@ -130,21 +162,30 @@ def cpu_baseline(wl, plan, dtype, hp, budget_s=12.0, max_matrices=None):
         data.append((b, W, G, Mo))
         if max_matrices is not None and len(data) >= max_matrices:
             break
+    # a full step on one very large matrix can take minutes here: then time the
+    # oracle's momentum + one Newton-Schulz step of it instead (same arithmetic)
+    b0 = data[0][0]
+    m0, n0 = min(b0.M, b0.N), max(b0.M, b0.N)
+    est = hp.ns_steps * (4.0 * m0 * m0 * n0 + 2.0 * m0 ** 3) / 0.3e12
+    steps = hp.ns_steps if est <= 2.5 * budget_s else 1
     t0 = time.perf_counter()
     while True:
         for (b, W, G, Mo) in data:
             kw = H.oracle_kwargs(hp, b.M, b.N)
+            kw["ns_steps"] = steps
+            if steps != hp.ns_steps:
+                kw["coeffs"] = kw["coeffs"][:3]
             ORC.muon_step_matrix(W, G, Mo, **kw)
             m, n = min(b.M, b.N), max(b.M, b.N)
-            flops += hp.ns_steps * (4.0 * m * m * n + 2.0 * m ** 3)
+            flops += steps * (4.0 * m * m * n + 2.0 * m ** 3)
             done += 1
         reps += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{len(data)} matrices of the workload x {reps} repetitions ({done} oracle steps, "
-                      f"{el:.1f} s, float64 NumPy)"}
+            "sample": f"{len(data)} matrices of the workload x {reps} repetitions ({done} oracle steps of "
+                      f"{steps} Newton-Schulz iterations, {el:.1f} s, float64 NumPy)"}
 
 
 def main():
@@ -158,6 +199,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (the reference for HBM byte counters)")
+    ap.add_argument("--device-inputs", action="store_true",
+                    help="draw the inputs on the GPU with seeded torch generators (large workloads)")
     ap.add_argument("--reuse-shapes", action="store_true",
                     help="batches of identical shape share generated input values (copied per batch)")
     args = ap.parse_args()
@@ -177,7 +220,10 @@ def main():
     hp = H.c_hparams(wl.hp, precision=prec)
     torch.cuda.set_device(0)
     plan = B.Plan([p.shape for p in wl.params])
-    bufs = make_device_batches(wl, plan, dtype, args.reuse_shapes)
+    if args.device_inputs:
+        bufs = make_device_batches_gpu(wl, plan, dtype)
+    else:
+        bufs = make_device_batches(wl, plan, dtype, args.reuse_shapes)
     ws_bytes = max(plan.workspace_bytes(b.index, prec) for b in plan.batches)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
@@ -253,7 +299,8 @@ def main():
     cfg = {"workload": wl.name, "matrices": int(sum(b.count for b in plan.batches)),
            "batches": [[b.count, b.M, b.N] for b in plan.batches], "param_dtype": dtype,
            "precision": prec, "ns_steps": hp.ns_steps, "coeffs": list(hp.coeffs),
-           "inputs": "seeded synthetic" + (", same-shape batches share values" if args.reuse_shapes else "")}
+           "inputs": ("seeded synthetic, drawn on the GPU (torch generators)" if args.device_inputs else
+                      "seeded synthetic" + (", same-shape batches share values" if args.reuse_shapes else ""))}
     out = {"metric": "Muon-step NS TFLOP/s (bf16 MFMA)", "value": value, "unit": "TFLOP/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if prec != "f32" else "f32",

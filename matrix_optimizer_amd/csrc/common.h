@@ -8,6 +8,7 @@ namespace muon {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // 16-byte register vector
 typedef uint16_t bf16_t;   // bf16 stored as raw bits
 
 constexpr int WAVE = 64;

@@ -26,8 +26,6 @@
 namespace muon {
 namespace {
 
-constexpr int GM_THREADS = 256;
-constexpr int BM = 128, BN = 128;
 
 // ---------------------------------------------------------------------------
 // momentum / norm partials
@@ -158,9 +156,39 @@ struct GemmArgs {
   int64_t m, n; int transposed;
 };
 
-template <typename OP> struct OpCfg;
-template <> struct OpCfg<bf16_t> { static constexpr int BK = 64, LD = 72; };   // 128 B rows + 16 B pad
-template <> struct OpCfg<float> { static constexpr int BK = 32, LD = 36; };
+// Tile configuration of the NT product kernel: BM x BN output tile per
+// workgroup, BK reduction slice per LDS stage, WAVES_M x WAVES_N waves, each
+// owning a (BM/WAVES_M) x (BN/WAVES_N) sub-tile of 32x32 MFMA blocks.  LDS rows
+// carry 16 bytes of padding so the MFMA fragment reads are bank-conflict free.
+template <typename OP, int BM_, int BN_, int BK_, int WGM_, int WGN_>
+struct GemmCfg {
+  typedef OP Op;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_;
+  static constexpr int WAVES_M = WGM_, WAVES_N = WGN_;
+  static constexpr int THREADS = 64 * WGM_ * WGN_;
+  static constexpr int WTM = BM / WGM_, WTN = BN / WGN_;
+  static constexpr int IB = WTM / 32, JB = WTN / 32;
+  static constexpr int EPV = 16 / (int)sizeof(OP);
+  static constexpr int LD = BK + EPV;
+  static constexpr int VPR = BK / EPV;
+  static constexpr int PV = BM * VPR / THREADS;
+  static constexpr int QV = BN * VPR / THREADS;
+  static constexpr int RPP = THREADS / VPR;          // tile rows per load pass
+  static constexpr int STAGE = (BM + BN) * LD;       // elements per LDS stage
+  static_assert(BM * VPR % THREADS == 0 && BN * VPR % THREADS == 0, "load split");
+};
+// bf16, 256x256 tiles, 8 waves of 128x64 (4x2 MFMA blocks): each fragment
+// read from LDS feeds more MFMAs than in the 128x128 tile.  Needs rows and
+// columns padded to 256.
+#ifndef MUON_BIG_WAVES_N
+#define MUON_BIG_WAVES_N 4
+#endif
+#ifndef MUON_BIG_BK
+#define MUON_BIG_BK 64
+#endif
+typedef GemmCfg<bf16_t, 256, 256, MUON_BIG_BK, 2, MUON_BIG_WAVES_N> CfgBig;
+typedef GemmCfg<bf16_t, 128, 128, 64, 2, 2> CfgSmall;
+typedef GemmCfg<float, 128, 128, 32, 2, 2> CfgF32;
 
 __device__ __forceinline__ void tri_tile(int64_t t, int64_t& ti, int64_t& tj) {
   int64_t r = (int64_t)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
@@ -170,155 +198,244 @@ __device__ __forceinline__ void tri_tile(int64_t t, int64_t& ti, int64_t& tj) {
   tj = t - r * (r + 1) / 2;
 }
 
-template <typename T>
-__device__ __forceinline__ void store_elem(void* base, int64_t i, float v) {
-  st_from_f32(reinterpret_cast<T*>(base), i, v);
+// 32 consecutive elements starting at a 16-byte aligned address, as 16-byte stores.
+__device__ __forceinline__ void store_run32(float* p, const float* o) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) *reinterpret_cast<f32x4*>(p + 4 * q) = f32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+}
+__device__ __forceinline__ void store_run32(bf16_t* p, const float* o) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    u32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = (uint32_t)f2bf(o[8 * q + 2 * e]) | ((uint32_t)f2bf(o[8 * q + 2 * e + 1]) << 16);
+    *reinterpret_cast<u32x4*>(p + 8 * q) = v;
+  }
 }
 
-template <typename OP, int EPI, typename PT>
-__global__ void __launch_bounds__(GM_THREADS)
+// Register staging of one k-slice of both operand tiles (16-byte vectors).
+// W[0..31] -= lr (wd W + s O[0..31]) on 32 consecutive, 16-byte aligned elements.
+__device__ __forceinline__ void update_run32(float* w, const float* o, float lr, float wd, float s) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    f32x4 v = *reinterpret_cast<const f32x4*>(w + 4 * q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = apply_update(v[e], o[4 * q + e], lr, wd, s);
+    *reinterpret_cast<f32x4*>(w + 4 * q) = v;
+  }
+}
+__device__ __forceinline__ void update_run32(bf16_t* w, const float* o, float lr, float wd, float s) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    u32x4 v = *reinterpret_cast<const u32x4*>(w + 8 * q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float w0 = __uint_as_float(v[e] << 16), w1 = __uint_as_float(v[e] & 0xffff0000u);
+      v[e] = (uint32_t)f2bf(apply_update(w0, o[8 * q + 2 * e], lr, wd, s)) |
+             ((uint32_t)f2bf(apply_update(w1, o[8 * q + 2 * e + 1], lr, wd, s)) << 16);
+    }
+    *reinterpret_cast<u32x4*>(w + 8 * q) = v;
+  }
+}
+
+template <class C> struct StageRegs {
+  u32x4 p[C::PV];
+  u32x4 q[C::QV];
+};
+
+template <class C>
+__device__ __forceinline__ void stage_load(StageRegs<C>& sr, const typename C::Op* Pp, const typename C::Op* Qp,
+                                           int64_t pstep, int64_t qstep, int64_t k0) {
+#pragma unroll
+  for (int i = 0; i < C::PV; ++i) sr.p[i] = *reinterpret_cast<const u32x4*>(Pp + i * pstep + k0);
+#pragma unroll
+  for (int i = 0; i < C::QV; ++i) sr.q[i] = *reinterpret_cast<const u32x4*>(Qp + i * qstep + k0);
+}
+
+// pl: this thread's first slot of the P rows of a stage; the Q rows follow BM rows later
+template <class C>
+__device__ __forceinline__ void stage_store(const StageRegs<C>& sr, typename C::Op* pl) {
+#pragma unroll
+  for (int i = 0; i < C::PV; ++i) *reinterpret_cast<u32x4*>(pl + i * C::RPP * C::LD) = sr.p[i];
+  typename C::Op* ql = pl + C::BM * C::LD;
+#pragma unroll
+  for (int i = 0; i < C::QV; ++i) *reinterpret_cast<u32x4*>(ql + i * C::RPP * C::LD) = sr.q[i];
+}
+
+template <class C, int EPI, typename PT>
+__global__ void __launch_bounds__(C::THREADS)
 tl_gemm(GemmArgs g) {
-  typedef OpCfg<OP> C;
-  __shared__ __attribute__((aligned(16))) OP Ps[BM * C::LD];
-  __shared__ __attribute__((aligned(16))) OP Qs[BN * C::LD];
+  typedef typename C::Op OP;
+  __shared__ __attribute__((aligned(16))) OP lds[2 * C::STAGE];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = t >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  const int64_t mat = blockIdx.x / g.tiles_per_mat;
-  const int64_t tt = blockIdx.x % g.tiles_per_mat;
+  const int wm = w / C::WAVES_N, wn = w % C::WAVES_N;
+  // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous
+  // range of tiles so the operand panels they share meet in the same L2.
+  int64_t bid = blockIdx.x;
+  const int64_t nb = gridDim.x;
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int64_t mat = bid / g.tiles_per_mat;
+  const int64_t tt = bid % g.tiles_per_mat;
   int64_t ti, tj;
   if (EPI == EPI_APPLY) { ti = tt / g.tiles_n; tj = tt % g.tiles_n; }
   else tri_tile(tt, ti, tj);
-  const int64_t i0 = ti * BM, j0 = tj * BN;
+  const int64_t i0 = ti * C::BM, j0 = tj * C::BN;
 
-  const OP* P = reinterpret_cast<const OP*>(g.P) + mat * g.strideP + i0 * g.ldp;
-  const OP* Q = reinterpret_cast<const OP*>(g.Q) + mat * g.strideQ + j0 * g.ldq;
+  const int r0 = t / C::VPR, cv = (t % C::VPR) * C::EPV;
+  const OP* Pp = reinterpret_cast<const OP*>(g.P) + mat * g.strideP + (i0 + r0) * g.ldp + cv;
+  const OP* Qp = reinterpret_cast<const OP*>(g.Q) + mat * g.strideQ + (j0 + r0) * g.ldq + cv;
+  const int64_t pstep = (int64_t)C::RPP * g.ldp, qstep = (int64_t)C::RPP * g.ldq;
 
-  // global -> register staging: 4 x 16 B per thread per operand
-  constexpr int VPR = C::BK * (int)sizeof(OP) / 16;   // 16-byte vectors per tile row (8)
-  constexpr int EPV = 16 / (int)sizeof(OP);            // elements per 16-byte vector
-  uint4 pr0, pr1, pr2, pr3, qr0, qr1, qr2, qr3;
-  const int r0 = t / VPR, cv = (t % VPR) * EPV;       // rows r0 + 32*it, it = 0..3
-  const OP* Pp = P + r0 * g.ldp + cv;
-  const OP* Qp = Q + r0 * g.ldq + cv;
-  const int64_t p32 = 32 * g.ldp, q32 = 32 * g.ldq;
-#define MUON_GLOAD(k0)                                                      \
-  do {                                                                      \
-    pr0 = *reinterpret_cast<const uint4*>(Pp + (k0));                       \
-    pr1 = *reinterpret_cast<const uint4*>(Pp + p32 + (k0));                 \
-    pr2 = *reinterpret_cast<const uint4*>(Pp + 2 * p32 + (k0));             \
-    pr3 = *reinterpret_cast<const uint4*>(Pp + 3 * p32 + (k0));             \
-    qr0 = *reinterpret_cast<const uint4*>(Qp + (k0));                       \
-    qr1 = *reinterpret_cast<const uint4*>(Qp + q32 + (k0));                 \
-    qr2 = *reinterpret_cast<const uint4*>(Qp + 2 * q32 + (k0));             \
-    qr3 = *reinterpret_cast<const uint4*>(Qp + 3 * q32 + (k0));             \
-  } while (0)
-  OP* Pl = &Ps[r0 * C::LD + cv];
-  OP* Ql = &Qs[r0 * C::LD + cv];
-  static_assert(GM_THREADS / VPR == 32, "staging assumes 32 rows per pass");
-
-  f32x16 acc[2][2];
+  StageRegs<C> sr;
+  f32x16 acc[C::IB][C::JB];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < C::IB; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+    for (int b = 0; b < C::JB; ++b) acc[a][b] = f32x16{};
 
   const int64_t KT = g.K / C::BK;
-  MUON_GLOAD(0);
+  stage_load<C>(sr, Pp, Qp, pstep, qstep, 0);
+  stage_store<C>(sr, lds + r0 * C::LD + cv);
+  __syncthreads();
   for (int64_t kt = 0; kt < KT; ++kt) {
-    __syncthreads();
-    *reinterpret_cast<uint4*>(Pl) = pr0;
-    *reinterpret_cast<uint4*>(Pl + 32 * C::LD) = pr1;
-    *reinterpret_cast<uint4*>(Pl + 64 * C::LD) = pr2;
-    *reinterpret_cast<uint4*>(Pl + 96 * C::LD) = pr3;
-    *reinterpret_cast<uint4*>(Ql) = qr0;
-    *reinterpret_cast<uint4*>(Ql + 32 * C::LD) = qr1;
-    *reinterpret_cast<uint4*>(Ql + 64 * C::LD) = qr2;
-    *reinterpret_cast<uint4*>(Ql + 96 * C::LD) = qr3;
-    __syncthreads();
-    if (kt + 1 < KT) MUON_GLOAD((kt + 1) * C::BK);
+    const int st = (int)(kt & 1);
+    if (kt + 1 < KT) stage_load<C>(sr, Pp, Qp, pstep, qstep, (kt + 1) * C::BK);
+    const OP* Ps = lds + st * C::STAGE + (wm * C::WTM + (lane & 31)) * C::LD;
+    const OP* Qs = lds + st * C::STAGE + (C::BM + wn * C::WTN + (lane & 31)) * C::LD;
     if constexpr (sizeof(OP) == 2) {
 #pragma unroll
       for (int kk = 0; kk < C::BK / 16; ++kk) {
-        bf16x8 av[2], bv[2];
+        bf16x8 av[C::IB], bv[C::JB];
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-          av[ib] = *reinterpret_cast<const bf16x8*>(&Ps[(wm * 64 + ib * 32 + (lane & 31)) * C::LD + kk * 16 + (lane >> 5) * 8]);
+        for (int ib = 0; ib < C::IB; ++ib)
+          av[ib] = *reinterpret_cast<const bf16x8*>(Ps + ib * 32 * C::LD + kk * 16 + (lane >> 5) * 8);
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
-          bv[jb] = *reinterpret_cast<const bf16x8*>(&Qs[(wn * 64 + jb * 32 + (lane & 31)) * C::LD + kk * 16 + (lane >> 5) * 8]);
+        for (int jb = 0; jb < C::JB; ++jb)
+          bv[jb] = *reinterpret_cast<const bf16x8*>(Qs + jb * 32 * C::LD + kk * 16 + (lane >> 5) * 8);
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
+        for (int ib = 0; ib < C::IB; ++ib)
 #pragma unroll
-          for (int jb = 0; jb < 2; ++jb)
+          for (int jb = 0; jb < C::JB; ++jb)
             acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ib], bv[jb], acc[ib][jb], 0, 0, 0);
       }
     } else {
 #pragma unroll
       for (int kk = 0; kk < C::BK / 2; ++kk) {
-        float av[2], bv[2];
+        float av[C::IB], bv[C::JB];
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-          av[ib] = reinterpret_cast<const float*>(Ps)[(wm * 64 + ib * 32 + (lane & 31)) * C::LD + kk * 2 + (lane >> 5)];
+        for (int ib = 0; ib < C::IB; ++ib) av[ib] = Ps[ib * 32 * C::LD + kk * 2 + (lane >> 5)];
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
-          bv[jb] = reinterpret_cast<const float*>(Qs)[(wn * 64 + jb * 32 + (lane & 31)) * C::LD + kk * 2 + (lane >> 5)];
+        for (int jb = 0; jb < C::JB; ++jb) bv[jb] = Qs[jb * 32 * C::LD + kk * 2 + (lane >> 5)];
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
+        for (int ib = 0; ib < C::IB; ++ib)
 #pragma unroll
-          for (int jb = 0; jb < 2; ++jb)
+          for (int jb = 0; jb < C::JB; ++jb)
             acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[ib], bv[jb], acc[ib][jb], 0, 0, 0);
       }
     }
+    if (kt + 1 < KT) stage_store<C>(sr, lds + (st ^ 1) * C::STAGE + r0 * C::LD + cv);
+    __syncthreads();
   }
 
-#undef MUON_GLOAD
-
-  // ---- epilogues -----------------------------------------------------------
+  // ---- epilogues -------------------------------------------------------------
+  // Each wave stages one 32 x 64 block row of its sub-tile in LDS per round;
+  // lane l then owns column l of that block: row-major outputs are written
+  // 64 lanes wide (coalesced) and transposed outputs as 16-byte vectors along
+  // the lane's own 32 contiguous elements.  Offsets inside one padded matrix
+  // fit in 32 bits (the planner caps a padded matrix at 2^31 elements).
+  static_assert(C::JB == 2, "epilogue stages 64-column wave tiles");
+  constexpr int SLD = 72;   // staging row stride (floats): conflict-free writes and reads
+  static_assert(C::THREADS / 64 * 32 * SLD * 4 <= 2 * C::STAGE * (int)sizeof(OP), "staging fits in LDS");
+  float* stg = reinterpret_cast<float*>(lds) + w * (32 * SLD);
+  const uint32_t jj = (uint32_t)(j0 + wn * C::WTN + lane);
   const bool diag = (EPI != EPI_APPLY) && (ti == tj);
+#pragma clang loop unroll(full)
+  for (int ib = 0; ib < C::IB; ++ib) {
 #pragma unroll
-  for (int ib = 0; ib < 2; ++ib) {
+    for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
+      for (int r = 0; r < 16; ++r) stg[mfma32_row(lane, r) * SLD + jb * 32 + (lane & 31)] = acc[ib][jb][r];
+    __syncthreads();
+    float o[32];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t i = i0 + wm * 64 + ib * 32 + mfma32_row(lane, r);
-        const int64_t j = j0 + wn * 64 + jb * 32 + mfma32_col(lane);
-        const float v = acc[ib][jb][r];
-        if constexpr (EPI == EPI_GRAM) {
-          const int64_t ab = mat * g.strideA;
-          g.A32[ab + i * g.lda + j] = v;
-          if (g.A16) g.A16[ab + i * g.lda + j] = f2bf(v);
-          if (!diag) {
-            g.A32[ab + j * g.lda + i] = v;
-            if (g.A16) g.A16[ab + j * g.lda + i] = f2bf(v);
-          }
-        } else if constexpr (EPI == EPI_POLY) {
-          const int64_t ab = mat * g.strideA;
-          const float o = g.cb * g.A32[ab + i * g.lda + j] + g.cc * v;
-          store_elem<OP>(g.PB, ab + i * g.lda + j, o);
-          if (!diag) store_elem<OP>(g.PB, ab + j * g.lda + i, o);
-        } else {
-          const int64_t xi = mat * g.strideX + i * g.ldx + j;
-          const float xo = g.X32 ? g.X32[xi] : ld_as_f32(reinterpret_cast<const OP*>(g.X), xi);
-          const float o = g.ca * xo + v;
-          if (!g.last) {
-            store_elem<OP>(g.X, xi, o);
-            if (g.X32) g.X32[xi] = o;
-            store_elem<OP>(g.XT, mat * g.strideX + j * g.ldxt + i, o);
-          } else if (i < g.m && j < g.n) {
-            const int64_t si = mat * g.m * g.n + (g.transposed ? j * g.m + i : i * g.n + j);
-            if (g.ns_out) g.ns_out[si] = o;
-            if (g.param) {
-              PT* W = reinterpret_cast<PT*>(g.param);
-              st_from_f32(W, si, apply_update(ld_as_f32(W, si), o, g.lr, g.wd, g.s));
+    for (int q = 0; q < 32; ++q) o[q] = stg[q * SLD + lane];
+    const uint32_t ib0 = (uint32_t)(i0 + wm * C::WTM + ib * 32);
+    if constexpr (EPI == EPI_GRAM) {
+      const uint32_t ld = (uint32_t)g.lda;
+      float* A32 = g.A32 + mat * g.strideA;
+#pragma unroll
+      for (int q = 0; q < 32; ++q) A32[(ib0 + q) * ld + jj] = o[q];
+      if (!diag) store_run32(A32 + jj * ld + ib0, o);
+      if (g.A16) {
+        bf16_t* A16 = g.A16 + mat * g.strideA;
+#pragma unroll
+        for (int q = 0; q < 32; ++q) A16[(ib0 + q) * ld + jj] = f2bf(o[q]);
+        if (!diag) store_run32(A16 + jj * ld + ib0, o);
+      }
+    } else if constexpr (EPI == EPI_POLY) {
+      const uint32_t ld = (uint32_t)g.lda;
+      const float* A32 = g.A32 + mat * g.strideA;
+      OP* PB = reinterpret_cast<OP*>(g.PB) + mat * g.strideA;
+#pragma unroll
+      for (int q = 0; q < 32; ++q) {
+        o[q] = g.cb * A32[(ib0 + q) * ld + jj] + g.cc * o[q];
+        st_from_f32(PB, (ib0 + q) * ld + jj, o[q]);
+      }
+      if (!diag) store_run32(PB + jj * ld + ib0, o);
+    } else if (!g.last) {
+      const uint32_t ldx = (uint32_t)g.ldx;
+      OP* X = reinterpret_cast<OP*>(g.X) + mat * g.strideX;
+      float* X32 = g.X32 ? g.X32 + mat * g.strideX : nullptr;
+#pragma unroll
+      for (int q = 0; q < 32; ++q) {
+        const uint32_t xi = (ib0 + q) * ldx + jj;
+        o[q] = g.ca * (X32 ? X32[xi] : ld_as_f32(X, xi)) + o[q];
+        if (X32) X32[xi] = o[q];
+        st_from_f32(X, xi, o[q]);
+      }
+      store_run32(reinterpret_cast<OP*>(g.XT) + mat * g.strideX + jj * (uint32_t)g.ldxt + ib0, o);
+    } else {
+      const uint32_t ldx = (uint32_t)g.ldx;
+      const OP* X = reinterpret_cast<const OP*>(g.X) + mat * g.strideX;
+      const float* X32 = g.X32 ? g.X32 + mat * g.strideX : nullptr;
+      PT* W = g.param ? reinterpret_cast<PT*>(g.param) + mat * g.m * g.n : nullptr;
+      float* O = g.ns_out ? g.ns_out + mat * g.m * g.n : nullptr;
+      const uint32_t m = (uint32_t)g.m, n = (uint32_t)g.n;
+      if (jj < n) {
+#pragma unroll
+        for (int q = 0; q < 32; ++q) {
+          const uint32_t xi = (ib0 + q) * ldx + jj;   // padded rows: always readable
+          o[q] = g.ca * (X32 ? X32[xi] : ld_as_f32(X, xi)) + o[q];
+        }
+        if (!g.transposed) {
+          // W row-major: lanes cover consecutive columns of each row
+#pragma unroll
+          for (int q = 0; q < 32; ++q) {
+            const uint32_t i = ib0 + q;
+            if (i < m) {
+              if (O) O[i * n + jj] = o[q];
+              if (W) st_from_f32(W, i * n + jj, apply_update(ld_as_f32(W, i * n + jj), o[q], g.lr, g.wd, g.s));
             }
+          }
+        } else if (ib0 + 32 <= m && (m % 8) == 0) {
+          // W is the transpose: this lane's 32 elements are contiguous and 16-byte aligned
+          const uint32_t base = jj * m + ib0;
+          if (O) store_run32(O + base, o);
+          if (W) update_run32(W + base, o, g.lr, g.wd, g.s);
+        } else {
+          for (uint32_t q = 0; q < 32 && ib0 + q < m; ++q) {
+            const uint32_t si = jj * m + ib0 + q;
+            if (O) O[si] = o[q];
+            if (W) st_from_f32(W, si, apply_update(ld_as_f32(W, si), o[q], g.lr, g.wd, g.s));
           }
         }
       }
     }
+    __syncthreads();
   }
 }
 
@@ -338,6 +455,61 @@ hipError_t launch_momentum(const StepArgs& a, int mode, float* ssp, int64_t npar
   MUON_LAUNCH(mode == 2 ? "momentum" : "tl_momentum_norm", (tl_momentum<GT>), grid, block, a.stream, mode, (const GT*)a.grad, a.mom, a.u_in,
                      a.u_out, ssp, elems, nparts, a.mu, a.nesterov);
   return hipGetLastError();
+}
+
+// The K Newton-Schulz steps as three NT products each, on tile config C.
+template <class C, typename PT>
+hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C::Op* X, typename C::Op* XT[2],
+                            float* X32, float* A32, bf16_t* A16, typename C::Op* PB, int64_t mp, int64_t np) {
+  typedef typename C::Op OP;
+  hipError_t e;
+  const int64_t tm = mp / C::BM, tn = np / C::BN;
+  const int64_t tri = tm * (tm + 1) / 2;
+  for (int k = 0; k < a.steps; ++k) {
+    const float ca = a.coeffs[3 * k], cb = a.coeffs[3 * k + 1], cc = a.coeffs[3 * k + 2];
+    GemmArgs g = {};
+    // Gram: A = X X^T
+    g.P = X; g.Q = X; g.ldp = np; g.ldq = np; g.strideP = mp * np; g.strideQ = mp * np; g.K = np;
+    g.tiles_n = tm; g.tiles_per_mat = tri;
+    g.A32 = A32; g.A16 = A16; g.lda = mp; g.strideA = mp * mp;
+    MUON_LAUNCH("tl_gram", (tl_gemm<C, EPI_GRAM, PT>), dim3((unsigned)(sh.count * tri)), dim3(C::THREADS),
+                a.stream, g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // poly: B = b A + c A A
+    g = GemmArgs{};
+    if (sizeof(OP) == 4) { g.P = A32; g.Q = A32; } else { g.P = A16; g.Q = A16; }
+    g.ldp = mp; g.ldq = mp; g.strideP = mp * mp; g.strideQ = mp * mp; g.K = mp;
+    g.tiles_n = tm; g.tiles_per_mat = tri;
+    g.A32 = A32; g.PB = PB; g.lda = mp; g.strideA = mp * mp; g.cb = cb; g.cc = cc;
+    MUON_LAUNCH("tl_poly", (tl_gemm<C, EPI_POLY, PT>), dim3((unsigned)(sh.count * tri)), dim3(C::THREADS),
+                a.stream, g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // apply: X' = a X + B X, B X read as B (X^T)^T
+    g = GemmArgs{};
+    g.P = PB; g.Q = XT[k & 1]; g.ldp = mp; g.ldq = mp; g.strideP = mp * mp; g.strideQ = np * mp; g.K = mp;
+    g.tiles_n = tn; g.tiles_per_mat = tm * tn;
+    g.ca = ca; g.X = X; g.X32 = X32; g.XT = XT[(k + 1) & 1]; g.ldx = np; g.ldxt = mp; g.strideX = mp * np;
+    g.last = (k == a.steps - 1);
+    g.param = a.phase == PH_FULL ? a.param : nullptr; g.param_bf16 = a.param_dtype == DT_BF16;
+    g.ns_out = a.ns_out; g.lr = a.lr; g.wd = a.wd; g.s = a.s;
+    g.m = sh.m; g.n = sh.n; g.transposed = sh.transposed;
+    MUON_LAUNCH(g.last ? "tl_apply_update" : "tl_apply", (tl_gemm<C, EPI_APPLY, PT>),
+                dim3((unsigned)(sh.count * tm * tn)), dim3(C::THREADS), a.stream, g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <typename OP, typename PT>
+hipError_t run_products(const StepArgs& a, const BatchShape& sh, OP* X, OP* XT[2], float* X32, float* A32,
+                        bf16_t* A16, OP* PB, int64_t mp, int64_t np) {
+  if constexpr (sizeof(OP) == 4) {
+    return run_products_cfg<CfgF32, PT>(a, sh, X, XT, X32, A32, A16, PB, mp, np);
+  } else {
+    if (mp % CfgBig::BM == 0 && np % CfgBig::BN == 0)
+      return run_products_cfg<CfgBig, PT>(a, sh, X, XT, X32, A32, A16, PB, mp, np);
+    return run_products_cfg<CfgSmall, PT>(a, sh, X, XT, X32, A32, A16, PB, mp, np);
+  }
 }
 
 template <typename OP, typename GT, typename PT>
@@ -367,41 +539,7 @@ hipError_t tiled_impl(const StepArgs& a, const WsLayout& L) {
                        (int)sh.transposed, a.mu, a.nesterov);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const int64_t tm = mp / BM, tn = np / BN;
-  const int64_t tri = tm * (tm + 1) / 2;
-  for (int k = 0; k < a.steps; ++k) {
-    const float ca = a.coeffs[3 * k], cb = a.coeffs[3 * k + 1], cc = a.coeffs[3 * k + 2];
-    GemmArgs g = {};
-    // Gram: A = X X^T
-    g.P = X; g.Q = X; g.ldp = np; g.ldq = np; g.strideP = mp * np; g.strideQ = mp * np; g.K = np;
-    g.tiles_n = tm; g.tiles_per_mat = tri;
-    g.A32 = A32; g.A16 = A16; g.lda = mp; g.strideA = mp * mp;
-    MUON_LAUNCH("tl_gram", (tl_gemm<OP, EPI_GRAM, PT>), dim3((unsigned)(sh.count * tri)), dim3(GM_THREADS),
-                a.stream, g);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    // poly: B = b A + c A A
-    g = GemmArgs{};
-    if (a.prec == PREC_F32) { g.P = A32; g.Q = A32; } else { g.P = A16; g.Q = A16; }
-    g.ldp = mp; g.ldq = mp; g.strideP = mp * mp; g.strideQ = mp * mp; g.K = mp;
-    g.tiles_n = tm; g.tiles_per_mat = tri;
-    g.A32 = A32; g.PB = PB; g.lda = mp; g.strideA = mp * mp; g.cb = cb; g.cc = cc;
-    MUON_LAUNCH("tl_poly", (tl_gemm<OP, EPI_POLY, PT>), dim3((unsigned)(sh.count * tri)), dim3(GM_THREADS),
-                a.stream, g);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    // apply: X' = a X + B X, B X read as B (X^T)^T
-    g = GemmArgs{};
-    g.P = PB; g.Q = XT[k & 1]; g.ldp = mp; g.ldq = mp; g.strideP = mp * mp; g.strideQ = np * mp; g.K = mp;
-    g.tiles_n = tn; g.tiles_per_mat = tm * tn;
-    g.ca = ca; g.X = X; g.X32 = X32; g.XT = XT[(k + 1) & 1]; g.ldx = np; g.ldxt = mp; g.strideX = mp * np;
-    g.last = (k == a.steps - 1);
-    g.param = a.phase == PH_FULL ? a.param : nullptr; g.param_bf16 = a.param_dtype == DT_BF16;
-    g.ns_out = a.ns_out; g.lr = a.lr; g.wd = a.wd; g.s = a.s;
-    g.m = sh.m; g.n = sh.n; g.transposed = sh.transposed;
-    MUON_LAUNCH(g.last ? "tl_apply_update" : "tl_apply", (tl_gemm<OP, EPI_APPLY, PT>),
-                dim3((unsigned)(sh.count * tm * tn)), dim3(GM_THREADS), a.stream, g);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  return hipSuccess;
+  return run_products<OP, PT>(a, sh, X, XT, X32, A32, A16, PB, mp, np);
 }
 
 template <typename OP>

@@ -96,6 +96,7 @@ SHAPE_SETS = {
     "tiled_square": [(130, 130)],
     "tiled_multi_tile": [(129, 400), (2, 129, 400)],
     "tiled_experts_tall": [(2, 300, 40)],
+    "tiled_256_tiles": [(256, 768), (2, 512, 256)],
 }
 
 
