@@ -40,7 +40,8 @@ def dsize(dtype: str) -> int:
 
 
 def kernel_model(name, count, M, N, prec, pdt, gdt, with_ns_out=False):
-    """(bound, algorithmic quantity per launch, unit) of one kernel launch.
+    """(bound, algorithmic quantity per launch, unit) of one kernel launch, or
+    None if the kernel does not run on this batch's path.
 
     Bytes are what the kernel's function needs to move once (inputs read once,
     outputs written once); flops are the products the algorithm needs (the
@@ -75,7 +76,34 @@ def kernel_model(name, count, M, N, prec, pdt, gdt, with_ns_out=False):
             return "mfma", count * 2 * m * m * n, "flop"
         if name == "tl_norm_finalize":
             return "hbm", count * 4 * 1024, "B"
-    return "hbm", 0, "B"
+    return None
+
+
+def kernel_sources_sha256() -> str:
+    """Hash of the HIP/C++ sources the kernels are built from."""
+    import hashlib
+    d = os.path.join(ROOT, "matrix_optimizer_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str, prec: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{prec}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k["bytes_per_launch"]
 
 
 def make_device_batches(wl, plan, dtype, reuse_shapes: bool):
@@ -264,15 +292,18 @@ def main():
     kernels = {k: {"launches_per_step": len(v) / args.steps, "avg_ms": float(np.mean(v)),
                    "total_ms_per_step": float(np.sum(v)) / args.steps} for k, v in per.items()}
     dom = max(kernels, key=lambda k: kernels[k]["total_ms_per_step"])
-    # algorithmic quantity of one launch of the dominant kernel (averaged over batches)
+    # algorithmic quantity of one launch of the dominant kernel, averaged over the
+    # batches it runs on (its launches per batch per step follow from the path)
     qty = 0.0
     nlaunch = 0
     bound, unit = "hbm", "B"
     for b in plan.batches:
-        bd, q, u = kernel_model(dom, b.count, b.M, b.N, prec, dtype, dtype)
+        res = kernel_model(dom, b.count, b.M, b.N, prec, dtype, dtype)
+        if res is None:
+            continue
+        bd, q, u = res
         per_batch = {"sk_ns_step": hp.ns_steps - 1, "sk_bprime": hp.ns_steps, "tl_gram": hp.ns_steps,
-                     "tl_poly": hp.ns_steps,
-                     "tl_apply": hp.ns_steps - 1}.get(dom, 1)
+                     "tl_poly": hp.ns_steps, "tl_apply": hp.ns_steps - 1}.get(dom, 1)
         qty += q * per_batch
         nlaunch += per_batch
         bound, unit = bd, u
@@ -287,6 +318,7 @@ def main():
         peak = FP32_PEAK_TFLOPS if prec == "f32" else BF16_PEAK_TFLOPS
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak, "traffic": None}
+    roof["traffic"] = measured_traffic(wl.name, dom, prec)
     roof["kernel"] = dom
     roof["avg_launch_ms"] = kernels[dom]["avg_ms"]
     roof["algorithmic_per_launch"] = qty_per_launch
