@@ -39,7 +39,7 @@ def dsize(dtype: str) -> int:
     return 2 if dtype == "bf16" else 4
 
 
-def kernel_model(name, count, M, N, prec, pdt, gdt, with_ns_out=False):
+def kernel_model(name, count, M, N, prec, pdt, gdt, with_ns_out=False, ns_steps=5):
     """(bound, algorithmic quantity per launch, unit) of one kernel launch, or
     None if the kernel does not run on this batch's path.
 
@@ -51,7 +51,7 @@ def kernel_model(name, count, M, N, prec, pdt, gdt, with_ns_out=False):
     xs = 2 if prec == "bf16" else 4
     gs, ps = dsize(gdt), dsize(pdt)
     if m <= SKINNY_MAX_ROWS:
-        L = 512 if prec == "bf16" else 256      # chunk widths of the skinny kernels
+        L = 512 if prec == "bf16" else 256      # chunk widths of the split-K skinny kernels
         S = math.ceil(n / L)
         T = m * (m + 1) // 2
         part = count * S * T * 4
@@ -59,6 +59,9 @@ def kernel_model(name, count, M, N, prec, pdt, gdt, with_ns_out=False):
             return "hbm", E * (gs + 4 + 4 + xs) + part + count * S * 4, "B"
         if name == "sk_ns_step":
             return "hbm", E * 2 * xs + 2 * part, "B"
+        if name == "sk_owner":      # the whole step in one launch
+            K = ns_steps
+            return "hbm", E * (gs + 8 + xs) + (K - 1) * E * 2 * xs + E * (xs + 2 * ps), "B"
         if name == "sk_bprime":
             return "hbm", part + count * 4096, "B"
         if name == "sk_ns_step_update":
@@ -227,6 +230,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (the reference for HBM byte counters)")
+    ap.add_argument("--skinny-kernel", type=int, default=0,
+                    help="short sides <= 32: 0 auto, 1 one workgroup per matrix, 2 split-K chunks")
     ap.add_argument("--device-inputs", action="store_true",
                     help="draw the inputs on the GPU with seeded torch generators (large workloads)")
     ap.add_argument("--reuse-shapes", action="store_true",
@@ -247,7 +252,7 @@ def main():
     dtype = wl.params[0].dtype
     hp = H.c_hparams(wl.hp, precision=prec)
     torch.cuda.set_device(0)
-    plan = B.Plan([p.shape for p in wl.params])
+    plan = B.Plan([p.shape for p in wl.params], skinny_kernel=args.skinny_kernel)
     if args.device_inputs:
         bufs = make_device_batches_gpu(wl, plan, dtype)
     else:
@@ -298,7 +303,7 @@ def main():
     nlaunch = 0
     bound, unit = "hbm", "B"
     for b in plan.batches:
-        res = kernel_model(dom, b.count, b.M, b.N, prec, dtype, dtype)
+        res = kernel_model(dom, b.count, b.M, b.N, prec, dtype, dtype, ns_steps=hp.ns_steps)
         if res is None:
             continue
         bd, q, u = res
@@ -329,7 +334,9 @@ def main():
         flops = flops / wl.hp.ns_steps * hp.ns_steps
     value = flops / (ms / 1e3) / 1e12
     cfg = {"workload": wl.name, "matrices": int(sum(b.count for b in plan.batches)),
-           "batches": [[b.count, b.M, b.N] for b in plan.batches], "param_dtype": dtype,
+           "batches": [[b.count, b.M, b.N] for b in plan.batches],
+           "kernels": [["tiled", "skinny_owner", "skinny_chunked"][b.path] for b in plan.batches],
+           "param_dtype": dtype,
            "precision": prec, "ns_steps": hp.ns_steps, "coeffs": list(hp.coeffs),
            "inputs": ("seeded synthetic, drawn on the GPU (torch generators)" if args.device_inputs else
                       "seeded synthetic" + (", same-shape batches share values" if args.reuse_shapes else ""))}

@@ -87,6 +87,9 @@ typedef struct {
                                still forms a batch of its own. */
   int32_t order;            /* 0: batches in descending element count (HyperParallel-FSDP
                                Figure 10(b)), ties in creation order; 1: creation order */
+  int32_t skinny_kernel;    /* matrices with a short side <= 32: 0 choose by a cost model (made
+                               for 5 Newton-Schulz steps); 1 one workgroup per matrix, the whole
+                               step in one launch; 2 split-K chunks over the chip, 2K+1 launches */
 } muon_plan_options;
 
 typedef struct muon_plan muon_plan;   /* opaque, host-only, immutable */
@@ -96,6 +99,9 @@ typedef struct {
   int64_t count;            /* matrices in the batch */
   int32_t transposed;       /* 1 if M > N: Newton-Schulz runs on the transpose */
   int32_t num_segments;
+  int32_t path;             /* 0 tiled products (short side > 32); 1 one workgroup per matrix;
+                               2 split-K chunks */
+  int32_t reserved;
 } muon_batch_info;
 
 /* A run of consecutive matrices of one parameter inside a batch. */

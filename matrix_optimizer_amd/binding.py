@@ -36,12 +36,13 @@ class muon_shape(C.Structure):
 
 
 class muon_plan_options(C.Structure):
-    _fields_ = [("max_batch_elems", C.c_int64), ("order", C.c_int32)]
+    _fields_ = [("max_batch_elems", C.c_int64), ("order", C.c_int32), ("skinny_kernel", C.c_int32)]
 
 
 class muon_batch_info(C.Structure):
     _fields_ = [("M", C.c_int64), ("N", C.c_int64), ("count", C.c_int64),
-                ("transposed", C.c_int32), ("num_segments", C.c_int32)]
+                ("transposed", C.c_int32), ("num_segments", C.c_int32), ("path", C.c_int32),
+                ("reserved", C.c_int32)]
 
 
 class muon_segment(C.Structure):
@@ -140,6 +141,7 @@ class BatchInfo:
     count: int
     transposed: bool
     segments: List[Tuple[int, int, int, int]]   # (param_index, first_matrix, num_matrices, elem_offset)
+    path: int = 0                               # 0 tiled, 1 skinny one workgroup per matrix, 2 skinny chunks
 
     @property
     def elems(self) -> int:
@@ -149,14 +151,15 @@ class BatchInfo:
 class Plan:
     """muon_plan_create / muon_plan_* on a list of parameter shapes."""
 
-    def __init__(self, shapes: Sequence[Sequence[int]], max_batch_elems: int = 0, order: int = 0):
+    def __init__(self, shapes: Sequence[Sequence[int]], max_batch_elems: int = 0, order: int = 0,
+                 skinny_kernel: int = 0):
         L = lib()
         arr = (muon_shape * len(shapes))()
         for i, s in enumerate(shapes):
             arr[i].ndim = len(s)
             for d in range(min(len(s), 3)):
                 arr[i].dims[d] = int(s[d])
-        opt = muon_plan_options(int(max_batch_elems), int(order))
+        opt = muon_plan_options(int(max_batch_elems), int(order), int(skinny_kernel))
         h = C.c_void_p()
         _check(L.muon_plan_create(arr, len(shapes), C.byref(opt), C.byref(h)), "muon_plan_create")
         self._h = h
@@ -169,7 +172,7 @@ class Plan:
             _check(L.muon_plan_segments(h, b, segs, info.num_segments), "muon_plan_segments")
             self.batches.append(BatchInfo(b, info.M, info.N, info.count, bool(info.transposed),
                                           [(s.param_index, s.first_matrix, s.num_matrices, s.elem_offset)
-                                           for s in segs[:info.num_segments]]))
+                                           for s in segs[:info.num_segments]], info.path))
 
     @property
     def handle(self):
@@ -280,9 +283,9 @@ class BatchedMuon:
     (parameters of a batch are views into its buffer, as in HyperParallel-FSDP
     §6.6's merged tensor) and one workspace sized for the largest batch."""
 
-    def __init__(self, shapes, dtype, hp: HParams, device="cuda", max_batch_elems=0, order=0):
+    def __init__(self, shapes, dtype, hp: HParams, device="cuda", max_batch_elems=0, order=0, skinny_kernel=0):
         import torch
-        self.plan = Plan(shapes, max_batch_elems, order)
+        self.plan = Plan(shapes, max_batch_elems, order, skinny_kernel)
         self.hp = hp
         self.dtype = dtype
         self.device = device

@@ -17,6 +17,7 @@ struct muon_plan {
   struct Batch {
     int64_t M, N, count;
     bool transposed;
+    int path;
     std::vector<muon_segment> segs;
   };
   std::vector<Batch> batches;
@@ -49,16 +50,21 @@ BatchShape shape_of(const muon_plan::Batch& b) {
 
 namespace muon {
 
-WsLayout workspace_layout(const BatchShape& b, int prec) {
+WsLayout workspace_layout(const BatchShape& b, int prec, int path) {
   prec = effective_prec(b.m, prec);
   WsLayout L;
+  L.path = path;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t at = off;
     off = align256(off + bytes);
     return at;
   };
-  if (b.m <= kSkinnyMaxRows) {
+  if (path == PATH_SKINNY_OWNER) {
+    L.skinny = true;
+    L.ldx = round_up(b.n, 64);
+    L.x = take(size_t(b.count) * b.m * L.ldx * (prec == PREC_BF16 ? 2 : 4));
+  } else if (path == PATH_SKINNY_CHUNKED) {
     L.skinny = true;
     const int64_t Lc = skinny_chunk(prec);
     L.ldx = round_up(b.n, Lc);
@@ -171,6 +177,14 @@ const muon_plan::Batch* get_batch(const muon_plan* plan, int32_t batch) {
 
 muon_status hip_status(hipError_t e) { return e == hipSuccess ? MUON_OK : MUON_ERR_HIP; }
 
+hipError_t dispatch(const StepArgs& a, const WsLayout& L) {
+  switch (L.path) {
+    case PATH_SKINNY_OWNER: return run_skinny_owner(a, L);
+    case PATH_SKINNY_CHUNKED: return run_skinny(a, L);
+    default: return run_tiled(a, L);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -195,11 +209,13 @@ muon_status muon_plan_create(const muon_shape* shapes, int32_t n, const muon_pla
   *out = nullptr;
   if (!shapes || n < 1) return MUON_ERR_INVALID_ARG;
   int64_t cap = kDefaultCap;
-  int32_t order = 0;
+  int32_t order = 0, skinny_kernel = 0;
   if (opt) {
     if (opt->max_batch_elems < 0 || (opt->order != 0 && opt->order != 1)) return MUON_ERR_INVALID_ARG;
+    if (opt->skinny_kernel < 0 || opt->skinny_kernel > 2) return MUON_ERR_INVALID_ARG;
     if (opt->max_batch_elems > 0) cap = opt->max_batch_elems;
     order = opt->order;
+    skinny_kernel = opt->skinny_kernel;
   }
   // core shape of every parameter (HyperParallel-FSDP §6.6: [A,B], [A,1,B], [N,A,B] -> (A,B))
   struct Core { int64_t nm, M, N; };
@@ -242,6 +258,11 @@ muon_status muon_plan_create(const muon_shape* shapes, int32_t n, const muon_pla
         const size_t end = std::min(mats.size(), start + (size_t)max_count);
         muon_plan::Batch b;
         b.M = M; b.N = N; b.count = (int64_t)(end - start); b.transposed = M > N;
+        const int64_t m = std::min(M, N), n = std::max(M, N);
+        if (m > kSkinnyMaxRows) b.path = PATH_TILED;
+        else if (skinny_kernel == 1) b.path = PATH_SKINNY_OWNER;
+        else if (skinny_kernel == 2) b.path = PATH_SKINNY_CHUNKED;
+        else b.path = skinny_path(b.count, m, n, 5);
         for (size_t k = start; k < end; ++k) {
           const int32_t pi = mats[k].first;
           const int64_t mi = mats[k].second;
@@ -279,6 +300,8 @@ muon_status muon_plan_batch_info(const muon_plan* plan, int32_t batch, muon_batc
   if (!b || !out) return MUON_ERR_INVALID_ARG;
   out->M = b->M; out->N = b->N; out->count = b->count; out->transposed = b->transposed ? 1 : 0;
   out->num_segments = (int32_t)b->segs.size();
+  out->path = b->path;
+  out->reserved = 0;
   return MUON_OK;
 }
 
@@ -295,7 +318,7 @@ muon_status muon_workspace_bytes(const muon_plan* plan, int32_t batch, muon_prec
   if (!b || !out) return MUON_ERR_INVALID_ARG;
   if (precision != MUON_PREC_BF16 && precision != MUON_PREC_BF16_X32 && precision != MUON_PREC_F32)
     return MUON_ERR_INVALID_ARG;
-  *out = workspace_layout(shape_of(*b), precision).total;
+  *out = workspace_layout(shape_of(*b), precision, b->path).total;
   return MUON_OK;
 }
 
@@ -307,7 +330,7 @@ muon_status muon_step(const muon_plan* plan, int32_t batch, const muon_batch_buf
   if (st != MUON_OK) return st;
   if (!valid_dtype(bufs->param_dtype) || !valid_dtype(bufs->grad_dtype)) return MUON_ERR_INVALID_ARG;
   const size_t elems = size_t(b->count) * b->M * b->N;
-  const WsLayout L = workspace_layout(shape_of(*b), hp->precision);
+  const WsLayout L = workspace_layout(shape_of(*b), hp->precision, b->path);
   if (workspace_bytes < L.total) return MUON_ERR_WORKSPACE_TOO_SMALL;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return MUON_ERR_INVALID_ARG;
   std::vector<Region> rs = {region(bufs->param, elems * dsize(bufs->param_dtype)),
@@ -323,7 +346,7 @@ muon_status muon_step(const muon_plan* plan, int32_t batch, const muon_batch_buf
   a.grad = bufs->grad; a.grad_dtype = bufs->grad_dtype == MUON_BF16 ? DT_BF16 : DT_F32;
   a.mom = bufs->momentum; a.ns_out = bufs->ns_out;
   a.ws = static_cast<char*>(workspace);
-  return hip_status(L.skinny ? run_skinny(a, L) : run_tiled(a, L));
+  return hip_status(dispatch(a, L));
 }
 
 muon_status muon_stage_momentum(const muon_plan* plan, int32_t batch, const void* grad, muon_dtype grad_dtype,
@@ -351,7 +374,7 @@ muon_status muon_stage_ns(const muon_plan* plan, int32_t batch, const float* u_i
   muon_status st = check_hparams(hp, true, false, false);
   if (st != MUON_OK) return st;
   const size_t elems = size_t(b->count) * b->M * b->N;
-  const WsLayout L = workspace_layout(shape_of(*b), hp->precision);
+  const WsLayout L = workspace_layout(shape_of(*b), hp->precision, b->path);
   if (workspace_bytes < L.total) return MUON_ERR_WORKSPACE_TOO_SMALL;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return MUON_ERR_INVALID_ARG;
   if (!regions_ok({region(u_in, elems * 4), region(o_out, elems * 4), region(workspace, L.total)}))
@@ -361,7 +384,7 @@ muon_status muon_stage_ns(const muon_plan* plan, int32_t batch, const float* u_i
   a.phase = PH_NS;
   a.u_in = u_in; a.ns_out = o_out;
   a.ws = static_cast<char*>(workspace);
-  return hip_status(L.skinny ? run_skinny(a, L) : run_tiled(a, L));
+  return hip_status(dispatch(a, L));
 }
 
 muon_status muon_stage_update(const muon_plan* plan, int32_t batch, void* param, muon_dtype param_dtype,

@@ -63,13 +63,13 @@ def test_plan_matches_rules_random(seed):
     _cmp_plans(shapes, cap, int(rng.integers(0, 2)))
 
 
-def _plan_status(shapes, cap=0, order=0):
+def _plan_status(shapes, cap=0, order=0, skinny_kernel=0):
     arr = (B.muon_shape * max(1, len(shapes)))()
     for i, s in enumerate(shapes):
         arr[i].ndim = len(s)
         for d in range(min(3, len(s))):
             arr[i].dims[d] = s[d]
-    opt = B.muon_plan_options(cap, order)
+    opt = B.muon_plan_options(cap, order, skinny_kernel)
     h = C.c_void_p()
     st = B.lib().muon_plan_create(arr, len(shapes), C.byref(opt), C.byref(h))
     if st == 0:
@@ -85,9 +85,26 @@ def test_plan_errors():
     assert _plan_status([]) == B.MUON_ERR_INVALID_ARG
     assert _plan_status([(2, 2)], cap=-1) == B.MUON_ERR_INVALID_ARG
     assert _plan_status([(2, 2)], order=2) == B.MUON_ERR_INVALID_ARG
+    assert _plan_status([(2, 2)], skinny_kernel=3) == B.MUON_ERR_INVALID_ARG
+    assert _plan_status([(2, 2)], skinny_kernel=-1) == B.MUON_ERR_INVALID_ARG
     assert _plan_status([(1 << 20, 1 << 20)]) == B.MUON_ERR_UNSUPPORTED   # above 2^31 elements
     assert _plan_status([(1 << 40, 1 << 40)]) == B.MUON_ERR_INVALID_ARG   # int64 overflow
     assert _plan_status([(1 << 62, 4, 1 << 30)]) == B.MUON_ERR_INVALID_ARG
+
+
+def test_batch_paths():
+    # short side <= 32: one of the two skinny kernels; the plan option forces either
+    p = B.Plan([(24, 10240)] * 74 + [(300, 200)])
+    paths = {(b.M, b.N): b.path for b in p.batches}
+    assert paths[(300, 200)] == 0 and paths[(24, 10240)] in (1, 2)
+    assert all(b.path in (0, 1) for b in B.Plan([(24, 10240)] * 4 + [(64, 64)], skinny_kernel=1).batches)
+    assert [b.path for b in B.Plan([(24, 10240)], skinny_kernel=2).batches] == [2]
+    # one matrix with an enormous long side goes to the chip-wide chunks
+    assert [b.path for b in B.Plan([(8, 1 << 24)]).batches] == [2]
+    for k in (1, 2):
+        q = B.Plan([(24, 1000)] * 3, skinny_kernel=k)
+        for prec in ("bf16", "bf16_x32", "f32"):
+            assert q.workspace_bytes(0, prec) % 256 == 0
 
 
 def test_workspace_bytes():

@@ -29,10 +29,10 @@ def _gpu():
     B.lib()
 
 
-def check_batch(wl, h: B.HParams, dtype: str, select=None, plan=None, batches=None):
+def check_batch(wl, h: B.HParams, dtype: str, select=None, plan=None, batches=None, skinny_kernel=0):
     """Run every (or the chosen) batch of wl's plan and compare the selected
     matrices with the oracle.  Returns the list of O errors."""
-    plan = plan or B.Plan([p.shape for p in wl.params])
+    plan = plan or B.Plan([p.shape for p in wl.params], skinny_kernel=skinny_kernel)
     errs = []
     for binfo in plan.batches:
         if batches is not None and binfo.index not in batches:
@@ -100,13 +100,21 @@ SHAPE_SETS = {
 }
 
 
+def _skinny(name):
+    return all(min(WL.ParamSpec("x", tuple(s)).matrix_shape) <= 32 for s in SHAPE_SETS[name])
+
+
+# skinny shapes run through both skinny kernels: 1 = one workgroup per matrix, 2 = split-K chunks
+SHAPE_CASES = [(n, k) for n in sorted(SHAPE_SETS) for k in ((1, 2) if _skinny(n) else (0,))]
+
+
 @pytest.mark.parametrize("prec", PRECS)
 @pytest.mark.parametrize("dtype", [WL.BF16, WL.F32])
-@pytest.mark.parametrize("name", sorted(SHAPE_SETS))
-def test_small_shapes(name, dtype, prec):
+@pytest.mark.parametrize("name,kernel", SHAPE_CASES, ids=[f"{n}-k{k}" for n, k in SHAPE_CASES])
+def test_small_shapes(name, kernel, dtype, prec):
     wl = WL.small_workload(name, SHAPE_SETS[name], dtype=dtype, momentum_recipe="normal",
                            wid=200 + sorted(SHAPE_SETS).index(name))
-    check_batch(wl, H.c_hparams(wl.hp, precision=prec), dtype)
+    check_batch(wl, H.c_hparams(wl.hp, precision=prec), dtype, skinny_kernel=kernel)
 
 
 # --------------------------------------------------------------------------
@@ -125,16 +133,18 @@ def test_hparam_variants(shapes, variant):
         "seven_steps": dict(ns_steps=7),
     }[variant]
     for prec in ("bf16", "f32"):
-        check_batch(wl, H.c_hparams(wl.hp, precision=prec, **over), WL.BF16)
+        for kernel in (1, 2):
+            check_batch(wl, H.c_hparams(wl.hp, precision=prec, **over), WL.BF16, skinny_kernel=kernel)
 
 
 # --------------------------------------------------------------------------
 # special cases
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("shapes", [[(24, 700)], [(200, 72)]], ids=["skinny", "tiled"])
-def test_zero_gradient_and_zero_lr(shapes):
+@pytest.mark.parametrize("shapes,kernel", [([(24, 700)], 1), ([(24, 700)], 2), ([(200, 72)], 0)],
+                         ids=["skinny-owner", "skinny-chunked", "tiled"])
+def test_zero_gradient_and_zero_lr(shapes, kernel):
     import torch
-    plan = B.Plan(shapes)
+    plan = B.Plan(shapes, skinny_kernel=kernel)
     b = plan.batches[0]
     wl = WL.small_workload("z", shapes, dtype=WL.F32, momentum_recipe="zeros", wid=301)
     arrays = H.batch_arrays(wl, b)
@@ -157,12 +167,13 @@ def test_zero_gradient_and_zero_lr(shapes):
 # --------------------------------------------------------------------------
 # determinism, batch independence, transpose symmetry
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("shapes", [[(24, 3000)] * 3, [(300, 500)] * 3], ids=["skinny", "tiled"])
+@pytest.mark.parametrize("shapes,kernel", [([(24, 3000)] * 3, 1), ([(24, 3000)] * 3, 2), ([(300, 500)] * 3, 0)],
+                         ids=["skinny-owner", "skinny-chunked", "tiled"])
 @pytest.mark.parametrize("prec", PRECS)
-def test_deterministic_and_batch_independent(shapes, prec):
+def test_deterministic_and_batch_independent(shapes, kernel, prec):
     wl = WL.small_workload("d", shapes, momentum_recipe="normal", wid=302)
     h = H.c_hparams(wl.hp, precision=prec)
-    plan = B.Plan(shapes)
+    plan = B.Plan(shapes, skinny_kernel=kernel)
     b = plan.batches[0]
     arrays = H.batch_arrays(wl, b)
     r1 = H.run_gpu_step(plan, b, arrays, WL.BF16, h)
@@ -170,19 +181,20 @@ def test_deterministic_and_batch_independent(shapes, prec):
     for x, y in zip(r1, r2):
         assert np.array_equal(x, y), "run-to-run results differ"
     # each matrix alone gives bitwise the batched result
-    single = B.Plan([shapes[0]])
+    single = B.Plan([shapes[0]], skinny_kernel=kernel)
     for q in range(len(shapes)):
         one = {k: v[q:q + 1].copy() for k, v in arrays.items()}
         Wq, Mq, Oq = H.run_gpu_step(single, single.batches[0], one, WL.BF16, h)
         assert np.array_equal(Oq[0], r1[2][q]) and np.array_equal(Wq[0], r1[0][q])
 
 
-@pytest.mark.parametrize("shape", [(24, 900), (96, 260)], ids=["skinny", "tiled"])
-def test_transpose_symmetry(shape):
+@pytest.mark.parametrize("shape,kernel", [((24, 900), 1), ((24, 900), 2), ((96, 260), 0)],
+                         ids=["skinny-owner", "skinny-chunked", "tiled"])
+def test_transpose_symmetry(shape, kernel):
     """NS(G^T) = NS(G)^T: the tall matrix runs on the transpose."""
     wl = WL.small_workload("t", [shape], dtype=WL.F32, momentum_recipe="normal", wid=303)
-    plan = B.Plan([shape])
-    planT = B.Plan([shape[::-1]])
+    plan = B.Plan([shape], skinny_kernel=kernel)
+    planT = B.Plan([shape[::-1]], skinny_kernel=kernel)
     arrays = H.batch_arrays(wl, plan.batches[0])
     arraysT = {k: np.ascontiguousarray(np.swapaxes(v, 1, 2)) for k, v in arrays.items()}
     for prec in ("bf16", "f32"):
@@ -195,12 +207,13 @@ def test_transpose_symmetry(shape):
 # --------------------------------------------------------------------------
 # stage entry points
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("shapes", [[(24, 1500), (24, 1500)], [(150, 260)], [(260, 150)]],
-                         ids=["skinny", "tiled", "tiled_tall"])
-def test_stage_entry_points(shapes):
+@pytest.mark.parametrize("shapes,kernel", [([(24, 1500), (24, 1500)], 1), ([(24, 1500), (24, 1500)], 2),
+                                           ([(150, 260)], 0), ([(260, 150)], 0)],
+                         ids=["skinny-owner", "skinny-chunked", "tiled", "tiled_tall"])
+def test_stage_entry_points(shapes, kernel):
     import torch
     wl = WL.small_workload("s", shapes, dtype=WL.BF16, momentum_recipe="normal", wid=304)
-    plan = B.Plan(shapes)
+    plan = B.Plan(shapes, skinny_kernel=kernel)
     b = plan.batches[0]
     arrays = H.batch_arrays(wl, b)
     for prec in PRECS:
@@ -233,10 +246,11 @@ def test_stage_entry_points(shapes):
 # --------------------------------------------------------------------------
 # the workloads at full size
 # --------------------------------------------------------------------------
-def test_fused_74x24x10240_full():
+@pytest.mark.parametrize("kernel", [0, 1, 2], ids=["auto", "owner", "chunked"])
+def test_fused_74x24x10240_full(kernel):
     wl = WL.WORKLOADS["fused_74x24x10240"]
-    errs = check_batch(wl, H.c_hparams(wl.hp), WL.BF16)
-    print(f"fused_74x24x10240: max O error {max(errs):.3g} over {len(errs)} matrices")
+    errs = check_batch(wl, H.c_hparams(wl.hp), WL.BF16, skinny_kernel=kernel)
+    print(f"fused_74x24x10240 kernel {kernel}: max O error {max(errs):.3g} over {len(errs)} matrices")
 
 
 def test_moe_experts_skinny_full():
