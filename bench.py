@@ -59,13 +59,12 @@ def kernel_model(name, count, M, N, prec, pdt, gdt, with_ns_out=False, ns_steps=
             return "hbm", E * (gs + 4 + 4 + xs) + part + count * S * 4, "B"
         if name == "sk_ns_step":
             return "hbm", E * 2 * xs + 2 * part, "B"
-        if name == "sk_owner":      # the whole step in one launch
-            K = ns_steps
-            return "hbm", E * (gs + 8 + xs) + (K - 1) * E * 2 * xs + E * (xs + 2 * ps), "B"
         if name == "sk_bprime":
             return "hbm", part + count * 4096, "B"
-        if name == "sk_ns_step_update":
-            return "hbm", E * (xs + 2 * ps + (4 if with_ns_out else 0)) + part, "B"
+        if name == "sk_gram_ns":
+            return "hbm", part + count * S * 4 + count * 4096, "B"
+        if name == "sk_apply_update":
+            return "hbm", E * (xs + 2 * ps + (4 if with_ns_out else 0)), "B"
     else:
         if name == "tl_momentum_norm":
             return "hbm", E * (gs + 8), "B"
@@ -231,7 +230,7 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (the reference for HBM byte counters)")
     ap.add_argument("--skinny-kernel", type=int, default=0,
-                    help="short sides <= 32: 0 auto, 1 one workgroup per matrix, 2 split-K chunks")
+                    help="short sides <= 32: 0 or 1 Newton-Schulz in Gram space, 2 step by step")
     ap.add_argument("--device-inputs", action="store_true",
                     help="draw the inputs on the GPU with seeded torch generators (large workloads)")
     ap.add_argument("--reuse-shapes", action="store_true",
@@ -335,7 +334,7 @@ def main():
     value = flops / (ms / 1e3) / 1e12
     cfg = {"workload": wl.name, "matrices": int(sum(b.count for b in plan.batches)),
            "batches": [[b.count, b.M, b.N] for b in plan.batches],
-           "kernels": [["tiled", "skinny_owner", "skinny_chunked"][b.path] for b in plan.batches],
+           "kernels": [["tiled", "skinny_gram", "skinny_stepwise"][b.path] for b in plan.batches],
            "param_dtype": dtype,
            "precision": prec, "ns_steps": hp.ns_steps, "coeffs": list(hp.coeffs),
            "inputs": ("seeded synthetic, drawn on the GPU (torch generators)" if args.device_inputs else

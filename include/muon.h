@@ -68,8 +68,10 @@ typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
  *                     operands; for ill-conditioned inputs.
  *  MUON_PREC_F32      every product and every stored intermediate in fp32
  *                     (the check path).
- * Matrices whose short side is at most 32 keep the Gram matrix, the polynomial
- * and the B X product in fp32 in every mode (the products are tiny); those
+ * Matrices whose short side is at most 32 form the Gram matrix of the stored X
+ * with fp32 accumulation, run the polynomial on it in fp64 (Gram space) or
+ * fp32 (step by step) and apply it with about 16-bit (bf16 hi + lo) or fp32
+ * operands in every mode (the small products are cheap); those
  * with a short side from 33 to 127 run every product on fp32 operands in every
  * mode, because bf16 rounding of A and B costs too much accuracy there. */
 typedef enum { MUON_PREC_BF16 = 0, MUON_PREC_BF16_X32 = 1, MUON_PREC_F32 = 2 } muon_precision;
@@ -87,9 +89,11 @@ typedef struct {
                                still forms a batch of its own. */
   int32_t order;            /* 0: batches in descending element count (HyperParallel-FSDP
                                Figure 10(b)), ties in creation order; 1: creation order */
-  int32_t skinny_kernel;    /* matrices with a short side <= 32: 0 choose by a cost model (made
-                               for 5 Newton-Schulz steps); 1 one workgroup per matrix, the whole
-                               step in one launch; 2 split-K chunks over the chip, 2K+1 launches */
+  int32_t skinny_kernel;    /* matrices with a short side <= 32 (split-K chunk kernels):
+                               0 or 1 Newton-Schulz in Gram space (the iteration runs on the
+                               m x m Gram matrix and multiplies back into X once, DMuon-2
+                               Appendix C.3; 3 launches); 2 step by step, X <- B' X each step
+                               (2K+1 launches) */
 } muon_plan_options;
 
 typedef struct muon_plan muon_plan;   /* opaque, host-only, immutable */
@@ -99,8 +103,8 @@ typedef struct {
   int64_t count;            /* matrices in the batch */
   int32_t transposed;       /* 1 if M > N: Newton-Schulz runs on the transpose */
   int32_t num_segments;
-  int32_t path;             /* 0 tiled products (short side > 32); 1 one workgroup per matrix;
-                               2 split-K chunks */
+  int32_t path;             /* 0 tiled products (short side > 32); 1 skinny, Gram space;
+                               2 skinny, step by step */
   int32_t reserved;
 } muon_batch_info;
 

@@ -141,7 +141,7 @@ class BatchInfo:
     count: int
     transposed: bool
     segments: List[Tuple[int, int, int, int]]   # (param_index, first_matrix, num_matrices, elem_offset)
-    path: int = 0                               # 0 tiled, 1 skinny one workgroup per matrix, 2 skinny chunks
+    path: int = 0                               # 0 tiled, 1 skinny Gram space, 2 skinny step by step
 
     @property
     def elems(self) -> int:

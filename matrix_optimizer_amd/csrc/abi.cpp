@@ -60,11 +60,7 @@ WsLayout workspace_layout(const BatchShape& b, int prec, int path) {
     off = align256(off + bytes);
     return at;
   };
-  if (path == PATH_SKINNY_OWNER) {
-    L.skinny = true;
-    L.ldx = round_up(b.n, 64);
-    L.x = take(size_t(b.count) * b.m * L.ldx * (prec == PREC_BF16 ? 2 : 4));
-  } else if (path == PATH_SKINNY_CHUNKED) {
+  if (path == PATH_SKINNY_GRAM || path == PATH_SKINNY_STEPWISE) {
     L.skinny = true;
     const int64_t Lc = skinny_chunk(prec);
     L.ldx = round_up(b.n, Lc);
@@ -73,9 +69,9 @@ WsLayout workspace_layout(const BatchShape& b, int prec, int path) {
     const size_t xs = prec == PREC_BF16 ? 2 : 4;
     L.x = take(size_t(b.count) * b.m * L.ldx * xs);
     L.gp0 = take(size_t(b.count) * L.S * L.T * 4);
-    L.gp1 = take(size_t(b.count) * L.S * L.T * 4);
+    if (path == PATH_SKINNY_STEPWISE) L.gp1 = take(size_t(b.count) * L.S * L.T * 4);
     L.sp = take(size_t(b.count) * L.S * 4);
-    L.bfrag = take(size_t(b.count) * 64 * 64);   // B' as MFMA fragments: 64 lanes x 64 bytes
+    L.bfrag = take(size_t(b.count) * 64 * 64);   // B' or Q as MFMA fragments: 64 lanes x 64 bytes
   } else {
     L.skinny = false;
     L.mp = round_up(b.m, kTilePad);
@@ -179,8 +175,8 @@ muon_status hip_status(hipError_t e) { return e == hipSuccess ? MUON_OK : MUON_E
 
 hipError_t dispatch(const StepArgs& a, const WsLayout& L) {
   switch (L.path) {
-    case PATH_SKINNY_OWNER: return run_skinny_owner(a, L);
-    case PATH_SKINNY_CHUNKED: return run_skinny(a, L);
+    case PATH_SKINNY_GRAM:
+    case PATH_SKINNY_STEPWISE: return run_skinny(a, L);
     default: return run_tiled(a, L);
   }
 }
@@ -260,9 +256,8 @@ muon_status muon_plan_create(const muon_shape* shapes, int32_t n, const muon_pla
         b.M = M; b.N = N; b.count = (int64_t)(end - start); b.transposed = M > N;
         const int64_t m = std::min(M, N), n = std::max(M, N);
         if (m > kSkinnyMaxRows) b.path = PATH_TILED;
-        else if (skinny_kernel == 1) b.path = PATH_SKINNY_OWNER;
-        else if (skinny_kernel == 2) b.path = PATH_SKINNY_CHUNKED;
-        else b.path = skinny_path(b.count, m, n, 5);
+        else if (skinny_kernel == 2) b.path = PATH_SKINNY_STEPWISE;
+        else b.path = PATH_SKINNY_GRAM;
         for (size_t k = start; k < end; ++k) {
           const int32_t pi = mats[k].first;
           const int64_t mi = mats[k].second;

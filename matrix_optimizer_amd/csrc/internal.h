@@ -54,23 +54,12 @@ struct BatchShape {
   bool transposed;       // M > N
 };
 
+// Kernel family of a batch: tiled products (short side > 32), or the skinny
+// chunk kernels with Newton-Schulz in Gram space (3 launches) or step by step
+// (2K + 1 launches).
+enum Path { PATH_TILED = 0, PATH_SKINNY_GRAM = 1, PATH_SKINNY_STEPWISE = 2 };
+
 // Device workspace carve-up of one batch (offsets in bytes from the base).
-// Kernel family of a batch.
-enum Path { PATH_TILED = 0, PATH_SKINNY_OWNER = 1, PATH_SKINNY_CHUNKED = 2 };
-
-// Skinny path choice: one workgroup per matrix (the whole step in one launch,
-// bounded by what one CU can stream) or split-K chunks over the whole chip
-// (2K+1 launches).  Picks the smaller of two time estimates; the constants are
-// measured on MI355X (per-CU stream rate, chip-wide rate of the chunk kernels,
-// cost of one chunk-kernel launch).
-inline int skinny_path(int64_t count, int64_t m, int64_t n, int steps) {
-  const double bytes = (double)m * (double)n * (14.0 + 4.0 * steps);   // per matrix, bf16 X
-  const double waves = (double)((count + 255) / 256);
-  const double t_owner = waves * bytes / 2.7e10;
-  const double t_chunked = (2.0 * steps + 1.0) * 7e-6 + (double)count * bytes / 3.5e12;
-  return t_owner <= t_chunked ? PATH_SKINNY_OWNER : PATH_SKINNY_CHUNKED;
-}
-
 struct WsLayout {
   bool skinny = false;
   int path = PATH_TILED;
@@ -118,7 +107,6 @@ void trace_end(hipStream_t s);
 
 // Each returns hipSuccess or the first launch error.
 hipError_t run_skinny(const StepArgs& a, const WsLayout& L);
-hipError_t run_skinny_owner(const StepArgs& a, const WsLayout& L);
 hipError_t run_tiled(const StepArgs& a, const WsLayout& L);
 hipError_t run_momentum_only(const StepArgs& a);
 hipError_t run_update_only(const StepArgs& a);

@@ -3,25 +3,37 @@
 //
 // The m x m Gram matrix is tiny and the long side n is long, so the work is
 // memory-bound.  X (m x n in the Newton-Schulz orientation, rows padded to 32)
-// is cut into chunks of L columns, one workgroup per chunk.  One
-// Newton-Schulz step (HyperParallel-FSDP Eq. (1)) is two launches:
+// is cut into chunks of L columns, one workgroup per chunk.  sk_first fuses
+// momentum, the Nesterov direction U, the Frobenius-norm partials and the
+// split-K Gram partial U_c U_c^T of each chunk (bf16 MFMA, fp32 accumulation)
+// and stores U.  Two forms of Newton-Schulz follow.
 //
-//   sk_bprime  one workgroup per matrix: A = X X^T from the chunks' split-K
-//              Gram partials (summed in chunk order), A A on fp32 MFMA, and
-//              B' = a I + b A + c A A, so that X' = a X + b A X + c A^2 X is
-//              the single product B' X.  B' is written as the per-lane MFMA
-//              operand fragments the chunk kernel loads straight into
-//              registers: a bf16 hi + lo pair (the product keeps about 16
-//              bits of B'), or fp32 on the check path.
-//   sk_iter    one workgroup per chunk: stage the chunk in LDS, X' = B' X on
-//              MFMA in place, write X' back with 16-byte stores and form its
-//              Gram partial X'_c X'_c^T on MFMA for the next step; the last
-//              step applies decay and update to W instead.
+// Gram space (default).  Every step left-multiplies X by a polynomial of the
+// Gram matrix, X_{k+1} = B_k X_k with B_k = a I + b A_k + c A_k^2 (the
+// HyperParallel-FSDP Eq. (1) step), so with A_0 = X_0 X_0^T
+//   A_{k+1} = B_k A_k B_k,   X_K = (B_{K-1} ... B_0) X_0,
+// exactly in exact arithmetic (the Gram Newton-Schulz of the DMuon-2 paper,
+// Appendix C.3: iterate on the Gram matrix, multiply back into X once).  All
+// B_k are polynomials in A_0, so they commute and stay symmetric.
+//   sk_gram_ns  one workgroup per matrix: A_0 from the chunk partials (summed
+//               in chunk order, fp64), then the K steps on 32x32 fp64 MFMA,
+//               Q = B_{K-1} ... B_0 / (||U||_F + eps) written as the per-lane
+//               MFMA operand fragments of the apply kernel: a bf16 hi + lo
+//               pair (the product keeps about 16 bits of Q), or fp32 on the
+//               check path.
+//   sk_iter<LAST>  one workgroup per chunk: O = Q U on MFMA, then decoupled
+//               decay and the update of W (or O written out).
+// Three launches and two passes over X, whatever K is.
 //
-// sk_first fuses momentum, the Nesterov direction, the Frobenius-norm partials
-// and the Gram partial of U; the norm enters the first step as a scale on A
-// and B'.  X stays in the L2 / Infinity Cache between launches.  Every
-// reduction has a fixed order, so results are bitwise reproducible.
+// Step by step.  The iteration in the pages' order, K rounds of
+//   sk_bprime   one workgroup per matrix: A = X X^T from the chunk partials,
+//               A A on fp32 MFMA, B' = a I + b A + c A A as fragments;
+//   sk_iter     one workgroup per chunk: stage the chunk in LDS, X' = B' X on
+//               MFMA in place, store X' and its Gram partial for the next
+//               step; the last step applies the update instead.
+//
+// X stays in the L2 / Infinity Cache between launches.  Every reduction has a
+// fixed order, so results are bitwise reproducible.
 #include "common.h"
 #include "internal.h"
 
@@ -32,8 +44,8 @@ constexpr int SK_THREADS = 256;
 constexpr int SK_WAVES = SK_THREADS / WAVE;
 constexpr int SK_MP = 32;  // rows padded to one 32x32 MFMA block
 
-// MODE 0: X stored bf16 (bf16 operands).  MODE 1: X stored fp32, bf16 hi+lo
-// operands for B' X, bf16 operands for the Gram.  MODE 2: fp32 everywhere.
+// MODE 0: X stored bf16 (bf16 operands).  MODE 1: X stored fp32, fp32 Gram
+// operands, bf16 hi+lo operands for B' X.  MODE 2: fp32 everywhere.
 template <int MODE> struct SkCfg;
 template <> struct SkCfg<0> { typedef bf16_t XS; static constexpr int L = MUON_SK_CHUNK_BF16, LDX = L + 8; };
 template <> struct SkCfg<1> { typedef float XS; static constexpr int L = MUON_SK_CHUNK_F32, LDX = L + 4; };
@@ -84,21 +96,6 @@ __device__ void gram_partial(unsigned char* lds_raw, float* __restrict__ out, in
 #pragma unroll 4
     for (int k0 = w * KW; k0 < (w + 1) * KW; k0 += 16) {
       bf16x8 v = *reinterpret_cast<const bf16x8*>(lx + row * C::LDX + k0 + koff);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, v, acc, 0, 0, 0);
-    }
-  } else if constexpr (MODE == 1) {
-    const float* lx = reinterpret_cast<const float*>(lds_raw);
-    const int koff = (lane >> 5) * 8;
-#pragma unroll 2
-    for (int k0 = w * KW; k0 < (w + 1) * KW; k0 += 16) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(lx + row * C::LDX + k0 + koff);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(lx + row * C::LDX + k0 + koff + 4);
-      bf16x8 v;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[q] = __builtin_bit_cast(__bf16, f2bf(a[q]));
-        v[q + 4] = __builtin_bit_cast(__bf16, f2bf(b[q]));
-      }
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, v, acc, 0, 0, 0);
     }
   } else {
@@ -249,6 +246,47 @@ __device__ void apply_bx(unsigned char* lds_raw, const BFrag& fr) {
   }
 }
 
+// Fragments of a 32x32 fp32 matrix Q (zero outside m x m) in the BFrag layout,
+// one lane each; called by the 64 lanes of one wave.
+template <int MODE>
+__device__ void write_frag(const float (*Q)[SK_MP + 1], BFrag* __restrict__ out, int lane) {
+  const int row = lane & 31;
+  BFrag f;
+  if constexpr (MODE == 2) {
+    float v[16];
+#pragma unroll
+    for (int kb = 0; kb < 16; ++kb) v[kb] = Q[row][2 * kb + (lane >> 5)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      f.q[i] = make_uint4(__float_as_uint(v[4 * i]), __float_as_uint(v[4 * i + 1]), __float_as_uint(v[4 * i + 2]),
+                          __float_as_uint(v[4 * i + 3]));
+  } else {
+    uint32_t hw[8], lw[8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        uint32_t h2 = 0, l2 = 0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float v = Q[row][kb * 16 + (lane >> 5) * 8 + 2 * p + e];
+          const bf16_t h = f2bf(v);
+          const bf16_t l = f2bf(v - bf2f(h));
+          h2 |= (uint32_t)h << (16 * e);
+          l2 |= (uint32_t)l << (16 * e);
+        }
+        hw[kb * 4 + p] = h2;
+        lw[kb * 4 + p] = l2;
+      }
+    }
+    f.q[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    f.q[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+    f.q[2] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    f.q[3] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+  }
+  out[lane] = f;
+}
+
 // ---------------------------------------------------------------------------
 // B' of one Newton-Schulz step, one workgroup per matrix.
 //   first: A and B' are scaled by inv^2 and inv, inv = 1/(||U||_F + eps)
@@ -313,43 +351,150 @@ sk_bprime(const float* __restrict__ gp, const float* __restrict__ sp, int first,
     }
   }
   __syncthreads();
+  if (t < WAVE) write_frag<MODE>(Bp, bfrag + b * WAVE, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Newton-Schulz in Gram space, one workgroup per matrix (four waves).
+// ---------------------------------------------------------------------------
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+constexpr int GSD = SK_MP + 1;                 // LDS row stride of the fp64 32x32 matrices
+constexpr int GS_MAT = SK_MP * GSD;            // doubles per matrix
+constexpr int GS_STAGE = 6144;                 // floats of partials staged per round
+static_assert(GS_STAGE * 4 <= 3 * GS_MAT * 8, "partials stage must fit in the three aliased matrices");
+static_assert(SK_MP * (SK_MP + 1) / 2 <= 3 * SK_THREADS, "each thread owns at most three Gram entries");
+
+// Per-step coefficients (a_k, b_k, c_k), k < 64, passed by value.
+struct Coeffs {
+  float c[3 * 64];
+};
+
+// Block (bi, bj) of X Y, 16x16, for 32x32 fp64 X and Y in LDS, on fp64 MFMA
+// (16x16x4).  Lane l supplies X[16 bi + l%16][k + l/16] and
+// Y[k + l/16][16 bj + l%16]; register r of the result is row
+// 16 bi + 4 r + l/16, column 16 bj + l%16.
+__device__ __forceinline__ f64x4 mul_blk(const double* X, const double* Y, int bi, int bj, int lane) {
+  f64x4 acc = {0., 0., 0., 0.};
+  const int i = 16 * bi + (lane & 15), j = 16 * bj + (lane & 15), g = lane >> 4;
+#pragma unroll
+  for (int k0 = 0; k0 < SK_MP; k0 += 4)
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(X[i * GSD + k0 + g], Y[(k0 + g) * GSD + j], acc, 0, 0, 0);
+  return acc;
+}
+__device__ __forceinline__ int blk_row(int bi, int r, int lane) { return 16 * bi + 4 * r + (lane >> 4); }
+__device__ __forceinline__ int blk_col(int bj, int lane) { return 16 * bj + (lane & 15); }
+__device__ __forceinline__ void put_blk(double* Z, const f64x4& v, int bi, int bj, int lane) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) Z[blk_row(bi, r, lane) * GSD + blk_col(bj, lane)] = v[r];
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(SK_THREADS)
+sk_gram_ns(const float* __restrict__ gp, const float* __restrict__ sp, float eps, int m, int S, int T, int steps,
+           Coeffs cf, BFrag* __restrict__ bfrag) {
+  __shared__ double mats[4 * GS_MAT];   // A | B | P | Tm; the partials stage aliases B, P and Tm
+  __shared__ float Qf[SK_MP][SK_MP + 1];
+  __shared__ double inv_s;
+  double* A = mats;
+  double* Bm = mats + GS_MAT;
+  double* P = mats + 2 * GS_MAT;
+  double* Tm = mats + 3 * GS_MAT;
+  float* stage = reinterpret_cast<float*>(Bm);
+
+  const int64_t b = blockIdx.x;
+  const int t = threadIdx.x;
+  const int lane = t & (WAVE - 1);
+  for (int e = t; e < GS_MAT; e += SK_THREADS) A[e] = 0.;
   if (t < WAVE) {
-    const int row = lane & 31;
-    BFrag f;
-    if constexpr (MODE == 2) {
-      float v[16];
+    // 1 / (||U||_F + eps) from the chunk norm partials, fp64
+    double v = 0.;
+    for (int q = lane; q < S; q += WAVE) v += (double)sp[b * S + q];
 #pragma unroll
-      for (int kb = 0; kb < 16; ++kb) v[kb] = Bp[row][2 * kb + (lane >> 5)];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        f.q[i] = make_uint4(__float_as_uint(v[4 * i]), __float_as_uint(v[4 * i + 1]), __float_as_uint(v[4 * i + 2]),
-                            __float_as_uint(v[4 * i + 3]));
-    } else {
-      uint32_t hw[8], lw[8];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          uint32_t h2 = 0, l2 = 0;
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const float v = Bp[row][kb * 16 + (lane >> 5) * 8 + 2 * p + e];
-            const bf16_t h = f2bf(v);
-            const bf16_t l = f2bf(v - bf2f(h));
-            h2 |= (uint32_t)h << (16 * e);
-            l2 |= (uint32_t)l << (16 * e);
-          }
-          hw[kb * 4 + p] = h2;
-          lw[kb * 4 + p] = l2;
-        }
-      }
-      f.q[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      f.q[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
-      f.q[2] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-      f.q[3] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
-    }
-    bfrag[b * WAVE + lane] = f;
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    const double den = sqrt(v) + (double)eps;
+    if (lane == 0) inv_s = den > 0. ? 1. / den : 0.;
   }
+
+  // A_0 entries: thread t owns packed entries t, t + 256, t + 512 and adds the
+  // chunk partials in chunk order; the partials pass through LDS in rounds.
+  double acc[3] = {0., 0., 0.};
+  const float* g = gp + b * (int64_t)S * T;
+  const int qb = GS_STAGE / T;
+  for (int q0 = 0; q0 < S; q0 += qb) {
+    const int nq = S - q0 < qb ? S - q0 : qb;
+    const int tot = nq * T;
+    const float* src = g + (int64_t)q0 * T;
+    for (int f0 = 0; f0 < tot; f0 += 8 * SK_THREADS) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int f = f0 + t + SK_THREADS * i;
+        v[i] = f < tot ? src[f] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int f = f0 + t + SK_THREADS * i;
+        if (f < tot) stage[f] = v[i];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const int e = t + SK_THREADS * u;
+      if (e < T)
+        for (int q = 0; q < nq; ++q) acc[u] += (double)stage[q * T + e];
+    }
+    __syncthreads();
+  }
+  const double inv = inv_s;
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    const int e = t + SK_THREADS * u;
+    if (e < T) {
+      int r, s;
+      tri_rc(e, r, s);
+      const double v = acc[u] * inv * inv;
+      A[r * GSD + s] = v;
+      A[s * GSD + r] = v;
+    }
+  }
+  for (int e = t; e < GS_MAT; e += SK_THREADS) P[e] = (e / GSD == e % GSD) ? 1. : 0.;
+  __syncthreads();
+
+  // K steps; wave w owns output block (w / 2, w % 2) of every product.
+  // Padded rows and columns of A stay zero; B and P are a multiple of I there.
+  const int w = t / WAVE, bi = w >> 1, bj = w & 1;
+  for (int k = 0; k < steps; ++k) {
+    const double ca = cf.c[3 * k], cb = cf.c[3 * k + 1], cc = cf.c[3 * k + 2];
+    const f64x4 a2 = mul_blk(A, A, bi, bj, lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = blk_row(bi, r, lane), j = blk_col(bj, lane);
+      Bm[i * GSD + j] = (i == j ? ca : 0.) + cb * A[i * GSD + j] + cc * a2[r];
+    }
+    __syncthreads();
+    const bool more = k + 1 < steps;
+    const f64x4 pn = mul_blk(Bm, P, bi, bj, lane);      // P <- B_k P
+    f64x4 tn = {0., 0., 0., 0.};
+    if (more) tn = mul_blk(A, Bm, bi, bj, lane);       // A_k B_k
+    __syncthreads();
+    put_blk(P, pn, bi, bj, lane);
+    if (more) put_blk(Tm, tn, bi, bj, lane);
+    __syncthreads();
+    if (more) {
+      put_blk(A, mul_blk(Tm, Bm, bi, bj, lane), bi, bj, lane);   // A_{k+1} = B_k A_k B_k
+      __syncthreads();
+    }
+  }
+
+  // Q = P / (||U||_F + eps): the result applies to the stored, unnormalised U
+  for (int e = t; e < SK_MP * SK_MP; e += SK_THREADS) {
+    const int i = e / SK_MP, j = e % SK_MP;
+    Qf[i][j] = (i < m && j < m) ? (float)(inv * P[i * GSD + j]) : 0.f;
+  }
+  __syncthreads();
+  if (t < WAVE) write_frag<MODE>(Qf, bfrag + b * WAVE, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -607,7 +752,7 @@ hipError_t launch_iters(const StepArgs& a, const WsLayout& L, int vec) {
                   (const BFrag*)bfrag, gp[(k + 1) & 1], (int)sh.m, sh.n, L.ldx, (int)L.S, (int)L.T,
                   (int)sh.transposed, vec, param, a.ns_out, a.lr, a.wd, a.s);
     else
-      MUON_LAUNCH("sk_ns_step_update", (sk_iter<MODE, PT, true>), grid, block, a.stream, (XS*)(a.ws + L.x),
+      MUON_LAUNCH("sk_apply_update", (sk_iter<MODE, PT, true>), grid, block, a.stream, (XS*)(a.ws + L.x),
                   (const BFrag*)bfrag, gp[(k + 1) & 1], (int)sh.m, sh.n, L.ldx, (int)L.S, (int)L.T,
                   (int)sh.transposed, vec, param, a.ns_out, a.lr, a.wd, a.s);
     e = hipGetLastError();
@@ -616,10 +761,31 @@ hipError_t launch_iters(const StepArgs& a, const WsLayout& L, int vec) {
   return hipSuccess;
 }
 
+template <int MODE, typename PT>
+hipError_t launch_gram(const StepArgs& a, const WsLayout& L, int vec) {
+  typedef typename SkCfg<MODE>::XS XS;
+  const BatchShape& sh = a.shape;
+  if (a.steps < 0 || a.steps > 64 || (int)a.coeffs.size() < 3 * a.steps) return hipErrorInvalidValue;
+  Coeffs cf = {};
+  for (int i = 0; i < 3 * a.steps; ++i) cf.c[i] = a.coeffs[i];
+  BFrag* bfrag = (BFrag*)(a.ws + L.bfrag);
+  MUON_LAUNCH("sk_gram_ns", (sk_gram_ns<MODE>), dim3((unsigned)sh.count), dim3(SK_THREADS), a.stream,
+              (const float*)(a.ws + L.gp0), (const float*)(a.ws + L.sp), a.eps, (int)sh.m, (int)L.S, (int)L.T,
+              a.steps, cf, bfrag);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  PT* param = a.phase == PH_FULL ? (PT*)a.param : nullptr;
+  MUON_LAUNCH("sk_apply_update", (sk_iter<MODE, PT, true>), dim3((unsigned)(sh.count * L.S)), dim3(SK_THREADS),
+              a.stream, (XS*)(a.ws + L.x), (const BFrag*)bfrag, (float*)nullptr, (int)sh.m, sh.n, L.ldx, (int)L.S,
+              (int)L.T, (int)sh.transposed, vec, param, a.ns_out, a.lr, a.wd, a.s);
+  return hipGetLastError();
+}
+
 template <int MODE>
 hipError_t run_mode(const StepArgs& a, const WsLayout& L) {
   // the workspace carve-up and the kernels must agree on the chunk width
   if (L.S * SkCfg<MODE>::L != L.ldx || L.ldx < a.shape.n) return hipErrorInvalidValue;
+  if (L.T != a.shape.m * (a.shape.m + 1) / 2 || a.shape.m > SK_MP) return hipErrorInvalidValue;
   const int mode = a.phase == PH_FULL ? 0 : 1;
   // 16-byte vectors along stored rows need rows = X rows and 8 | n
   const int vec = (!a.shape.transposed && a.shape.n % 8 == 0) ? 1 : 0;
@@ -627,6 +793,8 @@ hipError_t run_mode(const StepArgs& a, const WsLayout& L) {
                                          : launch_first<MODE, float>(a, L, mode, vec);
   if (e != hipSuccess) return e;
   const bool pbf = (a.phase == PH_FULL && a.param_dtype == DT_BF16);
+  if (L.path == PATH_SKINNY_GRAM)
+    return pbf ? launch_gram<MODE, bf16_t>(a, L, vec) : launch_gram<MODE, float>(a, L, vec);
   return pbf ? launch_iters<MODE, bf16_t>(a, L, vec) : launch_iters<MODE, float>(a, L, vec);
 }
 

@@ -93,18 +93,22 @@ def test_plan_errors():
 
 
 def test_batch_paths():
-    # short side <= 32: one of the two skinny kernels; the plan option forces either
+    # short side <= 32: Gram-space skinny kernels by default; option 2 forces step by step
     p = B.Plan([(24, 10240)] * 74 + [(300, 200)])
     paths = {(b.M, b.N): b.path for b in p.batches}
-    assert paths[(300, 200)] == 0 and paths[(24, 10240)] in (1, 2)
-    assert all(b.path in (0, 1) for b in B.Plan([(24, 10240)] * 4 + [(64, 64)], skinny_kernel=1).batches)
+    assert paths[(300, 200)] == 0 and paths[(24, 10240)] == 1
+    assert sorted(b.path for b in B.Plan([(24, 10240)] * 4 + [(64, 64)], skinny_kernel=1).batches) == [0, 1]
     assert [b.path for b in B.Plan([(24, 10240)], skinny_kernel=2).batches] == [2]
-    # one matrix with an enormous long side goes to the chip-wide chunks
-    assert [b.path for b in B.Plan([(8, 1 << 24)]).batches] == [2]
+    assert [b.path for b in B.Plan([(10240, 32)], skinny_kernel=2).batches] == [2]
+    assert [b.path for b in B.Plan([(33, 10240)], skinny_kernel=2).batches] == [0]
+    assert [b.path for b in B.Plan([(8, 1 << 24)]).batches] == [1]
     for k in (1, 2):
         q = B.Plan([(24, 1000)] * 3, skinny_kernel=k)
         for prec in ("bf16", "bf16_x32", "f32"):
             assert q.workspace_bytes(0, prec) % 256 == 0
+    # the step-by-step form keeps a second set of Gram partials
+    g, s = B.Plan([(24, 1000)] * 3, skinny_kernel=1), B.Plan([(24, 1000)] * 3, skinny_kernel=2)
+    assert s.workspace_bytes(0, "bf16") > g.workspace_bytes(0, "bf16")
 
 
 def test_workspace_bytes():

@@ -104,7 +104,7 @@ def _skinny(name):
     return all(min(WL.ParamSpec("x", tuple(s)).matrix_shape) <= 32 for s in SHAPE_SETS[name])
 
 
-# skinny shapes run through both skinny kernels: 1 = one workgroup per matrix, 2 = split-K chunks
+# skinny shapes run through both Newton-Schulz forms: 1 = Gram space, 2 = step by step
 SHAPE_CASES = [(n, k) for n in sorted(SHAPE_SETS) for k in ((1, 2) if _skinny(n) else (0,))]
 
 
@@ -141,7 +141,7 @@ def test_hparam_variants(shapes, variant):
 # special cases
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("shapes,kernel", [([(24, 700)], 1), ([(24, 700)], 2), ([(200, 72)], 0)],
-                         ids=["skinny-owner", "skinny-chunked", "tiled"])
+                         ids=["skinny-gram", "skinny-stepwise", "tiled"])
 def test_zero_gradient_and_zero_lr(shapes, kernel):
     import torch
     plan = B.Plan(shapes, skinny_kernel=kernel)
@@ -168,7 +168,7 @@ def test_zero_gradient_and_zero_lr(shapes, kernel):
 # determinism, batch independence, transpose symmetry
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("shapes,kernel", [([(24, 3000)] * 3, 1), ([(24, 3000)] * 3, 2), ([(300, 500)] * 3, 0)],
-                         ids=["skinny-owner", "skinny-chunked", "tiled"])
+                         ids=["skinny-gram", "skinny-stepwise", "tiled"])
 @pytest.mark.parametrize("prec", PRECS)
 def test_deterministic_and_batch_independent(shapes, kernel, prec):
     wl = WL.small_workload("d", shapes, momentum_recipe="normal", wid=302)
@@ -189,7 +189,7 @@ def test_deterministic_and_batch_independent(shapes, kernel, prec):
 
 
 @pytest.mark.parametrize("shape,kernel", [((24, 900), 1), ((24, 900), 2), ((96, 260), 0)],
-                         ids=["skinny-owner", "skinny-chunked", "tiled"])
+                         ids=["skinny-gram", "skinny-stepwise", "tiled"])
 def test_transpose_symmetry(shape, kernel):
     """NS(G^T) = NS(G)^T: the tall matrix runs on the transpose."""
     wl = WL.small_workload("t", [shape], dtype=WL.F32, momentum_recipe="normal", wid=303)
@@ -209,7 +209,7 @@ def test_transpose_symmetry(shape, kernel):
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("shapes,kernel", [([(24, 1500), (24, 1500)], 1), ([(24, 1500), (24, 1500)], 2),
                                            ([(150, 260)], 0), ([(260, 150)], 0)],
-                         ids=["skinny-owner", "skinny-chunked", "tiled", "tiled_tall"])
+                         ids=["skinny-gram", "skinny-stepwise", "tiled", "tiled_tall"])
 def test_stage_entry_points(shapes, kernel):
     import torch
     wl = WL.small_workload("s", shapes, dtype=WL.BF16, momentum_recipe="normal", wid=304)
@@ -246,7 +246,7 @@ def test_stage_entry_points(shapes, kernel):
 # --------------------------------------------------------------------------
 # the workloads at full size
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("kernel", [0, 1, 2], ids=["auto", "owner", "chunked"])
+@pytest.mark.parametrize("kernel", [0, 2], ids=["gram", "stepwise"])
 def test_fused_74x24x10240_full(kernel):
     wl = WL.WORKLOADS["fused_74x24x10240"]
     errs = check_batch(wl, H.c_hparams(wl.hp), WL.BF16, skinny_kernel=kernel)
