@@ -67,7 +67,10 @@ WsLayout workspace_layout(const BatchShape& b, int prec, int path) {
     L.S = L.ldx / Lc;
     L.T = b.m * (b.m + 1) / 2;
     const size_t xs = prec == PREC_BF16 ? 2 : 4;
-    L.x = take(size_t(b.count) * b.m * L.ldx * xs);
+    if (path == PATH_SKINNY_GRAM)   // U as 32-column x 8-row MFMA tiles
+      L.x = take(size_t(b.count) * size_t((b.n + 31) / 32) * size_t((b.m + 7) / 8) * 256 * xs);
+    else                            // X row-major, row stride ldx
+      L.x = take(size_t(b.count) * b.m * L.ldx * xs);
     L.gp0 = take(size_t(b.count) * L.S * L.T * 4);
     if (path == PATH_SKINNY_STEPWISE) L.gp1 = take(size_t(b.count) * L.S * L.T * 4);
     L.sp = take(size_t(b.count) * L.S * 4);

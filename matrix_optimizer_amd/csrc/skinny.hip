@@ -34,6 +34,8 @@
 //
 // X stays in the L2 / Infinity Cache between launches.  Every reduction has a
 // fixed order, so results are bitwise reproducible.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -170,6 +172,48 @@ __device__ void chunk_store(typename SkCfg<MODE>::XS* __restrict__ dst, const un
   }
 }
 
+// Gram path: U in MFMA-ready tiles.  For matrix b, 32-column block jb and
+// 8-row group g, a 256-element tile holds X[8 g + t][32 jb + c] at c * 8 + t;
+// tiles are ordered (b, jb, g), NB = ceil(n / 32) blocks, G = ceil(m / 8)
+// groups.  Rows >= m and columns >= n hold zeros.  A lane's MFMA operand (8
+// rows of one column) is one contiguous 16- or 32-byte run, and the 64 lanes
+// of a wave read 1 or 2 KB in one piece.
+__device__ __forceinline__ int64_t xg_tile(int64_t b, int64_t jb, int g, int64_t NB, int G) {
+  return ((b * NB + jb) * G + g) * 256;
+}
+
+// Staged chunk (columns [32 jb0, 32 jb0 + L)) -> tiles.
+template <int MODE>
+__device__ void chunk_store_xg(typename SkCfg<MODE>::XS* __restrict__ xg, const unsigned char* lds_raw, int64_t b,
+                               int64_t jb0, int64_t NB, int G) {
+  typedef SkCfg<MODE> C;
+  typedef typename C::XS XS;
+  const XS* lx = reinterpret_cast<const XS*>(lds_raw);
+  constexpr int NBC = C::L / 32;
+  const int nb = (int)(NB - jb0 < NBC ? NB - jb0 : NBC);
+  for (int v = threadIdx.x; v < nb * G * 32; v += SK_THREADS) {
+    const int c = v & 31, g = (v >> 5) % G, jl = (v >> 5) / G;
+    const XS* src = lx + (8 * g) * C::LDX + jl * 32 + c;
+    XS* dst = xg + xg_tile(b, jb0 + jl, g, NB, G) + c * 8;
+    if constexpr (sizeof(XS) == 2) {
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        w[q] = (uint32_t)src[(2 * q) * C::LDX] | ((uint32_t)src[(2 * q + 1) * C::LDX] << 16);
+      *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+    } else {
+      f32x4 lo, hi;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        lo[q] = src[q * C::LDX];
+        hi[q] = src[(q + 4) * C::LDX];
+      }
+      *reinterpret_cast<f32x4*>(dst) = lo;
+      *reinterpret_cast<f32x4*>(dst + 4) = hi;
+    }
+  }
+}
+
 // B' fragments of one lane, as written by sk_bprime and read by sk_iter:
 // 64 bytes per lane, 4 KB per matrix.
 //   bf16 modes: hi[kb][t], lo[kb][t] = B'[lane%32][kb*16 + (lane/32)*8 + t]  (kb < 2, t < 8)
@@ -247,15 +291,17 @@ __device__ void apply_bx(unsigned char* lds_raw, const BFrag& fr) {
 }
 
 // Fragments of a 32x32 fp32 matrix Q (zero outside m x m) in the BFrag layout,
-// one lane each; called by the 64 lanes of one wave.
-template <int MODE>
+// one lane each; called by the 64 lanes of one wave.  HALVES (fp32 only): the
+// K slot (kb, lane/32) is column 16 (lane/32) + kb instead of 2 kb + lane/32,
+// so that a lane's 16 slots are 16 consecutive rows of X.
+template <int MODE, bool HALVES = false>
 __device__ void write_frag(const float (*Q)[SK_MP + 1], BFrag* __restrict__ out, int lane) {
   const int row = lane & 31;
   BFrag f;
   if constexpr (MODE == 2) {
     float v[16];
 #pragma unroll
-    for (int kb = 0; kb < 16; ++kb) v[kb] = Q[row][2 * kb + (lane >> 5)];
+    for (int kb = 0; kb < 16; ++kb) v[kb] = Q[row][HALVES ? 16 * (lane >> 5) + kb : 2 * kb + (lane >> 5)];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       f.q[i] = make_uint4(__float_as_uint(v[4 * i]), __float_as_uint(v[4 * i + 1]), __float_as_uint(v[4 * i + 2]),
@@ -355,14 +401,17 @@ sk_bprime(const float* __restrict__ gp, const float* __restrict__ sp, int first,
 }
 
 // ---------------------------------------------------------------------------
-// Newton-Schulz in Gram space, one workgroup per matrix (four waves).
+// Newton-Schulz in Gram space, one workgroup per matrix (four waves).  The
+// 32x32 products run on 16x16x4 MFMA in fp32 (bf16 modes: the recurrence's
+// rounding stays near 1e-6 of O, far below what bf16 operands cost) or in
+// fp64 (fp32 check path).
 // ---------------------------------------------------------------------------
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-constexpr int GSD = SK_MP + 1;                 // LDS row stride of the fp64 32x32 matrices
-constexpr int GS_MAT = SK_MP * GSD;            // doubles per matrix
+constexpr int GSD = SK_MP + 1;                 // LDS row stride of the 32x32 matrices
+constexpr int GS_MAT = SK_MP * GSD;            // elements per matrix
 constexpr int GS_STAGE = 6144;                 // floats of partials staged per round
-static_assert(GS_STAGE * 4 <= 3 * GS_MAT * 8, "partials stage must fit in the three aliased matrices");
+static_assert(GS_STAGE % SK_THREADS == 0, "whole rounds of loads");
 static_assert(SK_MP * (SK_MP + 1) / 2 <= 3 * SK_THREADS, "each thread owns at most three Gram entries");
 
 // Per-step coefficients (a_k, b_k, c_k), k < 64, passed by value.
@@ -370,42 +419,93 @@ struct Coeffs {
   float c[3 * 64];
 };
 
-// Block (bi, bj) of X Y, 16x16, for 32x32 fp64 X and Y in LDS, on fp64 MFMA
-// (16x16x4).  Lane l supplies X[16 bi + l%16][k + l/16] and
-// Y[k + l/16][16 bj + l%16]; register r of the result is row
-// 16 bi + 4 r + l/16, column 16 bj + l%16.
-__device__ __forceinline__ f64x4 mul_blk(const double* X, const double* Y, int bi, int bj, int lane) {
-  f64x4 acc = {0., 0., 0., 0.};
+// 16x16x4 MFMA per scalar type.  Lane l supplies X[l%16][k + l/16] and
+// Y[k + l/16][l%16]; the result's register r is column l%16 and row row(r, l)
+// (the two types place rows differently).
+template <typename R> struct Mf;
+template <> struct Mf<double> {
+  typedef f64x4 V;
+  static __device__ __forceinline__ V mma(double a, double b, V c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ int row(int r, int lane) { return 4 * r + (lane >> 4); }
+};
+template <> struct Mf<float> {
+  typedef f32x4 V;
+  static __device__ __forceinline__ V mma(float a, float b, V c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ int row(int r, int lane) { return 4 * (lane >> 4) + r; }
+};
+
+// Block (bi, bj), 16x16, of X Y for 32x32 X, Y in LDS; only k < KM
+// contributes (rows and columns >= m are zero padding).
+template <typename R, int KM>
+__device__ __forceinline__ typename Mf<R>::V mul_blk(const R* X, const R* Y, int bi, int bj, int lane) {
+  typename Mf<R>::V acc = {};
   const int i = 16 * bi + (lane & 15), j = 16 * bj + (lane & 15), g = lane >> 4;
 #pragma unroll
-  for (int k0 = 0; k0 < SK_MP; k0 += 4)
-    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(X[i * GSD + k0 + g], Y[(k0 + g) * GSD + j], acc, 0, 0, 0);
+  for (int k0 = 0; k0 < KM; k0 += 4) acc = Mf<R>::mma(X[i * GSD + k0 + g], Y[(k0 + g) * GSD + j], acc);
   return acc;
 }
-__device__ __forceinline__ int blk_row(int bi, int r, int lane) { return 16 * bi + 4 * r + (lane >> 4); }
-__device__ __forceinline__ int blk_col(int bj, int lane) { return 16 * bj + (lane & 15); }
-__device__ __forceinline__ void put_blk(double* Z, const f64x4& v, int bi, int bj, int lane) {
+template <typename R>
+__device__ __forceinline__ void put_blk(R* Z, const typename Mf<R>::V& v, int bi, int bj, int lane) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) Z[blk_row(bi, r, lane) * GSD + blk_col(bj, lane)] = v[r];
+  for (int r = 0; r < 4; ++r) Z[(16 * bi + Mf<R>::row(r, lane)) * GSD + 16 * bj + (lane & 15)] = v[r];
+}
+
+// The K steps on A (= A_0 in, overwritten) and P (= I in, B_{K-1} ... B_0
+// out); wave w owns output block (w / 2, w % 2) of every product.  Padded
+// rows and columns of A stay zero and never reach the m x m corner of P.
+template <typename R, int KM>
+__device__ void gram_steps(R* A, R* Bm, R* P, R* Tm, int steps, const Coeffs& cf) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int w = threadIdx.x / WAVE, bi = w >> 1, bj = w & 1;
+  for (int k = 0; k < steps; ++k) {
+    const R ca = cf.c[3 * k], cb = cf.c[3 * k + 1], cc = cf.c[3 * k + 2];
+    const typename Mf<R>::V a2 = mul_blk<R, KM>(A, A, bi, bj, lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * bi + Mf<R>::row(r, lane), j = 16 * bj + (lane & 15);
+      Bm[i * GSD + j] = (i == j ? ca : R(0)) + cb * A[i * GSD + j] + cc * a2[r];
+    }
+    __syncthreads();
+    const bool more = k + 1 < steps;
+    const typename Mf<R>::V pn = mul_blk<R, KM>(Bm, P, bi, bj, lane);   // P <- B_k P
+    typename Mf<R>::V tn = {};
+    if (more) tn = mul_blk<R, KM>(A, Bm, bi, bj, lane);                 // A_k B_k
+    __syncthreads();
+    put_blk<R>(P, pn, bi, bj, lane);
+    if (more) put_blk<R>(Tm, tn, bi, bj, lane);
+    __syncthreads();
+    if (more) {
+      put_blk<R>(A, mul_blk<R, KM>(Tm, Bm, bi, bj, lane), bi, bj, lane);   // A_{k+1} = B_k A_k B_k
+      __syncthreads();
+    }
+  }
 }
 
 template <int MODE>
 __global__ void __launch_bounds__(SK_THREADS)
 sk_gram_ns(const float* __restrict__ gp, const float* __restrict__ sp, float eps, int m, int S, int T, int steps,
            Coeffs cf, BFrag* __restrict__ bfrag) {
-  __shared__ double mats[4 * GS_MAT];   // A | B | P | Tm; the partials stage aliases B, P and Tm
+  typedef typename std::conditional<MODE == 2, double, float>::type R;
+  constexpr int MATB = GS_MAT * (int)sizeof(R);
+  constexpr int RAW = 4 * MATB > MATB + 4 * GS_STAGE ? 4 * MATB : MATB + 4 * GS_STAGE;
+  // A | B | P | Tm; the partials stage aliases B, P and Tm (and beyond)
+  __shared__ __attribute__((aligned(16))) unsigned char raw[RAW];
   __shared__ float Qf[SK_MP][SK_MP + 1];
   __shared__ double inv_s;
-  double* A = mats;
-  double* Bm = mats + GS_MAT;
-  double* P = mats + 2 * GS_MAT;
-  double* Tm = mats + 3 * GS_MAT;
-  float* stage = reinterpret_cast<float*>(Bm);
+  R* A = reinterpret_cast<R*>(raw);
+  R* Bm = A + GS_MAT;
+  R* P = A + 2 * GS_MAT;
+  R* Tm = A + 3 * GS_MAT;
+  float* stage = reinterpret_cast<float*>(raw + MATB);
 
   const int64_t b = blockIdx.x;
   const int t = threadIdx.x;
   const int lane = t & (WAVE - 1);
-  for (int e = t; e < GS_MAT; e += SK_THREADS) A[e] = 0.;
+  for (int e = t; e < GS_MAT; e += SK_THREADS) A[e] = R(0);
   if (t < WAVE) {
     // 1 / (||U||_F + eps) from the chunk norm partials, fp64
     double v = 0.;
@@ -417,26 +517,26 @@ sk_gram_ns(const float* __restrict__ gp, const float* __restrict__ sp, float eps
   }
 
   // A_0 entries: thread t owns packed entries t, t + 256, t + 512 and adds the
-  // chunk partials in chunk order; the partials pass through LDS in rounds.
+  // chunk partials in chunk order (fp64); the partials pass through LDS in
+  // rounds of up to GS_STAGE floats, all loads of a round in flight at once.
   double acc[3] = {0., 0., 0.};
   const float* g = gp + b * (int64_t)S * T;
   const int qb = GS_STAGE / T;
+  constexpr int PER = GS_STAGE / SK_THREADS;
   for (int q0 = 0; q0 < S; q0 += qb) {
     const int nq = S - q0 < qb ? S - q0 : qb;
     const int tot = nq * T;
     const float* src = g + (int64_t)q0 * T;
-    for (int f0 = 0; f0 < tot; f0 += 8 * SK_THREADS) {
-      float v[8];
+    float v[PER];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int f = f0 + t + SK_THREADS * i;
-        v[i] = f < tot ? src[f] : 0.f;
-      }
+    for (int i = 0; i < PER; ++i) {
+      const int f = t + SK_THREADS * i;
+      v[i] = f < tot ? src[f] : 0.f;
+    }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int f = f0 + t + SK_THREADS * i;
-        if (f < tot) stage[f] = v[i];
-      }
+    for (int i = 0; i < PER; ++i) {
+      const int f = t + SK_THREADS * i;
+      if (f < tot) stage[f] = v[i];
     }
     __syncthreads();
 #pragma unroll
@@ -454,47 +554,28 @@ sk_gram_ns(const float* __restrict__ gp, const float* __restrict__ sp, float eps
     if (e < T) {
       int r, s;
       tri_rc(e, r, s);
-      const double v = acc[u] * inv * inv;
+      const R v = (R)(acc[u] * inv * inv);
       A[r * GSD + s] = v;
       A[s * GSD + r] = v;
     }
   }
-  for (int e = t; e < GS_MAT; e += SK_THREADS) P[e] = (e / GSD == e % GSD) ? 1. : 0.;
+  for (int e = t; e < GS_MAT; e += SK_THREADS) P[e] = (e / GSD == e % GSD) ? R(1) : R(0);
   __syncthreads();
 
-  // K steps; wave w owns output block (w / 2, w % 2) of every product.
-  // Padded rows and columns of A stay zero; B and P are a multiple of I there.
-  const int w = t / WAVE, bi = w >> 1, bj = w & 1;
-  for (int k = 0; k < steps; ++k) {
-    const double ca = cf.c[3 * k], cb = cf.c[3 * k + 1], cc = cf.c[3 * k + 2];
-    const f64x4 a2 = mul_blk(A, A, bi, bj, lane);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = blk_row(bi, r, lane), j = blk_col(bj, lane);
-      Bm[i * GSD + j] = (i == j ? ca : 0.) + cb * A[i * GSD + j] + cc * a2[r];
-    }
-    __syncthreads();
-    const bool more = k + 1 < steps;
-    const f64x4 pn = mul_blk(Bm, P, bi, bj, lane);      // P <- B_k P
-    f64x4 tn = {0., 0., 0., 0.};
-    if (more) tn = mul_blk(A, Bm, bi, bj, lane);       // A_k B_k
-    __syncthreads();
-    put_blk(P, pn, bi, bj, lane);
-    if (more) put_blk(Tm, tn, bi, bj, lane);
-    __syncthreads();
-    if (more) {
-      put_blk(A, mul_blk(Tm, Bm, bi, bj, lane), bi, bj, lane);   // A_{k+1} = B_k A_k B_k
-      __syncthreads();
-    }
+  switch ((m + 7) >> 3) {
+    case 1: gram_steps<R, 8>(A, Bm, P, Tm, steps, cf); break;
+    case 2: gram_steps<R, 16>(A, Bm, P, Tm, steps, cf); break;
+    case 3: gram_steps<R, 24>(A, Bm, P, Tm, steps, cf); break;
+    default: gram_steps<R, 32>(A, Bm, P, Tm, steps, cf); break;
   }
 
   // Q = P / (||U||_F + eps): the result applies to the stored, unnormalised U
   for (int e = t; e < SK_MP * SK_MP; e += SK_THREADS) {
     const int i = e / SK_MP, j = e % SK_MP;
-    Qf[i][j] = (i < m && j < m) ? (float)(inv * P[i * GSD + j]) : 0.f;
+    Qf[i][j] = (i < m && j < m) ? (float)(inv * (double)P[i * GSD + j]) : 0.f;
   }
   __syncthreads();
-  if (t < WAVE) write_frag<MODE>(Qf, bfrag + b * WAVE, lane);
+  if (t < WAVE) write_frag<MODE, true>(Qf, bfrag + b * WAVE, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -503,12 +584,14 @@ sk_gram_ns(const float* __restrict__ gp, const float* __restrict__ sp, float eps
 //   mode 0: M' = mu M + G (in place), U = G + mu M' (or M' without Nesterov)
 //   mode 1: U read from u_in
 // vec: stored rows are X rows and n % 8 == 0 (16-byte vectors along rows).
+// XG: U goes out as MFMA-ready tiles (Gram path), else row-major [m, ldx].
 // ---------------------------------------------------------------------------
-template <int MODE, typename GT>
+template <int MODE, typename GT, bool XG>
 __global__ void __launch_bounds__(SK_THREADS)
 sk_first(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const float* __restrict__ u_in,
          typename SkCfg<MODE>::XS* __restrict__ xws, float* __restrict__ gp_out, float* __restrict__ sp,
-         int m, int64_t n, int64_t ldx, int S, int T, int transposed, int vec, float mu, int nesterov) {
+         int m, int64_t n, int64_t ldx, int S, int T, int transposed, int vec, float mu, int nesterov,
+         int64_t NB, int G) {
   typedef SkCfg<MODE> C;
   typedef typename C::XS XS;
   __shared__ __attribute__((aligned(16))) unsigned char lds_raw[SkLds<MODE>::BYTES];
@@ -606,7 +689,8 @@ sk_first(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const f
   }
   const float tot = block_sum(ss, wsum);   // includes a barrier: the tile is complete
   if (threadIdx.x == 0) sp[blk] = tot;
-  chunk_store<MODE>(xws + b * m * ldx + j0, lds_raw, m, ldx);
+  if constexpr (XG) chunk_store_xg<MODE>(xws, lds_raw, b, j0 / 32, NB, G);
+  else chunk_store<MODE>(xws + b * m * ldx + j0, lds_raw, m, ldx);
   gram_partial<MODE>(lds_raw, gp_out + blk * T, T);
 }
 
@@ -719,15 +803,289 @@ sk_iter(typename SkCfg<MODE>::XS* __restrict__ xws, const BFrag* __restrict__ bf
   }
 }
 
+// ---------------------------------------------------------------------------
+// Gram path, last kernel: O = Q U and the update, one wave per 64 columns (two
+// 32-column blocks) of one matrix, no workgroup barriers.  The U operand comes
+// straight from the tiles, Q from the fragments.
+//   Row-major W (!TRANS): O^T = U^T Q^T (the same registers, operands
+//   swapped); the accumulators go to a wave-private LDS buffer as 16-byte
+//   quads (4 consecutive columns of one row), and W is read, updated and
+//   written as 128-byte row segments, 16 bytes per lane.
+//     vec: n % 8 == 0 (aligned 8-element runs inside the matrix).
+//   Stored-transposed W (TRANS): O = Q U straight from the accumulators, 4
+//   consecutive rows of one column per quad.
+//     vec: m % 4 == 0 (aligned 4-element runs).
+// ---------------------------------------------------------------------------
+template <typename PT> struct Quad;
+template <> struct Quad<bf16_t> {
+  typedef uint2 V;
+  static __device__ __forceinline__ float get(const V& v, int i) {
+    const uint32_t w = i < 2 ? v.x : v.y;
+    return (i & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+  }
+  static __device__ __forceinline__ V make(const float* f) {
+    return make_uint2((uint32_t)f2bf(f[0]) | ((uint32_t)f2bf(f[1]) << 16),
+                      (uint32_t)f2bf(f[2]) | ((uint32_t)f2bf(f[3]) << 16));
+  }
+};
+template <> struct Quad<float> {
+  typedef f32x4 V;
+  static __device__ __forceinline__ float get(const V& v, int i) { return v[i]; }
+  static __device__ __forceinline__ V make(const float* f) { return f32x4{f[0], f[1], f[2], f[3]}; }
+};
+
+constexpr int AP_LD = 68;   // LDS row stride (floats) of a wave's 32 x 64 O block
+
+// Order the LDS writes of a wave before its later reads of other lanes' data.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// 8 consecutive elements of PT <-> floats.
+template <typename PT> struct Oct;
+template <> struct Oct<bf16_t> {
+  typedef u32x4 V;
+  static __device__ __forceinline__ float get(const V& v, int i) {
+    const uint32_t w = v[i >> 1];
+    return (i & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+  }
+  static __device__ __forceinline__ void put(bf16_t* p, const float* f) {
+    u32x4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = (uint32_t)f2bf(f[2 * q]) | ((uint32_t)f2bf(f[2 * q + 1]) << 16);
+    *reinterpret_cast<u32x4*>(p) = v;
+  }
+  static __device__ __forceinline__ V load(const bf16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+};
+template <> struct Oct<float> {
+  struct V { f32x4 a, b; };
+  static __device__ __forceinline__ float get(const V& v, int i) { return i < 4 ? v.a[i] : v.b[i - 4]; }
+  static __device__ __forceinline__ void put(float* p, const float* f) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{f[0], f[1], f[2], f[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{f[4], f[5], f[6], f[7]};
+  }
+  static __device__ __forceinline__ V load(const float* p) {
+    return V{*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4)};
+  }
+};
+
+// O block of one 32-column block: acc = U^T Q^T (!TRANS) or Q U (TRANS).
+template <int MODE, bool TRANS>
+__device__ __forceinline__ f32x16 apply_block(const uint32_t (*xr)[MODE == 0 ? 4 : 8], const BFrag& fr) {
+  f32x16 acc = {};
+  if constexpr (MODE == 2) {
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const uint4 qw = fr.q[kk >> 2];
+      const uint32_t qb = (kk & 3) == 0 ? qw.x : (kk & 3) == 1 ? qw.y : (kk & 3) == 2 ? qw.z : qw.w;
+      const float qv = __uint_as_float(qb);
+      const float xv = __uint_as_float(xr[kk >> 3][kk & 7]);
+      if constexpr (!TRANS) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(xv, qv, acc, 0, 0, 0);
+      else acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv, xv, acc, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 qh = __builtin_bit_cast(bf16x8, fr.q[kb]);
+      const bf16x8 ql = __builtin_bit_cast(bf16x8, fr.q[2 + kb]);
+      if constexpr (MODE == 0) {
+        const bf16x8 xv = __builtin_bit_cast(bf16x8, u32x4{xr[kb][0], xr[kb][1], xr[kb][2], xr[kb][3]});
+        if constexpr (!TRANS) {
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xv, qh, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xv, ql, acc, 0, 0, 0);
+        } else {
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh, xv, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql, xv, acc, 0, 0, 0);
+        }
+      } else {
+        bf16x8 xh, xl;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float v = __uint_as_float(xr[kb][t]);
+          const bf16_t hb = f2bf(v);
+          xh[t] = __builtin_bit_cast(__bf16, hb);
+          xl[t] = __builtin_bit_cast(__bf16, f2bf(v - bf2f(hb)));
+        }
+        if constexpr (!TRANS) {
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh, qh, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xl, qh, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh, ql, acc, 0, 0, 0);
+        } else {
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh, xh, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh, xl, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql, xh, acc, 0, 0, 0);
+        }
+      }
+    }
+  }
+  return acc;
+}
+
+template <int MODE, typename PT, bool TRANS>
+__global__ void __launch_bounds__(SK_THREADS)
+sk_apply(const typename SkCfg<MODE>::XS* __restrict__ xg, const BFrag* __restrict__ qfrag, int m, int64_t n,
+         int64_t NB, int G, int64_t upm, int64_t units, int vec, PT* __restrict__ param, float* __restrict__ ns_out,
+         float lr, float wd, float s_scale) {
+  typedef typename SkCfg<MODE>::XS XS;
+  constexpr int XW = MODE == 0 ? 4 : 8;     // 32-bit words of U per lane per K block
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int w = threadIdx.x / WAVE;
+  const int h = lane >> 5, c = lane & 31;
+  const int64_t unit = (int64_t)blockIdx.x * SK_WAVES + w;
+  if (unit >= units) return;   // whole waves only; the kernel has no workgroup barriers
+  const int64_t b = unit / upm;
+  const int64_t jb0 = (unit % upm) * 2;
+  const int64_t mat = b * (int64_t)m * n;
+
+  // U operands of both blocks: bf16 modes K block kb = rows of group 2 kb + h,
+  // fp32 mode rows 16 h .. 16 h + 15 (groups 2 h, 2 h + 1)
+  uint32_t xr[2][2][XW];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int64_t jb = jb0 + jj;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int g = MODE == 2 ? 2 * h + kb : 2 * kb + h;
+      if (jb < NB && g < G) {
+        const XS* src = xg + xg_tile(b, jb, g, NB, G) + c * 8;
+        const u32x4 v0 = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xr[jj][kb][q] = v0[q];
+        if constexpr (XW == 8) {
+          const u32x4 v1 = *reinterpret_cast<const u32x4*>(src + 4);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) xr[jj][kb][4 + q] = v1[q];
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < XW; ++q) xr[jj][kb][q] = 0u;
+      }
+    }
+  }
+
+  if constexpr (!TRANS) {
+    __shared__ __attribute__((aligned(16))) float ob[SK_WAVES][32 * AP_LD];
+    typedef Oct<PT> OV;
+    // W rows 8 i + lane / 8, columns 64 jb0 / 2 + 8 (lane % 8) .. + 7
+    const int rr = lane >> 3, cc = (lane & 7) * 8;
+    const int64_t col0 = 32 * jb0 + cc;
+    typename OV::V wv[4];
+    if (param && vec) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 8 * i + rr;
+        if (i < G && row < m && col0 < n) wv[i] = OV::load(param + mat + (int64_t)row * n + col0);
+      }
+    }
+    const BFrag fr = qfrag[b * WAVE + lane];
+    float* o = ob[w];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const f32x16 acc = apply_block<MODE, false>(xr[jj], fr);
+      // lane holds O row c, columns 32 jj + 8 qd + 4 h + 0..3
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        *reinterpret_cast<f32x4*>(o + c * AP_LD + 32 * jj + 8 * qd + 4 * h) =
+            f32x4{acc[4 * qd], acc[4 * qd + 1], acc[4 * qd + 2], acc[4 * qd + 3]};
+    }
+    wave_sync();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 8 * i + rr;
+      if (i >= G || row >= m) continue;
+      float ov[8], nw[8];
+      const f32x4 o0 = *reinterpret_cast<const f32x4*>(o + row * AP_LD + cc);
+      const f32x4 o1 = *reinterpret_cast<const f32x4*>(o + row * AP_LD + cc + 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { ov[q] = o0[q]; ov[q + 4] = o1[q]; }
+      if (vec) {
+        if (col0 >= n) continue;
+        const int64_t idx = mat + (int64_t)row * n + col0;
+        if (ns_out) Oct<float>::put(ns_out + idx, ov);
+        if (param) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) nw[q] = apply_update(OV::get(wv[i], q), ov[q], lr, wd, s_scale);
+          OV::put(param + idx, nw);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if (col0 + q >= n) break;
+          const int64_t idx = mat + (int64_t)row * n + col0 + q;
+          if (ns_out) ns_out[idx] = ov[q];
+          if (param) st_from_f32(param, idx, apply_update(ld_as_f32(param, idx), ov[q], lr, wd, s_scale));
+        }
+      }
+    }
+  } else {
+    typedef Quad<PT> QV;
+    // W at the accumulator positions: quad qd of block jj holds rows
+    // 8 qd + 4 h + 0..3 of column 32 jb + c
+    typename QV::V wq[2][4];
+    if (param && vec) {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int64_t col = 32 * (jb0 + jj) + c;
+          const int d = 8 * qd + 4 * h;
+          if (col < n && d < m) wq[jj][qd] = *reinterpret_cast<const typename QV::V*>(param + mat + col * m + d);
+        }
+    }
+    const BFrag fr = qfrag[b * WAVE + lane];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int64_t col = 32 * (jb0 + jj) + c;
+      if (jb0 + jj >= NB) break;
+      const f32x16 acc = apply_block<MODE, true>(xr[jj], fr);
+      if (col >= n) continue;
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int d = 8 * qd + 4 * h;
+        float ov[4], nw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[i] = acc[4 * qd + i];
+        if (vec) {
+          if (d >= m) continue;
+          const int64_t idx = mat + col * m + d;
+          if (ns_out) *reinterpret_cast<f32x4*>(ns_out + idx) = f32x4{ov[0], ov[1], ov[2], ov[3]};
+          if (param) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) nw[i] = apply_update(QV::get(wq[jj][qd], i), ov[i], lr, wd, s_scale);
+            *reinterpret_cast<typename QV::V*>(param + idx) = QV::make(nw);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (d + i >= m) break;
+            const int64_t idx = mat + col * m + d + i;
+            if (ns_out) ns_out[idx] = ov[i];
+            if (param) st_from_f32(param, idx, apply_update(ld_as_f32(param, idx), ov[i], lr, wd, s_scale));
+          }
+        }
+      }
+    }
+  }
+}
+
 template <int MODE, typename GT>
 hipError_t launch_first(const StepArgs& a, const WsLayout& L, int mode, int vec) {
   typedef typename SkCfg<MODE>::XS XS;
   const BatchShape& sh = a.shape;
   dim3 grid((unsigned)(sh.count * L.S)), block(SK_THREADS);
-  MUON_LAUNCH(mode == 0 ? "sk_momentum_norm_gram" : "sk_norm_gram", (sk_first<MODE, GT>), grid, block,
-              a.stream, mode, (const GT*)a.grad, a.mom, a.u_in, (XS*)(a.ws + L.x), (float*)(a.ws + L.gp0),
-              (float*)(a.ws + L.sp), (int)sh.m, sh.n, L.ldx, (int)L.S, (int)L.T, (int)sh.transposed, vec, a.mu,
-              a.nesterov);
+  const char* name = mode == 0 ? "sk_momentum_norm_gram" : "sk_norm_gram";
+  const int64_t NB = (sh.n + 31) / 32;
+  const int G = (int)((sh.m + 7) / 8);
+  if (L.path == PATH_SKINNY_GRAM)
+    MUON_LAUNCH(name, (sk_first<MODE, GT, true>), grid, block, a.stream, mode, (const GT*)a.grad, a.mom, a.u_in,
+                (XS*)(a.ws + L.x), (float*)(a.ws + L.gp0), (float*)(a.ws + L.sp), (int)sh.m, sh.n, L.ldx, (int)L.S,
+                (int)L.T, (int)sh.transposed, vec, a.mu, a.nesterov, NB, G);
+  else
+    MUON_LAUNCH(name, (sk_first<MODE, GT, false>), grid, block, a.stream, mode, (const GT*)a.grad, a.mom, a.u_in,
+                (XS*)(a.ws + L.x), (float*)(a.ws + L.gp0), (float*)(a.ws + L.sp), (int)sh.m, sh.n, L.ldx, (int)L.S,
+                (int)L.T, (int)sh.transposed, vec, a.mu, a.nesterov, NB, G);
   return hipGetLastError();
 }
 
@@ -775,9 +1133,21 @@ hipError_t launch_gram(const StepArgs& a, const WsLayout& L, int vec) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   PT* param = a.phase == PH_FULL ? (PT*)a.param : nullptr;
-  MUON_LAUNCH("sk_apply_update", (sk_iter<MODE, PT, true>), dim3((unsigned)(sh.count * L.S)), dim3(SK_THREADS),
-              a.stream, (XS*)(a.ws + L.x), (const BFrag*)bfrag, (float*)nullptr, (int)sh.m, sh.n, L.ldx, (int)L.S,
-              (int)L.T, (int)sh.transposed, vec, param, a.ns_out, a.lr, a.wd, a.s);
+  const int64_t NB = (sh.n + 31) / 32;
+  const int G = (int)((sh.m + 7) / 8);
+  const int64_t upm = (NB + 1) / 2;                    // 64-column units per matrix
+  const int64_t units = sh.count * upm;
+  const dim3 grid((unsigned)((units + SK_WAVES - 1) / SK_WAVES));
+  const char* name = param ? "sk_apply_update" : "sk_apply";
+  if (!sh.transposed) {
+    const int vec = sh.n % 8 == 0 ? 1 : 0;
+    MUON_LAUNCH(name, (sk_apply<MODE, PT, false>), grid, dim3(SK_THREADS), a.stream, (const XS*)(a.ws + L.x),
+                (const BFrag*)bfrag, (int)sh.m, sh.n, NB, G, upm, units, vec, param, a.ns_out, a.lr, a.wd, a.s);
+  } else {
+    const int vec = sh.m % 4 == 0 ? 1 : 0;
+    MUON_LAUNCH(name, (sk_apply<MODE, PT, true>), grid, dim3(SK_THREADS), a.stream, (const XS*)(a.ws + L.x),
+                (const BFrag*)bfrag, (int)sh.m, sh.n, NB, G, upm, units, vec, param, a.ns_out, a.lr, a.wd, a.s);
+  }
   return hipGetLastError();
 }
 
