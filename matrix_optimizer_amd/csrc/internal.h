@@ -98,10 +98,14 @@ void trace_begin(const char* name, hipStream_t s);
 void trace_end(hipStream_t s);
 
 // Launch a kernel, bracketed by trace events when tracing is on.
-#define MUON_LAUNCH(NAME, KERNEL, GRID, BLOCK, STREAM, ...)             \
+#define MUON_LAUNCH(NAME, KERNEL, GRID, BLOCK, STREAM, ...) \
+  MUON_LAUNCH_SHM(NAME, KERNEL, GRID, BLOCK, 0, STREAM, __VA_ARGS__)
+
+// Same, with SHM bytes of dynamic LDS.
+#define MUON_LAUNCH_SHM(NAME, KERNEL, GRID, BLOCK, SHM, STREAM, ...)    \
   do {                                                                  \
     ::muon::trace_begin(NAME, STREAM);                                  \
-    hipLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, STREAM, __VA_ARGS__);    \
+    hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHM, STREAM, __VA_ARGS__);  \
     ::muon::trace_end(STREAM);                                          \
   } while (0)
 

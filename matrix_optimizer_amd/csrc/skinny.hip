@@ -84,12 +84,14 @@ template <int MODE> struct Vec {
 // Gram partial of the staged chunk: out[idx(r,s)] = sum_k X[r][k] X[s][k] over
 // the L staged columns, lower triangle packed (idx = r(r+1)/2 + s).  Wave w
 // takes columns [w L/4, (w+1) L/4); the four wave sums are added in order.
+// The tile holds mr rows (mr >= m, rows >= m zero); rows >= mr read as zero.
 template <int MODE>
-__device__ void gram_partial(unsigned char* lds_raw, float* __restrict__ out, int T) {
+__device__ void gram_partial(unsigned char* lds_raw, float* __restrict__ out, int T, int mr) {
   typedef SkCfg<MODE> C;
   const int lane = threadIdx.x & (WAVE - 1);
   const int w = threadIdx.x / WAVE;
-  const int row = lane & 31;
+  const bool live = (lane & 31) < mr;
+  const int row = live ? (lane & 31) : 0;
   f32x16 acc = {};
   constexpr int KW = C::L / SK_WAVES;
   if constexpr (MODE == 0) {
@@ -98,6 +100,7 @@ __device__ void gram_partial(unsigned char* lds_raw, float* __restrict__ out, in
 #pragma unroll 4
     for (int k0 = w * KW; k0 < (w + 1) * KW; k0 += 16) {
       bf16x8 v = *reinterpret_cast<const bf16x8*>(lx + row * C::LDX + k0 + koff);
+      if (!live) v = bf16x8{};
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, v, acc, 0, 0, 0);
     }
   } else {
@@ -105,7 +108,7 @@ __device__ void gram_partial(unsigned char* lds_raw, float* __restrict__ out, in
     const int koff = lane >> 5;
 #pragma unroll 8
     for (int k0 = w * KW; k0 < (w + 1) * KW; k0 += 2) {
-      float v = lx[row * C::LDX + k0 + koff];
+      const float v = live ? lx[row * C::LDX + k0 + koff] : 0.f;
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(v, v, acc, 0, 0, 0);
     }
   }
@@ -594,9 +597,11 @@ sk_first(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const f
          int64_t NB, int G) {
   typedef SkCfg<MODE> C;
   typedef typename C::XS XS;
-  __shared__ __attribute__((aligned(16))) unsigned char lds_raw[SkLds<MODE>::BYTES];
+  // dynamic LDS: max(mr rows of the tile, the Gram reduction buffer) bytes
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   __shared__ float wsum[SK_WAVES];
   XS* lx = reinterpret_cast<XS*>(lds_raw);
+  const int mr = (m + 7) & ~7;
 
   const int64_t blk = blockIdx.x;
   const int64_t b = blk / S;
@@ -606,7 +611,7 @@ sk_first(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const f
   float ss = 0.f;
 
   // zero the padding rows of the tile
-  for (int e = threadIdx.x; e < (SK_MP - m) * C::LDX; e += SK_THREADS) lx[m * C::LDX + e] = (XS)0;
+  for (int e = threadIdx.x; e < (mr - m) * C::LDX; e += SK_THREADS) lx[m * C::LDX + e] = (XS)0;
 
   if (vec) {
     // 8 consecutive columns of one row per item
@@ -691,7 +696,7 @@ sk_first(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const f
   if (threadIdx.x == 0) sp[blk] = tot;
   if constexpr (XG) chunk_store_xg<MODE>(xws, lds_raw, b, j0 / 32, NB, G);
   else chunk_store<MODE>(xws + b * m * ldx + j0, lds_raw, m, ldx);
-  gram_partial<MODE>(lds_raw, gp_out + blk * T, T);
+  gram_partial<MODE>(lds_raw, gp_out + blk * T, T, mr);
 }
 
 // ---------------------------------------------------------------------------
@@ -739,7 +744,7 @@ sk_iter(typename SkCfg<MODE>::XS* __restrict__ xws, const BFrag* __restrict__ bf
 
   if constexpr (!LAST) {
     chunk_store<MODE>(xws + b * m * ldx + j0, lds_raw, m, ldx);
-    gram_partial<MODE>(lds_raw, gp_out + blk * T, T);
+    gram_partial<MODE>(lds_raw, gp_out + blk * T, T, SK_MP);
   } else {
     if (vec) {
 #pragma unroll
@@ -966,7 +971,9 @@ sk_apply(const typename SkCfg<MODE>::XS* __restrict__ xg, const BFrag* __restric
   }
 
   if constexpr (!TRANS) {
-    __shared__ __attribute__((aligned(16))) float ob[SK_WAVES][32 * AP_LD];
+    // dynamic LDS: SK_WAVES x mr x AP_LD floats, one O buffer per wave
+    extern __shared__ __attribute__((aligned(16))) float ob_raw[];
+    const int mr = 8 * G;
     typedef Oct<PT> OV;
     // W rows 8 i + lane / 8, columns 64 jb0 / 2 + 8 (lane % 8) .. + 7
     const int rr = lane >> 3, cc = (lane & 7) * 8;
@@ -980,15 +987,17 @@ sk_apply(const typename SkCfg<MODE>::XS* __restrict__ xg, const BFrag* __restric
       }
     }
     const BFrag fr = qfrag[b * WAVE + lane];
-    float* o = ob[w];
+    float* o = ob_raw + w * mr * AP_LD;
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       const f32x16 acc = apply_block<MODE, false>(xr[jj], fr);
       // lane holds O row c, columns 32 jj + 8 qd + 4 h + 0..3
+      if (c < mr) {
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd)
-        *reinterpret_cast<f32x4*>(o + c * AP_LD + 32 * jj + 8 * qd + 4 * h) =
-            f32x4{acc[4 * qd], acc[4 * qd + 1], acc[4 * qd + 2], acc[4 * qd + 3]};
+        for (int qd = 0; qd < 4; ++qd)
+          *reinterpret_cast<f32x4*>(o + c * AP_LD + 32 * jj + 8 * qd + 4 * h) =
+              f32x4{acc[4 * qd], acc[4 * qd + 1], acc[4 * qd + 2], acc[4 * qd + 3]};
+      }
     }
     wave_sync();
 #pragma unroll
@@ -1078,14 +1087,17 @@ hipError_t launch_first(const StepArgs& a, const WsLayout& L, int mode, int vec)
   const char* name = mode == 0 ? "sk_momentum_norm_gram" : "sk_norm_gram";
   const int64_t NB = (sh.n + 31) / 32;
   const int G = (int)((sh.m + 7) / 8);
+  const size_t tile = (size_t)(8 * G) * SkCfg<MODE>::LDX * sizeof(XS);
+  const size_t red = (size_t)SK_WAVES * SK_MP * (SK_MP + 1) * 4;
+  const size_t shm = tile > red ? tile : red;
   if (L.path == PATH_SKINNY_GRAM)
-    MUON_LAUNCH(name, (sk_first<MODE, GT, true>), grid, block, a.stream, mode, (const GT*)a.grad, a.mom, a.u_in,
-                (XS*)(a.ws + L.x), (float*)(a.ws + L.gp0), (float*)(a.ws + L.sp), (int)sh.m, sh.n, L.ldx, (int)L.S,
-                (int)L.T, (int)sh.transposed, vec, a.mu, a.nesterov, NB, G);
+    MUON_LAUNCH_SHM(name, (sk_first<MODE, GT, true>), grid, block, shm, a.stream, mode, (const GT*)a.grad, a.mom,
+                    a.u_in, (XS*)(a.ws + L.x), (float*)(a.ws + L.gp0), (float*)(a.ws + L.sp), (int)sh.m, sh.n, L.ldx,
+                    (int)L.S, (int)L.T, (int)sh.transposed, vec, a.mu, a.nesterov, NB, G);
   else
-    MUON_LAUNCH(name, (sk_first<MODE, GT, false>), grid, block, a.stream, mode, (const GT*)a.grad, a.mom, a.u_in,
-                (XS*)(a.ws + L.x), (float*)(a.ws + L.gp0), (float*)(a.ws + L.sp), (int)sh.m, sh.n, L.ldx, (int)L.S,
-                (int)L.T, (int)sh.transposed, vec, a.mu, a.nesterov, NB, G);
+    MUON_LAUNCH_SHM(name, (sk_first<MODE, GT, false>), grid, block, shm, a.stream, mode, (const GT*)a.grad, a.mom,
+                    a.u_in, (XS*)(a.ws + L.x), (float*)(a.ws + L.gp0), (float*)(a.ws + L.sp), (int)sh.m, sh.n, L.ldx,
+                    (int)L.S, (int)L.T, (int)sh.transposed, vec, a.mu, a.nesterov, NB, G);
   return hipGetLastError();
 }
 
@@ -1141,7 +1153,8 @@ hipError_t launch_gram(const StepArgs& a, const WsLayout& L, int vec) {
   const char* name = param ? "sk_apply_update" : "sk_apply";
   if (!sh.transposed) {
     const int vec = sh.n % 8 == 0 ? 1 : 0;
-    MUON_LAUNCH(name, (sk_apply<MODE, PT, false>), grid, dim3(SK_THREADS), a.stream, (const XS*)(a.ws + L.x),
+    const size_t shm = (size_t)SK_WAVES * (8 * G) * AP_LD * 4;
+    MUON_LAUNCH_SHM(name, (sk_apply<MODE, PT, false>), grid, dim3(SK_THREADS), shm, a.stream, (const XS*)(a.ws + L.x),
                 (const BFrag*)bfrag, (int)sh.m, sh.n, NB, G, upm, units, vec, param, a.ns_out, a.lr, a.wd, a.s);
   } else {
     const int vec = sh.m % 4 == 0 ? 1 : 0;
