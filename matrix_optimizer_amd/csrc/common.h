@@ -48,6 +48,14 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ int mfma32_row(int lane, int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 __device__ __forceinline__ int mfma32_col(int lane) { return lane & 31; }
 
+// Order a wave's LDS writes before its later reads of other lanes' data (and
+// its reads before later overwrites), without a workgroup barrier.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Decoupled decay plus the orthogonal update on one element, fp32.
 __device__ __forceinline__ float apply_update(float w, float o, float lr, float wd, float s) {
   return w - lr * (wd * w + s * o);

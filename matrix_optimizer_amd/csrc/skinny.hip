@@ -841,13 +841,6 @@ template <> struct Quad<float> {
 
 constexpr int AP_LD = 68;   // LDS row stride (floats) of a wave's 32 x 64 O block
 
-// Order the LDS writes of a wave before its later reads of other lanes' data.
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // 8 consecutive elements of PT <-> floats.
 template <typename PT> struct Oct;
 template <> struct Oct<bf16_t> {

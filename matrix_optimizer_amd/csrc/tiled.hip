@@ -337,16 +337,57 @@ tl_gemm(GemmArgs g) {
             acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[ib], bv[jb], acc[ib][jb], 0, 0, 0);
       }
     }
+    if constexpr (EPI == EPI_APPLY) {
+      // a X term: the Q stage holds X^T[j][k] = X[k][j] for this k-slice; when
+      // the slice covers rows of this wave's output, add a X[i][j] from LDS to
+      // the accumulators (no global read in the epilogue).  The fp32 master
+      // (X32) is added in the epilogue instead.
+      if (!g.X32) {
+        const int64_t krel = kt * C::BK - (i0 + wm * C::WTM);
+        if (krel > -C::BK && krel < C::WTM) {
+#pragma unroll
+          for (int ib = 0; ib < C::IB; ++ib) {
+            const int off = ib * 32 - (int)krel;   // block row 0 relative to the slice
+            if (off < 0 || off >= C::BK) continue;
+#pragma unroll
+            for (int jb = 0; jb < C::JB; ++jb) {
+              const OP* xq = Qs + jb * 32 * C::LD + off + 4 * (lane >> 5);
+#pragma unroll
+              for (int qd = 0; qd < 4; ++qd) {
+                float xv[4];
+                if constexpr (sizeof(OP) == 2) {
+                  const uint2 u = *reinterpret_cast<const uint2*>(xq + 8 * qd);
+                  xv[0] = __uint_as_float(u.x << 16);
+                  xv[1] = __uint_as_float(u.x & 0xffff0000u);
+                  xv[2] = __uint_as_float(u.y << 16);
+                  xv[3] = __uint_as_float(u.y & 0xffff0000u);
+                } else {
+                  const f32x4 u = *reinterpret_cast<const f32x4*>(xq + 8 * qd);
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) xv[e] = u[e];
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[ib][jb][4 * qd + e] += g.ca * xv[e];
+              }
+            }
+          }
+        }
+      }
+    }
     if (kt + 1 < KT) stage_store<C>(sr, lds + (st ^ 1) * C::STAGE + r0 * C::LD + cv);
     __syncthreads();
   }
 
   // ---- epilogues -------------------------------------------------------------
-  // Each wave stages one 32 x 64 block row of its sub-tile in LDS per round;
-  // lane l then owns column l of that block: row-major outputs are written
-  // 64 lanes wide (coalesced) and transposed outputs as 16-byte vectors along
-  // the lane's own 32 contiguous elements.  Offsets inside one padded matrix
-  // fit in 32 bits (the planner caps a padded matrix at 2^31 elements).
+  // Each wave stages one 32 x 64 block row of its sub-tile in its own LDS
+  // region per round (the last main-loop barrier has retired every read of
+  // the operand stages, so wave-level ordering suffices from here on); lane l
+  // then owns column l of that block: row-major outputs are written 64 lanes
+  // wide (coalesced) and transposed outputs as 16-byte vectors along the
+  // lane's own 32 contiguous elements.  All global reads of a round are
+  // issued before any of its stores, so their latencies overlap.  Offsets
+  // inside one padded matrix fit in 32 bits (the planner caps a padded matrix
+  // at 2^31 elements).
   static_assert(C::JB == 2, "epilogue stages 64-column wave tiles");
   constexpr int SLD = 72;   // staging row stride (floats): conflict-free writes and reads
   static_assert(C::THREADS / 64 * 32 * SLD * 4 <= 2 * C::STAGE * (int)sizeof(OP), "staging fits in LDS");
@@ -355,11 +396,12 @@ tl_gemm(GemmArgs g) {
   const bool diag = (EPI != EPI_APPLY) && (ti == tj);
 #pragma clang loop unroll(full)
   for (int ib = 0; ib < C::IB; ++ib) {
+    if (ib > 0) wave_sync();   // this wave's reads of the previous round are done
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) stg[mfma32_row(lane, r) * SLD + jb * 32 + (lane & 31)] = acc[ib][jb][r];
-    __syncthreads();
+    wave_sync();
     float o[32];
 #pragma unroll
     for (int q = 0; q < 32; ++q) o[q] = stg[q * SLD + lane];
@@ -380,9 +422,12 @@ tl_gemm(GemmArgs g) {
       const uint32_t ld = (uint32_t)g.lda;
       const float* A32 = g.A32 + mat * g.strideA;
       OP* PB = reinterpret_cast<OP*>(g.PB) + mat * g.strideA;
+      float av[32];
+#pragma unroll
+      for (int q = 0; q < 32; ++q) av[q] = A32[(ib0 + q) * ld + jj];
 #pragma unroll
       for (int q = 0; q < 32; ++q) {
-        o[q] = g.cb * A32[(ib0 + q) * ld + jj] + g.cc * o[q];
+        o[q] = g.cb * av[q] + g.cc * o[q];
         st_from_f32(PB, (ib0 + q) * ld + jj, o[q]);
       }
       if (!diag) store_run32(PB + jj * ld + ib0, o);
@@ -390,12 +435,22 @@ tl_gemm(GemmArgs g) {
       const uint32_t ldx = (uint32_t)g.ldx;
       OP* X = reinterpret_cast<OP*>(g.X) + mat * g.strideX;
       float* X32 = g.X32 ? g.X32 + mat * g.strideX : nullptr;
+      // a X is in the accumulators already, except with the fp32 master;
+      // two halves of 16 rows: the reads of a half are issued together
 #pragma unroll
-      for (int q = 0; q < 32; ++q) {
-        const uint32_t xi = (ib0 + q) * ldx + jj;
-        o[q] = g.ca * (X32 ? X32[xi] : ld_as_f32(X, xi)) + o[q];
-        if (X32) X32[xi] = o[q];
-        st_from_f32(X, xi, o[q]);
+      for (int hh = 0; hh < 2; ++hh) {
+        if (X32) {
+          float xv[16];
+#pragma unroll
+          for (int q = 0; q < 16; ++q) xv[q] = X32[(ib0 + 16 * hh + q) * ldx + jj];
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            o[16 * hh + q] = g.ca * xv[q] + o[16 * hh + q];
+            X32[(ib0 + 16 * hh + q) * ldx + jj] = o[16 * hh + q];
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) st_from_f32(X, (ib0 + 16 * hh + q) * ldx + jj, o[16 * hh + q]);
       }
       store_run32(reinterpret_cast<OP*>(g.XT) + mat * g.strideX + jj * (uint32_t)g.ldxt + ib0, o);
     } else {
@@ -406,36 +461,53 @@ tl_gemm(GemmArgs g) {
       float* O = g.ns_out ? g.ns_out + mat * g.m * g.n : nullptr;
       const uint32_t m = (uint32_t)g.m, n = (uint32_t)g.n;
       if (jj < n) {
+        // two halves of 16 rows: X and W reads of a half are issued together
 #pragma unroll
-        for (int q = 0; q < 32; ++q) {
-          const uint32_t xi = (ib0 + q) * ldx + jj;   // padded rows: always readable
-          o[q] = g.ca * (X32 ? X32[xi] : ld_as_f32(X, xi)) + o[q];
-        }
-        if (!g.transposed) {
-          // W row-major: lanes cover consecutive columns of each row
+        for (int hh = 0; hh < 2; ++hh) {
+          float xv[16], wv[16];
+          if (X32) {
 #pragma unroll
-          for (int q = 0; q < 32; ++q) {
-            const uint32_t i = ib0 + q;
-            if (i < m) {
-              if (O) O[i * n + jj] = o[q];
-              if (W) st_from_f32(W, i * n + jj, apply_update(ld_as_f32(W, i * n + jj), o[q], g.lr, g.wd, g.s));
+            for (int q = 0; q < 16; ++q) xv[q] = X32[(ib0 + 16 * hh + q) * ldx + jj];   // padded rows: readable
+          }
+          if (!g.transposed && W) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+              const uint32_t i = ib0 + 16 * hh + q;
+              wv[q] = i < m ? ld_as_f32(W, i * n + jj) : 0.f;
             }
           }
-        } else if (ib0 + 32 <= m && (m % 8) == 0) {
-          // W is the transpose: this lane's 32 elements are contiguous and 16-byte aligned
-          const uint32_t base = jj * m + ib0;
-          if (O) store_run32(O + base, o);
-          if (W) update_run32(W + base, o, g.lr, g.wd, g.s);
-        } else {
-          for (uint32_t q = 0; q < 32 && ib0 + q < m; ++q) {
-            const uint32_t si = jj * m + ib0 + q;
-            if (O) O[si] = o[q];
-            if (W) st_from_f32(W, si, apply_update(ld_as_f32(W, si), o[q], g.lr, g.wd, g.s));
+          if (X32) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) o[16 * hh + q] = g.ca * xv[q] + o[16 * hh + q];
+          }
+          if (!g.transposed) {
+            // W row-major: lanes cover consecutive columns of each row
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+              const uint32_t i = ib0 + 16 * hh + q;
+              if (i < m) {
+                if (O) O[i * n + jj] = o[16 * hh + q];
+                if (W) st_from_f32(W, i * n + jj, apply_update(wv[q], o[16 * hh + q], g.lr, g.wd, g.s));
+              }
+            }
+          }
+        }
+        if (g.transposed) {
+          if (ib0 + 32 <= m && (m % 8) == 0) {
+            // W is the transpose: this lane's 32 elements are contiguous and 16-byte aligned
+            const uint32_t base = jj * m + ib0;
+            if (O) store_run32(O + base, o);
+            if (W) update_run32(W + base, o, g.lr, g.wd, g.s);
+          } else {
+            for (uint32_t q = 0; q < 32 && ib0 + q < m; ++q) {
+              const uint32_t si = jj * m + ib0 + q;
+              if (O) O[si] = o[q];
+              if (W) st_from_f32(W, si, apply_update(ld_as_f32(W, si), o[q], g.lr, g.wd, g.s));
+            }
           }
         }
       }
     }
-    __syncthreads();
   }
 }
 
