@@ -15,13 +15,9 @@ constexpr int WAVE = 64;
 
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.  gfx950
+// converts in hardware (v_cvt_pk_bf16_f32), branch-free.
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 // Load / store one element of a tensor whose dtype is a template parameter.
 template <typename T> __device__ __forceinline__ float ld_as_f32(const T* p, int64_t i);

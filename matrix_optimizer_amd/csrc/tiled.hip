@@ -140,12 +140,15 @@ tl_layout(int mode, const GT* __restrict__ grad, const float* __restrict__ mom, 
 // ---------------------------------------------------------------------------
 // NT product on MFMA with three epilogues.
 // ---------------------------------------------------------------------------
-enum { EPI_GRAM = 0, EPI_POLY = 1, EPI_APPLY = 2 };
+// EPI_APPLY writes X' (both layouts); EPI_LAST is the last step's apply,
+// which updates W (and writes O) instead.
+enum { EPI_GRAM = 0, EPI_POLY = 1, EPI_APPLY = 2, EPI_LAST = 3 };
 
 struct GemmArgs {
   const void* P; const void* Q;
   int64_t ldp, ldq, strideP, strideQ, K;
   int64_t tiles_n, tiles_per_mat;   // tiles along the output columns; tiles per matrix
+  int64_t tiles_total;              // tiles of the launch (all matrices)
   // EPI_GRAM: A32 (+ A16) out.  EPI_POLY: A32 in, PB out.
   float* A32; bf16_t* A16; void* PB; int64_t lda, strideA;
   float ca, cb, cc;
@@ -273,15 +276,19 @@ tl_gemm(GemmArgs g) {
   const int lane = t & 63;
   const int w = t >> 6;
   const int wm = w / C::WAVES_N, wn = w % C::WAVES_N;
-  // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous
-  // range of tiles so the operand panels they share meet in the same L2.
-  int64_t bid = blockIdx.x;
-  const int64_t nb = gridDim.x;
-  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  // Persistent: workgroup b takes tiles b, b + gridDim, ...  A tile's
+  // epilogue stores drain while the next tile's main loop runs.
+  // Workgroups are dealt round-robin to the 8 XCDs, so with gridDim % 8 == 0
+  // a workgroup's tiles stay on one XCD; give each XCD a contiguous range of
+  // tiles so the operand panels its concurrent tiles share meet in its L2.
+  const int64_t total = g.tiles_total;
+  const bool xcd_map = (total & 7) == 0 && (gridDim.x & 7) == 0;
+  for (int64_t lin = blockIdx.x; lin < total; lin += gridDim.x) {
+  const int64_t bid = xcd_map ? (lin & 7) * (total >> 3) + (lin >> 3) : lin;
   const int64_t mat = bid / g.tiles_per_mat;
   const int64_t tt = bid % g.tiles_per_mat;
   int64_t ti, tj;
-  if (EPI == EPI_APPLY) { ti = tt / g.tiles_n; tj = tt % g.tiles_n; }
+  if (EPI >= EPI_APPLY) { ti = tt / g.tiles_n; tj = tt % g.tiles_n; }
   else tri_tile(tt, ti, tj);
   const int64_t i0 = ti * C::BM, j0 = tj * C::BN;
 
@@ -337,7 +344,7 @@ tl_gemm(GemmArgs g) {
             acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[ib], bv[jb], acc[ib][jb], 0, 0, 0);
       }
     }
-    if constexpr (EPI == EPI_APPLY) {
+    if constexpr (EPI >= EPI_APPLY) {
       // a X term: the Q stage holds X^T[j][k] = X[k][j] for this k-slice; when
       // the slice covers rows of this wave's output, add a X[i][j] from LDS to
       // the accumulators (no global read in the epilogue).  The fp32 master
@@ -388,19 +395,21 @@ tl_gemm(GemmArgs g) {
   // issued before any of its stores, so their latencies overlap.  Offsets
   // inside one padded matrix fit in 32 bits (the planner caps a padded matrix
   // at 2^31 elements).
-  static_assert(C::JB == 2, "epilogue stages 64-column wave tiles");
+  static_assert(C::JB % 2 == 0, "epilogue stages 64-column blocks");
   constexpr int SLD = 72;   // staging row stride (floats): conflict-free writes and reads
   static_assert(C::THREADS / 64 * 32 * SLD * 4 <= 2 * C::STAGE * (int)sizeof(OP), "staging fits in LDS");
   float* stg = reinterpret_cast<float*>(lds) + w * (32 * SLD);
-  const uint32_t jj = (uint32_t)(j0 + wn * C::WTN + lane);
-  const bool diag = (EPI != EPI_APPLY) && (ti == tj);
+  const bool diag = (EPI < EPI_APPLY) && (ti == tj);
 #pragma clang loop unroll(full)
-  for (int ib = 0; ib < C::IB; ++ib) {
-    if (ib > 0) wave_sync();   // this wave's reads of the previous round are done
+  for (int rb = 0; rb < C::IB * C::JB / 2; ++rb) {
+    const int ib = rb / (C::JB / 2), jp = rb % (C::JB / 2);
+    const uint32_t jj = (uint32_t)(j0 + wn * C::WTN + jp * 64 + lane);
+    if (rb > 0) wave_sync();   // this wave's reads of the previous round are done
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) stg[mfma32_row(lane, r) * SLD + jb * 32 + (lane & 31)] = acc[ib][jb][r];
+      for (int r = 0; r < 16; ++r)
+        stg[mfma32_row(lane, r) * SLD + jb * 32 + (lane & 31)] = acc[ib][2 * jp + jb][r];
     wave_sync();
     float o[32];
 #pragma unroll
@@ -411,7 +420,9 @@ tl_gemm(GemmArgs g) {
       float* A32 = g.A32 + mat * g.strideA;
 #pragma unroll
       for (int q = 0; q < 32; ++q) A32[(ib0 + q) * ld + jj] = o[q];
-      if (!diag) store_run32(A32 + jj * ld + ib0, o);
+      // the fp32 copy feeds the poly epilogue (lower-triangle tiles only),
+      // except on the fp32 path where it is also the full product operand
+      if (!diag && !g.A16) store_run32(A32 + jj * ld + ib0, o);
       if (g.A16) {
         bf16_t* A16 = g.A16 + mat * g.strideA;
 #pragma unroll
@@ -422,35 +433,38 @@ tl_gemm(GemmArgs g) {
       const uint32_t ld = (uint32_t)g.lda;
       const float* A32 = g.A32 + mat * g.strideA;
       OP* PB = reinterpret_cast<OP*>(g.PB) + mat * g.strideA;
-      float av[32];
 #pragma unroll
-      for (int q = 0; q < 32; ++q) av[q] = A32[(ib0 + q) * ld + jj];
+      for (int hh = 0; hh < 2; ++hh) {
+        float av[16];
 #pragma unroll
-      for (int q = 0; q < 32; ++q) {
-        o[q] = g.cb * av[q] + g.cc * o[q];
-        st_from_f32(PB, (ib0 + q) * ld + jj, o[q]);
+        for (int q = 0; q < 16; ++q) av[q] = A32[(ib0 + 16 * hh + q) * ld + jj];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          o[16 * hh + q] = g.cb * av[q] + g.cc * o[16 * hh + q];
+          st_from_f32(PB, (ib0 + 16 * hh + q) * ld + jj, o[16 * hh + q]);
+        }
       }
       if (!diag) store_run32(PB + jj * ld + ib0, o);
-    } else if (!g.last) {
+    } else if constexpr (EPI == EPI_APPLY) {
       const uint32_t ldx = (uint32_t)g.ldx;
       OP* X = reinterpret_cast<OP*>(g.X) + mat * g.strideX;
       float* X32 = g.X32 ? g.X32 + mat * g.strideX : nullptr;
       // a X is in the accumulators already, except with the fp32 master;
-      // two halves of 16 rows: the reads of a half are issued together
+      // four quarters of 8 rows: the reads of a quarter are issued together
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
+      for (int hh = 0; hh < 4; ++hh) {
         if (X32) {
-          float xv[16];
+          float xv[8];
 #pragma unroll
-          for (int q = 0; q < 16; ++q) xv[q] = X32[(ib0 + 16 * hh + q) * ldx + jj];
+          for (int q = 0; q < 8; ++q) xv[q] = X32[(ib0 + 8 * hh + q) * ldx + jj];
 #pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            o[16 * hh + q] = g.ca * xv[q] + o[16 * hh + q];
-            X32[(ib0 + 16 * hh + q) * ldx + jj] = o[16 * hh + q];
+          for (int q = 0; q < 8; ++q) {
+            o[8 * hh + q] = g.ca * xv[q] + o[8 * hh + q];
+            X32[(ib0 + 8 * hh + q) * ldx + jj] = o[8 * hh + q];
           }
         }
 #pragma unroll
-        for (int q = 0; q < 16; ++q) st_from_f32(X, (ib0 + 16 * hh + q) * ldx + jj, o[16 * hh + q]);
+        for (int q = 0; q < 8; ++q) st_from_f32(X, (ib0 + 8 * hh + q) * ldx + jj, o[8 * hh + q]);
       }
       store_run32(reinterpret_cast<OP*>(g.XT) + mat * g.strideX + jj * (uint32_t)g.ldxt + ib0, o);
     } else {
@@ -461,33 +475,33 @@ tl_gemm(GemmArgs g) {
       float* O = g.ns_out ? g.ns_out + mat * g.m * g.n : nullptr;
       const uint32_t m = (uint32_t)g.m, n = (uint32_t)g.n;
       if (jj < n) {
-        // two halves of 16 rows: X and W reads of a half are issued together
+        // four quarters of 8 rows: X and W reads of a quarter are issued together
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          float xv[16], wv[16];
+        for (int hh = 0; hh < 4; ++hh) {
+          float xv[8], wv[8];
           if (X32) {
 #pragma unroll
-            for (int q = 0; q < 16; ++q) xv[q] = X32[(ib0 + 16 * hh + q) * ldx + jj];   // padded rows: readable
+            for (int q = 0; q < 8; ++q) xv[q] = X32[(ib0 + 8 * hh + q) * ldx + jj];   // padded rows: readable
           }
           if (!g.transposed && W) {
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-              const uint32_t i = ib0 + 16 * hh + q;
+            for (int q = 0; q < 8; ++q) {
+              const uint32_t i = ib0 + 8 * hh + q;
               wv[q] = i < m ? ld_as_f32(W, i * n + jj) : 0.f;
             }
           }
           if (X32) {
 #pragma unroll
-            for (int q = 0; q < 16; ++q) o[16 * hh + q] = g.ca * xv[q] + o[16 * hh + q];
+            for (int q = 0; q < 8; ++q) o[8 * hh + q] = g.ca * xv[q] + o[8 * hh + q];
           }
           if (!g.transposed) {
             // W row-major: lanes cover consecutive columns of each row
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-              const uint32_t i = ib0 + 16 * hh + q;
+            for (int q = 0; q < 8; ++q) {
+              const uint32_t i = ib0 + 8 * hh + q;
               if (i < m) {
-                if (O) O[i * n + jj] = o[16 * hh + q];
-                if (W) st_from_f32(W, i * n + jj, apply_update(wv[q], o[16 * hh + q], g.lr, g.wd, g.s));
+                if (O) O[i * n + jj] = o[8 * hh + q];
+                if (W) st_from_f32(W, i * n + jj, apply_update(wv[q], o[8 * hh + q], g.lr, g.wd, g.s));
               }
             }
           }
@@ -509,6 +523,8 @@ tl_gemm(GemmArgs g) {
       }
     }
   }
+  __syncthreads();   // every wave is done with its staging region before the next tile's stage 0
+  }  // tiles
 }
 
 template <typename PT>
@@ -529,6 +545,26 @@ hipError_t launch_momentum(const StepArgs& a, int mode, float* ssp, int64_t npar
   return hipGetLastError();
 }
 
+// Persistent grid of tl_gemm<C, EPI, PT>: one wave of resident workgroups
+// (a multiple of 8, so each stays on one XCD), or fewer if there are fewer
+// tiles.
+template <class C, int EPI, typename PT>
+unsigned gemm_grid(int64_t tiles) {
+  static int per_dev[64] = {0};   // resident workgroups of this kernel per device
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (per_dev[dev] == 0) {
+    int cus = 0, blocks = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, tl_gemm<C, EPI, PT>, C::THREADS, 0) != hipSuccess ||
+        blocks <= 0)
+      blocks = 1;
+    per_dev[dev] = cus * blocks;
+  }
+  const int64_t slots = per_dev[dev];
+  return (unsigned)(tiles < slots ? tiles : slots);
+}
+
 // The K Newton-Schulz steps as three NT products each, on tile config C.
 template <class C, typename PT>
 hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C::Op* X, typename C::Op* XT[2],
@@ -542,31 +578,35 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
     GemmArgs g = {};
     // Gram: A = X X^T
     g.P = X; g.Q = X; g.ldp = np; g.ldq = np; g.strideP = mp * np; g.strideQ = mp * np; g.K = np;
-    g.tiles_n = tm; g.tiles_per_mat = tri;
+    g.tiles_n = tm; g.tiles_per_mat = tri; g.tiles_total = sh.count * tri;
     g.A32 = A32; g.A16 = A16; g.lda = mp; g.strideA = mp * mp;
-    MUON_LAUNCH("tl_gram", (tl_gemm<C, EPI_GRAM, PT>), dim3((unsigned)(sh.count * tri)), dim3(C::THREADS),
-                a.stream, g);
+    MUON_LAUNCH("tl_gram", (tl_gemm<C, EPI_GRAM, PT>), dim3(gemm_grid<C, EPI_GRAM, PT>(g.tiles_total)),
+                dim3(C::THREADS), a.stream, g);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // poly: B = b A + c A A
     g = GemmArgs{};
     if (sizeof(OP) == 4) { g.P = A32; g.Q = A32; } else { g.P = A16; g.Q = A16; }
     g.ldp = mp; g.ldq = mp; g.strideP = mp * mp; g.strideQ = mp * mp; g.K = mp;
-    g.tiles_n = tm; g.tiles_per_mat = tri;
+    g.tiles_n = tm; g.tiles_per_mat = tri; g.tiles_total = sh.count * tri;
     g.A32 = A32; g.PB = PB; g.lda = mp; g.strideA = mp * mp; g.cb = cb; g.cc = cc;
-    MUON_LAUNCH("tl_poly", (tl_gemm<C, EPI_POLY, PT>), dim3((unsigned)(sh.count * tri)), dim3(C::THREADS),
-                a.stream, g);
+    MUON_LAUNCH("tl_poly", (tl_gemm<C, EPI_POLY, PT>), dim3(gemm_grid<C, EPI_POLY, PT>(g.tiles_total)),
+                dim3(C::THREADS), a.stream, g);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // apply: X' = a X + B X, B X read as B (X^T)^T
     g = GemmArgs{};
     g.P = PB; g.Q = XT[k & 1]; g.ldp = mp; g.ldq = mp; g.strideP = mp * mp; g.strideQ = np * mp; g.K = mp;
-    g.tiles_n = tn; g.tiles_per_mat = tm * tn;
+    g.tiles_n = tn; g.tiles_per_mat = tm * tn; g.tiles_total = sh.count * tm * tn;
     g.ca = ca; g.X = X; g.X32 = X32; g.XT = XT[(k + 1) & 1]; g.ldx = np; g.ldxt = mp; g.strideX = mp * np;
     g.last = (k == a.steps - 1);
     g.param = a.phase == PH_FULL ? a.param : nullptr; g.param_bf16 = a.param_dtype == DT_BF16;
     g.ns_out = a.ns_out; g.lr = a.lr; g.wd = a.wd; g.s = a.s;
     g.m = sh.m; g.n = sh.n; g.transposed = sh.transposed;
-    MUON_LAUNCH(g.last ? "tl_apply_update" : "tl_apply", (tl_gemm<C, EPI_APPLY, PT>),
-                dim3((unsigned)(sh.count * tm * tn)), dim3(C::THREADS), a.stream, g);
+    if (g.last)
+      MUON_LAUNCH("tl_apply_update", (tl_gemm<C, EPI_LAST, PT>), dim3(gemm_grid<C, EPI_LAST, PT>(g.tiles_total)),
+                  dim3(C::THREADS), a.stream, g);
+    else
+      MUON_LAUNCH("tl_apply", (tl_gemm<C, EPI_APPLY, PT>), dim3(gemm_grid<C, EPI_APPLY, PT>(g.tiles_total)),
+                  dim3(C::THREADS), a.stream, g);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
