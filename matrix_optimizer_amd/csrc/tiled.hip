@@ -169,6 +169,9 @@ struct GemmCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int WAVES_M = WGM_, WAVES_N = WGN_;
   static constexpr int THREADS = 64 * WGM_ * WGN_;
+  // at least two waves per SIMD: 8-wave tiles by construction, 4-wave tiles
+  // so that two workgroups share a CU (register budget 256 per lane)
+  static constexpr int WAVES_PER_SIMD = 2;
   static constexpr int WTM = BM / WGM_, WTN = BN / WGN_;
   static constexpr int IB = WTM / 32, JB = WTN / 32;
   static constexpr int EPV = 16 / (int)sizeof(OP);
@@ -178,6 +181,7 @@ struct GemmCfg {
   static constexpr int QV = BN * VPR / THREADS;
   static constexpr int RPP = THREADS / VPR;          // tile rows per load pass
   static constexpr int STAGE = (BM + BN) * LD;       // elements per LDS stage
+  static_assert(BM == BN || BM == 2 * BN, "symmetric products tile BM = BN or 2 BN");
   static_assert(BM * VPR % THREADS == 0 && BN * VPR % THREADS == 0, "load split");
 };
 // bf16, 256x256 tiles, 8 waves of 128x64 (4x2 MFMA blocks): each fragment
@@ -191,14 +195,21 @@ struct GemmCfg {
 #endif
 typedef GemmCfg<bf16_t, 256, 256, MUON_BIG_BK, 2, MUON_BIG_WAVES_N> CfgBig;
 typedef GemmCfg<bf16_t, 128, 128, 64, 2, 2> CfgSmall;
+
 typedef GemmCfg<float, 128, 128, 32, 2, 2> CfgF32;
 
+// Tiles of a symmetric product that cover its lower triangle, for tiles of
+// BM = R x BN (R = 1 or 2): block row ti holds column tiles tj = 0 .. R ti +
+// R - 1, the last R of them inside the diagonal block (computed whole, no
+// mirror); tile t of a matrix in row-major order.
+template <int R>
 __device__ __forceinline__ void tri_tile(int64_t t, int64_t& ti, int64_t& tj) {
-  int64_t r = (int64_t)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
-  while (r * (r + 1) / 2 > t) --r;
-  while ((r + 1) * (r + 2) / 2 <= t) ++r;
+  // tiles before row r: R r (r + 1) / 2
+  int64_t r = (int64_t)((sqrt(8.0 * (double)t / R + 1.0) - 1.0) * 0.5);
+  while (r > 0 && R * r * (r + 1) / 2 > t) --r;
+  while (R * (r + 1) * (r + 2) / 2 <= t) ++r;
   ti = r;
-  tj = t - r * (r + 1) / 2;
+  tj = t - R * r * (r + 1) / 2;
 }
 
 // 32 consecutive elements starting at a 16-byte aligned address, as 16-byte stores.
@@ -267,7 +278,7 @@ __device__ __forceinline__ void stage_store(const StageRegs<C>& sr, typename C::
 }
 
 template <class C, int EPI, typename PT>
-__global__ void __launch_bounds__(C::THREADS)
+__global__ void __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD)
 tl_gemm(GemmArgs g) {
   typedef typename C::Op OP;
   __shared__ __attribute__((aligned(16))) OP lds[2 * C::STAGE];
@@ -289,7 +300,7 @@ tl_gemm(GemmArgs g) {
   const int64_t tt = bid % g.tiles_per_mat;
   int64_t ti, tj;
   if (EPI >= EPI_APPLY) { ti = tt / g.tiles_n; tj = tt % g.tiles_n; }
-  else tri_tile(tt, ti, tj);
+  else tri_tile<C::BM / C::BN>(tt, ti, tj);
   const int64_t i0 = ti * C::BM, j0 = tj * C::BN;
 
   const int r0 = t / C::VPR, cv = (t % C::VPR) * C::EPV;
@@ -399,7 +410,7 @@ tl_gemm(GemmArgs g) {
   constexpr int SLD = 72;   // staging row stride (floats): conflict-free writes and reads
   static_assert(C::THREADS / 64 * 32 * SLD * 4 <= 2 * C::STAGE * (int)sizeof(OP), "staging fits in LDS");
   float* stg = reinterpret_cast<float*>(lds) + w * (32 * SLD);
-  const bool diag = (EPI < EPI_APPLY) && (ti == tj);
+  const bool diag = (EPI < EPI_APPLY) && (tj >= (C::BM / C::BN) * ti);   // inside the diagonal block
 #pragma clang loop unroll(full)
   for (int rb = 0; rb < C::IB * C::JB / 2; ++rb) {
     const int ib = rb / (C::JB / 2), jp = rb % (C::JB / 2);
@@ -572,7 +583,7 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
   typedef typename C::Op OP;
   hipError_t e;
   const int64_t tm = mp / C::BM, tn = np / C::BN;
-  const int64_t tri = tm * (tm + 1) / 2;
+  const int64_t tri = (C::BM / C::BN) * tm * (tm + 1) / 2;   // triangle tiles
   for (int k = 0; k < a.steps; ++k) {
     const float ca = a.coeffs[3 * k], cb = a.coeffs[3 * k + 1], cc = a.coeffs[3 * k + 2];
     GemmArgs g = {};
