@@ -662,10 +662,15 @@ sk_first(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const f
         for (int q = 0; q < 8; ++q) u[q] = 0.f;
       }
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        ss += u[q] * u[q];
-        if constexpr (MODE == 0) lx[r * C::LDX + jl + q] = f2bf(u[q]);
-        else lx[r * C::LDX + jl + q] = u[q];
+      for (int q = 0; q < 8; ++q) ss += u[q] * u[q];
+      if constexpr (MODE == 0) {
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = (uint32_t)f2bf(u[2 * q]) | ((uint32_t)f2bf(u[2 * q + 1]) << 16);
+        *reinterpret_cast<u32x4*>(lx + r * C::LDX + jl) = w;
+      } else {
+        *reinterpret_cast<f32x4*>(lx + r * C::LDX + jl) = f32x4{u[0], u[1], u[2], u[3]};
+        *reinterpret_cast<f32x4*>(lx + r * C::LDX + jl + 4) = f32x4{u[4], u[5], u[6], u[7]};
       }
     }
   } else {

@@ -269,3 +269,56 @@ def test_moe_experts_2048x7168_sampled():
     errs = check_batch(wl, H.c_hparams(wl.hp), WL.BF16, plan=plan, batches=idx,
                        select=lambda b: sorted({0, b.count - 1, int(rng.integers(1, b.count - 1))}))
     print(f"moe [64,2048,7168] sampled: O errors {errs}")
+
+
+# --------------------------------------------------------------------------
+# full-size configurations, sampled
+# --------------------------------------------------------------------------
+def test_decoder_full_size_sampled():
+    """One full-size batch per decoder shape (4096x4096, 11008x4096 through
+    the transpose path, 4096x11008), as the plan cuts them; the last matrix of
+    each is checked against the oracle."""
+    wl = WL.WORKLOADS["decoder32_h4096_f11008"]
+    plan = B.Plan([p.shape for p in wl.params])
+    pick = {}
+    for b in plan.batches:
+        if (b.M, b.N) not in pick or b.count < pick[(b.M, b.N)].count:
+            pick[(b.M, b.N)] = b
+    assert len(pick) == 3
+    errs = check_batch(wl, H.c_hparams(wl.hp), WL.BF16, plan=plan, batches=[b.index for b in pick.values()],
+                       select=lambda b: [b.count - 1])
+    print(f"decoder full-size sampled: O errors {errs}")
+
+
+def test_large_8192x28672_golden_samples():
+    """The first batch of each orientation of the 8192x28672 workload at full
+    size (two matrices each, the bf16 + fp32-master placement); matrix 0 of
+    each is compared at 4096 positions with oracle values stored by
+    tests/golden/large_8192x28672_samples.py."""
+    import json
+    import os
+    gold = np.load(os.path.join(os.path.dirname(__file__), "golden", "large_8192x28672_samples.npz"))
+    meta = json.loads(str(gold["meta"]))
+    wl = WL.WORKLOADS[meta["workload"]]
+    h = H.c_hparams(wl.hp)
+    assert meta["hparams"] == {k: (list(v) if isinstance(v, tuple) else v)
+                               for k, v in H.oracle_kwargs(h, 8192, 28672).items()}
+    plan = B.Plan([p.shape for p in wl.params])
+    for pi in meta["params"]:
+        binfo = next(b for b in plan.batches if any(s[0] == pi and s[1] == 0 for s in b.segments))
+        q = next(s[3] // (binfo.M * binfo.N) for s in binfo.segments if s[0] == pi and s[1] == 0)
+        arrays = H.batch_arrays(wl, binfo)
+        Wp, Mp, O = H.run_gpu_step(plan, binfo, arrays, WL.BF16, h)
+        rows, cols = gold[f"p{pi}_rows"], gold[f"p{pi}_cols"]
+        o = O[q][rows, cols].astype(np.float64)
+        e = H.rel_fro(o, gold[f"p{pi}_O"])
+        print(f"large param {pi} ({binfo.M}x{binfo.N}, batch of {binfo.count}): sampled O error {e:.3g}")
+        assert np.all(np.isfinite(O[q]))
+        assert e <= H.o_tolerance(h.precision)
+        W0 = H.decode(arrays["param"][q][rows, cols])
+        dW = H.decode(Wp[q][rows, cols]) - W0
+        dW_ref = gold[f"p{pi}_W"] - W0
+        half_ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(gold[f"p{pi}_W"]), 1e-38))) - 8)
+        slack = np.linalg.norm(half_ulp) / np.linalg.norm(dW_ref)
+        assert H.rel_fro(dW, dW_ref) <= H.o_tolerance(h.precision) + slack + 1e-6
+        del arrays, Wp, Mp, O
