@@ -18,6 +18,7 @@ all inputs resident in device memory.  Prints ONE JSON line with:
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -229,6 +230,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (the reference for HBM byte counters)")
+    ap.add_argument("--launch", choices=["graph", "eager"], default="eager",
+                    help="timed steps as eager muon_step calls (default) or replays of one captured HIP graph")
     ap.add_argument("--skinny-kernel", type=int, default=0,
                     help="short sides <= 32: 0 or 1 Newton-Schulz in Gram space, 2 step by step")
     ap.add_argument("--device-inputs", action="store_true",
@@ -259,20 +262,35 @@ def main():
     ws_bytes = max(plan.workspace_bytes(b.index, prec) for b in plan.batches)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
+    # lr and decay from device scalars, so a captured step needs no recapture
+    lr_wd = torch.tensor([hp.lr, hp.weight_decay], dtype=torch.float32, device="cuda")
+    hp_run = dataclasses.replace(hp, lr_wd=lr_wd)
 
     def step():
+        # on the current stream (the capture stream while a graph is recorded)
         for b in plan.batches:
             d = bufs[b.index]
-            B.muon_step(plan, b.index, d["param"], d["grad"], d["momentum"], hp, ws, stream=stream.cuda_stream)
+            B.muon_step(plan, b.index, d["param"], d["grad"], d["momentum"], hp_run, ws)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    run = step
+    if args.launch == "graph":
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                step()
+        stream.wait_stream(side)
+        run = graph.replay
+        run()   # one untimed replay
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(args.steps):
-        step()
+        run()
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
@@ -332,7 +350,7 @@ def main():
     if hp.ns_steps != wl.hp.ns_steps:
         flops = flops / wl.hp.ns_steps * hp.ns_steps
     value = flops / (ms / 1e3) / 1e12
-    cfg = {"workload": wl.name, "matrices": int(sum(b.count for b in plan.batches)),
+    cfg = {"workload": wl.name, "matrices": int(sum(b.count for b in plan.batches)), "launch": args.launch,
            "batches": [[b.count, b.M, b.N] for b in plan.batches],
            "kernels": [["tiled", "skinny_gram", "skinny_stepwise"][b.path] for b in plan.batches],
            "param_dtype": dtype,

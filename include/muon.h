@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 1
+#define MUON_ABI_VERSION 2
 
 typedef enum {
   MUON_OK = 0,
@@ -128,6 +128,14 @@ typedef struct {
   int32_t num_coeff_sets;   /* 1 or ns_steps */
   muon_scale scale;
   muon_precision precision;
+  const float* lr_wd_device;  /* optional: device address of 2 floats {lr, weight_decay} that the
+                               update kernels read when they run, in place of the two host
+                               fields above (which are still validated).  Lets a caller capture
+                               muon_step into a HIP graph once and change the learning rate
+                               and decay between replays (the DMuon-2 paper, App. C.3, keeps
+                               them outside its captured graphs).  4-byte aligned; the caller
+                               keeps it valid until the launches have run.  NULL: use lr and
+                               weight_decay as given. */
 } muon_hparams;
 
 typedef struct {

@@ -54,7 +54,7 @@ class muon_hparams(C.Structure):
     _fields_ = [("lr", C.c_float), ("momentum", C.c_float), ("weight_decay", C.c_float),
                 ("eps", C.c_float), ("nesterov", C.c_int32), ("ns_steps", C.c_int32),
                 ("coeffs", C.POINTER(C.c_float)), ("num_coeff_sets", C.c_int32),
-                ("scale", C.c_int32), ("precision", C.c_int32)]
+                ("scale", C.c_int32), ("precision", C.c_int32), ("lr_wd_device", C.c_void_p)]
 
 
 class muon_batch_buffers(C.Structure):
@@ -202,13 +202,15 @@ class HParams:
     coeffs: Tuple[float, ...] = (3.4445, -4.7750, 2.0315)
     scale: str = "rms"
     precision: str = "bf16"
+    lr_wd: object = None   # optional device float32 tensor [lr, weight_decay], read when the kernels run
 
     def to_c(self):
         """(struct, keep-alive coefficient array)."""
         arr = (C.c_float * len(self.coeffs))(*self.coeffs)
         hp = muon_hparams(self.lr, self.momentum, self.weight_decay, self.eps, int(bool(self.nesterov)),
                           int(self.ns_steps), C.cast(arr, C.POINTER(C.c_float)), len(self.coeffs) // 3,
-                          SCALES[self.scale], PRECISIONS[self.precision])
+                          SCALES[self.scale], PRECISIONS[self.precision],
+                          None if self.lr_wd is None else self.lr_wd.data_ptr())
         return hp, arr
 
 
@@ -302,3 +304,18 @@ class BatchedMuon:
         for b in self.plan.batches:
             muon_step(self.plan, b.index, self.params[b.index], self.grads[b.index], self.moms[b.index],
                       self.hp, self.workspace, None if ns_outs is None else ns_outs[b.index], stream)
+
+    def capture_graph(self):
+        """Record one step (every batch) into a HIP graph (torch.cuda.CUDAGraph)
+        and return it; graph.replay() then runs a step on the same buffers.
+        With hp.lr_wd set, the learning rate and decay written into that
+        device tensor before a replay are the ones the replay uses."""
+        import torch
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                self.step()
+        torch.cuda.current_stream().wait_stream(side)
+        return graph

@@ -123,6 +123,7 @@ muon_status check_hparams(const muon_hparams* hp, bool need_ns, bool need_update
     if (!finite(hp->lr) || hp->lr < 0.f) return MUON_ERR_INVALID_ARG;
     if (!finite(hp->weight_decay) || hp->weight_decay < 0.f) return MUON_ERR_INVALID_ARG;
     if (hp->scale != MUON_SCALE_NONE && hp->scale != MUON_SCALE_RMS) return MUON_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(hp->lr_wd_device) & 3u) return MUON_ERR_INVALID_ARG;
   }
   return MUON_OK;
 }
@@ -156,6 +157,7 @@ void fill_common(StepArgs& a, const muon_plan::Batch& b, const muon_hparams* hp,
   a.ns_out = nullptr; a.o_in = nullptr; a.ws = nullptr;
   a.param_dtype = DT_F32; a.grad_dtype = DT_F32;
   a.lr = hp->lr; a.mu = hp->momentum; a.wd = hp->weight_decay; a.eps = hp->eps;
+  a.lrwd = hp->lr_wd_device;
   a.nesterov = hp->nesterov;
   a.s = hp->scale == MUON_SCALE_RMS ? float(0.2 * std::sqrt(double(std::max(b.M, b.N)))) : 1.0f;
   a.steps = hp->ns_steps;

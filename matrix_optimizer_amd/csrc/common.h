@@ -52,6 +52,15 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// lr and wd of the update: from device memory when given (graph replays pick
+// up new values), else the launch arguments.  Uniform loads.
+__device__ __forceinline__ void update_scalars(const float* lrwd, float& lr, float& wd) {
+  if (lrwd) {
+    lr = lrwd[0];
+    wd = lrwd[1];
+  }
+}
+
 // Decoupled decay plus the orthogonal update on one element, fp32.
 __device__ __forceinline__ float apply_update(float w, float o, float lr, float wd, float s) {
   return w - lr * (wd * w + s * o);

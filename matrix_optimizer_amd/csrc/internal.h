@@ -85,6 +85,7 @@ struct StepArgs {
   float* ns_out;         // O output (PH_FULL optional, PH_NS required)
   const float* o_in;     // PH_UPDATE input
   float lr, mu, wd, eps, s;
+  const float* lrwd;     // optional device {lr, wd}, read by the update kernels
   int nesterov;
   int steps;
   std::vector<float> coeffs;   // 3 * steps (expanded)

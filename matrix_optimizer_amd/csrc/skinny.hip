@@ -712,8 +712,10 @@ template <int MODE, typename PT, bool LAST>
 __global__ void __launch_bounds__(SK_THREADS)
 sk_iter(typename SkCfg<MODE>::XS* __restrict__ xws, const BFrag* __restrict__ bfrag, float* __restrict__ gp_out,
         int m, int64_t n, int64_t ldx, int S, int T, int transposed, int vec,
-        PT* __restrict__ param, float* __restrict__ ns_out, float lr, float wd, float s_scale) {
+        PT* __restrict__ param, float* __restrict__ ns_out, float lr, float wd, float s_scale,
+        const float* __restrict__ lrwd) {
   typedef SkCfg<MODE> C;
+  if constexpr (LAST) update_scalars(lrwd, lr, wd);
   typedef typename C::XS XS;
   __shared__ __attribute__((aligned(16))) unsigned char lds_raw[SkLds<MODE>::BYTES];
   XS* lx = reinterpret_cast<XS*>(lds_raw);
@@ -930,7 +932,8 @@ template <int MODE, typename PT, bool TRANS>
 __global__ void __launch_bounds__(SK_THREADS)
 sk_apply(const typename SkCfg<MODE>::XS* __restrict__ xg, const BFrag* __restrict__ qfrag, int m, int64_t n,
          int64_t NB, int G, int64_t upm, int64_t units, int vec, PT* __restrict__ param, float* __restrict__ ns_out,
-         float lr, float wd, float s_scale) {
+         float lr, float wd, float s_scale, const float* __restrict__ lrwd) {
+  update_scalars(lrwd, lr, wd);
   typedef typename SkCfg<MODE>::XS XS;
   constexpr int XW = MODE == 0 ? 4 : 8;     // 32-bit words of U per lane per K block
   const int lane = threadIdx.x & (WAVE - 1);
@@ -1118,11 +1121,11 @@ hipError_t launch_iters(const StepArgs& a, const WsLayout& L, int vec) {
     if (k < a.steps - 1)
       MUON_LAUNCH("sk_ns_step", (sk_iter<MODE, PT, false>), grid, block, a.stream, (XS*)(a.ws + L.x),
                   (const BFrag*)bfrag, gp[(k + 1) & 1], (int)sh.m, sh.n, L.ldx, (int)L.S, (int)L.T,
-                  (int)sh.transposed, vec, param, a.ns_out, a.lr, a.wd, a.s);
+                  (int)sh.transposed, vec, param, a.ns_out, a.lr, a.wd, a.s, a.lrwd);
     else
       MUON_LAUNCH("sk_apply_update", (sk_iter<MODE, PT, true>), grid, block, a.stream, (XS*)(a.ws + L.x),
                   (const BFrag*)bfrag, gp[(k + 1) & 1], (int)sh.m, sh.n, L.ldx, (int)L.S, (int)L.T,
-                  (int)sh.transposed, vec, param, a.ns_out, a.lr, a.wd, a.s);
+                  (int)sh.transposed, vec, param, a.ns_out, a.lr, a.wd, a.s, a.lrwd);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1153,11 +1156,11 @@ hipError_t launch_gram(const StepArgs& a, const WsLayout& L, int vec) {
     const int vec = sh.n % 8 == 0 ? 1 : 0;
     const size_t shm = (size_t)SK_WAVES * (8 * G) * AP_LD * 4;
     MUON_LAUNCH_SHM(name, (sk_apply<MODE, PT, false>), grid, dim3(SK_THREADS), shm, a.stream, (const XS*)(a.ws + L.x),
-                (const BFrag*)bfrag, (int)sh.m, sh.n, NB, G, upm, units, vec, param, a.ns_out, a.lr, a.wd, a.s);
+                (const BFrag*)bfrag, (int)sh.m, sh.n, NB, G, upm, units, vec, param, a.ns_out, a.lr, a.wd, a.s, a.lrwd);
   } else {
     const int vec = sh.m % 4 == 0 ? 1 : 0;
     MUON_LAUNCH(name, (sk_apply<MODE, PT, true>), grid, dim3(SK_THREADS), a.stream, (const XS*)(a.ws + L.x),
-                (const BFrag*)bfrag, (int)sh.m, sh.n, NB, G, upm, units, vec, param, a.ns_out, a.lr, a.wd, a.s);
+                (const BFrag*)bfrag, (int)sh.m, sh.n, NB, G, upm, units, vec, param, a.ns_out, a.lr, a.wd, a.s, a.lrwd);
   }
   return hipGetLastError();
 }

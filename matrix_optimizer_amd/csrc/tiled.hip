@@ -156,6 +156,7 @@ struct GemmArgs {
   void* X; float* X32; void* XT; int64_t ldx, ldxt, strideX;
   int last;
   void* param; int param_bf16; float* ns_out; float lr, wd, s;
+  const float* lrwd;   // optional device {lr, wd}
   int64_t m, n; int transposed;
 };
 
@@ -479,6 +480,8 @@ tl_gemm(GemmArgs g) {
       }
       store_run32(reinterpret_cast<OP*>(g.XT) + mat * g.strideX + jj * (uint32_t)g.ldxt + ib0, o);
     } else {
+      float ulr = g.lr, uwd = g.wd;
+      update_scalars(g.lrwd, ulr, uwd);
       const uint32_t ldx = (uint32_t)g.ldx;
       const OP* X = reinterpret_cast<const OP*>(g.X) + mat * g.strideX;
       const float* X32 = g.X32 ? g.X32 + mat * g.strideX : nullptr;
@@ -512,7 +515,7 @@ tl_gemm(GemmArgs g) {
               const uint32_t i = ib0 + 8 * hh + q;
               if (i < m) {
                 if (O) O[i * n + jj] = o[8 * hh + q];
-                if (W) st_from_f32(W, i * n + jj, apply_update(wv[q], o[8 * hh + q], g.lr, g.wd, g.s));
+                if (W) st_from_f32(W, i * n + jj, apply_update(wv[q], o[8 * hh + q], ulr, uwd, g.s));
               }
             }
           }
@@ -522,12 +525,12 @@ tl_gemm(GemmArgs g) {
             // W is the transpose: this lane's 32 elements are contiguous and 16-byte aligned
             const uint32_t base = jj * m + ib0;
             if (O) store_run32(O + base, o);
-            if (W) update_run32(W + base, o, g.lr, g.wd, g.s);
+            if (W) update_run32(W + base, o, ulr, uwd, g.s);
           } else {
             for (uint32_t q = 0; q < 32 && ib0 + q < m; ++q) {
               const uint32_t si = jj * m + ib0 + q;
               if (O) O[si] = o[q];
-              if (W) st_from_f32(W, si, apply_update(ld_as_f32(W, si), o[q], g.lr, g.wd, g.s));
+              if (W) st_from_f32(W, si, apply_update(ld_as_f32(W, si), o[q], ulr, uwd, g.s));
             }
           }
         }
@@ -540,7 +543,9 @@ tl_gemm(GemmArgs g) {
 
 template <typename PT>
 __global__ void __launch_bounds__(256)
-tl_update(PT* __restrict__ W, const float* __restrict__ O, int64_t total, float lr, float wd, float s) {
+tl_update(PT* __restrict__ W, const float* __restrict__ O, int64_t total, float lr, float wd, float s,
+          const float* __restrict__ lrwd) {
+  update_scalars(lrwd, lr, wd);
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256)
     st_from_f32(W, i, apply_update(ld_as_f32(W, i), O[i], lr, wd, s));
 }
@@ -610,7 +615,7 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
     g.ca = ca; g.X = X; g.X32 = X32; g.XT = XT[(k + 1) & 1]; g.ldx = np; g.ldxt = mp; g.strideX = mp * np;
     g.last = (k == a.steps - 1);
     g.param = a.phase == PH_FULL ? a.param : nullptr; g.param_bf16 = a.param_dtype == DT_BF16;
-    g.ns_out = a.ns_out; g.lr = a.lr; g.wd = a.wd; g.s = a.s;
+    g.ns_out = a.ns_out; g.lr = a.lr; g.wd = a.wd; g.s = a.s; g.lrwd = a.lrwd;
     g.m = sh.m; g.n = sh.n; g.transposed = sh.transposed;
     if (g.last)
       MUON_LAUNCH("tl_apply_update", (tl_gemm<C, EPI_LAST, PT>), dim3(gemm_grid<C, EPI_LAST, PT>(g.tiles_total)),
@@ -692,10 +697,10 @@ hipError_t run_update_only(const StepArgs& a) {
   if (blocks > 65536) blocks = 65536;
   if (a.param_dtype == DT_BF16)
     MUON_LAUNCH("update", (tl_update<bf16_t>), dim3((unsigned)blocks), dim3(256), a.stream, (bf16_t*)a.param,
-                a.o_in, total, a.lr, a.wd, a.s);
+                a.o_in, total, a.lr, a.wd, a.s, a.lrwd);
   else
     MUON_LAUNCH("update", (tl_update<float>), dim3((unsigned)blocks), dim3(256), a.stream, (float*)a.param,
-                a.o_in, total, a.lr, a.wd, a.s);
+                a.o_in, total, a.lr, a.wd, a.s, a.lrwd);
   return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.EXPORTED)
-    assert B.muon_abi_version() == 1
+    assert B.muon_abi_version() == 2
 
 
 def _cmp_plans(shapes, cap=0, order=0):
@@ -197,6 +197,10 @@ def test_step_rejects_bad_hparams(plan_fb):
     assert B.lib().muon_step(p.handle, 0, C.byref(bufs), C.byref(hpc), fb.ptr("ws"), 1 << 40, None) == 1
     hpc.scale = 1
     hpc.coeffs = C.cast(None, C.POINTER(C.c_float))
+    assert B.lib().muon_step(p.handle, 0, C.byref(bufs), C.byref(hpc), fb.ptr("ws"), 1 << 40, None) == 1
+    # the device {lr, wd} pointer must be 4-byte aligned
+    hpc, keep = B.HParams().to_c()
+    hpc.lr_wd_device = fb.ptr("ws", 2)
     assert B.lib().muon_step(p.handle, 0, C.byref(bufs), C.byref(hpc), fb.ptr("ws"), 1 << 40, None) == 1
     assert fb.untouched()
 
