@@ -140,9 +140,10 @@ tl_layout(int mode, const GT* __restrict__ grad, const float* __restrict__ mom, 
 // ---------------------------------------------------------------------------
 // NT product on MFMA with three epilogues.
 // ---------------------------------------------------------------------------
-// EPI_APPLY writes X' (both layouts); EPI_LAST is the last step's apply,
-// which updates W (and writes O) instead.
-enum { EPI_GRAM = 0, EPI_POLY = 1, EPI_APPLY = 2, EPI_LAST = 3 };
+// EPI_APPLY writes X' (both layouts); EPI_LAST / EPI_LAST_T are the last
+// step's apply for row-major / stored-transposed W, which update W (and
+// write O) instead.
+enum { EPI_GRAM = 0, EPI_POLY = 1, EPI_APPLY = 2, EPI_LAST = 3, EPI_LAST_T = 4 };
 
 struct GemmArgs {
   const void* P; const void* Q;
@@ -252,6 +253,28 @@ __device__ __forceinline__ void update_run32(bf16_t* w, const float* o, float lr
     }
     *reinterpret_cast<u32x4*>(w + 8 * q) = v;
   }
+}
+
+// 8 consecutive elements at a 16-byte aligned address, as floats.
+__device__ __forceinline__ void load8(const float* p, float* f) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) { f[q] = a[q]; f[q + 4] = b[q]; }
+}
+__device__ __forceinline__ void load8(const bf16_t* p, float* f) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) { f[2 * q] = __uint_as_float(v[q] << 16); f[2 * q + 1] = __uint_as_float(v[q] & 0xffff0000u); }
+}
+__device__ __forceinline__ void store8(float* p, const float* f) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{f[0], f[1], f[2], f[3]};
+  *reinterpret_cast<f32x4*>(p + 4) = f32x4{f[4], f[5], f[6], f[7]};
+}
+__device__ __forceinline__ void store8(bf16_t* p, const float* f) {
+  u32x4 v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = (uint32_t)f2bf(f[2 * q]) | ((uint32_t)f2bf(f[2 * q + 1]) << 16);
+  *reinterpret_cast<u32x4*>(p) = v;
 }
 
 template <class C> struct StageRegs {
@@ -424,8 +447,10 @@ tl_gemm(GemmArgs g) {
         stg[mfma32_row(lane, r) * SLD + jb * 32 + (lane & 31)] = acc[ib][2 * jp + jb][r];
     wave_sync();
     float o[32];
+    if constexpr (EPI != EPI_LAST) {   // lane l: column l of the block, 32 rows
 #pragma unroll
-    for (int q = 0; q < 32; ++q) o[q] = stg[q * SLD + lane];
+      for (int q = 0; q < 32; ++q) o[q] = stg[q * SLD + lane];
+    }
     const uint32_t ib0 = (uint32_t)(i0 + wm * C::WTM + ib * 32);
     if constexpr (EPI == EPI_GRAM) {
       const uint32_t ld = (uint32_t)g.lda;
@@ -483,44 +508,64 @@ tl_gemm(GemmArgs g) {
       float ulr = g.lr, uwd = g.wd;
       update_scalars(g.lrwd, ulr, uwd);
       const uint32_t ldx = (uint32_t)g.ldx;
-      const OP* X = reinterpret_cast<const OP*>(g.X) + mat * g.strideX;
       const float* X32 = g.X32 ? g.X32 + mat * g.strideX : nullptr;
       PT* W = g.param ? reinterpret_cast<PT*>(g.param) + mat * g.m * g.n : nullptr;
       float* O = g.ns_out ? g.ns_out + mat * g.m * g.n : nullptr;
       const uint32_t m = (uint32_t)g.m, n = (uint32_t)g.n;
-      if (jj < n) {
-        // four quarters of 8 rows: X and W reads of a quarter are issued together
+      if constexpr (EPI == EPI_LAST) {
+        // W row-major: the lane takes 8 consecutive columns of rows rr, rr + 8,
+        // rr + 16, rr + 24 of the staged block, so W, the fp32 master and O move
+        // as 16-byte vectors (8 lanes per 128-byte row segment), and all reads
+        // of the round are issued before its stores.
+        const int rr = lane >> 3, cc = (lane & 7) * 8;
+        const uint32_t j = (uint32_t)(j0 + wn * C::WTN + jp * 64 + cc);
+        const bool vec = (n % 8) == 0;   // aligned runs of 8 inside the matrix
 #pragma unroll
-        for (int hh = 0; hh < 4; ++hh) {
-          float xv[8], wv[8];
+        for (int p = 0; p < 4; ++p) {   // row group p: its reads are issued before its stores
+          float ov[8], xv[8], wv[8];
+          const f32x4 a = *reinterpret_cast<const f32x4*>(stg + (rr + 8 * p) * SLD + cc);
+          const f32x4 b = *reinterpret_cast<const f32x4*>(stg + (rr + 8 * p) * SLD + cc + 4);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) { ov[q] = a[q]; ov[q + 4] = b[q]; }
+          const uint32_t i = ib0 + rr + 8 * p;
+          if (X32) load8(X32 + i * ldx + j, xv);   // padded rows and columns: always readable
+          if (W && vec && i < m && j < n) load8(W + i * n + j, wv);
           if (X32) {
 #pragma unroll
-            for (int q = 0; q < 8; ++q) xv[q] = X32[(ib0 + 8 * hh + q) * ldx + jj];   // padded rows: readable
+            for (int q = 0; q < 8; ++q) ov[q] = g.ca * xv[q] + ov[q];
           }
-          if (!g.transposed && W) {
+          if (i >= m) continue;
+          if (vec) {
+            if (j >= n) continue;
+            if (O) store8(O + i * n + j, ov);
+            if (W) {
+              float nw[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              const uint32_t i = ib0 + 8 * hh + q;
-              wv[q] = i < m ? ld_as_f32(W, i * n + jj) : 0.f;
+              for (int q = 0; q < 8; ++q) nw[q] = apply_update(wv[q], ov[q], ulr, uwd, g.s);
+              store8(W + i * n + j, nw);
             }
-          }
-          if (X32) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) o[8 * hh + q] = g.ca * xv[q] + o[8 * hh + q];
-          }
-          if (!g.transposed) {
-            // W row-major: lanes cover consecutive columns of each row
+          } else {
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-              const uint32_t i = ib0 + 8 * hh + q;
-              if (i < m) {
-                if (O) O[i * n + jj] = o[8 * hh + q];
-                if (W) st_from_f32(W, i * n + jj, apply_update(wv[q], o[8 * hh + q], ulr, uwd, g.s));
-              }
+              if (j + q >= n) break;
+              if (O) O[i * n + j + q] = ov[q];
+              if (W) st_from_f32(W, i * n + j + q, apply_update(ld_as_f32(W, i * n + j + q), ov[q], ulr, uwd, g.s));
             }
           }
         }
-        if (g.transposed) {
+      } else {
+        if (jj < n) {
+          if (X32) {
+            // four quarters of 8 rows: the reads of a quarter are issued together
+#pragma unroll
+            for (int hh = 0; hh < 4; ++hh) {
+              float xh[8];
+#pragma unroll
+              for (int q = 0; q < 8; ++q) xh[q] = X32[(ib0 + 8 * hh + q) * ldx + jj];   // padded rows: readable
+#pragma unroll
+              for (int q = 0; q < 8; ++q) o[8 * hh + q] = g.ca * xh[q] + o[8 * hh + q];
+            }
+          }
           if (ib0 + 32 <= m && (m % 8) == 0) {
             // W is the transpose: this lane's 32 elements are contiguous and 16-byte aligned
             const uint32_t base = jj * m + ib0;
@@ -617,9 +662,12 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
     g.param = a.phase == PH_FULL ? a.param : nullptr; g.param_bf16 = a.param_dtype == DT_BF16;
     g.ns_out = a.ns_out; g.lr = a.lr; g.wd = a.wd; g.s = a.s; g.lrwd = a.lrwd;
     g.m = sh.m; g.n = sh.n; g.transposed = sh.transposed;
-    if (g.last)
+    if (g.last && !sh.transposed)
       MUON_LAUNCH("tl_apply_update", (tl_gemm<C, EPI_LAST, PT>), dim3(gemm_grid<C, EPI_LAST, PT>(g.tiles_total)),
                   dim3(C::THREADS), a.stream, g);
+    else if (g.last)
+      MUON_LAUNCH("tl_apply_update", (tl_gemm<C, EPI_LAST_T, PT>),
+                  dim3(gemm_grid<C, EPI_LAST_T, PT>(g.tiles_total)), dim3(C::THREADS), a.stream, g);
     else
       MUON_LAUNCH("tl_apply", (tl_gemm<C, EPI_APPLY, PT>), dim3(gemm_grid<C, EPI_APPLY, PT>(g.tiles_total)),
                   dim3(C::THREADS), a.stream, g);
