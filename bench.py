@@ -67,10 +67,8 @@ def kernel_model(name, count, M, N, prec, pdt, gdt, with_ns_out=False, ns_steps=
         if name == "sk_apply_update":
             return "hbm", E * (xs + 2 * ps + (4 if with_ns_out else 0)), "B"
     else:
-        if name == "tl_momentum_norm":
-            return "hbm", E * (gs + 8), "B"
-        if name == "tl_layout":
-            return "hbm", E * (gs + 4) + E * (2 * xs + (4 if prec == "bf16_x32" else 0)), "B"
+        if name == "tl_momentum_layout":
+            return "hbm", E * (gs + 8) + E * (2 * xs + (4 if prec == "bf16_x32" else 0)), "B"
         if name == "tl_gram":
             return "mfma", count * m * (m + 1) * n, "flop"
         if name == "tl_poly":

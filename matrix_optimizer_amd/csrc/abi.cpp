@@ -79,7 +79,7 @@ WsLayout workspace_layout(const BatchShape& b, int prec, int path) {
     L.skinny = false;
     L.mp = round_up(b.m, kTilePad);
     L.np = round_up(b.n, kTilePad);
-    L.nparts = norm_parts(b.M * b.N);
+    L.nparts = (L.mp / 64) * (L.np / 64);   // one ||U||^2 partial per 64x64 tile
     const size_t op = prec == PREC_F32 ? 4 : 2;
     const size_t xe = size_t(b.count) * L.mp * L.np;
     const size_t ae = size_t(b.count) * L.mp * L.mp;

@@ -39,12 +39,6 @@ constexpr int64_t kTiledBf16MinRows = 128;
 inline int effective_prec(int64_t m, int prec) {
   return (m > kSkinnyMaxRows && m < kTiledBf16MinRows) ? PREC_F32 : prec;
 }
-// Tiled path: workgroups per matrix that reduce ||U||_F^2.
-inline int64_t norm_parts(int64_t elems) {
-  int64_t p = (elems + 16383) / 16384;
-  return p < 1 ? 1 : (p > 1024 ? 1024 : p);
-}
-
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 

@@ -28,43 +28,19 @@ namespace {
 
 
 // ---------------------------------------------------------------------------
-// momentum / norm partials
-//   mode 0: M' = mu M + G in place; partial sum of U^2 (U = G + mu M' or M')
-//   mode 1: partial sum of U^2 of a given U (u_in)
-//   mode 2: M' = mu M + G in place and U written to u_out (no partials)
+// Momentum stage alone (muon_stage_momentum): M' = mu M + G in place and U
+// (G + mu M', or M') written to u_out.
 // ---------------------------------------------------------------------------
 template <typename GT>
 __global__ void __launch_bounds__(256)
-tl_momentum(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const float* __restrict__ u_in,
-            float* __restrict__ u_out, float* __restrict__ ssp, int64_t elems, int64_t nparts,
+tl_momentum(const GT* __restrict__ grad, float* __restrict__ mom, float* __restrict__ u_out, int64_t total,
             float mu, int nesterov) {
-  __shared__ float wsum[4];
-  const int64_t b = blockIdx.x / nparts;
-  const int64_t p = blockIdx.x % nparts;
-  const int64_t chunk = ((elems + nparts - 1) / nparts + 1023) / 1024 * 1024;
-  const int64_t lo = p * chunk;
-  const int64_t hi = lo + chunk < elems ? lo + chunk : elems;
-  const int64_t base = b * elems;
-  float ss = 0.f;
-  for (int64_t e = lo + threadIdx.x; e < hi; e += 256) {
-    const int64_t i = base + e;
-    float u;
-    if (mode == 1) {
-      u = u_in[i];
-    } else {
-      const float g = ld_as_f32(grad, i);
-      const float mn = mu * mom[i] + g;
-      mom[i] = mn;
-      u = nesterov ? g + mu * mn : mn;
-      if (mode == 2) u_out[i] = u;
-    }
-    ss += u * u;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const float g = ld_as_f32(grad, i);
+    const float mn = mu * mom[i] + g;
+    mom[i] = mn;
+    u_out[i] = nesterov ? g + mu * mn : mn;
   }
-  if (mode == 2) return;
-  ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  if (threadIdx.x == 0) ssp[blockIdx.x] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
 }
 
 // inv[b] = 1 / (sqrt(sum of partials) + eps), or 0 if that denominator is 0.
@@ -84,45 +60,54 @@ tl_norm_finalize(const float* __restrict__ ssp, int64_t nparts, float eps, float
 }
 
 // ---------------------------------------------------------------------------
-// X0 = U * inv in both layouts (and the fp32 master), 64x64 tiles through LDS.
-//   mode 0: U = G + mu M' (M' already updated) or M'
+// First pass of the tiled path, one 64x64 tile (Newton-Schulz orientation)
+// per workgroup: momentum and the Nesterov direction U (or a given U), the
+// tile's share of ||U||_F^2, and U, unnormalised, in both layouts (and the fp32
+// master).  The first Newton-Schulz step applies 1 / (||U||_F + eps): the Gram
+// epilogue scales by its square, the apply epilogue by it.  One pass over G
+// and M instead of two.
+//   mode 0: M' = mu M + G (in place), U = G + mu M' or M'
 //   mode 1: U from u_in
-// Tiles are in the Newton-Schulz orientation: (i, j), i < mp, j < np.
+// ssp[blockIdx.x] = sum of U^2 over the tile (fixed order).
 // ---------------------------------------------------------------------------
 template <typename GT, typename XO>
 __global__ void __launch_bounds__(256)
-tl_layout(int mode, const GT* __restrict__ grad, const float* __restrict__ mom, const float* __restrict__ u_in,
-          const float* __restrict__ inv, XO* __restrict__ X, XO* __restrict__ XT, float* __restrict__ X32,
-          int64_t m, int64_t n, int64_t mp, int64_t np, int transposed, float mu, int nesterov) {
+tl_first(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const float* __restrict__ u_in,
+         float* __restrict__ ssp, XO* __restrict__ X, XO* __restrict__ XT, float* __restrict__ X32,
+         int64_t m, int64_t n, int64_t mp, int64_t np, int transposed, float mu, int nesterov) {
   __shared__ float tile[64][65];
+  __shared__ float wsum[4];
   const int64_t tiles_j = np / 64;
   const int64_t tiles_per = (mp / 64) * tiles_j;
   const int64_t b = blockIdx.x / tiles_per;
   const int64_t tt = blockIdx.x % tiles_per;
   const int64_t i0 = (tt / tiles_j) * 64, j0 = (tt % tiles_j) * 64;
-  const float sc = inv[b];
   const int64_t sbase = b * m * n;
+  float ss = 0.f;
   for (int e = threadIdx.x; e < 64 * 64; e += 256) {
     int li, lj;
     if (!transposed) { li = e >> 6; lj = e & 63; }   // stored rows are X rows
     else { lj = e >> 6; li = e & 63; }               // stored rows are X columns
     const int64_t i = i0 + li, j = j0 + lj;
-    float v = 0.f;
+    float u = 0.f;
     if (i < m && j < n) {
       const int64_t si = sbase + (transposed ? j * m + i : i * n + j);
-      float u;
       if (mode == 1) {
         u = u_in[si];
       } else {
         const float g = ld_as_f32(grad, si);
-        const float mn = mom[si];
+        const float mn = mu * mom[si] + g;
+        mom[si] = mn;
         u = nesterov ? g + mu * mn : mn;
       }
-      v = u * sc;
     }
-    tile[li][lj] = v;
+    ss += u * u;
+    tile[li][lj] = u;
   }
-  __syncthreads();
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
+  __syncthreads();   // also: the tile is complete
+  if (threadIdx.x == 0) ssp[blockIdx.x] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
   const int64_t xb = b * mp * np;
   for (int e = threadIdx.x; e < 64 * 64; e += 256) {
     const int li = e >> 6, lj = e & 63;
@@ -150,6 +135,7 @@ struct GemmArgs {
   int64_t ldp, ldq, strideP, strideQ, K;
   int64_t tiles_n, tiles_per_mat;   // tiles along the output columns; tiles per matrix
   int64_t tiles_total;              // tiles of the launch (all matrices)
+  const float* inv0;                // first step: per-matrix 1/(||U||+eps) (X holds U unscaled), else null
   // EPI_GRAM: A32 (+ A16) out.  EPI_POLY: A32 in, PB out.
   float* A32; bf16_t* A16; void* PB; int64_t lda, strideA;
   float ca, cb, cc;
@@ -323,7 +309,18 @@ tl_gemm(GemmArgs g) {
   const int64_t mat = bid / g.tiles_per_mat;
   const int64_t tt = bid % g.tiles_per_mat;
   int64_t ti, tj;
-  if (EPI >= EPI_APPLY) { ti = tt / g.tiles_n; tj = tt % g.tiles_n; }
+  if (EPI >= EPI_APPLY) {
+    // grouped order: GM tile rows at a time, column by column, so the 32
+    // tiles an XCD runs at once form a GM x (32 / GM) block that shares few
+    // operand panels in its L2
+    constexpr int64_t GM = 4;
+    const int64_t tmm = g.tiles_per_mat / g.tiles_n;
+    const int64_t first = (tt / (GM * g.tiles_n)) * GM;
+    const int64_t rows = tmm - first < GM ? tmm - first : GM;
+    const int64_t tin = tt - first * g.tiles_n;
+    ti = first + tin % rows;
+    tj = tin / rows;
+  }
   else tri_tile<C::BM / C::BN>(tt, ti, tj);
   const int64_t i0 = ti * C::BM, j0 = tj * C::BN;
 
@@ -453,6 +450,11 @@ tl_gemm(GemmArgs g) {
     }
     const uint32_t ib0 = (uint32_t)(i0 + wm * C::WTM + ib * 32);
     if constexpr (EPI == EPI_GRAM) {
+      if (g.inv0) {   // A = inv^2 U U^T
+        const float sc = g.inv0[mat] * g.inv0[mat];
+#pragma unroll
+        for (int q = 0; q < 32; ++q) o[q] *= sc;
+      }
       const uint32_t ld = (uint32_t)g.lda;
       float* A32 = g.A32 + mat * g.strideA;
 #pragma unroll
@@ -487,7 +489,9 @@ tl_gemm(GemmArgs g) {
       OP* X = reinterpret_cast<OP*>(g.X) + mat * g.strideX;
       float* X32 = g.X32 ? g.X32 + mat * g.strideX : nullptr;
       // a X is in the accumulators already, except with the fp32 master;
+      // first step: X' = inv (a U + B U).
       // four quarters of 8 rows: the reads of a quarter are issued together
+      const float sc = g.inv0 ? g.inv0[mat] : 1.f;
 #pragma unroll
       for (int hh = 0; hh < 4; ++hh) {
         if (X32) {
@@ -496,9 +500,12 @@ tl_gemm(GemmArgs g) {
           for (int q = 0; q < 8; ++q) xv[q] = X32[(ib0 + 8 * hh + q) * ldx + jj];
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
-            o[8 * hh + q] = g.ca * xv[q] + o[8 * hh + q];
+            o[8 * hh + q] = sc * (g.ca * xv[q] + o[8 * hh + q]);
             X32[(ib0 + 8 * hh + q) * ldx + jj] = o[8 * hh + q];
           }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) o[8 * hh + q] *= sc;
         }
 #pragma unroll
         for (int q = 0; q < 8; ++q) st_from_f32(X, (ib0 + 8 * hh + q) * ldx + jj, o[8 * hh + q]);
@@ -534,6 +541,11 @@ tl_gemm(GemmArgs g) {
 #pragma unroll
             for (int q = 0; q < 8; ++q) ov[q] = g.ca * xv[q] + ov[q];
           }
+          if (g.inv0) {   // K = 1: X held U unscaled
+            const float sc = g.inv0[mat];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) ov[q] *= sc;
+          }
           if (i >= m) continue;
           if (vec) {
             if (j >= n) continue;
@@ -566,6 +578,11 @@ tl_gemm(GemmArgs g) {
               for (int q = 0; q < 8; ++q) o[8 * hh + q] = g.ca * xh[q] + o[8 * hh + q];
             }
           }
+          if (g.inv0) {   // K = 1: X held U unscaled
+            const float sc = g.inv0[mat];
+#pragma unroll
+            for (int q = 0; q < 32; ++q) o[q] *= sc;
+          }
           if (ib0 + 32 <= m && (m % 8) == 0) {
             // W is the transpose: this lane's 32 elements are contiguous and 16-byte aligned
             const uint32_t base = jj * m + ib0;
@@ -596,16 +613,6 @@ tl_update(PT* __restrict__ W, const float* __restrict__ O, int64_t total, float 
 }
 
 // ---------------------------------------------------------------------------
-template <typename GT>
-hipError_t launch_momentum(const StepArgs& a, int mode, float* ssp, int64_t nparts) {
-  const BatchShape& sh = a.shape;
-  const int64_t elems = sh.M * sh.N;
-  dim3 grid((unsigned)(sh.count * nparts)), block(256);
-  MUON_LAUNCH(mode == 2 ? "momentum" : "tl_momentum_norm", (tl_momentum<GT>), grid, block, a.stream, mode, (const GT*)a.grad, a.mom, a.u_in,
-                     a.u_out, ssp, elems, nparts, a.mu, a.nesterov);
-  return hipGetLastError();
-}
-
 // Persistent grid of tl_gemm<C, EPI, PT>: one wave of resident workgroups
 // (a multiple of 8, so each stays on one XCD), or fewer if there are fewer
 // tiles.
@@ -629,7 +636,8 @@ unsigned gemm_grid(int64_t tiles) {
 // The K Newton-Schulz steps as three NT products each, on tile config C.
 template <class C, typename PT>
 hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C::Op* X, typename C::Op* XT[2],
-                            float* X32, float* A32, bf16_t* A16, typename C::Op* PB, int64_t mp, int64_t np) {
+                            float* X32, float* A32, bf16_t* A16, typename C::Op* PB, int64_t mp, int64_t np,
+                            const float* inv) {
   typedef typename C::Op OP;
   hipError_t e;
   const int64_t tm = mp / C::BM, tn = np / C::BN;
@@ -640,6 +648,7 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
     // Gram: A = X X^T
     g.P = X; g.Q = X; g.ldp = np; g.ldq = np; g.strideP = mp * np; g.strideQ = mp * np; g.K = np;
     g.tiles_n = tm; g.tiles_per_mat = tri; g.tiles_total = sh.count * tri;
+    g.inv0 = k == 0 ? inv : nullptr;
     g.A32 = A32; g.A16 = A16; g.lda = mp; g.strideA = mp * mp;
     MUON_LAUNCH("tl_gram", (tl_gemm<C, EPI_GRAM, PT>), dim3(gemm_grid<C, EPI_GRAM, PT>(g.tiles_total)),
                 dim3(C::THREADS), a.stream, g);
@@ -657,6 +666,7 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
     g = GemmArgs{};
     g.P = PB; g.Q = XT[k & 1]; g.ldp = mp; g.ldq = mp; g.strideP = mp * mp; g.strideQ = np * mp; g.K = mp;
     g.tiles_n = tn; g.tiles_per_mat = tm * tn; g.tiles_total = sh.count * tm * tn;
+    g.inv0 = k == 0 ? inv : nullptr;
     g.ca = ca; g.X = X; g.X32 = X32; g.XT = XT[(k + 1) & 1]; g.ldx = np; g.ldxt = mp; g.strideX = mp * np;
     g.last = (k == a.steps - 1);
     g.param = a.phase == PH_FULL ? a.param : nullptr; g.param_bf16 = a.param_dtype == DT_BF16;
@@ -678,13 +688,13 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
 
 template <typename OP, typename PT>
 hipError_t run_products(const StepArgs& a, const BatchShape& sh, OP* X, OP* XT[2], float* X32, float* A32,
-                        bf16_t* A16, OP* PB, int64_t mp, int64_t np) {
+                        bf16_t* A16, OP* PB, int64_t mp, int64_t np, const float* inv) {
   if constexpr (sizeof(OP) == 4) {
-    return run_products_cfg<CfgF32, PT>(a, sh, X, XT, X32, A32, A16, PB, mp, np);
+    return run_products_cfg<CfgF32, PT>(a, sh, X, XT, X32, A32, A16, PB, mp, np, inv);
   } else {
     if (mp % CfgBig::BM == 0 && np % CfgBig::BN == 0)
-      return run_products_cfg<CfgBig, PT>(a, sh, X, XT, X32, A32, A16, PB, mp, np);
-    return run_products_cfg<CfgSmall, PT>(a, sh, X, XT, X32, A32, A16, PB, mp, np);
+      return run_products_cfg<CfgBig, PT>(a, sh, X, XT, X32, A32, A16, PB, mp, np, inv);
+    return run_products_cfg<CfgSmall, PT>(a, sh, X, XT, X32, A32, A16, PB, mp, np, inv);
   }
 }
 
@@ -694,12 +704,6 @@ hipError_t tiled_impl(const StepArgs& a, const WsLayout& L) {
   const int mode = a.phase == PH_FULL ? 0 : 1;
   float* ssp = (float*)(a.ws + L.ssp);
   float* inv = (float*)(a.ws + L.inv);
-  hipError_t e = launch_momentum<GT>(a, mode, ssp, L.nparts);
-  if (e != hipSuccess) return e;
-  MUON_LAUNCH("tl_norm_finalize", tl_norm_finalize, dim3((unsigned)sh.count), dim3(256), a.stream, ssp, L.nparts,
-              a.eps, inv);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-
   OP* X = (OP*)(a.ws + L.x);
   OP* XT[2] = {(OP*)(a.ws + L.xt0), (OP*)(a.ws + L.xt1)};
   float* X32 = a.prec == PREC_BF16_X32 ? (float*)(a.ws + L.x32) : nullptr;
@@ -707,15 +711,17 @@ hipError_t tiled_impl(const StepArgs& a, const WsLayout& L) {
   bf16_t* A16 = a.prec == PREC_F32 ? nullptr : (bf16_t*)(a.ws + L.a16);
   OP* PB = (OP*)(a.ws + L.pb);
   const int64_t mp = L.mp, np = L.np;
+  if (L.nparts != (mp / 64) * (np / 64)) return hipErrorInvalidValue;   // one norm partial per 64x64 tile
 
-  {
-    const unsigned blocks = (unsigned)(sh.count * (mp / 64) * (np / 64));
-    MUON_LAUNCH("tl_layout", (tl_layout<GT, OP>), dim3(blocks), dim3(256), a.stream, mode, (const GT*)a.grad,
-                       (const float*)a.mom, a.u_in, (const float*)inv, X, XT[0], X32, sh.m, sh.n, mp, np,
-                       (int)sh.transposed, a.mu, a.nesterov);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  return run_products<OP, PT>(a, sh, X, XT, X32, A32, A16, PB, mp, np);
+  MUON_LAUNCH("tl_momentum_layout", (tl_first<GT, OP>), dim3((unsigned)(sh.count * L.nparts)), dim3(256), a.stream,
+              mode, (const GT*)a.grad, a.mom, a.u_in, ssp, X, XT[0], X32, sh.m, sh.n, mp, np, (int)sh.transposed,
+              a.mu, a.nesterov);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  MUON_LAUNCH("tl_norm_finalize", tl_norm_finalize, dim3((unsigned)sh.count), dim3(256), a.stream, ssp, L.nparts,
+              a.eps, inv);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return run_products<OP, PT>(a, sh, X, XT, X32, A32, A16, PB, mp, np, inv);
 }
 
 template <typename OP>
@@ -734,9 +740,16 @@ hipError_t run_tiled(const StepArgs& a, const WsLayout& L) {
 }
 
 hipError_t run_momentum_only(const StepArgs& a) {
-  const int64_t nparts = norm_parts(a.shape.M * a.shape.N);
-  if (a.grad_dtype == DT_BF16) return launch_momentum<bf16_t>(a, 2, nullptr, nparts);
-  return launch_momentum<float>(a, 2, nullptr, nparts);
+  const int64_t total = a.shape.count * a.shape.M * a.shape.N;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (a.grad_dtype == DT_BF16)
+    MUON_LAUNCH("momentum", (tl_momentum<bf16_t>), dim3((unsigned)blocks), dim3(256), a.stream,
+                (const bf16_t*)a.grad, a.mom, a.u_out, total, a.mu, a.nesterov);
+  else
+    MUON_LAUNCH("momentum", (tl_momentum<float>), dim3((unsigned)blocks), dim3(256), a.stream,
+                (const float*)a.grad, a.mom, a.u_out, total, a.mu, a.nesterov);
+  return hipGetLastError();
 }
 
 hipError_t run_update_only(const StepArgs& a) {
