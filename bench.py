@@ -111,15 +111,21 @@ def device_info() -> dict:
 
 
 def kernel_sources_sha256() -> str:
-    """Hash of the HIP/C++ sources the kernels are built from."""
+    """Hash of the code in the HIP/C++ sources the kernels are built from:
+    comments are removed and whitespace runs collapsed first, so an edit that
+    touches only comments or layout keeps counter summaries valid."""
     import hashlib
+    import re
     d = os.path.join(ROOT, "matrix_optimizer_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(d)):
         if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(d, f), encoding="utf-8") as fh:
+                src = fh.read()
+            src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+            src = re.sub(r"//[^\n]*", " ", src)
             h.update(f.encode())
-            with open(os.path.join(d, f), "rb") as fh:
-                h.update(fh.read())
+            h.update(" ".join(src.split()).encode())
     return h.hexdigest()
 
 

@@ -6,7 +6,8 @@
 // is cut into chunks of L columns, one workgroup per chunk.  sk_first fuses
 // momentum, the Nesterov direction U, the Frobenius-norm partials and the
 // split-K Gram partial U_c U_c^T of each chunk (bf16 MFMA, fp32 accumulation)
-// and stores U.  Two forms of Newton-Schulz follow.
+// and stores U, unnormalised, in MFMA-ready 32-column x 8-row tiles.  Two
+// forms of Newton-Schulz follow.
 //
 // Gram space (default).  Every step left-multiplies X by a polynomial of the
 // Gram matrix, X_{k+1} = B_k X_k with B_k = a I + b A_k + c A_k^2 (the
@@ -15,15 +16,20 @@
 // exactly in exact arithmetic (the Gram Newton-Schulz of the DMuon-2 paper,
 // Appendix C.3: iterate on the Gram matrix, multiply back into X once).  All
 // B_k are polynomials in A_0, so they commute and stay symmetric.
-//   sk_gram_ns  one workgroup per matrix: A_0 from the chunk partials (summed
-//               in chunk order, fp64), then the K steps on 32x32 fp64 MFMA,
-//               Q = B_{K-1} ... B_0 / (||U||_F + eps) written as the per-lane
-//               MFMA operand fragments of the apply kernel: a bf16 hi + lo
-//               pair (the product keeps about 16 bits of Q), or fp32 on the
-//               check path.
-//   sk_iter<LAST>  one workgroup per chunk: O = Q U on MFMA, then decoupled
-//               decay and the update of W (or O written out).
-// Three launches and two passes over X, whatever K is.
+//   sk_gram_ns  one workgroup per matrix: A_0 = (sum of the chunk partials,
+//               in chunk order, fp64) / (||U||_F + eps)^2, then the K steps
+//               on 16x16x4 MFMA (fp32 on the bf16 paths, fp64 on the check
+//               path), Q = B_{K-1} ... B_0 / (||U||_F + eps) written as the
+//               per-lane operand fragments of the apply kernel: a bf16 hi +
+//               lo pair (the product keeps about 16 bits of Q), or fp32.
+//   sk_apply    one wave per 64 columns: O = Q U on 32x32 MFMA, then the
+//               decoupled decay and the update of W (or O written out).  A
+//               wide W gets O^T = U^T Q (Q is symmetric; the MFMA operands
+//               swapped) through a wave-private LDS buffer, so W is read and
+//               written as 16-byte row segments; for a tall W, whose rows are
+//               the columns of U, O = Q U leaves each lane a run of 4
+//               consecutive elements of one W row.
+// Three launches and two passes over U, whatever K is.
 //
 // Step by step.  The iteration in the pages' order, K rounds of
 //   sk_bprime   one workgroup per matrix: A = X X^T from the chunk partials,
