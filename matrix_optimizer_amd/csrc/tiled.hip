@@ -151,37 +151,42 @@ struct GemmArgs {
 // workgroup, BK reduction slice per LDS stage, WAVES_M x WAVES_N waves, each
 // owning a (BM/WAVES_M) x (BN/WAVES_N) sub-tile of 32x32 MFMA blocks.  LDS rows
 // carry 16 bytes of padding so the MFMA fragment reads are bank-conflict free.
-template <typename OP, int BM_, int BN_, int BK_, int WGM_, int WGN_>
+template <typename OP, int BM_, int BN_, int BK_, int WGM_, int WGN_, bool DIRECT_ = false>
 struct GemmCfg {
   typedef OP Op;
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int WAVES_M = WGM_, WAVES_N = WGN_;
   static constexpr int THREADS = 64 * WGM_ * WGN_;
+  static constexpr int WAVES = WGM_ * WGN_;
   // at least two waves per SIMD: 8-wave tiles by construction, 4-wave tiles
   // so that two workgroups share a CU (register budget 256 per lane)
   static constexpr int WAVES_PER_SIMD = 2;
   static constexpr int WTM = BM / WGM_, WTN = BN / WGN_;
   static constexpr int IB = WTM / 32, JB = WTN / 32;
   static constexpr int EPV = 16 / (int)sizeof(OP);
-  static constexpr int LD = BK + EPV;
+  // DIRECT: operand tiles go from global memory straight into LDS (no
+  // register staging), rows unpadded with 16-byte chunk c of row r stored in
+  // slot c ^ (r & 7); else register-staged into rows padded by 16 bytes.
+  static constexpr bool DIRECT = DIRECT_;
+  static constexpr int LD = DIRECT ? BK : BK + EPV;
   static constexpr int VPR = BK / EPV;
   static constexpr int PV = BM * VPR / THREADS;
   static constexpr int QV = BN * VPR / THREADS;
   static constexpr int RPP = THREADS / VPR;          // tile rows per load pass
   static constexpr int STAGE = (BM + BN) * LD;       // elements per LDS stage
+  // direct loads: one wave instruction fills RPI whole rows (1 KB); LPW
+  // instructions per wave per stage, the first half in P's rows
+  static constexpr int RPI = 64 / VPR;
+  static constexpr int LPW = (BM + BN) / RPI / WAVES;
   static_assert(BM == BN || BM == 2 * BN, "symmetric products tile BM = BN or 2 BN");
   static_assert(BM * VPR % THREADS == 0 && BN * VPR % THREADS == 0, "load split");
+  static_assert(!DIRECT || (sizeof(OP) == 2 && BK == 64 && BM == BN && (BM / RPI) % WAVES == 0),
+                "direct loads: bf16, 8 chunks per row, P rows in whole instructions");
 };
 // bf16, 256x256 tiles, 8 waves of 128x64 (4x2 MFMA blocks): each fragment
 // read from LDS feeds more MFMAs than in the 128x128 tile.  Needs rows and
 // columns padded to 256.
-#ifndef MUON_BIG_WAVES_N
-#define MUON_BIG_WAVES_N 4
-#endif
-#ifndef MUON_BIG_BK
-#define MUON_BIG_BK 64
-#endif
-typedef GemmCfg<bf16_t, 256, 256, MUON_BIG_BK, 2, MUON_BIG_WAVES_N> CfgBig;
+typedef GemmCfg<bf16_t, 256, 256, 64, 2, 4, true> CfgBig;
 typedef GemmCfg<bf16_t, 128, 128, 64, 2, 2> CfgSmall;
 
 typedef GemmCfg<float, 128, 128, 32, 2, 2> CfgF32;
@@ -287,28 +292,17 @@ __device__ __forceinline__ void stage_store(const StageRegs<C>& sr, typename C::
   for (int i = 0; i < C::QV; ++i) *reinterpret_cast<u32x4*>(ql + i * C::RPP * C::LD) = sr.q[i];
 }
 
-template <class C, int EPI, typename PT>
-__global__ void __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD)
-tl_gemm(GemmArgs g) {
-  typedef typename C::Op OP;
-  __shared__ __attribute__((aligned(16))) OP lds[2 * C::STAGE];
-
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int w = t >> 6;
-  const int wm = w / C::WAVES_N, wn = w % C::WAVES_N;
-  // Persistent: workgroup b takes tiles b, b + gridDim, ...  A tile's
-  // epilogue stores drain while the next tile's main loop runs.
-  // Workgroups are dealt round-robin to the 8 XCDs, so with gridDim % 8 == 0
-  // a workgroup's tiles stay on one XCD; give each XCD a contiguous range of
-  // tiles so the operand panels its concurrent tiles share meet in its L2.
+// Tile (ti, tj) of matrix mat for launch-linear tile index lin.  Workgroups
+// are dealt round-robin to the 8 XCDs, so with gridDim % 8 == 0 a workgroup's
+// tiles stay on one XCD; each XCD gets a contiguous range of tiles so the
+// operand panels its concurrent tiles share meet in its L2.
+template <class C, int EPI>
+__device__ __forceinline__ void tile_coords(const GemmArgs& g, int64_t lin, bool xcd_map, int64_t& mat, int64_t& ti,
+                                            int64_t& tj) {
   const int64_t total = g.tiles_total;
-  const bool xcd_map = (total & 7) == 0 && (gridDim.x & 7) == 0;
-  for (int64_t lin = blockIdx.x; lin < total; lin += gridDim.x) {
   const int64_t bid = xcd_map ? (lin & 7) * (total >> 3) + (lin >> 3) : lin;
-  const int64_t mat = bid / g.tiles_per_mat;
+  mat = bid / g.tiles_per_mat;
   const int64_t tt = bid % g.tiles_per_mat;
-  int64_t ti, tj;
   if (EPI >= EPI_APPLY) {
     // grouped order: GM tile rows at a time, column by column, so the 32
     // tiles an XCD runs at once form a GM x (32 / GM) block that shares few
@@ -320,23 +314,258 @@ tl_gemm(GemmArgs g) {
     const int64_t tin = tt - first * g.tiles_n;
     ti = first + tin % rows;
     tj = tin / rows;
+  } else {
+    tri_tile<C::BM / C::BN>(tt, ti, tj);
   }
-  else tri_tile<C::BM / C::BN>(tt, ti, tj);
+}
+
+// A wave-uniform 64-bit value moved to scalar registers (the compiler
+// computes uniform divisions in vector registers; these stay live across a
+// tile's main loop).
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint64_t u = (uint64_t)v;
+  // readfirstlane returns int: each half goes through uint32_t (no sign extension)
+  return (int64_t)((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)u) |
+                   ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(u >> 32)) << 32));
+}
+template <typename T> __device__ __forceinline__ T* uniform_ptr(T* p) {
+  return reinterpret_cast<T*>((uintptr_t)uniform64((int64_t)(uintptr_t)p));
+}
+
+// Waits (on this wave's counter) until at most n vector-memory operations
+// are outstanding.
+__device__ __forceinline__ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// 16 bytes per lane from global memory (uniform base + per-lane 32-bit byte
+// offset) straight into LDS at lds_addr + 16 lane.  Written as asm: the
+// compiler neither waits on it nor recycles its address registers early
+// (either would serialise the prefetch); the caller waits with vmcnt before
+// the data is read.
+// M0 is written here and nowhere else in these kernels (the generated code
+// holds no other use of it), so clobbering the reserved register is safe.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
+  // base and lds_addr are wave-uniform; make that visible to the compiler
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  // (readfirstlane returns int: go through uint32_t so the low half is not
+  // sign-extended into the high half)
+  const uint64_t sb = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b) |
+                      ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32);
+  const uint32_t sl = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sb), "s"(sl) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Workgroup barrier without the release/acquire fences of __syncthreads,
+// which would also wait for every outstanding global store and LDS-DMA load;
+// the caller waits for what it needs.  This wave's LDS accesses complete
+// first, and the compiler moves no memory access across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Spreads a block of N MFMAs with V vector-memory reads and D LDS reads in
+// between (one MFMA, then the next share of each).
+template <int N, int V, int D, int I = 0>
+__device__ __forceinline__ void sched_mfma_block() {
+  if constexpr (I < N) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int v = V * (I + 1) / N - V * I / N;
+    constexpr int d = D * (I + 1) / N - D * I / N;
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);
+    if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(0x100, d, 0);
+    sched_mfma_block<N, V, D, I + 1>();
+  }
+}
+
+template <class C, int EPI, typename PT>
+__global__ void __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD)
+tl_gemm(GemmArgs g) {
+  typedef typename C::Op OP;
+  // epilogue staging: one 32 x SLD fp32 block per wave; with direct loads it
+  // sits above stage 0, which receives the next tile's first k-slice meanwhile
+  constexpr int SLD = 72;   // staging row stride (floats): conflict-free writes and reads
+  constexpr int STG_ELEMS = C::WAVES * 32 * SLD * 4 / (int)sizeof(OP);
+  constexpr int STG_OFF = C::DIRECT ? C::STAGE : 0;
+  constexpr int LDS_ELEMS = 2 * C::STAGE > STG_OFF + STG_ELEMS ? 2 * C::STAGE : STG_OFF + STG_ELEMS;
+  __shared__ __attribute__((aligned(16))) OP lds[LDS_ELEMS];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
+  const int wm = w / C::WAVES_N, wn = w % C::WAVES_N;
+  // Persistent: workgroup b takes tiles b, b + gridDim, ...  A tile's
+  // epilogue stores drain while the next tile's main loop runs.
+  const int64_t total = g.tiles_total;
+  const bool xcd_map = (total & 7) == 0 && (gridDim.x & 7) == 0;
+
+  // direct loads: instruction i of this wave fills rows (w + i WAVES) RPI ..
+  // + RPI - 1 of the stage (P's rows first, then Q's); the lane's byte offset
+  // within its operand is the same for every instruction of that operand up
+  // to a uniform multiple of WAVES RPI rows, which goes into the scalar base
+  [[maybe_unused]] uint32_t voff_p = 0, voff_q = 0;
+  if constexpr (C::DIRECT) {
+    const int lrow = lane / C::VPR;
+    const int lchunk = (lane % C::VPR) ^ (lrow & 7);
+    const int row = w * C::RPI + lrow;
+    voff_p = (uint32_t)((row * g.ldp + lchunk * C::EPV) * (int64_t)sizeof(OP));
+    voff_q = (uint32_t)((row * g.ldq + lchunk * C::EPV) * (int64_t)sizeof(OP));
+  }
+  // direct loads of k-slice k0 of the tile whose operand rows start at
+  // pbase / qbase into stage st
+  [[maybe_unused]] auto dma_slice = [&](int st, const OP* pbase, const OP* qbase, int64_t k0) {
+    constexpr int HALF = C::LPW / 2;
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i) {
+      const int ins = w + i * C::WAVES;
+      const int64_t rows = (int64_t)(i % HALF) * C::WAVES * C::RPI;
+      const OP* src = i < HALF ? pbase + rows * g.ldp + k0 : qbase + rows * g.ldq + k0;
+      const uint32_t la =
+          (uint32_t)(uintptr_t)(__attribute__((address_space(3))) OP*)(lds + st * C::STAGE + ins * C::RPI * C::LD);
+      lds_dma16(src, i < HALF ? voff_p : voff_q, la);
+    }
+  };
+  bool stage0_ready = false;   // direct loads: stage 0 already holds this tile's first k-slice
+
+  for (int64_t lin = blockIdx.x; lin < total; lin += gridDim.x) {
+  int64_t mat, ti, tj;
+  tile_coords<C, EPI>(g, lin, xcd_map, mat, ti, tj);
+  mat = uniform64(mat); ti = uniform64(ti); tj = uniform64(tj);
   const int64_t i0 = ti * C::BM, j0 = tj * C::BN;
 
+  f32x16 acc[C::IB][C::JB];
+#pragma unroll
+  for (int a = 0; a < C::IB; ++a)
+#pragma unroll
+    for (int b = 0; b < C::JB; ++b) acc[a][b] = f32x16{};
+  const int64_t KT = g.K / C::BK;
+
+  // a X term of the apply products: the Q stage holds X^T[j][k] = X[k][j]
+  // for this k-slice; when the slice covers rows of this wave's output, add
+  // a X[i][j] from LDS to the accumulators (no global read in the epilogue).
+  // The fp32 master (X32) is added in the epilogue instead.
+  auto add_ax = [&](const OP* Qs, int64_t kt) {
+    if constexpr (EPI >= EPI_APPLY) {
+      if (!g.X32) {
+        const int64_t krel = kt * C::BK - (i0 + wm * C::WTM);
+        if (krel > -C::BK && krel < C::WTM) {
+#pragma unroll
+          for (int ib = 0; ib < C::IB; ++ib) {
+            const int off = ib * 32 - (int)krel;   // block row 0 relative to the slice
+            if (off < 0 || off >= C::BK) continue;
+#pragma unroll
+            for (int jb = 0; jb < C::JB; ++jb) {
+              const OP* xrow = Qs + jb * 32 * C::LD;
+#pragma unroll
+              for (int qd = 0; qd < 4; ++qd) {
+                // elements off + 8 qd + 4 (lane / 32) .. + 3 of the lane's row
+                const int chunk = (off + 8 * qd) / C::EPV;
+                const int within = (off + 8 * qd) % C::EPV + 4 * (lane >> 5);
+                const int slot = C::DIRECT ? (chunk ^ (lane & 7)) : chunk;
+                const OP* xq = xrow + slot * C::EPV + within;
+                float xv[4];
+                if constexpr (sizeof(OP) == 2) {
+                  const uint2 u = *reinterpret_cast<const uint2*>(xq);
+                  xv[0] = __uint_as_float(u.x << 16);
+                  xv[1] = __uint_as_float(u.x & 0xffff0000u);
+                  xv[2] = __uint_as_float(u.y << 16);
+                  xv[3] = __uint_as_float(u.y & 0xffff0000u);
+                } else {
+                  const f32x4 u = *reinterpret_cast<const f32x4*>(xq);
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) xv[e] = u[e];
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[ib][jb][4 * qd + e] += g.ca * xv[e];
+              }
+            }
+          }
+        }
+      }
+    }
+  };
+
+  if constexpr (C::DIRECT) {
+    // Two LDS stages; k-slice kt + 1 is loaded (direct) while slice kt is
+    // multiplied, its loads and the fragment reads spread among the MFMAs.
+    // The last slice of a tile loads the next tile's first slice instead, so
+    // a tile starts without waiting for the previous epilogue's stores.
+    // K is a multiple of 2 BK: slice kt uses stage kt & 1.
+    const OP* pb = reinterpret_cast<const OP*>(g.P) + mat * g.strideP + i0 * g.ldp;
+    const OP* qb = reinterpret_cast<const OP*>(g.Q) + mat * g.strideQ + j0 * g.ldq;
+    const OP* npb = pb;
+    const OP* nqb = qb;
+    if (lin + gridDim.x < total) {
+      int64_t nmat, nti, ntj;
+      tile_coords<C, EPI>(g, lin + gridDim.x, xcd_map, nmat, nti, ntj);
+      npb = reinterpret_cast<const OP*>(g.P) + nmat * g.strideP + nti * C::BM * g.ldp;
+      nqb = reinterpret_cast<const OP*>(g.Q) + nmat * g.strideQ + ntj * C::BN * g.ldq;
+    }
+    npb = uniform_ptr(npb);
+    nqb = uniform_ptr(nqb);
+    if (!stage0_ready) {
+      dma_slice(0, pb, qb, 0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      lds_barrier();
+    }
+    bf16x8 fa[2][C::IB], fb[2][C::JB];
+    const OP* Pw = lds + (wm * C::WTM + (lane & 31)) * C::LD;
+    const OP* Qw = lds + (C::BM + wn * C::WTN + (lane & 31)) * C::LD;
+    auto read_frags = [&](int buf, int st, int kk) {
+      const int slot = (2 * kk + (lane >> 5)) ^ (lane & 7);
+#pragma unroll
+      for (int ib = 0; ib < C::IB; ++ib)
+        fa[buf][ib] = *reinterpret_cast<const bf16x8*>(Pw + st * C::STAGE + ib * 32 * C::LD + slot * 8);
+#pragma unroll
+      for (int jb = 0; jb < C::JB; ++jb)
+        fb[buf][jb] = *reinterpret_cast<const bf16x8*>(Qw + st * C::STAGE + jb * 32 * C::LD + slot * 8);
+    };
+    auto mfmas = [&](int buf) {
+#pragma unroll
+      for (int ib = 0; ib < C::IB; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < C::JB; ++jb)
+          acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][ib], fb[buf][jb], acc[ib][jb], 0, 0, 0);
+    };
+    read_frags(0, 0, 0);
+    auto slice = [&](int st, int64_t kt) {
+      const bool last = kt + 1 == KT;
+      dma_slice(st ^ 1, last ? npb : pb, last ? nqb : qb, last ? 0 : (kt + 1) * C::BK);
+      read_frags(1, st, 1);
+      mfmas(0);
+      sched_mfma_block<C::IB * C::JB, C::LPW, C::IB + C::JB>();
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(0, st, 2);
+      mfmas(1);
+      sched_mfma_block<C::IB * C::JB, 0, C::IB + C::JB>();
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(1, st, 3);
+      mfmas(0);
+      sched_mfma_block<C::IB * C::JB, 0, C::IB + C::JB>();
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(1);
+      __builtin_amdgcn_sched_barrier(0);
+      add_ax(lds + st * C::STAGE + (C::BM + wn * C::WTN + (lane & 31)) * C::LD, kt);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this wave's loads of the next slice
+      lds_barrier();                               // everyone's; stage st is free again
+      if (!last) read_frags(0, st ^ 1, 0);
+    };
+    for (int64_t kt = 0; kt < KT; kt += 2) {
+      slice(0, kt);
+      slice(1, kt + 1);
+    }
+    stage0_ready = lin + gridDim.x < total;
+  } else {
   const int r0 = t / C::VPR, cv = (t % C::VPR) * C::EPV;
   const OP* Pp = reinterpret_cast<const OP*>(g.P) + mat * g.strideP + (i0 + r0) * g.ldp + cv;
   const OP* Qp = reinterpret_cast<const OP*>(g.Q) + mat * g.strideQ + (j0 + r0) * g.ldq + cv;
   const int64_t pstep = (int64_t)C::RPP * g.ldp, qstep = (int64_t)C::RPP * g.ldq;
 
   StageRegs<C> sr;
-  f32x16 acc[C::IB][C::JB];
-#pragma unroll
-  for (int a = 0; a < C::IB; ++a)
-#pragma unroll
-    for (int b = 0; b < C::JB; ++b) acc[a][b] = f32x16{};
-
-  const int64_t KT = g.K / C::BK;
   stage_load<C>(sr, Pp, Qp, pstep, qstep, 0);
   stage_store<C>(sr, lds + r0 * C::LD + cv);
   __syncthreads();
@@ -376,45 +605,10 @@ tl_gemm(GemmArgs g) {
             acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[ib], bv[jb], acc[ib][jb], 0, 0, 0);
       }
     }
-    if constexpr (EPI >= EPI_APPLY) {
-      // a X term: the Q stage holds X^T[j][k] = X[k][j] for this k-slice; when
-      // the slice covers rows of this wave's output, add a X[i][j] from LDS to
-      // the accumulators (no global read in the epilogue).  The fp32 master
-      // (X32) is added in the epilogue instead.
-      if (!g.X32) {
-        const int64_t krel = kt * C::BK - (i0 + wm * C::WTM);
-        if (krel > -C::BK && krel < C::WTM) {
-#pragma unroll
-          for (int ib = 0; ib < C::IB; ++ib) {
-            const int off = ib * 32 - (int)krel;   // block row 0 relative to the slice
-            if (off < 0 || off >= C::BK) continue;
-#pragma unroll
-            for (int jb = 0; jb < C::JB; ++jb) {
-              const OP* xq = Qs + jb * 32 * C::LD + off + 4 * (lane >> 5);
-#pragma unroll
-              for (int qd = 0; qd < 4; ++qd) {
-                float xv[4];
-                if constexpr (sizeof(OP) == 2) {
-                  const uint2 u = *reinterpret_cast<const uint2*>(xq + 8 * qd);
-                  xv[0] = __uint_as_float(u.x << 16);
-                  xv[1] = __uint_as_float(u.x & 0xffff0000u);
-                  xv[2] = __uint_as_float(u.y << 16);
-                  xv[3] = __uint_as_float(u.y & 0xffff0000u);
-                } else {
-                  const f32x4 u = *reinterpret_cast<const f32x4*>(xq + 8 * qd);
-#pragma unroll
-                  for (int e = 0; e < 4; ++e) xv[e] = u[e];
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[ib][jb][4 * qd + e] += g.ca * xv[e];
-              }
-            }
-          }
-        }
-      }
-    }
+    add_ax(Qs, kt);
     if (kt + 1 < KT) stage_store<C>(sr, lds + (st ^ 1) * C::STAGE + r0 * C::LD + cv);
     __syncthreads();
+  }
   }
 
   // ---- epilogues -------------------------------------------------------------
@@ -428,9 +622,7 @@ tl_gemm(GemmArgs g) {
   // inside one padded matrix fit in 32 bits (the planner caps a padded matrix
   // at 2^31 elements).
   static_assert(C::JB % 2 == 0, "epilogue stages 64-column blocks");
-  constexpr int SLD = 72;   // staging row stride (floats): conflict-free writes and reads
-  static_assert(C::THREADS / 64 * 32 * SLD * 4 <= 2 * C::STAGE * (int)sizeof(OP), "staging fits in LDS");
-  float* stg = reinterpret_cast<float*>(lds) + w * (32 * SLD);
+  float* stg = reinterpret_cast<float*>(lds + STG_OFF) + w * (32 * SLD);
   const bool diag = (EPI < EPI_APPLY) && (tj >= (C::BM / C::BN) * ti);   // inside the diagonal block
 #pragma clang loop unroll(full)
   for (int rb = 0; rb < C::IB * C::JB / 2; ++rb) {
@@ -599,7 +791,10 @@ tl_gemm(GemmArgs g) {
       }
     }
   }
-  __syncthreads();   // every wave is done with its staging region before the next tile's stage 0
+  // every wave is done with its staging region before the next tile's
+  // loads land there (no wait for this tile's stores)
+  if constexpr (C::DIRECT) lds_barrier();
+  else __syncthreads();
   }  // tiles
 }
 
