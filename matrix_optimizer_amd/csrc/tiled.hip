@@ -166,7 +166,7 @@ struct GemmCfg {
   static constexpr int EPV = 16 / (int)sizeof(OP);
   // DIRECT: operand tiles go from global memory straight into LDS (no
   // register staging), rows unpadded with 16-byte chunk c of row r stored in
-  // slot c ^ (r & 7); else register-staged into rows padded by 16 bytes.
+  // slot c ^ swz(r); else register-staged into rows padded by 16 bytes.
   static constexpr bool DIRECT = DIRECT_;
   static constexpr int LD = DIRECT ? BK : BK + EPV;
   static constexpr int VPR = BK / EPV;
@@ -319,6 +319,14 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& g, int64_t lin, bool
   }
 }
 
+// Slot swizzle of the direct-load LDS tiles: 16-byte chunk c of row r sits in
+// slot c ^ swz(r).  LDS serves a 16-byte read for 16 lanes per cycle (64
+// banks); the 16 rows an MFMA fragment read touches per cycle (two 128-byte
+// rows per bank sweep) then hit 16 different bank groups.  (r & 7 would
+// leave rows r and r + 8 on the same banks: SQ_LDS_BANK_CONFLICT counted
+// 1.0e8 cycles on an 8192^3 product with it, none with this one.)
+__device__ __forceinline__ int lds_swz(int r) { return (r >> 1) & 7; }
+
 // A wave-uniform 64-bit value moved to scalar registers (the compiler
 // computes uniform divisions in vector registers; these stay live across a
 // tile's main loop).
@@ -410,7 +418,9 @@ tl_gemm(GemmArgs g) {
   [[maybe_unused]] uint32_t voff_p = 0, voff_q = 0;
   if constexpr (C::DIRECT) {
     const int lrow = lane / C::VPR;
-    const int lchunk = (lane % C::VPR) ^ (lrow & 7);
+    // the lane's stage row is 8 (w + WAVES i) + lrow; its swizzle does not
+    // depend on i
+    const int lchunk = (lane % C::VPR) ^ lds_swz(8 * w + lrow);
     const int row = w * C::RPI + lrow;
     voff_p = (uint32_t)((row * g.ldp + lchunk * C::EPV) * (int64_t)sizeof(OP));
     voff_q = (uint32_t)((row * g.ldq + lchunk * C::EPV) * (int64_t)sizeof(OP));
@@ -465,7 +475,7 @@ tl_gemm(GemmArgs g) {
                 // elements off + 8 qd + 4 (lane / 32) .. + 3 of the lane's row
                 const int chunk = (off + 8 * qd) / C::EPV;
                 const int within = (off + 8 * qd) % C::EPV + 4 * (lane >> 5);
-                const int slot = C::DIRECT ? (chunk ^ (lane & 7)) : chunk;
+                const int slot = C::DIRECT ? (chunk ^ lds_swz(lane & 31)) : chunk;
                 const OP* xq = xrow + slot * C::EPV + within;
                 float xv[4];
                 if constexpr (sizeof(OP) == 2) {
@@ -516,7 +526,7 @@ tl_gemm(GemmArgs g) {
     const OP* Pw = lds + (wm * C::WTM + (lane & 31)) * C::LD;
     const OP* Qw = lds + (C::BM + wn * C::WTN + (lane & 31)) * C::LD;
     auto read_frags = [&](int buf, int st, int kk) {
-      const int slot = (2 * kk + (lane >> 5)) ^ (lane & 7);
+      const int slot = (2 * kk + (lane >> 5)) ^ lds_swz(lane & 31);
 #pragma unroll
       for (int ib = 0; ib < C::IB; ++ib)
         fa[buf][ib] = *reinterpret_cast<const bf16x8*>(Pw + st * C::STAGE + ib * 32 * C::LD + slot * 8);
