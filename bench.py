@@ -110,34 +110,60 @@ def device_info() -> dict:
     return info
 
 
-def kernel_sources_sha256() -> str:
+def kernel_sources_sha256(files=None):
     """Hash of the code in the HIP/C++ sources the kernels are built from:
     comments are removed and whitespace runs collapsed first, so an edit that
-    touches only comments or layout keeps counter summaries valid."""
+    touches only comments or layout keeps counter summaries valid.  With
+    `files`, a dict {file: hash} over just those files; else one hash over
+    all of them."""
     import hashlib
     import re
     d = os.path.join(ROOT, "matrix_optimizer_amd", "csrc")
+
+    def code(f):
+        with open(os.path.join(d, f), encoding="utf-8") as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        return " ".join(src.split()).encode()
+
+    if files is not None:
+        return {f: hashlib.sha256(code(f)).hexdigest() for f in files}
     h = hashlib.sha256()
     for f in sorted(os.listdir(d)):
         if f.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(d, f), encoding="utf-8") as fh:
-                src = fh.read()
-            src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
-            src = re.sub(r"//[^\n]*", " ", src)
             h.update(f.encode())
-            h.update(" ".join(src.split()).encode())
+            h.update(code(f))
     return h.hexdigest()
+
+
+# source files whose code decides each traced kernel's memory traffic
+KERNEL_SOURCES = {"sk_": ["common.h", "internal.h", "skinny.hip"], "tl_": ["common.h", "internal.h", "tiled.hip"]}
+
+
+def kernel_source_files(kernel: str):
+    for prefix, files in KERNEL_SOURCES.items():
+        if kernel.startswith(prefix):
+            return files
+    return None
 
 
 def measured_traffic(workload: str, kernel: str, prec: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel sources (else None)."""
+    summary, if it was taken on the current code of the kernel's sources
+    (else None)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{prec}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    if rec.get("sources_sha256") != kernel_sources_sha256():
+    recorded = rec.get("sources_sha256")
+    if not isinstance(recorded, dict) or not recorded:
+        return None
+    files = kernel_source_files(kernel)
+    if files is None or any(f not in recorded for f in files):
+        return None
+    if kernel_sources_sha256(files) != {f: recorded[f] for f in files}:
         return None
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else k["bytes_per_launch"]
