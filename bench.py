@@ -68,7 +68,12 @@ def kernel_model(name, count, M, N, prec, pdt, gdt, with_ns_out=False, ns_steps=
             return "hbm", E * (xs + 2 * ps + (4 if with_ns_out else 0)), "B"
     else:
         if name == "tl_momentum_layout":
-            return "hbm", E * (gs + 8) + E * (2 * xs + (4 if prec == "bf16_x32" else 0)), "B"
+            # G read, M read and written, X written (bf16 operands unless f32),
+            # X^T too unless the products use 256 x 256 tiles, the fp32 master
+            ops = 4 if prec == "f32" else 2
+            mp, np_ = -(-m // 128) * 128, -(-n // 128) * 128
+            big = prec != "f32" and mp % 256 == 0 and np_ % 256 == 0
+            return "hbm", E * (gs + 8) + E * (ops * (1 if big else 2) + (4 if prec == "bf16_x32" else 0)), "B"
         if name == "tl_gram":
             return "mfma", count * m * (m + 1) * n, "flop"
         if name == "tl_poly":

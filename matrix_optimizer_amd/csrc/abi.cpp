@@ -83,9 +83,14 @@ WsLayout workspace_layout(const BatchShape& b, int prec, int path) {
     const size_t op = prec == PREC_F32 ? 4 : 2;
     const size_t xe = size_t(b.count) * L.mp * L.np;
     const size_t ae = size_t(b.count) * L.mp * L.mp;
+    L.big_tiles = use_big_tiles(L.mp, L.np, prec);
     L.x = take(xe * op);
-    L.xt0 = take(xe * op);
-    L.xt1 = take(xe * op);
+    if (L.big_tiles) {
+      L.x1 = take(xe * op);
+    } else {
+      L.xt0 = take(xe * op);
+      L.xt1 = take(xe * op);
+    }
     if (prec == PREC_BF16_X32) L.x32 = take(xe * 4);
     L.a32 = take(ae * 4);
     if (prec != PREC_F32) L.a16 = take(ae * 2);

@@ -61,10 +61,20 @@ struct WsLayout {
   // skinny path
   int64_t ldx = 0, S = 0, T = 0;
   size_t x = 0, gp0 = 0, gp1 = 0, sp = 0, bfrag = 0;
-  // tiled path
+  // tiled path.  With 256 x 256 tiles (big_tiles) the apply products read X
+  // row-major, and X ping-pongs between x and x1; otherwise they read X^T,
+  // kept in xt0 / xt1 beside x.
   int64_t mp = 0, np = 0, nparts = 0;
-  size_t xt0 = 0, xt1 = 0, x32 = 0, a32 = 0, a16 = 0, pb = 0, ssp = 0, inv = 0;
+  bool big_tiles = false;
+  size_t x1 = 0, xt0 = 0, xt1 = 0, x32 = 0, a32 = 0, a16 = 0, pb = 0, ssp = 0, inv = 0;
 };
+
+// The tiled products use 256 x 256 tiles (direct loads, row-major X operand
+// of the apply) when both padded sides are multiples of 256 and the operands
+// are bf16.
+inline bool use_big_tiles(int64_t mp, int64_t np, int prec) {
+  return prec != PREC_F32 && mp % 256 == 0 && np % 256 == 0;
+}
 
 WsLayout workspace_layout(const BatchShape& b, int prec, int path);
 

@@ -62,8 +62,8 @@ tl_norm_finalize(const float* __restrict__ ssp, int64_t nparts, float eps, float
 // ---------------------------------------------------------------------------
 // First pass of the tiled path, one 64x64 tile (Newton-Schulz orientation)
 // per workgroup: momentum and the Nesterov direction U (or a given U), the
-// tile's share of ||U||_F^2, and U, unnormalised, in both layouts (and the fp32
-// master).  The first Newton-Schulz step applies 1 / (||U||_F + eps): the Gram
+// tile's share of ||U||_F^2, and U, unnormalised, row-major, transposed when
+// the apply products read X^T (XT non-null), and as the fp32 master.  The first Newton-Schulz step applies 1 / (||U||_F + eps): the Gram
 // epilogue scales by its square, the apply epilogue by it.  One pass over G
 // and M instead of two.
 //   mode 0: M' = mu M + G (in place), U = G + mu M' or M'
@@ -116,9 +116,11 @@ tl_first(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const f
     st_from_f32(X, xi, v);
     if (X32) X32[xi] = v;
   }
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int lj = e >> 6, li = e & 63;
-    st_from_f32(XT, xb + (j0 + lj) * mp + i0 + li, tile[li][lj]);
+  if (XT) {
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+      const int lj = e >> 6, li = e & 63;
+      st_from_f32(XT, xb + (j0 + lj) * mp + i0 + li, tile[li][lj]);
+    }
   }
 }
 
@@ -319,6 +321,24 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& g, int64_t lin, bool
   }
 }
 
+// Row-major X tile of the apply products (BK rows of BN = 256 columns, bf16):
+// 16-byte chunk c of row k sits in slot c ^ qn_swz(k), which spreads the 4
+// rows one transposing read touches per 16-lane group over all 64 banks.
+__device__ __forceinline__ int qn_swz(int k) { return 4 * (k & 3); }
+__device__ __forceinline__ int qn_index(int row, int col) {
+  return row * 256 + ((((col >> 3) ^ qn_swz(row))) << 3) + (col & 7);
+}
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// i % 4 of the 4-element reads of lanes i / 4 + 4 q, q = 0..3 (measured).
+// With lane s reading row k0 + s / 4 at columns c0 + 4 (s % 4) .. + 3, lane i
+// gets column c0 + i at rows k0 .. k0 + 3: a transposed 4 x 16 block.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const bf16_t* p) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(__attribute__((address_space(3))) bf16_t*)p);
+}
+
 // Slot swizzle of the direct-load LDS tiles: 16-byte chunk c of row r sits in
 // slot c ^ swz(r).  LDS serves a 16-byte read for 16 lanes per cycle (64
 // banks); the 16 rows an MFMA fragment read touches per cycle (two 128-byte
@@ -401,6 +421,11 @@ tl_gemm(GemmArgs g) {
   constexpr int STG_OFF = C::DIRECT ? C::STAGE : 0;
   constexpr int LDS_ELEMS = 2 * C::STAGE > STG_OFF + STG_ELEMS ? 2 * C::STAGE : STG_OFF + STG_ELEMS;
   __shared__ __attribute__((aligned(16))) OP lds[LDS_ELEMS];
+  // The apply products on direct-load tiles read X row-major (an NN
+  // product): the Q stage holds BK rows of X, BN columns each, and the MFMA
+  // operand comes out of it through transposing LDS reads.
+  constexpr bool QN = C::DIRECT && EPI >= EPI_APPLY;
+  static_assert(!QN || (C::BK == 64 && C::BN == 256 && C::WAVES == 8), "row-major X operand: 64 x 256 Q stage");
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -423,19 +448,38 @@ tl_gemm(GemmArgs g) {
     const int lchunk = (lane % C::VPR) ^ lds_swz(8 * w + lrow);
     const int row = w * C::RPI + lrow;
     voff_p = (uint32_t)((row * g.ldp + lchunk * C::EPV) * (int64_t)sizeof(OP));
-    voff_q = (uint32_t)((row * g.ldq + lchunk * C::EPV) * (int64_t)sizeof(OP));
+    if constexpr (QN) {
+      // row-major X tile: one instruction fills 2 rows of BN columns; chunk
+      // c of row k sits in slot c ^ qn_swz(k)
+      const int qrow = 2 * w + lane / 32;
+      voff_q = (uint32_t)((qrow * g.ldq + ((lane % 32) ^ qn_swz(qrow)) * C::EPV) * (int64_t)sizeof(OP));
+    } else {
+      voff_q = (uint32_t)((row * g.ldq + lchunk * C::EPV) * (int64_t)sizeof(OP));
+    }
   }
-  // direct loads of k-slice k0 of the tile whose operand rows start at
-  // pbase / qbase into stage st
+  // direct loads of k-slice k0 of the tile whose operands start at pbase
+  // (its first row) and qbase (first row, or first column when QN) into
+  // stage st
   [[maybe_unused]] auto dma_slice = [&](int st, const OP* pbase, const OP* qbase, int64_t k0) {
     constexpr int HALF = C::LPW / 2;
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
       const int ins = w + i * C::WAVES;
       const int64_t rows = (int64_t)(i % HALF) * C::WAVES * C::RPI;
-      const OP* src = i < HALF ? pbase + rows * g.ldp + k0 : qbase + rows * g.ldq + k0;
-      const uint32_t la =
-          (uint32_t)(uintptr_t)(__attribute__((address_space(3))) OP*)(lds + st * C::STAGE + ins * C::RPI * C::LD);
+      const OP* src;
+      int lofs;
+      if (i < HALF) {
+        src = pbase + rows * g.ldp + k0;
+        lofs = ins * C::RPI * C::LD;
+      } else if constexpr (QN) {   // k rows k0 + 16 (i - HALF) + 2 w + lane / 32
+        const int qi = w + (i - HALF) * C::WAVES;
+        src = qbase + (k0 + 16 * (i - HALF)) * g.ldq;
+        lofs = C::BM * C::LD + qi * 2 * C::BN;
+      } else {
+        src = qbase + rows * g.ldq + k0;
+        lofs = ins * C::RPI * C::LD;
+      }
+      const uint32_t la = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) OP*)(lds + st * C::STAGE + lofs);
       lds_dma16(src, i < HALF ? voff_p : voff_q, la);
     }
   };
@@ -467,6 +511,21 @@ tl_gemm(GemmArgs g) {
           for (int ib = 0; ib < C::IB; ++ib) {
             const int off = ib * 32 - (int)krel;   // block row 0 relative to the slice
             if (off < 0 || off >= C::BK) continue;
+            if constexpr (QN) {
+              // Qs: the stage's row-major X rows; element (row, column) of
+              // accumulator register r of this lane
+#pragma unroll
+              for (int jb = 0; jb < C::JB; ++jb) {
+                const int col = wn * C::WTN + jb * 32 + (lane & 31);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                  const int row = off + mfma32_row(lane, r);
+                  const float xv = __uint_as_float((uint32_t)Qs[qn_index(row, col)] << 16);
+                  acc[ib][jb][r] += g.ca * xv;
+                }
+              }
+              continue;
+            }
 #pragma unroll
             for (int jb = 0; jb < C::JB; ++jb) {
               const OP* xrow = Qs + jb * 32 * C::LD;
@@ -506,14 +565,14 @@ tl_gemm(GemmArgs g) {
     // a tile starts without waiting for the previous epilogue's stores.
     // K is a multiple of 2 BK: slice kt uses stage kt & 1.
     const OP* pb = reinterpret_cast<const OP*>(g.P) + mat * g.strideP + i0 * g.ldp;
-    const OP* qb = reinterpret_cast<const OP*>(g.Q) + mat * g.strideQ + j0 * g.ldq;
+    const OP* qb = reinterpret_cast<const OP*>(g.Q) + mat * g.strideQ + (QN ? j0 : j0 * g.ldq);
     const OP* npb = pb;
     const OP* nqb = qb;
     if (lin + gridDim.x < total) {
       int64_t nmat, nti, ntj;
       tile_coords<C, EPI>(g, lin + gridDim.x, xcd_map, nmat, nti, ntj);
       npb = reinterpret_cast<const OP*>(g.P) + nmat * g.strideP + nti * C::BM * g.ldp;
-      nqb = reinterpret_cast<const OP*>(g.Q) + nmat * g.strideQ + ntj * C::BN * g.ldq;
+      nqb = reinterpret_cast<const OP*>(g.Q) + nmat * g.strideQ + (QN ? ntj * C::BN : ntj * C::BN * g.ldq);
     }
     npb = uniform_ptr(npb);
     nqb = uniform_ptr(nqb);
@@ -530,9 +589,26 @@ tl_gemm(GemmArgs g) {
 #pragma unroll
       for (int ib = 0; ib < C::IB; ++ib)
         fa[buf][ib] = *reinterpret_cast<const bf16x8*>(Pw + st * C::STAGE + ib * 32 * C::LD + slot * 8);
+      if constexpr (QN) {
+        // 16-lane group G, lane s: two transposing reads give k = 16 kk +
+        // 8 (G / 2) + 0..7 of column 16 (G % 2) + s of the block
+        const int G = lane >> 4, s4 = lane & 15;
 #pragma unroll
-      for (int jb = 0; jb < C::JB; ++jb)
-        fb[buf][jb] = *reinterpret_cast<const bf16x8*>(Qw + st * C::STAGE + jb * 32 * C::LD + slot * 8);
+        for (int jb = 0; jb < C::JB; ++jb) {
+          bf16x4 h[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int row = 16 * kk + 8 * (G >> 1) + 4 * hh + (s4 >> 2);
+            const int col = wn * C::WTN + jb * 32 + 16 * (G & 1) + 4 * (s4 & 3);
+            h[hh] = lds_read_tr16(lds + st * C::STAGE + C::BM * C::LD + qn_index(row, col));
+          }
+          fb[buf][jb] = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      } else {
+#pragma unroll
+        for (int jb = 0; jb < C::JB; ++jb)
+          fb[buf][jb] = *reinterpret_cast<const bf16x8*>(Qw + st * C::STAGE + jb * 32 * C::LD + slot * 8);
+      }
     };
     auto mfmas = [&](int buf) {
 #pragma unroll
@@ -559,7 +635,8 @@ tl_gemm(GemmArgs g) {
       __builtin_amdgcn_sched_barrier(0);
       mfmas(1);
       __builtin_amdgcn_sched_barrier(0);
-      add_ax(lds + st * C::STAGE + (C::BM + wn * C::WTN + (lane & 31)) * C::LD, kt);
+      if constexpr (QN) add_ax(lds + st * C::STAGE + C::BM * C::LD, kt);
+      else add_ax(lds + st * C::STAGE + (C::BM + wn * C::WTN + (lane & 31)) * C::LD, kt);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this wave's loads of the next slice
       lds_barrier();                               // everyone's; stage st is free again
       if (!last) read_frags(0, st ^ 1, 0);
@@ -712,7 +789,8 @@ tl_gemm(GemmArgs g) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) st_from_f32(X, (ib0 + 8 * hh + q) * ldx + jj, o[8 * hh + q]);
       }
-      store_run32(reinterpret_cast<OP*>(g.XT) + mat * g.strideX + jj * (uint32_t)g.ldxt + ib0, o);
+      if constexpr (!QN)   // the next apply reads X^T
+        store_run32(reinterpret_cast<OP*>(g.XT) + mat * g.strideX + jj * (uint32_t)g.ldxt + ib0, o);
     } else {
       float ulr = g.lr, uwd = g.wd;
       update_scalars(g.lrwd, ulr, uwd);
@@ -839,19 +917,26 @@ unsigned gemm_grid(int64_t tiles) {
 }
 
 // The K Newton-Schulz steps as three NT products each, on tile config C.
+// X: the step's input X (row-major).  Direct-load tiles: X1 is the second
+// row-major buffer, the apply reads X row-major and writes the next X to
+// the other buffer.  Otherwise XT holds X^T (ping-pong) and X is updated in
+// place.
 template <class C, typename PT>
-hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C::Op* X, typename C::Op* XT[2],
-                            float* X32, float* A32, bf16_t* A16, typename C::Op* PB, int64_t mp, int64_t np,
-                            const float* inv) {
+hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C::Op* X, typename C::Op* X1,
+                            typename C::Op* XT[2], float* X32, float* A32, bf16_t* A16, typename C::Op* PB,
+                            int64_t mp, int64_t np, const float* inv) {
   typedef typename C::Op OP;
   hipError_t e;
+  if (C::DIRECT ? X1 == nullptr : (XT[0] == nullptr || XT[1] == nullptr)) return hipErrorInvalidValue;
+  OP* Xb[2] = {X, X1};
   const int64_t tm = mp / C::BM, tn = np / C::BN;
   const int64_t tri = (C::BM / C::BN) * tm * (tm + 1) / 2;   // triangle tiles
   for (int k = 0; k < a.steps; ++k) {
     const float ca = a.coeffs[3 * k], cb = a.coeffs[3 * k + 1], cc = a.coeffs[3 * k + 2];
+    OP* Xk = C::DIRECT ? Xb[k & 1] : X;
     GemmArgs g = {};
     // Gram: A = X X^T
-    g.P = X; g.Q = X; g.ldp = np; g.ldq = np; g.strideP = mp * np; g.strideQ = mp * np; g.K = np;
+    g.P = Xk; g.Q = Xk; g.ldp = np; g.ldq = np; g.strideP = mp * np; g.strideQ = mp * np; g.K = np;
     g.tiles_n = tm; g.tiles_per_mat = tri; g.tiles_total = sh.count * tri;
     g.inv0 = k == 0 ? inv : nullptr;
     g.A32 = A32; g.A16 = A16; g.lda = mp; g.strideA = mp * mp;
@@ -867,12 +952,23 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
     MUON_LAUNCH("tl_poly", (tl_gemm<C, EPI_POLY, PT>), dim3(gemm_grid<C, EPI_POLY, PT>(g.tiles_total)),
                 dim3(C::THREADS), a.stream, g);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // apply: X' = a X + B X, B X read as B (X^T)^T
+    // apply: X' = a X + B X, with X read row-major (direct-load tiles) or as
+    // (X^T)^T
     g = GemmArgs{};
-    g.P = PB; g.Q = XT[k & 1]; g.ldp = mp; g.ldq = mp; g.strideP = mp * mp; g.strideQ = np * mp; g.K = mp;
+    g.P = PB; g.ldp = mp; g.strideP = mp * mp; g.K = mp;
+    if (C::DIRECT) {
+      g.Q = Xk; g.ldq = np; g.strideQ = mp * np;
+    } else {
+      g.Q = XT[k & 1]; g.ldq = mp; g.strideQ = np * mp;
+    }
     g.tiles_n = tn; g.tiles_per_mat = tm * tn; g.tiles_total = sh.count * tm * tn;
     g.inv0 = k == 0 ? inv : nullptr;
-    g.ca = ca; g.X = X; g.X32 = X32; g.XT = XT[(k + 1) & 1]; g.ldx = np; g.ldxt = mp; g.strideX = mp * np;
+    g.ca = ca; g.X32 = X32; g.ldx = np; g.ldxt = mp; g.strideX = mp * np;
+    if (C::DIRECT) {
+      g.X = Xb[(k + 1) & 1]; g.XT = nullptr;
+    } else {
+      g.X = X; g.XT = XT[(k + 1) & 1];
+    }
     g.last = (k == a.steps - 1);
     g.param = a.phase == PH_FULL ? a.param : nullptr; g.param_bf16 = a.param_dtype == DT_BF16;
     g.ns_out = a.ns_out; g.lr = a.lr; g.wd = a.wd; g.s = a.s; g.lrwd = a.lrwd;
@@ -892,14 +988,18 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
 }
 
 template <typename OP, typename PT>
-hipError_t run_products(const StepArgs& a, const BatchShape& sh, OP* X, OP* XT[2], float* X32, float* A32,
-                        bf16_t* A16, OP* PB, int64_t mp, int64_t np, const float* inv) {
+hipError_t run_products(const StepArgs& a, const BatchShape& sh, OP* X, OP* X1, OP* XT[2], float* X32, float* A32,
+                        bf16_t* A16, OP* PB, int64_t mp, int64_t np, bool big_tiles, const float* inv) {
   if constexpr (sizeof(OP) == 4) {
-    return run_products_cfg<CfgF32, PT>(a, sh, X, XT, X32, A32, A16, PB, mp, np, inv);
+    if (big_tiles) return hipErrorInvalidValue;
+    return run_products_cfg<CfgF32, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, inv);
   } else {
-    if (mp % CfgBig::BM == 0 && np % CfgBig::BN == 0)
-      return run_products_cfg<CfgBig, PT>(a, sh, X, XT, X32, A32, A16, PB, mp, np, inv);
-    return run_products_cfg<CfgSmall, PT>(a, sh, X, XT, X32, A32, A16, PB, mp, np, inv);
+    // the tile choice is the workspace's (use_big_tiles)
+    if (big_tiles) {
+      if (mp % CfgBig::BM != 0 || np % CfgBig::BN != 0) return hipErrorInvalidValue;
+      return run_products_cfg<CfgBig, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, inv);
+    }
+    return run_products_cfg<CfgSmall, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, inv);
   }
 }
 
@@ -910,7 +1010,8 @@ hipError_t tiled_impl(const StepArgs& a, const WsLayout& L) {
   float* ssp = (float*)(a.ws + L.ssp);
   float* inv = (float*)(a.ws + L.inv);
   OP* X = (OP*)(a.ws + L.x);
-  OP* XT[2] = {(OP*)(a.ws + L.xt0), (OP*)(a.ws + L.xt1)};
+  OP* X1 = L.big_tiles ? (OP*)(a.ws + L.x1) : nullptr;
+  OP* XT[2] = {L.big_tiles ? nullptr : (OP*)(a.ws + L.xt0), L.big_tiles ? nullptr : (OP*)(a.ws + L.xt1)};
   float* X32 = a.prec == PREC_BF16_X32 ? (float*)(a.ws + L.x32) : nullptr;
   float* A32 = (float*)(a.ws + L.a32);
   bf16_t* A16 = a.prec == PREC_F32 ? nullptr : (bf16_t*)(a.ws + L.a16);
@@ -926,7 +1027,7 @@ hipError_t tiled_impl(const StepArgs& a, const WsLayout& L) {
   MUON_LAUNCH("tl_norm_finalize", tl_norm_finalize, dim3((unsigned)sh.count), dim3(256), a.stream, ssp, L.nparts,
               a.eps, inv);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return run_products<OP, PT>(a, sh, X, XT, X32, A32, A16, PB, mp, np, inv);
+  return run_products<OP, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, L.big_tiles, inv);
 }
 
 template <typename OP>
