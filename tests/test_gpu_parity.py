@@ -97,6 +97,9 @@ SHAPE_SETS = {
     "tiled_multi_tile": [(129, 400), (2, 129, 400)],
     "tiled_experts_tall": [(2, 300, 40)],
     "tiled_256_tiles": [(256, 768), (2, 512, 256)],
+    # 256 x 256 tiles over 3 x 4 tile grids with ragged edges: off-diagonal
+    # triangle tiles, several tiles per workgroup, both orientations
+    "tiled_256_ragged": [(700, 900), (2, 900, 700)],
 }
 
 
