@@ -248,6 +248,29 @@ __device__ __forceinline__ void update_run32(bf16_t* w, const float* o, float lr
   }
 }
 
+// 8 consecutive stored elements at a 16-byte aligned address, kept in their
+// stored form (4 registers for bf16, 8 for fp32) until converted.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> {
+  u32x4 v;
+  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ void to_f32(float* f) const {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { f[2 * q] = __uint_as_float(v[q] << 16); f[2 * q + 1] = __uint_as_float(v[q] & 0xffff0000u); }
+  }
+};
+template <> struct Raw8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4*>(p);
+    b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ void to_f32(float* f) const {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { f[q] = a[q]; f[q + 4] = b[q]; }
+  }
+};
+
 // 8 consecutive elements at a 16-byte aligned address, as floats.
 __device__ __forceinline__ void load8(const float* p, float* f) {
   const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
@@ -807,16 +830,27 @@ tl_gemm(GemmArgs g) {
         const int rr = lane >> 3, cc = (lane & 7) * 8;
         const uint32_t j = (uint32_t)(j0 + wn * C::WTN + jp * 64 + cc);
         const bool vec = (n % 8) == 0;   // aligned runs of 8 inside the matrix
+        // The read of W for row group p + 1 is issued before the stores of
+        // row group p (the stores could alias the reads, so the compiler would
+        // otherwise wait out one memory latency per row group); W stays in its
+        // stored form until used (4 registers for bf16).
+        Raw8<PT> wr[2];
+        auto load_group = [&](int p, int buf) __attribute__((always_inline)) {
+          const uint32_t i = ib0 + rr + 8 * p;
+          if (W && vec && i < m && j < n) wr[buf].load(W + i * n + j);
+        };
+        load_group(0, 0);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {   // row group p: its reads are issued before its stores
-          float ov[8], xv[8], wv[8];
+        for (int p = 0; p < 4; ++p) {
+          float xv[8];
+          if (X32) load8(X32 + (ib0 + rr + 8 * p) * ldx + j, xv);   // padded rows and columns: always readable
+          if (p + 1 < 4) load_group(p + 1, (p + 1) & 1);
+          float ov[8];
           const f32x4 a = *reinterpret_cast<const f32x4*>(stg + (rr + 8 * p) * SLD + cc);
           const f32x4 b = *reinterpret_cast<const f32x4*>(stg + (rr + 8 * p) * SLD + cc + 4);
 #pragma unroll
           for (int q = 0; q < 4; ++q) { ov[q] = a[q]; ov[q + 4] = b[q]; }
           const uint32_t i = ib0 + rr + 8 * p;
-          if (X32) load8(X32 + i * ldx + j, xv);   // padded rows and columns: always readable
-          if (W && vec && i < m && j < n) load8(W + i * n + j, wv);
           if (X32) {
 #pragma unroll
             for (int q = 0; q < 8; ++q) ov[q] = g.ca * xv[q] + ov[q];
@@ -831,7 +865,8 @@ tl_gemm(GemmArgs g) {
             if (j >= n) continue;
             if (O) store8(O + i * n + j, ov);
             if (W) {
-              float nw[8];
+              float wv[8], nw[8];
+              wr[p & 1].to_f32(wv);
 #pragma unroll
               for (int q = 0; q < 8; ++q) nw[q] = apply_update(wv[q], ov[q], ulr, uwd, g.s);
               store8(W + i * n + j, nw);
