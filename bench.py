@@ -451,12 +451,14 @@ def main():
         roof["frac_of_measured_copy"] = roof["achieved"] / copy_gbps
 
     if ms < 20.0:
-        # cold steps: a 512 MiB write between steps evicts the 256 MB Infinity
-        # Cache, so each timed step starts from HBM (the warm value above may be
-        # served partly from that cache)
+        # cold steps: reading 1 GiB between steps evicts the 256 MB Infinity
+        # Cache with clean lines, so each timed step starts from HBM (the warm
+        # value above may be served partly from that cache) and pays for no
+        # write-back of someone else's data
         cold = []
+        flush = torch.cat([src.view(torch.int32), dst.view(torch.int32)])
         for _ in range(min(args.steps, 10)):
-            dst.fill_(0)
+            flush.sum()
             a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a0.record(stream)
             step()
@@ -466,6 +468,7 @@ def main():
         out["detail"]["cold_ms_per_step"] = float(np.median(cold))
         out["detail"]["cold_tflops"] = flops / (np.median(cold) / 1e3) / 1e12
     del src, dst
+    flush = None
     if not args.no_cpu_baseline:
         maxm = None if min(wl.params[0].matrix_shape) <= SKINNY_MAX_ROWS else 1
         out["cpu_baseline"] = cpu_baseline(wl, plan, dtype, hp, args.cpu_budget, maxm)

@@ -61,6 +61,29 @@ __device__ __forceinline__ void update_scalars(const float* lrwd, float& lr, flo
   }
 }
 
+// 8 consecutive stored elements at a 16-byte aligned address, kept in their
+// stored form (4 registers for bf16, 8 for fp32) until converted.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> {
+  u32x4 v;
+  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ void to_f32(float* f) const {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { f[2 * q] = __uint_as_float(v[q] << 16); f[2 * q + 1] = __uint_as_float(v[q] & 0xffff0000u); }
+  }
+};
+template <> struct Raw8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4*>(p);
+    b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ void to_f32(float* f) const {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { f[q] = a[q]; f[q + 4] = b[q]; }
+  }
+};
+
 // Decoupled decay plus the orthogonal update on one element, fp32.
 __device__ __forceinline__ float apply_update(float w, float o, float lr, float wd, float s) {
   return w - lr * (wd * w + s * o);

@@ -515,15 +515,6 @@ sk_gram_ns(const float* __restrict__ gp, const float* __restrict__ sp, float eps
   const int t = threadIdx.x;
   const int lane = t & (WAVE - 1);
   for (int e = t; e < GS_MAT; e += SK_THREADS) A[e] = R(0);
-  if (t < WAVE) {
-    // 1 / (||U||_F + eps) from the chunk norm partials, fp64
-    double v = 0.;
-    for (int q = lane; q < S; q += WAVE) v += (double)sp[b * S + q];
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
-    const double den = sqrt(v) + (double)eps;
-    if (lane == 0) inv_s = den > 0. ? 1. / den : 0.;
-  }
 
   // A_0 entries: thread t owns packed entries t, t + 256, t + 512 and adds the
   // chunk partials in chunk order (fp64); the partials pass through LDS in
@@ -541,6 +532,16 @@ sk_gram_ns(const float* __restrict__ gp, const float* __restrict__ sp, float eps
     for (int i = 0; i < PER; ++i) {
       const int f = t + SK_THREADS * i;
       v[i] = f < tot ? src[f] : 0.f;
+    }
+    if (q0 == 0 && t < WAVE) {
+      // 1 / (||U||_F + eps) from the chunk norm partials, fp64 (its loads
+      // overlap the first round of Gram partials)
+      double sv = 0.;
+      for (int q = lane; q < S; q += WAVE) sv += (double)sp[b * S + q];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) sv += __shfl_xor(sv, o, WAVE);
+      const double den = sqrt(sv) + (double)eps;
+      if (lane == 0) inv_s = den > 0. ? 1. / den : 0.;
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -622,51 +623,10 @@ sk_first(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const f
   if (vec) {
     // 8 consecutive columns of one row per item
     constexpr int PR = C::L / 8;
-    for (int v = threadIdx.x; v < m * PR; v += SK_THREADS) {
+    const int items = m * PR;
+    // U of item v into the tile and the norm partial
+    auto finish = [&](int v, const float* u) __attribute__((always_inline)) {
       const int r = v / PR, jl = (v % PR) * 8;
-      const int64_t j = j0 + jl;
-      float u[8];
-      if (j < n) {   // n % 8 == 0: the 8 columns are all in range or all out
-        const int64_t si = mat + (int64_t)r * n + j;
-        if (mode == 0) {
-          float g[8];
-          if constexpr (sizeof(GT) == 2) {
-            const uint4 gv = *reinterpret_cast<const uint4*>(grad + si);
-            const uint32_t w4[4] = {gv.x, gv.y, gv.z, gv.w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              g[2 * q] = __uint_as_float(w4[q] << 16);
-              g[2 * q + 1] = __uint_as_float(w4[q] & 0xffff0000u);
-            }
-          } else {
-            const f32x4 g0 = *reinterpret_cast<const f32x4*>(grad + si);
-            const f32x4 g1 = *reinterpret_cast<const f32x4*>(grad + si + 4);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) { g[q] = g0[q]; g[q + 4] = g1[q]; }
-          }
-          f32x4 m0 = *reinterpret_cast<const f32x4*>(mom + si);
-          f32x4 m1 = *reinterpret_cast<const f32x4*>(mom + si + 4);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float a0 = mu * m0[q] + g[q];
-            const float a1 = mu * m1[q] + g[q + 4];
-            m0[q] = a0;
-            m1[q] = a1;
-            u[q] = nesterov ? g[q] + mu * a0 : a0;
-            u[q + 4] = nesterov ? g[q + 4] + mu * a1 : a1;
-          }
-          *reinterpret_cast<f32x4*>(mom + si) = m0;
-          *reinterpret_cast<f32x4*>(mom + si + 4) = m1;
-        } else {
-          const f32x4 u0 = *reinterpret_cast<const f32x4*>(u_in + si);
-          const f32x4 u1 = *reinterpret_cast<const f32x4*>(u_in + si + 4);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) { u[q] = u0[q]; u[q + 4] = u1[q]; }
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) u[q] = 0.f;
-      }
 #pragma unroll
       for (int q = 0; q < 8; ++q) ss += u[q] * u[q];
       if constexpr (MODE == 0) {
@@ -677,6 +637,70 @@ sk_first(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const f
       } else {
         *reinterpret_cast<f32x4*>(lx + r * C::LDX + jl) = f32x4{u[0], u[1], u[2], u[3]};
         *reinterpret_cast<f32x4*>(lx + r * C::LDX + jl + 4) = f32x4{u[4], u[5], u[6], u[7]};
+      }
+    };
+    if (mode == 0) {
+      // momentum: a thread's next item is loaded before the current item's
+      // momentum is stored (the stores could alias the loads, so the compiler
+      // would otherwise wait out one memory latency per item)
+      Raw8<GT> gc, gn;
+      f32x4 mc0 = {}, mc1 = {}, mn0 = {}, mn1 = {};
+      auto load_item = [&](int v, Raw8<GT>& gr, f32x4& m0, f32x4& m1) __attribute__((always_inline)) {
+        if (v >= items) return;
+        const int r = v / PR, jl = (v % PR) * 8;
+        const int64_t j = j0 + jl;
+        if (j >= n) return;   // n % 8 == 0: the 8 columns are all in range or all out
+        const int64_t si = mat + (int64_t)r * n + j;
+        gr.load(grad + si);
+        m0 = *reinterpret_cast<const f32x4*>(mom + si);
+        m1 = *reinterpret_cast<const f32x4*>(mom + si + 4);
+      };
+      load_item(threadIdx.x, gc, mc0, mc1);
+      for (int v = threadIdx.x; v < items; v += SK_THREADS) {
+        load_item(v + SK_THREADS, gn, mn0, mn1);
+        const int r = v / PR, jl = (v % PR) * 8;
+        const int64_t j = j0 + jl;
+        float u[8];
+        if (j < n) {
+          const int64_t si = mat + (int64_t)r * n + j;
+          float g[8];
+          gc.to_f32(g);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float a0 = mu * mc0[q] + g[q];
+            const float a1 = mu * mc1[q] + g[q + 4];
+            mc0[q] = a0;
+            mc1[q] = a1;
+            u[q] = nesterov ? g[q] + mu * a0 : a0;
+            u[q + 4] = nesterov ? g[q + 4] + mu * a1 : a1;
+          }
+          *reinterpret_cast<f32x4*>(mom + si) = mc0;
+          *reinterpret_cast<f32x4*>(mom + si + 4) = mc1;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) u[q] = 0.f;
+        }
+        finish(v, u);
+        gc = gn;
+        mc0 = mn0;
+        mc1 = mn1;
+      }
+    } else {
+      for (int v = threadIdx.x; v < items; v += SK_THREADS) {
+        const int r = v / PR, jl = (v % PR) * 8;
+        const int64_t j = j0 + jl;
+        float u[8];
+        if (j < n) {
+          const int64_t si = mat + (int64_t)r * n + j;
+          const f32x4 u0 = *reinterpret_cast<const f32x4*>(u_in + si);
+          const f32x4 u1 = *reinterpret_cast<const f32x4*>(u_in + si + 4);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) { u[q] = u0[q]; u[q + 4] = u1[q]; }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) u[q] = 0.f;
+        }
+        finish(v, u);
       }
     }
   } else {
