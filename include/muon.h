@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 2
+#define MUON_ABI_VERSION 3
 
 typedef enum {
   MUON_OK = 0,
@@ -69,9 +69,9 @@ typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
  *  MUON_PREC_F32      every product and every stored intermediate in fp32
  *                     (the check path).
  * Matrices whose short side is at most 32 form the Gram matrix of the stored X
- * with fp32 accumulation, run the polynomial on it in fp64 (Gram space) or
- * fp32 (step by step) and apply it with about 16-bit (bf16 hi + lo) or fp32
- * operands in every mode (the small products are cheap); those
+ * with fp32 accumulation, run the polynomial on it in fp32 (fp64 on the check
+ * path) and apply it with about 16-bit (bf16 hi + lo) or fp32 operands in
+ * every mode (the small products are cheap); those
  * with a short side from 33 to 127 run every product on fp32 operands in every
  * mode, because bf16 rounding of A and B costs too much accuracy there. */
 typedef enum { MUON_PREC_BF16 = 0, MUON_PREC_BF16_X32 = 1, MUON_PREC_F32 = 2 } muon_precision;
@@ -148,6 +148,25 @@ typedef struct {
                                direction, in W's orientation, before the scale s); NULL to skip */
 } muon_batch_buffers;
 
+/* A batch's matrices at independent addresses (zero-copy batching: the
+ * parameters need not be packed into one [count,M,N] buffer).  Each field is
+ * a device array of `count` pointers; pointer i addresses matrix i of the
+ * batch (in segment order) as an [M,N] row-major region of the stated type.
+ * For a 3-D expert tensor the caller passes one pointer per expert.  The
+ * arrays are read by the kernels when they run, never by the host, so the
+ * library cannot check the addresses they hold: each must be 16-byte aligned
+ * and the regions must not overlap one another or the workspace; the caller
+ * keeps the arrays valid until the launches have run (as for lr_wd_device,
+ * a captured graph replays with whatever they then hold). */
+typedef struct {
+  void* const* params;        /* device array [count]: param_dtype matrices, updated in place */
+  muon_dtype param_dtype;
+  const void* const* grads;   /* device array [count]: grad_dtype matrices */
+  muon_dtype grad_dtype;
+  float* const* momenta;      /* device array [count]: fp32 matrices, updated in place */
+  float* const* ns_out;       /* optional device array [count]: fp32 matrices receiving O; NULL to skip */
+} muon_batch_ptrs;
+
 int32_t muon_abi_version(void);
 const char* muon_status_str(muon_status s);
 
@@ -175,6 +194,14 @@ muon_status muon_workspace_bytes(const muon_plan* plan, int32_t batch, muon_prec
  * workspace; device pointers must be 16-byte aligned. */
 muon_status muon_step(const muon_plan* plan, int32_t batch, const muon_batch_buffers* bufs,
                       const muon_hparams* hp, void* workspace, size_t workspace_bytes, void* stream);
+
+/* muon_step on per-matrix addresses (muon_batch_ptrs) instead of contiguous
+ * batch buffers; the same kernels, results bitwise equal to muon_step on the
+ * same data.  The pointer arrays must be non-NULL (ns_out optional), 16-byte
+ * aligned and must not overlap one another or the workspace; the addresses
+ * they hold are the caller's responsibility (see muon_batch_ptrs). */
+muon_status muon_step_ptrs(const muon_plan* plan, int32_t batch, const muon_batch_ptrs* bufs,
+                           const muon_hparams* hp, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Stage entry points, same validation.  They run the stages of muon_step one
  * at a time so each can be checked on its own.

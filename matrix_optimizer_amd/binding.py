@@ -25,7 +25,7 @@ MUON_SCALE_NONE, MUON_SCALE_RMS = 0, 1
 PRECISIONS = {"bf16": MUON_PREC_BF16, "bf16_x32": MUON_PREC_BF16_X32, "f32": MUON_PREC_F32}
 SCALES = {"none": MUON_SCALE_NONE, "rms": MUON_SCALE_RMS}
 
-EXPORTED = ["muon_abi_version", "muon_status_str", "muon_plan_create", "muon_plan_destroy",
+EXPORTED = ["muon_abi_version", "muon_status_str", "muon_plan_create", "muon_plan_destroy", "muon_step_ptrs",
             "muon_plan_num_batches", "muon_plan_batch_info", "muon_plan_segments",
             "muon_workspace_bytes", "muon_step", "muon_stage_momentum", "muon_stage_ns",
             "muon_stage_update", "muon_trace_start", "muon_trace_stop"]
@@ -60,6 +60,11 @@ class muon_hparams(C.Structure):
 class muon_batch_buffers(C.Structure):
     _fields_ = [("param", C.c_void_p), ("param_dtype", C.c_int32), ("grad", C.c_void_p),
                 ("grad_dtype", C.c_int32), ("momentum", C.c_void_p), ("ns_out", C.c_void_p)]
+
+
+class muon_batch_ptrs(C.Structure):
+    _fields_ = [("params", C.c_void_p), ("param_dtype", C.c_int32), ("grads", C.c_void_p),
+                ("grad_dtype", C.c_int32), ("momenta", C.c_void_p), ("ns_out", C.c_void_p)]
 
 
 class MuonError(RuntimeError):
@@ -100,6 +105,9 @@ def lib():
     L.muon_step.restype = C.c_int32
     L.muon_step.argtypes = [C.c_void_p, C.c_int32, C.POINTER(muon_batch_buffers), C.POINTER(muon_hparams),
                             C.c_void_p, C.c_size_t, C.c_void_p]
+    L.muon_step_ptrs.restype = C.c_int32
+    L.muon_step_ptrs.argtypes = [C.c_void_p, C.c_int32, C.POINTER(muon_batch_ptrs), C.POINTER(muon_hparams),
+                                 C.c_void_p, C.c_size_t, C.c_void_p]
     L.muon_stage_momentum.restype = C.c_int32
     L.muon_stage_momentum.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
                                       C.POINTER(muon_hparams), C.c_void_p]
@@ -244,6 +252,52 @@ def muon_step(plan: Plan, batch: int, param, grad, momentum, hp: HParams, worksp
     st = lib().muon_step(plan.handle, batch, C.byref(bufs), C.byref(hpc), _ptr(workspace),
                          workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "muon_step")
+
+
+def pointer_table(tensors, device="cuda"):
+    """Device array (int64 tensor) of the data pointers of `tensors`, one per
+    matrix, for muon_step_ptrs.  Keep it alive until the step has run."""
+    import torch
+    return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
+
+
+def muon_step_ptrs(plan: Plan, batch: int, params, grads, momenta, hp: HParams, workspace,
+                   ns_out=None, stream=None, param_dtype=None, grad_dtype=None) -> None:
+    """muon_step on per-matrix tensors (muon_step_ptrs): params, grads,
+    momenta (and optionally ns_out) are sequences of `count` [M, N] device
+    tensors, matrix i of the batch each, or device pointer tables made with
+    pointer_table (then param_dtype / grad_dtype, "bf16" or "f32", say what
+    they point at).  Nothing is packed or copied."""
+    import torch
+
+    def is_table(x):
+        return isinstance(x, torch.Tensor) and x.dtype == torch.int64 and x.dim() == 1
+
+    def table(x):
+        if x is None:
+            return None
+        return x if is_table(x) else pointer_table(x)
+
+    def dtype_of(x, given, what):
+        if not is_table(x):
+            return _dtype_code(x[0])
+        if given not in ("bf16", "f32"):
+            raise ValueError(f"{what} must be 'bf16' or 'f32' with a pointer table")
+        return MUON_BF16 if given == "bf16" else MUON_F32
+
+    tp, tg, tm, tn = table(params), table(grads), table(momenta), table(ns_out)
+    if stream is not None:   # tables made here stay allocated until that stream has run the step
+        ext = torch.cuda.ExternalStream(int(stream))
+        for t in (tp, tg, tm, tn):
+            if t is not None:
+                t.record_stream(ext)
+    pdt = dtype_of(params, param_dtype, "param_dtype")
+    gdt = dtype_of(grads, grad_dtype, "grad_dtype")
+    hpc, keep = hp.to_c()
+    bufs = muon_batch_ptrs(_ptr(tp), pdt, _ptr(tg), gdt, _ptr(tm), _ptr(tn))
+    st = lib().muon_step_ptrs(plan.handle, batch, C.byref(bufs), C.byref(hpc), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "muon_step_ptrs")
 
 
 def muon_stage_momentum(plan: Plan, batch: int, grad, momentum, u_out, hp: HParams, stream=None) -> None:

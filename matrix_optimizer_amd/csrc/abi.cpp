@@ -354,6 +354,37 @@ muon_status muon_step(const muon_plan* plan, int32_t batch, const muon_batch_buf
   return hip_status(dispatch(a, L));
 }
 
+muon_status muon_step_ptrs(const muon_plan* plan, int32_t batch, const muon_batch_ptrs* bufs, const muon_hparams* hp,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  const muon_plan::Batch* b = get_batch(plan, batch);
+  if (!b || !bufs) return MUON_ERR_INVALID_ARG;
+  muon_status st = check_hparams(hp, true, true, true);
+  if (st != MUON_OK) return st;
+  if (!valid_dtype(bufs->param_dtype) || !valid_dtype(bufs->grad_dtype)) return MUON_ERR_INVALID_ARG;
+  if (!bufs->params || !bufs->grads || !bufs->momenta) return MUON_ERR_INVALID_ARG;
+  const WsLayout L = workspace_layout(shape_of(*b), hp->precision, b->path);
+  if (workspace_bytes < L.total) return MUON_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return MUON_ERR_INVALID_ARG;
+  const size_t tab_bytes = size_t(b->count) * sizeof(void*);
+  std::vector<Region> rs = {region(bufs->params, tab_bytes), region(bufs->grads, tab_bytes),
+                            region(bufs->momenta, tab_bytes), region(workspace, L.total)};
+  if (bufs->ns_out) rs.push_back(region(bufs->ns_out, tab_bytes));
+  if (!regions_ok(rs)) return MUON_ERR_INVALID_ARG;
+
+  StepArgs a;
+  fill_common(a, *b, hp, stream);
+  a.phase = PH_FULL;
+  a.param = nullptr; a.param_dtype = bufs->param_dtype == MUON_BF16 ? DT_BF16 : DT_F32;
+  a.grad = nullptr; a.grad_dtype = bufs->grad_dtype == MUON_BF16 ? DT_BF16 : DT_F32;
+  a.mom = nullptr; a.ns_out = nullptr;
+  a.tabs.param = reinterpret_cast<const void* const*>(bufs->params);
+  a.tabs.grad = bufs->grads;
+  a.tabs.mom = reinterpret_cast<const void* const*>(bufs->momenta);
+  a.tabs.ns = reinterpret_cast<const void* const*>(bufs->ns_out);
+  a.ws = static_cast<char*>(workspace);
+  return hip_status(dispatch(a, L));
+}
+
 muon_status muon_stage_momentum(const muon_plan* plan, int32_t batch, const void* grad, muon_dtype grad_dtype,
                                 float* momentum, float* u_out, const muon_hparams* hp, void* stream) {
   const muon_plan::Batch* b = get_batch(plan, batch);

@@ -84,6 +84,16 @@ template <> struct Raw8<float> {
   }
 };
 
+// A pointer P such that P + b mn + e addresses element e of matrix b: the
+// contiguous base itself, or matrix b's own address from the table moved
+// back by b mn elements (on integers; only that matrix's elements are
+// accessed through it).  b is uniform across the wave.
+template <typename T>
+__device__ __forceinline__ T* batch_view(T* contig, const void* const* tab, int64_t b, int64_t mn) {
+  if (!tab) return contig;
+  return reinterpret_cast<T*>(reinterpret_cast<uintptr_t>(tab[b]) - (uintptr_t)(b * mn) * sizeof(T));
+}
+
 // Decoupled decay plus the orthogonal update on one element, fp32.
 __device__ __forceinline__ float apply_update(float w, float o, float lr, float wd, float s) {
   return w - lr * (wd * w + s * o);

@@ -78,6 +78,16 @@ inline bool use_big_tiles(int64_t mp, int64_t np, int prec) {
 
 WsLayout workspace_layout(const BatchShape& b, int prec, int path);
 
+// Per-matrix addresses of a batch's caller buffers (zero-copy batching):
+// device arrays of one pointer per matrix, or null where the buffer is one
+// contiguous [count, M, N] region.
+struct MatTabs {
+  const void* const* param;
+  const void* const* grad;
+  const void* const* mom;
+  const void* const* ns;
+};
+
 struct StepArgs {
   BatchShape shape;
   int phase;
@@ -90,6 +100,7 @@ struct StepArgs {
   const float* o_in;     // PH_UPDATE input
   float lr, mu, wd, eps, s;
   const float* lrwd;     // optional device {lr, wd}, read by the update kernels
+  MatTabs tabs = {};     // per-matrix pointer tables (PH_FULL), null for contiguous buffers
   int nesterov;
   int steps;
   std::vector<float> coeffs;   // 3 * steps (expanded)

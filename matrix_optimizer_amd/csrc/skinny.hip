@@ -601,7 +601,7 @@ __global__ void __launch_bounds__(SK_THREADS)
 sk_first(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const float* __restrict__ u_in,
          typename SkCfg<MODE>::XS* __restrict__ xws, float* __restrict__ gp_out, float* __restrict__ sp,
          int m, int64_t n, int64_t ldx, int S, int T, int transposed, int vec, float mu, int nesterov,
-         int64_t NB, int G) {
+         int64_t NB, int G, MatTabs tabs) {
   typedef SkCfg<MODE> C;
   typedef typename C::XS XS;
   // dynamic LDS: max(mr rows of the tile, the Gram reduction buffer) bytes
@@ -615,6 +615,8 @@ sk_first(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const f
   const int c = (int)(blk % S);
   const int64_t j0 = (int64_t)c * C::L;
   const int64_t mat = b * (int64_t)m * n;
+  grad = batch_view(grad, tabs.grad, b, (int64_t)m * n);
+  mom = batch_view(mom, tabs.mom, b, (int64_t)m * n);
   float ss = 0.f;
 
   // zero the padding rows of the tile
@@ -743,7 +745,7 @@ __global__ void __launch_bounds__(SK_THREADS)
 sk_iter(typename SkCfg<MODE>::XS* __restrict__ xws, const BFrag* __restrict__ bfrag, float* __restrict__ gp_out,
         int m, int64_t n, int64_t ldx, int S, int T, int transposed, int vec,
         PT* __restrict__ param, float* __restrict__ ns_out, float lr, float wd, float s_scale,
-        const float* __restrict__ lrwd) {
+        const float* __restrict__ lrwd, MatTabs tabs) {
   typedef SkCfg<MODE> C;
   if constexpr (LAST) update_scalars(lrwd, lr, wd);
   typedef typename C::XS XS;
@@ -756,6 +758,10 @@ sk_iter(typename SkCfg<MODE>::XS* __restrict__ xws, const BFrag* __restrict__ bf
   const int64_t j0 = (int64_t)c * C::L;
   const int t = threadIdx.x;
   const int64_t mat = b * (int64_t)m * n;
+  if constexpr (LAST) {
+    param = batch_view(param, tabs.param, b, (int64_t)m * n);
+    ns_out = batch_view(ns_out, tabs.ns, b, (int64_t)m * n);
+  }
   constexpr int PR8 = C::L / 8;                      // 8-column items per row
   constexpr int NI = SK_MP * PR8 / SK_THREADS;       // items per thread (upper bound)
 
@@ -962,7 +968,7 @@ template <int MODE, typename PT, bool TRANS>
 __global__ void __launch_bounds__(SK_THREADS)
 sk_apply(const typename SkCfg<MODE>::XS* __restrict__ xg, const BFrag* __restrict__ qfrag, int m, int64_t n,
          int64_t NB, int G, int64_t upm, int64_t units, int vec, PT* __restrict__ param, float* __restrict__ ns_out,
-         float lr, float wd, float s_scale, const float* __restrict__ lrwd) {
+         float lr, float wd, float s_scale, const float* __restrict__ lrwd, MatTabs tabs) {
   update_scalars(lrwd, lr, wd);
   typedef typename SkCfg<MODE>::XS XS;
   constexpr int XW = MODE == 0 ? 4 : 8;     // 32-bit words of U per lane per K block
@@ -974,6 +980,8 @@ sk_apply(const typename SkCfg<MODE>::XS* __restrict__ xg, const BFrag* __restric
   const int64_t b = unit / upm;
   const int64_t jb0 = (unit % upm) * 2;
   const int64_t mat = b * (int64_t)m * n;
+  param = batch_view(param, tabs.param, b, (int64_t)m * n);
+  ns_out = batch_view(ns_out, tabs.ns, b, (int64_t)m * n);
 
   // U operands of both blocks: bf16 modes K block kb = rows of group 2 kb + h,
   // fp32 mode rows 16 h .. 16 h + 15 (groups 2 h, 2 h + 1)
@@ -1124,11 +1132,11 @@ hipError_t launch_first(const StepArgs& a, const WsLayout& L, int mode, int vec)
   if (L.path == PATH_SKINNY_GRAM)
     MUON_LAUNCH_SHM(name, (sk_first<MODE, GT, true>), grid, block, shm, a.stream, mode, (const GT*)a.grad, a.mom,
                     a.u_in, (XS*)(a.ws + L.x), (float*)(a.ws + L.gp0), (float*)(a.ws + L.sp), (int)sh.m, sh.n, L.ldx,
-                    (int)L.S, (int)L.T, (int)sh.transposed, vec, a.mu, a.nesterov, NB, G);
+                    (int)L.S, (int)L.T, (int)sh.transposed, vec, a.mu, a.nesterov, NB, G, a.tabs);
   else
     MUON_LAUNCH_SHM(name, (sk_first<MODE, GT, false>), grid, block, shm, a.stream, mode, (const GT*)a.grad, a.mom,
                     a.u_in, (XS*)(a.ws + L.x), (float*)(a.ws + L.gp0), (float*)(a.ws + L.sp), (int)sh.m, sh.n, L.ldx,
-                    (int)L.S, (int)L.T, (int)sh.transposed, vec, a.mu, a.nesterov, NB, G);
+                    (int)L.S, (int)L.T, (int)sh.transposed, vec, a.mu, a.nesterov, NB, G, a.tabs);
   return hipGetLastError();
 }
 
@@ -1151,11 +1159,11 @@ hipError_t launch_iters(const StepArgs& a, const WsLayout& L, int vec) {
     if (k < a.steps - 1)
       MUON_LAUNCH("sk_ns_step", (sk_iter<MODE, PT, false>), grid, block, a.stream, (XS*)(a.ws + L.x),
                   (const BFrag*)bfrag, gp[(k + 1) & 1], (int)sh.m, sh.n, L.ldx, (int)L.S, (int)L.T,
-                  (int)sh.transposed, vec, param, a.ns_out, a.lr, a.wd, a.s, a.lrwd);
+                  (int)sh.transposed, vec, param, a.ns_out, a.lr, a.wd, a.s, a.lrwd, a.tabs);
     else
       MUON_LAUNCH("sk_apply_update", (sk_iter<MODE, PT, true>), grid, block, a.stream, (XS*)(a.ws + L.x),
                   (const BFrag*)bfrag, gp[(k + 1) & 1], (int)sh.m, sh.n, L.ldx, (int)L.S, (int)L.T,
-                  (int)sh.transposed, vec, param, a.ns_out, a.lr, a.wd, a.s, a.lrwd);
+                  (int)sh.transposed, vec, param, a.ns_out, a.lr, a.wd, a.s, a.lrwd, a.tabs);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1181,16 +1189,18 @@ hipError_t launch_gram(const StepArgs& a, const WsLayout& L, int vec) {
   const int64_t upm = (NB + 1) / 2;                    // 64-column units per matrix
   const int64_t units = sh.count * upm;
   const dim3 grid((unsigned)((units + SK_WAVES - 1) / SK_WAVES));
-  const char* name = param ? "sk_apply_update" : "sk_apply";
+  const char* name = (param || a.tabs.param) ? "sk_apply_update" : "sk_apply";
   if (!sh.transposed) {
     const int vec = sh.n % 8 == 0 ? 1 : 0;
     const size_t shm = (size_t)SK_WAVES * (8 * G) * AP_LD * 4;
     MUON_LAUNCH_SHM(name, (sk_apply<MODE, PT, false>), grid, dim3(SK_THREADS), shm, a.stream, (const XS*)(a.ws + L.x),
-                (const BFrag*)bfrag, (int)sh.m, sh.n, NB, G, upm, units, vec, param, a.ns_out, a.lr, a.wd, a.s, a.lrwd);
+                (const BFrag*)bfrag, (int)sh.m, sh.n, NB, G, upm, units, vec, param, a.ns_out, a.lr, a.wd, a.s, a.lrwd,
+                a.tabs);
   } else {
     const int vec = sh.m % 4 == 0 ? 1 : 0;
     MUON_LAUNCH(name, (sk_apply<MODE, PT, true>), grid, dim3(SK_THREADS), a.stream, (const XS*)(a.ws + L.x),
-                (const BFrag*)bfrag, (int)sh.m, sh.n, NB, G, upm, units, vec, param, a.ns_out, a.lr, a.wd, a.s, a.lrwd);
+                (const BFrag*)bfrag, (int)sh.m, sh.n, NB, G, upm, units, vec, param, a.ns_out, a.lr, a.wd, a.s, a.lrwd,
+                a.tabs);
   }
   return hipGetLastError();
 }

@@ -74,7 +74,7 @@ template <typename GT, typename XO>
 __global__ void __launch_bounds__(256)
 tl_first(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const float* __restrict__ u_in,
          float* __restrict__ ssp, XO* __restrict__ X, XO* __restrict__ XT, float* __restrict__ X32,
-         int64_t m, int64_t n, int64_t mp, int64_t np, int transposed, float mu, int nesterov) {
+         int64_t m, int64_t n, int64_t mp, int64_t np, int transposed, float mu, int nesterov, MatTabs tabs) {
   __shared__ float tile[64][65];
   __shared__ float wsum[4];
   const int64_t tiles_j = np / 64;
@@ -83,6 +83,8 @@ tl_first(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const f
   const int64_t tt = blockIdx.x % tiles_per;
   const int64_t i0 = (tt / tiles_j) * 64, j0 = (tt % tiles_j) * 64;
   const int64_t sbase = b * m * n;
+  grad = batch_view(grad, tabs.grad, b, m * n);
+  mom = batch_view(mom, tabs.mom, b, m * n);
   float ss = 0.f;
   for (int e = threadIdx.x; e < 64 * 64; e += 256) {
     int li, lj;
@@ -146,6 +148,7 @@ struct GemmArgs {
   int last;
   void* param; int param_bf16; float* ns_out; float lr, wd, s;
   const float* lrwd;   // optional device {lr, wd}
+  MatTabs tabs;        // per-matrix W / O addresses (zero-copy batching), or null
   int64_t m, n; int transposed;
 };
 
@@ -796,8 +799,10 @@ tl_gemm(GemmArgs g) {
       update_scalars(g.lrwd, ulr, uwd);
       const uint32_t ldx = (uint32_t)g.ldx;
       const float* X32 = g.X32 ? g.X32 + mat * g.strideX : nullptr;
-      PT* W = g.param ? reinterpret_cast<PT*>(g.param) + mat * g.m * g.n : nullptr;
-      float* O = g.ns_out ? g.ns_out + mat * g.m * g.n : nullptr;
+      PT* W = batch_view(reinterpret_cast<PT*>(g.param), g.tabs.param, mat, g.m * g.n);
+      float* O = batch_view(g.ns_out, g.tabs.ns, mat, g.m * g.n);
+      if (W) W += mat * g.m * g.n;
+      if (O) O += mat * g.m * g.n;
       const uint32_t m = (uint32_t)g.m, n = (uint32_t)g.n;
       if constexpr (EPI == EPI_LAST) {
         // W row-major: the lane takes 8 consecutive columns of rows rr, rr + 8,
@@ -984,6 +989,7 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
     g.last = (k == a.steps - 1);
     g.param = a.phase == PH_FULL ? a.param : nullptr; g.param_bf16 = a.param_dtype == DT_BF16;
     g.ns_out = a.ns_out; g.lr = a.lr; g.wd = a.wd; g.s = a.s; g.lrwd = a.lrwd;
+    g.tabs = a.phase == PH_FULL ? a.tabs : MatTabs{};
     g.m = sh.m; g.n = sh.n; g.transposed = sh.transposed;
     if (g.last && !sh.transposed)
       MUON_LAUNCH("tl_apply_update", (tl_gemm<C, EPI_LAST, PT>), dim3(gemm_grid<C, EPI_LAST, PT>(g.tiles_total)),
@@ -1033,7 +1039,7 @@ hipError_t tiled_impl(const StepArgs& a, const WsLayout& L) {
 
   MUON_LAUNCH("tl_momentum_layout", (tl_first<GT, OP>), dim3((unsigned)(sh.count * L.nparts)), dim3(256), a.stream,
               mode, (const GT*)a.grad, a.mom, a.u_in, ssp, X, XT[0], X32, sh.m, sh.n, mp, np, (int)sh.transposed,
-              a.mu, a.nesterov);
+              a.mu, a.nesterov, a.phase == PH_FULL ? a.tabs : MatTabs{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   MUON_LAUNCH("tl_norm_finalize", tl_norm_finalize, dim3((unsigned)sh.count), dim3(256), a.stream, ssp, L.nparts,

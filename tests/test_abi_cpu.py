@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.EXPORTED)
-    assert B.muon_abi_version() == 2
+    assert B.muon_abi_version() == 3
 
 
 def _cmp_plans(shapes, cap=0, order=0):
@@ -222,6 +222,38 @@ def test_step_rejects_bad_buffers(plan_fb):
     hpc, keep = B.HParams().to_c()
     assert B.lib().muon_step(p.handle, 0, None, C.byref(hpc), fb.ptr("ws"), need, None) == 1
     assert B.lib().muon_step(None, 0, None, C.byref(hpc), fb.ptr("ws"), need, None) == 1
+    assert fb.untouched()
+
+
+def test_step_ptrs_rejects_bad_args(plan_fb):
+    """muon_step_ptrs: the pointer tables are checked like buffers (non-null,
+    16-byte aligned, not overlapping each other or the workspace); what they
+    hold is device data the host never reads."""
+    p, fb = plan_fb
+    L = B.lib()
+    need = p.workspace_bytes(0, "bf16")
+    hpc, keep = B.HParams().to_c()
+
+    def call(params=None, grads=None, moms=None, outs=None, ws=None, wsb=need, pdt=B.MUON_BF16, batch=0):
+        bufs = B.muon_batch_ptrs(params if params is not None else fb.ptr("param"), pdt,
+                                 grads if grads is not None else fb.ptr("grad"), B.MUON_BF16,
+                                 moms if moms is not None else fb.ptr("mom"), outs)
+        return L.muon_step_ptrs(p.handle, batch, C.byref(bufs), C.byref(hpc),
+                                ws if ws is not None else fb.ptr("ws"), wsb, None)
+
+    assert call(wsb=need - 1) == B.MUON_ERR_WORKSPACE_TOO_SMALL
+    assert call(params=0) == B.MUON_ERR_INVALID_ARG
+    assert call(grads=0) == B.MUON_ERR_INVALID_ARG
+    assert call(moms=0) == B.MUON_ERR_INVALID_ARG
+    assert call(grads=fb.ptr("grad", 8)) == B.MUON_ERR_INVALID_ARG      # table not 16-byte aligned
+    assert call(grads=fb.ptr("param")) == B.MUON_ERR_INVALID_ARG        # same table twice
+    assert call(outs=fb.ptr("ws")) == B.MUON_ERR_INVALID_ARG            # table inside the workspace
+    assert call(pdt=5) == B.MUON_ERR_INVALID_ARG
+    assert call(batch=9) == B.MUON_ERR_INVALID_ARG
+    assert L.muon_step_ptrs(p.handle, 0, None, C.byref(hpc), fb.ptr("ws"), need, None) == 1
+    bad, _ = B.HParams(ns_steps=0).to_c()
+    bufs = B.muon_batch_ptrs(fb.ptr("param"), 1, fb.ptr("grad"), 1, fb.ptr("mom"), None)
+    assert L.muon_step_ptrs(p.handle, 0, C.byref(bufs), C.byref(bad), fb.ptr("ws"), need, None) == 1
     assert fb.untouched()
 
 
