@@ -973,7 +973,9 @@ sk_apply(const typename SkCfg<MODE>::XS* __restrict__ xg, const BFrag* __restric
   typedef typename SkCfg<MODE>::XS XS;
   constexpr int XW = MODE == 0 ? 4 : 8;     // 32-bit words of U per lane per K block
   const int lane = threadIdx.x & (WAVE - 1);
-  const int w = threadIdx.x / WAVE;
+  // wave index as a scalar: the matrix index and the pointers taken from the
+  // tables stay in scalar registers and the null tests stay uniform branches
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
   const int h = lane >> 5, c = lane & 31;
   const int64_t unit = (int64_t)blockIdx.x * SK_WAVES + w;
   if (unit >= units) return;   // whole waves only; the kernel has no workgroup barriers
