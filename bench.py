@@ -4,14 +4,17 @@
 
 A step is one full muon_step over every batch of the workload (momentum,
 normalisation, transpose-first, K Newton-Schulz steps, decay and update), with
-all inputs resident in device memory.  Prints ONE JSON line with:
+all inputs resident in device memory; several batches are spread over
+--streams streams (muon_step_batches).  Prints ONE JSON line with:
 
 * value: Newton-Schulz TFLOP/s, counting 4 m^2 n + 2 m^3 flops per
   Newton-Schulz step per matrix (m <= n), divided by the full step time;
 * ms_per_step: batched step latency;
 * roofline: the dominant kernel (largest share of traced time), its
   algorithmic bytes (or flops) per launch over its average launch time,
-  measured with HIP events recorded by the library on the launch stream;
+  measured with HIP events recorded by the library on the launch stream
+  (with batches on several streams a launch's time includes what it shares
+  with the other lanes' kernels);
 * cpu_baseline: the float64 CPU oracle timed on a bounded sample of the same
   workload on this host.
 """
@@ -301,6 +304,9 @@ def main():
                     help="short sides <= 32: 0 or 1 Newton-Schulz in Gram space, 2 step by step")
     ap.add_argument("--device-inputs", action="store_true",
                     help="draw the inputs on the GPU with seeded torch generators (large workloads)")
+    ap.add_argument("--streams", type=int, default=2,
+                    help="spread the batches of a step over this many streams (muon_step_batches; at most the "
+                         "number of batches; 1 = the batches in plan order on one stream)")
     ap.add_argument("--reuse-shapes", action="store_true",
                     help="batches of identical shape share generated input values (copied per batch)")
     args = ap.parse_args()
@@ -324,18 +330,26 @@ def main():
         bufs = make_device_batches_gpu(wl, plan, dtype)
     else:
         bufs = make_device_batches(wl, plan, dtype, args.reuse_shapes)
-    ws_bytes = max(plan.workspace_bytes(b.index, prec) for b in plan.batches)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     # lr and decay from device scalars, so a captured step needs no recapture
     lr_wd = torch.tensor([hp.lr, hp.weight_decay], dtype=torch.float32, device="cuda")
     hp_run = dataclasses.replace(hp, lr_wd=lr_wd)
+    nstreams = max(1, min(args.streams, len(plan.batches)))
+    bidx = [b.index for b in plan.batches]
+    lane_of, lane_ws = B.plan_lanes(plan, bidx, hp_run, nstreams)
+    wss = [torch.empty(max(n, 256), dtype=torch.uint8, device="cuda") if n else None for n in lane_ws]
+    side = [torch.cuda.Stream() for _ in range(nstreams - 1)]
+    step_bufs = [(bufs[i]["param"], bufs[i]["grad"], bufs[i]["momentum"]) for i in bidx]
 
     def step():
-        # on the current stream (the capture stream while a graph is recorded)
-        for b in plan.batches:
-            d = bufs[b.index]
-            B.muon_step(plan, b.index, d["param"], d["grad"], d["momentum"], hp_run, ws)
+        # the caller's part on the current stream (the capture stream while a
+        # graph is recorded), the other lanes on side streams
+        if nstreams == 1:
+            for b in plan.batches:
+                d = bufs[b.index]
+                B.muon_step(plan, b.index, d["param"], d["grad"], d["momentum"], hp_run, wss[0])
+        else:
+            B.muon_step_batches(plan, bidx, step_bufs, hp_run, wss, [None] + [s.cuda_stream for s in side])
 
     for _ in range(args.warmup):
         step()
@@ -416,6 +430,7 @@ def main():
         flops = flops / wl.hp.ns_steps * hp.ns_steps
     value = flops / (ms / 1e3) / 1e12
     cfg = {"workload": wl.name, "matrices": int(sum(b.count for b in plan.batches)), "launch": args.launch,
+           "streams": nstreams, "lanes": lane_of,
            "batches": [[b.count, b.M, b.N] for b in plan.batches],
            "kernels": [["tiled", "skinny_gram", "skinny_stepwise"][b.path] for b in plan.batches],
            "param_dtype": dtype,

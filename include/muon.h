@@ -25,7 +25,9 @@
  * batch, param, grad, momentum and ns_out are contiguous row-major
  * [count, M, N] regions (a parameter's matrices sit at the segment offsets
  * that muon_plan_segments reports).  The library never allocates, frees or
- * synchronises device memory or streams; its only state is the host-side plan.
+ * synchronises device memory or streams; its state is the host-side plan, plus
+ * a few HIP events per device that muon_step_batches creates on first use
+ * (fork and join markers, no device memory) and keeps until the process ends.
  * All kernels are enqueued on `stream` (a hipStream_t; NULL = the null stream)
  * and the call returns without waiting for them.
  *
@@ -48,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 3
+#define MUON_ABI_VERSION 4
 
 typedef enum {
   MUON_OK = 0,
@@ -202,6 +204,42 @@ muon_status muon_step(const muon_plan* plan, int32_t batch, const muon_batch_buf
  * they hold are the caller's responsibility (see muon_batch_ptrs). */
 muon_status muon_step_ptrs(const muon_plan* plan, int32_t batch, const muon_batch_ptrs* bufs,
                            const muon_hparams* hp, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Several batches of one step on several streams.
+ *
+ * Each batch is its own batched Newton-Schulz iteration (HyperParallel-FSDP
+ * §6.6: one sequence of batched products per core-shape group), so one batch's
+ * kernels can run beside another's.  The pages run the batches of a step as
+ * one stream of compute (§6.6, Figure 10(b)); here a second stream fills the
+ * last, partial round of tiles that most tiled launches leave on 256 CUs with
+ * another batch's tiles.
+ *
+ * Lanes.  Batches are taken in decreasing estimated run time (tiled: flops of
+ * the K Gram, polynomial and apply products; skinny: bytes moved), ties in
+ * the order given, and each goes to the lane with the least estimated time so
+ * far (ties: the lowest lane).  Lane l runs its batches, in that order, on
+ * streams[l] with workspaces[l].  muon_plan_lanes reports the assignment and
+ * each lane's workspace size; it is a pure host computation.
+ *
+ * muon_step_batches: bufs[i] holds the buffers of batch batches[i] (as for
+ * muon_step).  streams[0] is the caller's stream: the step runs after the work
+ * already enqueued there and work enqueued there after the call runs after
+ * the whole step (the other lanes wait for an event recorded on streams[0],
+ * and streams[0] waits for an event recorded at the end of each of them).
+ * The streams must belong to the current device; with nstreams = 1 the call
+ * is muon_step on each batch in lane order.  Results are bitwise those of
+ * muon_step on each batch.  Batch indices must be distinct; every buffer and
+ * every used lane's workspace (workspaces[l] may be NULL for a lane with no
+ * batch) must be disjoint from all others, since lanes run concurrently.
+ * A HIP error part-way returns MUON_ERR_HIP with some batches enqueued.
+ * Capturable into a HIP graph on streams[0] (the fork and join are event
+ * records and waits). */
+#define MUON_MAX_STREAMS 8
+muon_status muon_plan_lanes(const muon_plan* plan, int32_t n, const int32_t* batches, const muon_hparams* hp,
+                            int32_t nstreams, int32_t* lane_of, size_t* lane_workspace_bytes);
+muon_status muon_step_batches(const muon_plan* plan, int32_t n, const int32_t* batches,
+                              const muon_batch_buffers* bufs, const muon_hparams* hp, void* const* workspaces,
+                              const size_t* workspace_bytes, void* const* streams, int32_t nstreams);
 
 /* Stage entry points, same validation.  They run the stages of muon_step one
  * at a time so each can be checked on its own.

@@ -28,7 +28,8 @@ SCALES = {"none": MUON_SCALE_NONE, "rms": MUON_SCALE_RMS}
 EXPORTED = ["muon_abi_version", "muon_status_str", "muon_plan_create", "muon_plan_destroy", "muon_step_ptrs",
             "muon_plan_num_batches", "muon_plan_batch_info", "muon_plan_segments",
             "muon_workspace_bytes", "muon_step", "muon_stage_momentum", "muon_stage_ns",
-            "muon_stage_update", "muon_trace_start", "muon_trace_stop"]
+            "muon_stage_update", "muon_trace_start", "muon_trace_stop", "muon_plan_lanes",
+            "muon_step_batches"]
 
 
 class muon_shape(C.Structure):
@@ -108,6 +109,13 @@ def lib():
     L.muon_step_ptrs.restype = C.c_int32
     L.muon_step_ptrs.argtypes = [C.c_void_p, C.c_int32, C.POINTER(muon_batch_ptrs), C.POINTER(muon_hparams),
                                  C.c_void_p, C.c_size_t, C.c_void_p]
+    L.muon_plan_lanes.restype = C.c_int32
+    L.muon_plan_lanes.argtypes = [C.c_void_p, C.c_int32, C.POINTER(C.c_int32), C.POINTER(muon_hparams), C.c_int32,
+                                  C.POINTER(C.c_int32), C.POINTER(C.c_size_t)]
+    L.muon_step_batches.restype = C.c_int32
+    L.muon_step_batches.argtypes = [C.c_void_p, C.c_int32, C.POINTER(C.c_int32), C.POINTER(muon_batch_buffers),
+                                    C.POINTER(muon_hparams), C.POINTER(C.c_void_p), C.POINTER(C.c_size_t),
+                                    C.POINTER(C.c_void_p), C.c_int32]
     L.muon_stage_momentum.restype = C.c_int32
     L.muon_stage_momentum.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
                                       C.POINTER(muon_hparams), C.c_void_p]
@@ -300,6 +308,40 @@ def muon_step_ptrs(plan: Plan, batch: int, params, grads, momenta, hp: HParams, 
     _check(st, "muon_step_ptrs")
 
 
+def plan_lanes(plan: Plan, batches, hp: HParams, nstreams: int):
+    """(lane of each batch, workspace bytes of each lane) for muon_step_batches
+    over `nstreams` streams (muon_plan_lanes)."""
+    n = len(batches)
+    arr = (C.c_int32 * n)(*batches)
+    lane_of = (C.c_int32 * n)()
+    wsb = (C.c_size_t * max(int(nstreams), 1))()
+    hpc, keep = hp.to_c()
+    _check(lib().muon_plan_lanes(plan.handle, n, arr, C.byref(hpc), int(nstreams), lane_of, wsb), "muon_plan_lanes")
+    return list(lane_of), list(wsb)[:int(nstreams)]
+
+
+def muon_step_batches(plan: Plan, batches, bufs, hp: HParams, workspaces, streams) -> None:
+    """One step over several batches on several streams (muon_step_batches).
+    bufs[i] = (param, grad, momentum[, ns_out]) of batch batches[i];
+    workspaces[l] (uint8 tensor, or None for a lane with no batch) and
+    streams[l] (hipStream_t handle as an int; None in place 0 = the current
+    stream) per lane."""
+    n, ns = len(batches), len(streams)
+    if len(bufs) != n or len(workspaces) != ns:
+        raise ValueError("muon_step_batches: one buffer set per batch and one workspace per stream")
+    arr = (C.c_int32 * n)(*batches)
+    fb = (muon_batch_buffers * n)()
+    for i, t in enumerate(bufs):
+        param, grad, mom = t[0], t[1], t[2]
+        out = t[3] if len(t) > 3 else None
+        fb[i] = muon_batch_buffers(_ptr(param), _dtype_code(param), _ptr(grad), _dtype_code(grad), _ptr(mom), _ptr(out))
+    wp = (C.c_void_p * ns)(*[_ptr(w) for w in workspaces])
+    wb = (C.c_size_t * ns)(*[0 if w is None else w.numel() * w.element_size() for w in workspaces])
+    sp = (C.c_void_p * ns)(*[_stream(s) if i == 0 else int(s) for i, s in enumerate(streams)])
+    hpc, keep = hp.to_c()
+    _check(lib().muon_step_batches(plan.handle, n, arr, fb, C.byref(hpc), wp, wb, sp, ns), "muon_step_batches")
+
+
 def muon_stage_momentum(plan: Plan, batch: int, grad, momentum, u_out, hp: HParams, stream=None) -> None:
     hpc, keep = hp.to_c()
     _check(lib().muon_stage_momentum(plan.handle, batch, _ptr(grad), _dtype_code(grad), _ptr(momentum),
@@ -337,9 +379,13 @@ def muon_trace_stop() -> List[Tuple[str, float]]:
 class BatchedMuon:
     """All batches of a plan with per-batch contiguous [count, M, N] buffers
     (parameters of a batch are views into its buffer, as in HyperParallel-FSDP
-    §6.6's merged tensor) and one workspace sized for the largest batch."""
+    §6.6's merged tensor).  streams = 1: the batches run in plan order on the
+    caller's stream with one workspace sized for the largest batch; streams > 1:
+    muon_step_batches spreads them over the caller's stream and streams - 1
+    side streams (default priority), one workspace per lane."""
 
-    def __init__(self, shapes, dtype, hp: HParams, device="cuda", max_batch_elems=0, order=0, skinny_kernel=0):
+    def __init__(self, shapes, dtype, hp: HParams, device="cuda", max_batch_elems=0, order=0, skinny_kernel=0,
+                 streams=1):
         import torch
         self.plan = Plan(shapes, max_batch_elems, order, skinny_kernel)
         self.hp = hp
@@ -351,13 +397,27 @@ class BatchedMuon:
             self.params.append(torch.empty(shp, dtype=dtype, device=device))
             self.grads.append(torch.empty(shp, dtype=dtype, device=device))
             self.moms.append(torch.zeros(shp, dtype=torch.float32, device=device))
-        ws = max(self.plan.workspace_bytes(b.index, hp.precision) for b in self.plan.batches)
-        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+        self.nstreams = max(1, min(int(streams), len(self.plan.batches)))
+        if self.nstreams == 1:
+            ws = max(self.plan.workspace_bytes(b.index, hp.precision) for b in self.plan.batches)
+            self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+        else:
+            idx = [b.index for b in self.plan.batches]
+            self.lane_of, need = plan_lanes(self.plan, idx, hp, self.nstreams)
+            self.workspaces = [torch.empty(max(w, 256), dtype=torch.uint8, device=device) if w else None
+                               for w in need]
+            self.side_streams = [torch.cuda.Stream(device=device) for _ in range(self.nstreams - 1)]
 
     def step(self, ns_outs=None, stream=None):
-        for b in self.plan.batches:
-            muon_step(self.plan, b.index, self.params[b.index], self.grads[b.index], self.moms[b.index],
-                      self.hp, self.workspace, None if ns_outs is None else ns_outs[b.index], stream)
+        if self.nstreams == 1:
+            for b in self.plan.batches:
+                muon_step(self.plan, b.index, self.params[b.index], self.grads[b.index], self.moms[b.index],
+                          self.hp, self.workspace, None if ns_outs is None else ns_outs[b.index], stream)
+            return
+        bufs = [(self.params[b.index], self.grads[b.index], self.moms[b.index],
+                 None if ns_outs is None else ns_outs[b.index]) for b in self.plan.batches]
+        muon_step_batches(self.plan, [b.index for b in self.plan.batches], bufs, self.hp, self.workspaces,
+                          [stream] + [s.cuda_stream for s in self.side_streams])
 
     def capture_graph(self):
         """Record one step (every batch) into a HIP graph (torch.cuda.CUDAGraph)

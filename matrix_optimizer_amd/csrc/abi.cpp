@@ -5,6 +5,8 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -189,6 +191,77 @@ hipError_t dispatch(const StepArgs& a, const WsLayout& L) {
     case PATH_SKINNY_STEPWISE: return run_skinny(a, L);
     default: return run_tiled(a, L);
   }
+}
+
+// ---- several batches on several streams -----------------------------------
+
+// Estimated run time of a batch, only for ordering: tiled batches by the flops
+// of K Gram, polynomial and apply products at 1 PFLOP/s, skinny ones by about
+// 20 bytes per element at 6 TB/s.
+double batch_cost(const muon_plan::Batch& b, int steps) {
+  const double m = double(std::min(b.M, b.N)), n = double(std::max(b.M, b.N)), c = double(b.count);
+  if (b.path == PATH_TILED) return c * steps * (m * (m + 1) * n + m * m * (m + 1) + 2 * m * m * n) / 1.0e15;
+  return c * m * n * 20.0 / 6.0e12;
+}
+
+// Lanes by longest estimated time first onto the least-loaded lane.  order
+// receives positions into batches[] in that order.
+void assign_lanes(const muon_plan* plan, int32_t n, const int32_t* batches, int steps, int32_t nlanes,
+                  int32_t* lane_of, std::vector<int32_t>& order) {
+  std::vector<double> cost(n);
+  order.resize(n);
+  for (int32_t i = 0; i < n; ++i) {
+    cost[i] = batch_cost(plan->batches[batches[i]], steps);
+    order[i] = i;
+  }
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return cost[x] > cost[y]; });
+  std::vector<double> load(nlanes, 0.0);
+  for (int32_t i : order) {
+    int32_t best = 0;
+    for (int32_t l = 1; l < nlanes; ++l)
+      if (load[l] < load[best]) best = l;
+    lane_of[i] = best;
+    load[best] += cost[i];
+  }
+}
+
+// Common checks of muon_plan_lanes and muon_step_batches.
+muon_status check_batch_list(const muon_plan* plan, int32_t n, const int32_t* batches, int32_t nstreams) {
+  if (!plan || n < 1 || !batches || nstreams < 1 || nstreams > MUON_MAX_STREAMS) return MUON_ERR_INVALID_ARG;
+  std::vector<bool> seen(plan->batches.size(), false);
+  for (int32_t i = 0; i < n; ++i) {
+    if (!get_batch(plan, batches[i]) || seen[batches[i]]) return MUON_ERR_INVALID_ARG;
+    seen[batches[i]] = true;
+  }
+  return MUON_OK;
+}
+
+// Disjointness of many regions (null, misaligned or empty ones rejected).
+bool regions_disjoint(std::vector<Region> rs) {
+  for (const Region& r : rs)
+    if (r.lo == 0 || (r.lo & 15u) || r.hi <= r.lo) return false;
+  std::sort(rs.begin(), rs.end(), [](const Region& a, const Region& b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < rs.size(); ++i)
+    if (rs[i].lo < rs[i - 1].hi) return false;
+  return true;
+}
+
+// Fork / join events, per device, created on first use and never released.
+// Calls hold the lock from the first record to the last wait, so the events
+// of concurrent calls are not re-recorded before their waits are enqueued.
+std::mutex g_ev_mu;
+std::map<int, std::vector<hipEvent_t>> g_events;
+
+hipError_t device_events(int dev, size_t count, std::vector<hipEvent_t>*& out) {
+  std::vector<hipEvent_t>& v = g_events[dev];
+  while (v.size() < count) {
+    hipEvent_t e;
+    const hipError_t err = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+    if (err != hipSuccess) return err;
+    v.push_back(e);
+  }
+  out = &v;
+  return hipSuccess;
 }
 
 }  // namespace
@@ -383,6 +456,105 @@ muon_status muon_step_ptrs(const muon_plan* plan, int32_t batch, const muon_batc
   a.tabs.ns = reinterpret_cast<const void* const*>(bufs->ns_out);
   a.ws = static_cast<char*>(workspace);
   return hip_status(dispatch(a, L));
+}
+
+muon_status muon_plan_lanes(const muon_plan* plan, int32_t n, const int32_t* batches, const muon_hparams* hp,
+                            int32_t nstreams, int32_t* lane_of, size_t* lane_workspace_bytes) {
+  muon_status st = check_batch_list(plan, n, batches, nstreams);
+  if (st != MUON_OK) return st;
+  if (!lane_of || !lane_workspace_bytes) return MUON_ERR_INVALID_ARG;
+  st = check_hparams(hp, true, false, false);
+  if (st != MUON_OK) return st;
+  std::vector<int32_t> order;
+  try {
+    assign_lanes(plan, n, batches, hp->ns_steps, nstreams, lane_of, order);
+  } catch (const std::bad_alloc&) {
+    return MUON_ERR_NO_MEMORY;
+  }
+  for (int32_t l = 0; l < nstreams; ++l) lane_workspace_bytes[l] = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const muon_plan::Batch& b = plan->batches[batches[i]];
+    const size_t need = workspace_layout(shape_of(b), hp->precision, b.path).total;
+    lane_workspace_bytes[lane_of[i]] = std::max(lane_workspace_bytes[lane_of[i]], need);
+  }
+  return MUON_OK;
+}
+
+muon_status muon_step_batches(const muon_plan* plan, int32_t n, const int32_t* batches,
+                              const muon_batch_buffers* bufs, const muon_hparams* hp, void* const* workspaces,
+                              const size_t* workspace_bytes, void* const* streams, int32_t nstreams) {
+  muon_status st = check_batch_list(plan, n, batches, nstreams);
+  if (st != MUON_OK) return st;
+  if (!bufs || !workspaces || !workspace_bytes || !streams) return MUON_ERR_INVALID_ARG;
+  st = check_hparams(hp, true, true, true);
+  if (st != MUON_OK) return st;
+  try {
+    std::vector<int32_t> lane_of(n), order;
+    assign_lanes(plan, n, batches, hp->ns_steps, nstreams, lane_of.data(), order);
+    std::vector<size_t> need(nstreams, 0);
+    std::vector<Region> rs;
+    for (int32_t i = 0; i < n; ++i) {
+      const muon_plan::Batch& b = plan->batches[batches[i]];
+      const muon_batch_buffers& f = bufs[i];
+      if (!valid_dtype(f.param_dtype) || !valid_dtype(f.grad_dtype)) return MUON_ERR_INVALID_ARG;
+      const size_t elems = size_t(b.count) * b.M * b.N;
+      rs.push_back(region(f.param, elems * dsize(f.param_dtype)));
+      rs.push_back(region(f.grad, elems * dsize(f.grad_dtype)));
+      rs.push_back(region(f.momentum, elems * 4));
+      if (f.ns_out) rs.push_back(region(f.ns_out, elems * 4));
+      need[lane_of[i]] = std::max(need[lane_of[i]], workspace_layout(shape_of(b), hp->precision, b.path).total);
+    }
+    for (int32_t l = 0; l < nstreams; ++l) {
+      if (need[l] == 0) continue;
+      if (workspace_bytes[l] < need[l]) return MUON_ERR_WORKSPACE_TOO_SMALL;
+      if (!workspaces[l] || (reinterpret_cast<uintptr_t>(workspaces[l]) & 255u)) return MUON_ERR_INVALID_ARG;
+      rs.push_back(region(workspaces[l], need[l]));
+    }
+    if (!regions_disjoint(rs)) return MUON_ERR_INVALID_ARG;
+
+    auto run_lane = [&](int32_t l) -> hipError_t {
+      for (int32_t i : order) {
+        if (lane_of[i] != l) continue;
+        const muon_plan::Batch& b = plan->batches[batches[i]];
+        const muon_batch_buffers& f = bufs[i];
+        StepArgs a;
+        fill_common(a, b, hp, streams[l]);
+        a.phase = PH_FULL;
+        a.param = f.param; a.param_dtype = f.param_dtype == MUON_BF16 ? DT_BF16 : DT_F32;
+        a.grad = f.grad; a.grad_dtype = f.grad_dtype == MUON_BF16 ? DT_BF16 : DT_F32;
+        a.mom = f.momentum; a.ns_out = f.ns_out;
+        a.ws = static_cast<char*>(workspaces[l]);
+        const hipError_t e = dispatch(a, workspace_layout(a.shape, hp->precision, b.path));
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
+    };
+    int32_t used = 0;
+    for (int32_t l = 1; l < nstreams; ++l) used += need[l] > 0;
+    if (used == 0) return hip_status(run_lane(0));
+
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return MUON_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_ev_mu);
+    std::vector<hipEvent_t>* ev = nullptr;   // [0] fork, [l] join of lane l
+    if ((e = device_events(dev, size_t(nstreams), ev)) != hipSuccess) return MUON_ERR_HIP;
+    const hipStream_t s0 = reinterpret_cast<hipStream_t>(streams[0]);
+    if ((e = hipEventRecord((*ev)[0], s0)) != hipSuccess) return MUON_ERR_HIP;
+    for (int32_t l = 1; l < nstreams; ++l)
+      if (need[l] > 0 && (e = hipStreamWaitEvent(reinterpret_cast<hipStream_t>(streams[l]), (*ev)[0], 0)) != hipSuccess)
+        return MUON_ERR_HIP;
+    for (int32_t l = 0; l < nstreams; ++l)
+      if ((l == 0 || need[l] > 0) && (e = run_lane(l)) != hipSuccess) return MUON_ERR_HIP;
+    for (int32_t l = 1; l < nstreams; ++l) {
+      if (need[l] == 0) continue;
+      if ((e = hipEventRecord((*ev)[l], reinterpret_cast<hipStream_t>(streams[l]))) != hipSuccess) return MUON_ERR_HIP;
+      if ((e = hipStreamWaitEvent(s0, (*ev)[l], 0)) != hipSuccess) return MUON_ERR_HIP;
+    }
+    return MUON_OK;
+  } catch (const std::bad_alloc&) {
+    return MUON_ERR_NO_MEMORY;
+  }
 }
 
 muon_status muon_stage_momentum(const muon_plan* plan, int32_t batch, const void* grad, muon_dtype grad_dtype,

@@ -59,6 +59,28 @@ tl_norm_finalize(const float* __restrict__ ssp, int64_t nparts, float eps, float
   }
 }
 
+// 8 consecutive elements at a 16-byte aligned address, as floats.
+__device__ __forceinline__ void load8(const float* p, float* f) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) { f[q] = a[q]; f[q + 4] = b[q]; }
+}
+__device__ __forceinline__ void load8(const bf16_t* p, float* f) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) { f[2 * q] = __uint_as_float(v[q] << 16); f[2 * q + 1] = __uint_as_float(v[q] & 0xffff0000u); }
+}
+__device__ __forceinline__ void store8(float* p, const float* f) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{f[0], f[1], f[2], f[3]};
+  *reinterpret_cast<f32x4*>(p + 4) = f32x4{f[4], f[5], f[6], f[7]};
+}
+__device__ __forceinline__ void store8(bf16_t* p, const float* f) {
+  u32x4 v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = (uint32_t)f2bf(f[2 * q]) | ((uint32_t)f2bf(f[2 * q + 1]) << 16);
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
 // ---------------------------------------------------------------------------
 // First pass of the tiled path, one 64x64 tile (Newton-Schulz orientation)
 // per workgroup: momentum and the Nesterov direction U (or a given U), the
@@ -69,10 +91,14 @@ tl_norm_finalize(const float* __restrict__ ssp, int64_t nparts, float eps, float
 //   mode 0: M' = mu M + G (in place), U = G + mu M' or M'
 //   mode 1: U from u_in
 // ssp[blockIdx.x] = sum of U^2 over the tile (fixed order).
+// vec (mode 0, no X^T, stored rows a multiple of 8 long): each lane moves
+// runs of 8 consecutive stored elements, 16-byte accesses, and issues the
+// loads of both its runs before any store; X comes straight from registers
+// (through the LDS tile when the stored rows are X columns).
 // ---------------------------------------------------------------------------
 template <typename GT, typename XO>
 __global__ void __launch_bounds__(256)
-tl_first(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const float* __restrict__ u_in,
+tl_first(int mode, int vec, const GT* __restrict__ grad, float* __restrict__ mom, const float* __restrict__ u_in,
          float* __restrict__ ssp, XO* __restrict__ X, XO* __restrict__ XT, float* __restrict__ X32,
          int64_t m, int64_t n, int64_t mp, int64_t np, int transposed, float mu, int nesterov, MatTabs tabs) {
   __shared__ float tile[64][65];
@@ -83,40 +109,101 @@ tl_first(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const f
   const int64_t tt = blockIdx.x % tiles_per;
   const int64_t i0 = (tt / tiles_j) * 64, j0 = (tt % tiles_j) * 64;
   const int64_t sbase = b * m * n;
+  const int64_t xb = b * mp * np;
   grad = batch_view(grad, tabs.grad, b, m * n);
   mom = batch_view(mom, tabs.mom, b, m * n);
   float ss = 0.f;
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    int li, lj;
-    if (!transposed) { li = e >> 6; lj = e & 63; }   // stored rows are X rows
-    else { lj = e >> 6; li = e & 63; }               // stored rows are X columns
-    const int64_t i = i0 + li, j = j0 + lj;
-    float u = 0.f;
-    if (i < m && j < n) {
-      const int64_t si = sbase + (transposed ? j * m + i : i * n + j);
-      if (mode == 1) {
-        u = u_in[si];
-      } else {
-        const float g = ld_as_f32(grad, si);
-        const float mn = mu * mom[si] + g;
-        mom[si] = mn;
-        u = nesterov ? g + mu * mn : mn;
+  if (vec) {
+    // run h of a lane: stored row sr of the tile, elements sc .. sc + 7
+    Raw8<GT> gr[2];
+    Raw8<float> mr[2];
+    bool ok[2];
+    int64_t si[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int v = threadIdx.x + 256 * h, sr = v >> 3, sc = (v & 7) * 8;
+      const int64_t i = transposed ? i0 + sc : i0 + sr, j = transposed ? j0 + sr : j0 + sc;
+      ok[h] = i < m && j < n;   // whole runs: the stored row length is a multiple of 8
+      si[h] = sbase + (transposed ? j * m + i : i * n + j);
+      if (ok[h]) {
+        gr[h].load(grad + si[h]);
+        mr[h].load(mom + si[h]);
       }
     }
-    ss += u * u;
-    tile[li][lj] = u;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int v = threadIdx.x + 256 * h, sr = v >> 3, sc = (v & 7) * 8;
+      float u[8];
+      if (ok[h]) {
+        float g[8], mo[8];
+        gr[h].to_f32(g);
+        mr[h].to_f32(mo);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          mo[q] = mu * mo[q] + g[q];
+          u[q] = nesterov ? g[q] + mu * mo[q] : mo[q];
+        }
+        store8(mom + si[h], mo);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) u[q] = 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) ss += u[q] * u[q];
+      if (transposed) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) tile[sc + q][sr] = u[q];
+      } else {
+        const int64_t xi = xb + (i0 + sr) * np + j0 + sc;
+        store8(X + xi, u);
+        if (X32) store8(X32 + xi, u);
+      }
+    }
+  } else {
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+      int li, lj;
+      if (!transposed) { li = e >> 6; lj = e & 63; }   // stored rows are X rows
+      else { lj = e >> 6; li = e & 63; }               // stored rows are X columns
+      const int64_t i = i0 + li, j = j0 + lj;
+      float u = 0.f;
+      if (i < m && j < n) {
+        const int64_t si = sbase + (transposed ? j * m + i : i * n + j);
+        if (mode == 1) {
+          u = u_in[si];
+        } else {
+          const float g = ld_as_f32(grad, si);
+          const float mn = mu * mom[si] + g;
+          mom[si] = mn;
+          u = nesterov ? g + mu * mn : mn;
+        }
+      }
+      ss += u * u;
+      tile[li][lj] = u;
+    }
   }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
   __syncthreads();   // also: the tile is complete
   if (threadIdx.x == 0) ssp[blockIdx.x] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
-  const int64_t xb = b * mp * np;
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int li = e >> 6, lj = e & 63;
-    const float v = tile[li][lj];
-    const int64_t xi = xb + (i0 + li) * np + j0 + lj;
-    st_from_f32(X, xi, v);
-    if (X32) X32[xi] = v;
+  if (!vec) {
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+      const int li = e >> 6, lj = e & 63;
+      const float v = tile[li][lj];
+      const int64_t xi = xb + (i0 + li) * np + j0 + lj;
+      st_from_f32(X, xi, v);
+      if (X32) X32[xi] = v;
+    }
+  } else if (transposed) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int v = threadIdx.x + 256 * h, li = v >> 3, lj = (v & 7) * 8;
+      float u[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) u[q] = tile[li][lj + q];
+      const int64_t xi = xb + (i0 + li) * np + j0 + lj;
+      store8(X + xi, u);
+      if (X32) store8(X32 + xi, u);
+    }
   }
   if (XT) {
     for (int e = threadIdx.x; e < 64 * 64; e += 256) {
@@ -249,28 +336,6 @@ __device__ __forceinline__ void update_run32(bf16_t* w, const float* o, float lr
     }
     *reinterpret_cast<u32x4*>(w + 8 * q) = v;
   }
-}
-
-// 8 consecutive elements at a 16-byte aligned address, as floats.
-__device__ __forceinline__ void load8(const float* p, float* f) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) { f[q] = a[q]; f[q + 4] = b[q]; }
-}
-__device__ __forceinline__ void load8(const bf16_t* p, float* f) {
-  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) { f[2 * q] = __uint_as_float(v[q] << 16); f[2 * q + 1] = __uint_as_float(v[q] & 0xffff0000u); }
-}
-__device__ __forceinline__ void store8(float* p, const float* f) {
-  *reinterpret_cast<f32x4*>(p) = f32x4{f[0], f[1], f[2], f[3]};
-  *reinterpret_cast<f32x4*>(p + 4) = f32x4{f[4], f[5], f[6], f[7]};
-}
-__device__ __forceinline__ void store8(bf16_t* p, const float* f) {
-  u32x4 v;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) v[q] = (uint32_t)f2bf(f[2 * q]) | ((uint32_t)f2bf(f[2 * q + 1]) << 16);
-  *reinterpret_cast<u32x4*>(p) = v;
 }
 
 template <class C> struct StageRegs {
@@ -1037,8 +1102,10 @@ hipError_t tiled_impl(const StepArgs& a, const WsLayout& L) {
   const int64_t mp = L.mp, np = L.np;
   if (L.nparts != (mp / 64) * (np / 64)) return hipErrorInvalidValue;   // one norm partial per 64x64 tile
 
+  // vector form: 16-byte runs of a stored row (n elements, m when stored transposed)
+  const int vec = mode == 0 && !XT[0] && (sh.transposed ? sh.m : sh.n) % 8 == 0;
   MUON_LAUNCH("tl_momentum_layout", (tl_first<GT, OP>), dim3((unsigned)(sh.count * L.nparts)), dim3(256), a.stream,
-              mode, (const GT*)a.grad, a.mom, a.u_in, ssp, X, XT[0], X32, sh.m, sh.n, mp, np, (int)sh.transposed,
+              mode, vec, (const GT*)a.grad, a.mom, a.u_in, ssp, X, XT[0], X32, sh.m, sh.n, mp, np, (int)sh.transposed,
               a.mu, a.nesterov, a.phase == PH_FULL ? a.tabs : MatTabs{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.EXPORTED)
-    assert B.muon_abi_version() == 3
+    assert B.muon_abi_version() == 4
 
 
 def _cmp_plans(shapes, cap=0, order=0):
@@ -279,3 +279,95 @@ def test_status_strings():
     for s in range(7):
         assert B.status_str(s)
     assert B.status_str(42) == "unknown status"
+
+
+def test_plan_lanes():
+    """muon_plan_lanes: the longest batch first, each onto the least-loaded
+    lane; a lane's workspace is the largest of its batches'."""
+    p = B.Plan([(2048, 7168)] * 64 + [(24, 10240)] * 32)
+    idx = [b.index for b in p.batches]
+    assert [(b.count, b.M, b.N) for b in p.batches] == [(36, 2048, 7168), (28, 2048, 7168), (32, 24, 10240)]
+    hp = B.HParams()
+    ws = [p.workspace_bytes(i, "bf16") for i in idx]
+    lanes, need = B.plan_lanes(p, idx, hp, 1)
+    assert lanes == [0, 0, 0] and need == [max(ws)]
+    lanes, need = B.plan_lanes(p, idx, hp, 2)
+    assert lanes == [0, 1, 1] and need == [ws[0], max(ws[1], ws[2])]
+    lanes, need = B.plan_lanes(p, idx, hp, 4)
+    assert lanes == [0, 1, 2] and need == ws + [0]   # three batches: one lane each, lane 3 empty
+    # the order given does not change which batch goes where
+    lanes_r, _ = B.plan_lanes(p, idx[::-1], hp, 2)
+    assert lanes_r == [1, 1, 0]
+    # equal batches alternate lanes in the order given
+    q = B.Plan([(256, 512)] * 4, max_batch_elems=256 * 512)
+    lanes, need = B.plan_lanes(q, [0, 1, 2, 3], hp, 2)
+    assert lanes == [0, 1, 0, 1] and need[0] == need[1] == q.workspace_bytes(0, "bf16")
+    L = B.lib()
+    hpc, keep = hp.to_c()
+    lo = (C.c_int32 * 3)()
+    wb = (C.c_size_t * 9)()
+    for batches, ns in [([0, 0], 2), ([0, 5], 2), ([0], 0), ([0], 9), ([-1], 1)]:
+        arr = (C.c_int32 * len(batches))(*batches)
+        assert L.muon_plan_lanes(p.handle, len(batches), arr, C.byref(hpc), ns, lo, wb) == B.MUON_ERR_INVALID_ARG
+    arr = (C.c_int32 * 1)(0)
+    assert L.muon_plan_lanes(p.handle, 0, arr, C.byref(hpc), 1, lo, wb) == B.MUON_ERR_INVALID_ARG
+    assert L.muon_plan_lanes(p.handle, 1, arr, C.byref(hpc), 1, None, wb) == B.MUON_ERR_INVALID_ARG
+    bad, _ = B.HParams(ns_steps=0).to_c()
+    assert L.muon_plan_lanes(p.handle, 1, arr, C.byref(bad), 1, lo, wb) == B.MUON_ERR_INVALID_ARG
+
+
+def test_step_batches_rejects_bad_args():
+    """muon_step_batches checks every batch's buffers and every used lane's
+    workspace, and that all of them are disjoint (lanes run concurrently),
+    before anything is enqueued."""
+    if _gpu_visible():
+        pytest.skip("fake-pointer validation tests run only where no GPU is visible")
+    p = B.Plan([(24, 1000)] * 2 + [(100, 40)])
+    assert len(p.batches) == 2
+    fbs = [FakeBuffers(p, 0), FakeBuffers(p, 1)]
+    hp = B.HParams()
+    lanes, need = B.plan_lanes(p, [0, 1], hp, 2)
+    assert sorted(lanes) == [0, 1]
+    ws_of = {lanes[i]: fbs[i].ptr("ws") for i in range(2)}
+    L = B.lib()
+    hpc, keep = hp.to_c()
+
+    def call(batches=(0, 1), bufs=None, wsp=None, wsb=None, streams=(None, None), hpp=None, n=None):
+        bl = list(batches)
+        fb = (B.muon_batch_buffers * 2)()
+        for i in range(2):
+            f = fbs[i]
+            fb[i] = B.muon_batch_buffers(f.ptr("param"), 1, f.ptr("grad"), 1, f.ptr("mom"), None)
+        if bufs:
+            for i, v in bufs.items():
+                fb[i] = v
+        w = wsp if wsp is not None else [ws_of[0], ws_of[1]]
+        wb = wsb if wsb is not None else list(need)
+        arr = (C.c_int32 * len(bl))(*bl)
+        return L.muon_step_batches(p.handle, len(bl) if n is None else n, arr, fb, C.byref(hpp or hpc),
+                                   (C.c_void_p * 2)(*w), (C.c_size_t * 2)(*wb), (C.c_void_p * 2)(*streams),
+                                   2)
+
+    assert call(wsb=[need[0] - 1, need[1]]) == B.MUON_ERR_WORKSPACE_TOO_SMALL
+    assert call(wsb=[need[0], need[1] - 1]) == B.MUON_ERR_WORKSPACE_TOO_SMALL
+    assert call(wsp=[0, ws_of[1]]) == B.MUON_ERR_INVALID_ARG                     # used lane without workspace
+    assert call(wsp=[ws_of[0], ws_of[0]]) == B.MUON_ERR_INVALID_ARG              # lanes share a workspace
+    assert call(wsp=[ws_of[0] + 16, ws_of[1]]) == B.MUON_ERR_INVALID_ARG         # not 256-byte aligned
+    f0, f1 = fbs
+    # batch 1's momentum inside batch 0's: both lanes would write it
+    assert call(bufs={1: B.muon_batch_buffers(f1.ptr("param"), 1, f1.ptr("grad"), 1, f0.ptr("mom"), None)}) == 1
+    # an output inside the other lane's workspace
+    assert call(bufs={0: B.muon_batch_buffers(f0.ptr("param"), 1, f0.ptr("grad"), 1, f0.ptr("mom"),
+                                              ws_of[lanes[1]])}) == 1
+    assert call(bufs={0: B.muon_batch_buffers(f0.ptr("param"), 7, f0.ptr("grad"), 1, f0.ptr("mom"), None)}) == 1
+    assert call(batches=(0, 0)) == B.MUON_ERR_INVALID_ARG
+    assert call(batches=(0, 2)) == B.MUON_ERR_INVALID_ARG
+    assert call(n=0) == B.MUON_ERR_INVALID_ARG
+    bad, _ = B.HParams(lr=float("nan")).to_c()
+    assert call(hpp=bad) == B.MUON_ERR_INVALID_ARG
+    arr = (C.c_int32 * 2)(0, 1)
+    fb = (B.muon_batch_buffers * 2)()
+    assert L.muon_step_batches(p.handle, 2, arr, fb, C.byref(hpc), None, None, None, 2) == B.MUON_ERR_INVALID_ARG
+    assert L.muon_step_batches(p.handle, 2, arr, fb, C.byref(hpc), (C.c_void_p * 9)(), (C.c_size_t * 9)(),
+                               (C.c_void_p * 9)(), 9) == B.MUON_ERR_INVALID_ARG
+    assert all(f.untouched() for f in fbs)

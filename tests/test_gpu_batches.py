@@ -1,0 +1,103 @@
+"""muon_step_batches: the batches of a plan spread over several streams give
+bitwise the parameters, momentum and O of muon_step run on each batch in turn.
+
+The plan mixes tiled batches (128 x 128 and 256 x 256 tiles, a transposed
+one), skinny batches in both orientations and an expert tensor, with a batch
+cap that splits one shape into two batches, so lanes hold batches of every
+path.  Lanes run concurrently on separate workspaces; every kernel's
+reductions have a fixed order, so overlap changes no bit.
+"""
+import pytest
+
+from matrix_optimizer_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = ([(300, 700)] * 3 + [(24, 1000)] * 4 + [(1000, 20)] + [(3, 200, 72)] + [(512, 768)] * 2
+          + [(900, 256)])
+CAP = 2 * 300 * 700
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+
+
+def _filled(plan, dtype, seed):
+    import torch
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    out = []
+    for b in plan.batches:
+        shp = (b.count, b.M, b.N)
+        out.append((torch.randn(shp, device="cuda", generator=gen).mul_(0.02).to(dtype),
+                    torch.randn(shp, device="cuda", generator=gen).to(dtype),
+                    torch.randn(shp, device="cuda", generator=gen),
+                    torch.zeros(shp, device="cuda")))
+    return out
+
+
+@pytest.mark.parametrize("prec", ["bf16", "bf16_x32", "f32"])
+@pytest.mark.parametrize("streams", [2, 3])
+def test_step_batches_matches_sequential(streams, prec):
+    import torch
+    plan = B.Plan(SHAPES, max_batch_elems=CAP)
+    assert len(plan.batches) >= 6 and {b.path for b in plan.batches} >= {0, 1}
+    hp = B.HParams(precision=prec)
+    ref = _filled(plan, torch.bfloat16, 21)
+    mine = [tuple(t.clone() for t in bufs) for bufs in ref]
+    ws = torch.zeros(max(plan.workspace_bytes(b.index, prec) for b in plan.batches), dtype=torch.uint8,
+                     device="cuda")
+    for b in plan.batches:
+        P, G, M, O = ref[b.index]
+        B.muon_step(plan, b.index, P, G, M, hp, ws, ns_out=O)
+
+    idx = [b.index for b in plan.batches]
+    lane_of, need = B.plan_lanes(plan, idx, hp, streams)
+    assert sorted(set(lane_of)) == list(range(streams))
+    wss = [torch.zeros(n, dtype=torch.uint8, device="cuda") for n in need]
+    side = [torch.cuda.Stream() for _ in range(streams - 1)]
+    B.muon_step_batches(plan, idx, mine, hp, wss, [None] + [s.cuda_stream for s in side])
+    torch.cuda.synchronize()
+    for b in plan.batches:
+        for k, name in enumerate(["param", "grad", "momentum", "O"]):
+            assert torch.equal(mine[b.index][k], ref[b.index][k]), (streams, prec, b.index, name)
+
+
+def test_step_batches_orders_after_and_before_caller_stream():
+    """Work enqueued on the caller's stream before the call is seen by every
+    lane, and work enqueued after it sees every lane's results."""
+    import torch
+    plan = B.Plan(SHAPES, max_batch_elems=CAP)
+    hp = B.HParams()
+    base = _filled(plan, torch.bfloat16, 4)
+    ref = [tuple(t.clone() for t in bufs) for bufs in base]
+    mine = [tuple(torch.empty_like(t) for t in bufs) for bufs in base]
+    ws = torch.zeros(max(plan.workspace_bytes(b.index, "bf16") for b in plan.batches), dtype=torch.uint8,
+                     device="cuda")
+    for b in plan.batches:
+        P, G, M, O = ref[b.index]
+        B.muon_step(plan, b.index, P, G, M, hp, ws, ns_out=O)
+    idx = [b.index for b in plan.batches]
+    lane_of, need = B.plan_lanes(plan, idx, hp, 2)
+    wss = [torch.zeros(n, dtype=torch.uint8, device="cuda") for n in need]
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    # inputs written on the caller's stream right before the call, after a
+    # long unrelated product, so a lane that did not wait would read garbage
+    junk = torch.randn(4096, 4096, device="cuda")
+    for _ in range(4):
+        junk = junk @ junk.mul_(1e-2)
+    for i, bufs in enumerate(base):
+        for k in range(4):
+            mine[i][k].copy_(bufs[k])
+    B.muon_step_batches(plan, idx, mine, hp, wss, [None, side.cuda_stream])
+    # read back on the caller's stream without synchronising first
+    copies = [tuple(t.clone() for t in bufs) for bufs in mine]
+    cur.synchronize()
+    for b in plan.batches:
+        for k in range(4):
+            assert torch.equal(copies[b.index][k], ref[b.index][k]), (b.index, k)

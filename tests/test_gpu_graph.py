@@ -5,7 +5,9 @@ and synchronisations in between, and with new lr / weight-decay values written
 to the device scalars (muon_hparams.lr_wd_device) before each replay; every
 replay must leave parameters and momentum bit-identical to the same step run
 eagerly with those values passed on the host.  Skinny (both the Gram-space
-and the transposed form) and tiled batches are covered.
+and the transposed form) and tiled batches are covered, with the batches on
+one stream and spread over two (muon_step_batches: the side stream forks from
+and joins the capture stream inside the graph).
 """
 import pytest
 
@@ -24,12 +26,13 @@ def _gpu():
     B.lib()
 
 
+@pytest.mark.parametrize("streams", [1, 2])
 @pytest.mark.parametrize("prec", ["bf16", "f32"])
-def test_graph_replays_match_eager(prec):
+def test_graph_replays_match_eager(prec, streams):
     import torch
     gen = torch.Generator(device="cuda").manual_seed(5)
     lr_wd = torch.tensor([0.02, 0.1], dtype=torch.float32, device="cuda")
-    graphed = B.BatchedMuon(SHAPES, torch.bfloat16, B.HParams(precision=prec, lr_wd=lr_wd))
+    graphed = B.BatchedMuon(SHAPES, torch.bfloat16, B.HParams(precision=prec, lr_wd=lr_wd), streams=streams)
     eager = B.BatchedMuon(SHAPES, torch.bfloat16, B.HParams(precision=prec))
     for i in range(len(graphed.params)):
         graphed.params[i].normal_(0.0, 0.02, generator=gen)
@@ -51,8 +54,8 @@ def test_graph_replays_match_eager(prec):
         junk = torch.randn(256, 256, device="cuda") @ torch.randn(256, 256, device="cuda")   # unrelated eager work
         torch.cuda.synchronize()
         for i in range(len(graphed.params)):
-            assert torch.equal(graphed.params[i], eager.params[i]), (prec, rep, i)
-            assert torch.equal(graphed.moms[i], eager.moms[i]), (prec, rep, i)
+            assert torch.equal(graphed.params[i], eager.params[i]), (prec, streams, rep, i)
+            assert torch.equal(graphed.moms[i], eager.moms[i]), (prec, streams, rep, i)
         for i in range(len(graphed.params)):   # next step's gradients
             graphed.grads[i].normal_(generator=gen)
             eager.grads[i].copy_(graphed.grads[i])
