@@ -463,13 +463,17 @@ __device__ __forceinline__ void put_blk(R* Z, const typename Mf<R>::V& v, int bi
   for (int r = 0; r < 4; ++r) Z[(16 * bi + Mf<R>::row(r, lane)) * GSD + 16 * bj + (lane & 15)] = v[r];
 }
 
-// The K steps on A (= A_0 in, overwritten) and P (= I in, B_{K-1} ... B_0
-// out); wave w owns output block (w / 2, w % 2) of every product.  Padded
-// rows and columns of A stay zero and never reach the m x m corner of P.
+// The K steps on A (= A_0 in, overwritten) and P (= I in P0; the result,
+// B_{K-1} ... B_0, is returned: P0 or P1, which alternate so that a step's
+// new P needs no barrier against the reads of the old one); wave w owns
+// output block (w / 2, w % 2) of every product, three barriers per step.
+// Padded rows and columns of A stay zero and never reach the m x m corner of P.
 template <typename R, int KM>
-__device__ void gram_steps(R* A, R* Bm, R* P, R* Tm, int steps, const Coeffs& cf) {
+__device__ R* gram_steps(R* A, R* Bm, R* P0, R* P1, R* Tm, int steps, const Coeffs& cf) {
   const int lane = threadIdx.x & (WAVE - 1);
   const int w = threadIdx.x / WAVE, bi = w >> 1, bj = w & 1;
+  R* P = P0;
+  R* Pn = P1;
   for (int k = 0; k < steps; ++k) {
     const R ca = cf.c[3 * k], cb = cf.c[3 * k + 1], cc = cf.c[3 * k + 2];
     const typename Mf<R>::V a2 = mul_blk<R, KM>(A, A, bi, bj, lane);
@@ -480,18 +484,16 @@ __device__ void gram_steps(R* A, R* Bm, R* P, R* Tm, int steps, const Coeffs& cf
     }
     __syncthreads();
     const bool more = k + 1 < steps;
-    const typename Mf<R>::V pn = mul_blk<R, KM>(Bm, P, bi, bj, lane);   // P <- B_k P
-    typename Mf<R>::V tn = {};
-    if (more) tn = mul_blk<R, KM>(A, Bm, bi, bj, lane);                 // A_k B_k
+    put_blk<R>(Pn, mul_blk<R, KM>(Bm, P, bi, bj, lane), bi, bj, lane);                // B_k P
+    if (more) put_blk<R>(Tm, mul_blk<R, KM>(A, Bm, bi, bj, lane), bi, bj, lane);      // A_k B_k
     __syncthreads();
-    put_blk<R>(P, pn, bi, bj, lane);
-    if (more) put_blk<R>(Tm, tn, bi, bj, lane);
-    __syncthreads();
+    R* t = P; P = Pn; Pn = t;
     if (more) {
       put_blk<R>(A, mul_blk<R, KM>(Tm, Bm, bi, bj, lane), bi, bj, lane);   // A_{k+1} = B_k A_k B_k
       __syncthreads();
     }
   }
+  return P;
 }
 
 template <int MODE>
@@ -500,15 +502,16 @@ sk_gram_ns(const float* __restrict__ gp, const float* __restrict__ sp, float eps
            Coeffs cf, BFrag* __restrict__ bfrag) {
   typedef typename std::conditional<MODE == 2, double, float>::type R;
   constexpr int MATB = GS_MAT * (int)sizeof(R);
-  constexpr int RAW = 4 * MATB > MATB + 4 * GS_STAGE ? 4 * MATB : MATB + 4 * GS_STAGE;
-  // A | B | P | Tm; the partials stage aliases B, P and Tm (and beyond)
+  constexpr int RAW = 5 * MATB > MATB + 4 * GS_STAGE ? 5 * MATB : MATB + 4 * GS_STAGE;
+  // A | B | P0 | P1 | Tm; the partials stage aliases B, P0, P1 and Tm (and beyond)
   __shared__ __attribute__((aligned(16))) unsigned char raw[RAW];
   __shared__ float Qf[SK_MP][SK_MP + 1];
   __shared__ double inv_s;
   R* A = reinterpret_cast<R*>(raw);
   R* Bm = A + GS_MAT;
   R* P = A + 2 * GS_MAT;
-  R* Tm = A + 3 * GS_MAT;
+  R* P1 = A + 3 * GS_MAT;
+  R* Tm = A + 4 * GS_MAT;
   float* stage = reinterpret_cast<float*>(raw + MATB);
 
   const int64_t b = blockIdx.x;
@@ -573,10 +576,10 @@ sk_gram_ns(const float* __restrict__ gp, const float* __restrict__ sp, float eps
   __syncthreads();
 
   switch ((m + 7) >> 3) {
-    case 1: gram_steps<R, 8>(A, Bm, P, Tm, steps, cf); break;
-    case 2: gram_steps<R, 16>(A, Bm, P, Tm, steps, cf); break;
-    case 3: gram_steps<R, 24>(A, Bm, P, Tm, steps, cf); break;
-    default: gram_steps<R, 32>(A, Bm, P, Tm, steps, cf); break;
+    case 1: P = gram_steps<R, 8>(A, Bm, P, P1, Tm, steps, cf); break;
+    case 2: P = gram_steps<R, 16>(A, Bm, P, P1, Tm, steps, cf); break;
+    case 3: P = gram_steps<R, 24>(A, Bm, P, P1, Tm, steps, cf); break;
+    default: P = gram_steps<R, 32>(A, Bm, P, P1, Tm, steps, cf); break;
   }
 
   // Q = P / (||U||_F + eps): the result applies to the stored, unnormalised U
