@@ -569,10 +569,13 @@ tl_gemm(GemmArgs g) {
   // a X term of the apply products: the Q stage holds X^T[j][k] = X[k][j]
   // for this k-slice; when the slice covers rows of this wave's output, add
   // a X[i][j] from LDS to the accumulators (no global read in the epilogue).
-  // The fp32 master (X32) is added in the epilogue instead.
+  // The fp32 master (X32) is added in the epilogue instead.  The poly
+  // product reads the same way: its Q stage holds A[j][k] = A[k][j], and
+  // without an fp32 A (A32 null) it adds (b / c) A[i][j] here, the epilogue
+  // scaling the sum by c.
   auto add_ax = [&](const OP* Qs, int64_t kt) {
-    if constexpr (EPI >= EPI_APPLY) {
-      if (!g.X32) {
+    if constexpr (EPI >= EPI_APPLY || EPI == EPI_POLY) {
+      if (EPI == EPI_POLY ? g.A32 == nullptr : g.X32 == nullptr) {
         const int64_t krel = kt * C::BK - (i0 + wm * C::WTM);
         if (krel > -C::BK && krel < C::WTM) {
 #pragma unroll
@@ -803,12 +806,15 @@ tl_gemm(GemmArgs g) {
         for (int q = 0; q < 32; ++q) o[q] *= sc;
       }
       const uint32_t ld = (uint32_t)g.lda;
-      float* A32 = g.A32 + mat * g.strideA;
-#pragma unroll
-      for (int q = 0; q < 32; ++q) A32[(ib0 + q) * ld + jj] = o[q];
       // the fp32 copy feeds the poly epilogue (lower-triangle tiles only),
-      // except on the fp32 path where it is also the full product operand
-      if (!diag && !g.A16) store_run32(A32 + jj * ld + ib0, o);
+      // except on the fp32 path where it is also the full product operand;
+      // none when the poly takes b A from its bf16 operand tiles
+      if (g.A32) {
+        float* A32 = g.A32 + mat * g.strideA;
+#pragma unroll
+        for (int q = 0; q < 32; ++q) A32[(ib0 + q) * ld + jj] = o[q];
+        if (!diag && !g.A16) store_run32(A32 + jj * ld + ib0, o);
+      }
       if (g.A16) {
         bf16_t* A16 = g.A16 + mat * g.strideA;
 #pragma unroll
@@ -817,17 +823,25 @@ tl_gemm(GemmArgs g) {
       }
     } else if constexpr (EPI == EPI_POLY) {
       const uint32_t ld = (uint32_t)g.lda;
-      const float* A32 = g.A32 + mat * g.strideA;
       OP* PB = reinterpret_cast<OP*>(g.PB) + mat * g.strideA;
+      if (g.A32) {
+        const float* A32 = g.A32 + mat * g.strideA;
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        float av[16];
+        for (int hh = 0; hh < 2; ++hh) {
+          float av[16];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) av[q] = A32[(ib0 + 16 * hh + q) * ld + jj];
+          for (int q = 0; q < 16; ++q) av[q] = A32[(ib0 + 16 * hh + q) * ld + jj];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          o[16 * hh + q] = g.cb * av[q] + g.cc * o[16 * hh + q];
-          st_from_f32(PB, (ib0 + 16 * hh + q) * ld + jj, o[16 * hh + q]);
+          for (int q = 0; q < 16; ++q) {
+            o[16 * hh + q] = g.cb * av[q] + g.cc * o[16 * hh + q];
+            st_from_f32(PB, (ib0 + 16 * hh + q) * ld + jj, o[16 * hh + q]);
+          }
+        }
+      } else {   // the accumulators hold A A + (b / c) A
+#pragma unroll
+        for (int q = 0; q < 32; ++q) {
+          o[q] *= g.cc;
+          st_from_f32(PB, (ib0 + q) * ld + jj, o[q]);
         }
       }
       if (!diag) store_run32(PB + jj * ld + ib0, o);
@@ -1015,13 +1029,17 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
   const int64_t tri = (C::BM / C::BN) * tm * (tm + 1) / 2;   // triangle tiles
   for (int k = 0; k < a.steps; ++k) {
     const float ca = a.coeffs[3 * k], cb = a.coeffs[3 * k + 1], cc = a.coeffs[3 * k + 2];
+    // bf16 products without the fp32 master: the poly takes b A from its bf16
+    // A operand tiles in LDS (as the products' A is bf16 anyway), so the Gram
+    // writes no fp32 copy of A
+    const bool a_in_lds = sizeof(OP) == 2 && X32 == nullptr && cc != 0.f;
     OP* Xk = C::DIRECT ? Xb[k & 1] : X;
     GemmArgs g = {};
     // Gram: A = X X^T
     g.P = Xk; g.Q = Xk; g.ldp = np; g.ldq = np; g.strideP = mp * np; g.strideQ = mp * np; g.K = np;
     g.tiles_n = tm; g.tiles_per_mat = tri; g.tiles_total = sh.count * tri;
     g.inv0 = k == 0 ? inv : nullptr;
-    g.A32 = A32; g.A16 = A16; g.lda = mp; g.strideA = mp * mp;
+    g.A32 = a_in_lds ? nullptr : A32; g.A16 = A16; g.lda = mp; g.strideA = mp * mp;
     MUON_LAUNCH("tl_gram", (tl_gemm<C, EPI_GRAM, PT>), dim3(gemm_grid<C, EPI_GRAM, PT>(g.tiles_total)),
                 dim3(C::THREADS), a.stream, g);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1030,7 +1048,8 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
     if (sizeof(OP) == 4) { g.P = A32; g.Q = A32; } else { g.P = A16; g.Q = A16; }
     g.ldp = mp; g.ldq = mp; g.strideP = mp * mp; g.strideQ = mp * mp; g.K = mp;
     g.tiles_n = tm; g.tiles_per_mat = tri; g.tiles_total = sh.count * tri;
-    g.A32 = A32; g.PB = PB; g.lda = mp; g.strideA = mp * mp; g.cb = cb; g.cc = cc;
+    g.A32 = a_in_lds ? nullptr : A32; g.PB = PB; g.lda = mp; g.strideA = mp * mp; g.cb = cb; g.cc = cc;
+    g.ca = a_in_lds ? cb / cc : 0.f;   // the factor add_ax applies
     MUON_LAUNCH("tl_poly", (tl_gemm<C, EPI_POLY, PT>), dim3(gemm_grid<C, EPI_POLY, PT>(g.tiles_total)),
                 dim3(C::THREADS), a.stream, g);
     if ((e = hipGetLastError()) != hipSuccess) return e;
