@@ -94,7 +94,10 @@ __device__ __forceinline__ void store8(bf16_t* p, const float* f) {
 // vec (mode 0, no X^T, stored rows a multiple of 8 long): each lane moves
 // runs of 8 consecutive stored elements, 16-byte accesses, and issues the
 // loads of both its runs before any store; X comes straight from registers
-// (through the LDS tile when the stored rows are X columns).
+// (through the LDS tile when the stored rows are X columns).  Stored rows
+// that are X rows in a padded width that is a multiple of 256 are taken as
+// 16 x 256 regions instead of 64 x 64: the same 4096 elements (and partial
+// count), but 512-byte runs of each gradient row for the HBM pages.
 // ---------------------------------------------------------------------------
 template <typename GT, typename XO>
 __global__ void __launch_bounds__(256)
@@ -103,25 +106,28 @@ tl_first(int mode, int vec, const GT* __restrict__ grad, float* __restrict__ mom
          int64_t m, int64_t n, int64_t mp, int64_t np, int transposed, float mu, int nesterov, MatTabs tabs) {
   __shared__ float tile[64][65];
   __shared__ float wsum[4];
-  const int64_t tiles_j = np / 64;
-  const int64_t tiles_per = (mp / 64) * tiles_j;
+  const bool wide = vec && !transposed && np % 256 == 0;
+  const int rh = wide ? 16 : 64, rw = wide ? 256 : 64;   // region rows x columns
+  const int lg = wide ? 5 : 3;                          // log2 of the 8-element runs per region row
+  const int64_t tiles_j = np / rw;
+  const int64_t tiles_per = (mp / rh) * tiles_j;
   const int64_t b = blockIdx.x / tiles_per;
   const int64_t tt = blockIdx.x % tiles_per;
-  const int64_t i0 = (tt / tiles_j) * 64, j0 = (tt % tiles_j) * 64;
+  const int64_t i0 = (tt / tiles_j) * rh, j0 = (tt % tiles_j) * rw;
   const int64_t sbase = b * m * n;
   const int64_t xb = b * mp * np;
   grad = batch_view(grad, tabs.grad, b, m * n);
   mom = batch_view(mom, tabs.mom, b, m * n);
   float ss = 0.f;
   if (vec) {
-    // run h of a lane: stored row sr of the tile, elements sc .. sc + 7
+    // run h of a lane: stored row sr of the region, elements sc .. sc + 7
     Raw8<GT> gr[2];
     Raw8<float> mr[2];
     bool ok[2];
     int64_t si[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int v = threadIdx.x + 256 * h, sr = v >> 3, sc = (v & 7) * 8;
+      const int v = threadIdx.x + 256 * h, sr = v >> lg, sc = (v & ((1 << lg) - 1)) * 8;
       const int64_t i = transposed ? i0 + sc : i0 + sr, j = transposed ? j0 + sr : j0 + sc;
       ok[h] = i < m && j < n;   // whole runs: the stored row length is a multiple of 8
       si[h] = sbase + (transposed ? j * m + i : i * n + j);
@@ -132,7 +138,7 @@ tl_first(int mode, int vec, const GT* __restrict__ grad, float* __restrict__ mom
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int v = threadIdx.x + 256 * h, sr = v >> 3, sc = (v & 7) * 8;
+      const int v = threadIdx.x + 256 * h, sr = v >> lg, sc = (v & ((1 << lg) - 1)) * 8;
       float u[8];
       if (ok[h]) {
         float g[8], mo[8];
