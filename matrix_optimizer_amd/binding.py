@@ -262,6 +262,49 @@ def muon_step(plan: Plan, batch: int, param, grad, momentum, hp: HParams, worksp
     _check(st, "muon_step")
 
 
+class PreparedStep:
+    """muon_step (one batch) or muon_step_batches (several, on several streams)
+    with every argument marshalled once: each call is then one foreign call,
+    for loops that repeat the same step on the same buffers.  Addresses,
+    hyperparameters and streams are fixed at construction (the stream that is
+    current then, if none is given); values behind hp.lr_wd may change
+    between calls.  Keeps the tensors alive."""
+
+    def __init__(self, plan: Plan, batches, bufs, hp: HParams, workspaces, streams=None):
+        self._hpc, self._keep = hp.to_c()
+        self._refs = (plan, bufs, workspaces, hp.lr_wd)
+        L = lib()
+        if isinstance(batches, int):   # one batch: muon_step
+            param, grad, mom = bufs[0], bufs[1], bufs[2]
+            out = bufs[3] if len(bufs) > 3 else None
+            self._bufs = muon_batch_buffers(_ptr(param), _dtype_code(param), _ptr(grad), _dtype_code(grad),
+                                            _ptr(mom), _ptr(out))
+            ws = workspaces
+            self._fn, self._where = L.muon_step, "muon_step"
+            self._args = (plan.handle, batches, C.byref(self._bufs), C.byref(self._hpc), _ptr(ws),
+                          ws.numel() * ws.element_size(), _stream(streams))
+            return
+        n, ns = len(batches), len(streams)
+        if len(bufs) != n or len(workspaces) != ns:
+            raise ValueError("PreparedStep: one buffer set per batch and one workspace per stream")
+        self._arr = (C.c_int32 * n)(*batches)
+        self._fb = (muon_batch_buffers * n)()
+        for i, t in enumerate(bufs):
+            out = t[3] if len(t) > 3 else None
+            self._fb[i] = muon_batch_buffers(_ptr(t[0]), _dtype_code(t[0]), _ptr(t[1]), _dtype_code(t[1]),
+                                             _ptr(t[2]), _ptr(out))
+        self._wp = (C.c_void_p * ns)(*[_ptr(w) for w in workspaces])
+        self._wb = (C.c_size_t * ns)(*[0 if w is None else w.numel() * w.element_size() for w in workspaces])
+        self._sp = (C.c_void_p * ns)(*[_stream(s) if i == 0 else int(s) for i, s in enumerate(streams)])
+        self._fn, self._where = L.muon_step_batches, "muon_step_batches"
+        self._args = (plan.handle, n, self._arr, self._fb, C.byref(self._hpc), self._wp, self._wb, self._sp, ns)
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != MUON_OK:
+            raise MuonError(st, self._where)
+
+
 def pointer_table(tensors, device="cuda"):
     """Device array (int64 tensor) of the data pointers of `tensors`, one per
     matrix, for muon_step_ptrs.  Keep it alive until the step has run."""
