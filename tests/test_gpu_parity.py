@@ -100,6 +100,10 @@ SHAPE_SETS = {
     # 256 x 256 tiles over 3 x 4 tile grids with ragged edges: off-diagonal
     # triangle tiles, several tiles per workgroup, both orientations
     "tiled_256_ragged": [(700, 900), (2, 900, 700)],
+    # the same with stored rows a multiple of 8 long: the first pass moves
+    # 16-byte runs (16 x 256 regions for the wide form, 64 x 64 through the
+    # LDS transpose for the tall one) and must zero the ragged padding
+    "tiled_256_ragged_vec": [(696, 904), (2, 904, 696)],
 }
 
 
@@ -124,12 +128,16 @@ def test_small_shapes(name, kernel, dtype, prec):
 # hyperparameter variants
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("shapes", [[(24, 500)], [(160, 200)]], ids=["skinny", "tiled"])
-@pytest.mark.parametrize("variant", ["one_step", "schedule", "no_nesterov", "no_scale", "eps_zero", "seven_steps"])
+@pytest.mark.parametrize("variant", ["one_step", "schedule", "c_zero", "no_nesterov", "no_scale", "eps_zero",
+                                     "seven_steps"])
 def test_hparam_variants(shapes, variant):
     wl = WL.small_workload("v", shapes, momentum_recipe="normal", wid=300)
     over = {
         "one_step": dict(ns_steps=1),
         "schedule": dict(ns_steps=3, coeffs=(3.0, -3.2, 1.2, 3.4445, -4.7750, 2.0315, 2.0, -1.5, 0.5)),
+        # a cubic step (c = 0) between quintic ones: the tiled bf16 poly then
+        # takes b A from the fp32 copy of A instead of its operand tiles
+        "c_zero": dict(ns_steps=3, coeffs=(3.4445, -4.7750, 2.0315, 1.5, -0.5, 0.0, 3.4445, -4.7750, 2.0315)),
         "no_nesterov": dict(nesterov=False),
         "no_scale": dict(scale="none"),
         "eps_zero": dict(eps=0.0),
