@@ -312,8 +312,8 @@ def main():
                     help="batches of identical shape share generated input values (copied per batch)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the step shards by whole matrices; see the design notes).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the step would shard by whole matrices, one owner GPU per matrix).", file=sys.stderr)
         sys.exit(2)
 
     import torch
