@@ -23,7 +23,7 @@ written in the order and notation of the pages:
 * 3-D expert tensors are E independent matrices -- HyperParallel-FSDP §6.3;
   DMuon-2 Appendix C.5.
 
-Readings taken where the pages are silent (also listed in the design notes):
+Readings taken where the pages are silent:
 
 * Nesterov form: U = G + mu * M_t, with M_t = mu M_{t-1} + G.
 * The normalised quantity is the NS input U.
