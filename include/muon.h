@@ -254,8 +254,9 @@ muon_status muon_stage_update(const muon_plan* plan, int32_t batch, void* param,
                               const float* o_in, const muon_hparams* hp, void* stream);
 
 /* Launch tracing, for measurement.  muon_trace_start(n) makes the next (at
- * most n) kernel launches of muon_step and the stage calls record a HIP event
- * before and after themselves on their stream.  muon_trace_stop waits for
+ * most n) kernel launches of the step and stage calls carry a start and a
+ * stop HIP event that the runtime records at the kernel's start and end
+ * (hipExtLaunchKernel), so they time its execution.  muon_trace_stop waits for
  * those events, writes up to `capacity` durations (ms) and kernel names
  * (static strings) in launch order, releases the events and returns the
  * number of launches traced (-1 if tracing was not started).  Tracing state

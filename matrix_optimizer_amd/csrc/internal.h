@@ -1,6 +1,7 @@
 // Internal host-side interface between the C ABI (abi.cpp) and the kernel
 // launchers (skinny.hip, tiled.hip).  Not part of the public ABI.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -109,20 +110,24 @@ struct StepArgs {
   hipStream_t stream;
 };
 
-// Launch tracing (trace.cpp): no-ops unless muon_trace_start is active.
-void trace_begin(const char* name, hipStream_t s);
-void trace_end(hipStream_t s);
+// Launch tracing (trace.cpp): while muon_trace_start is active, hands out
+// the start and stop events of the next traced launch (false otherwise).
+bool trace_take(const char* name, hipEvent_t* start, hipEvent_t* stop);
 
-// Launch a kernel, bracketed by trace events when tracing is on.
+// Launch a kernel.  While tracing, the launch goes through
+// hipExtLaunchKernelGGL, whose start and stop events the runtime records with
+// the dispatch itself, so they time the kernel's execution.
 #define MUON_LAUNCH(NAME, KERNEL, GRID, BLOCK, STREAM, ...) \
   MUON_LAUNCH_SHM(NAME, KERNEL, GRID, BLOCK, 0, STREAM, __VA_ARGS__)
 
 // Same, with SHM bytes of dynamic LDS.
-#define MUON_LAUNCH_SHM(NAME, KERNEL, GRID, BLOCK, SHM, STREAM, ...)    \
-  do {                                                                  \
-    ::muon::trace_begin(NAME, STREAM);                                  \
-    hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHM, STREAM, __VA_ARGS__);  \
-    ::muon::trace_end(STREAM);                                          \
+#define MUON_LAUNCH_SHM(NAME, KERNEL, GRID, BLOCK, SHM, STREAM, ...)                                \
+  do {                                                                                            \
+    hipEvent_t muon_ev0_ = nullptr, muon_ev1_ = nullptr;                                          \
+    if (::muon::trace_take(NAME, &muon_ev0_, &muon_ev1_))                                         \
+      hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHM, STREAM, muon_ev0_, muon_ev1_, 0u, __VA_ARGS__); \
+    else                                                                                          \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHM, STREAM, __VA_ARGS__);                          \
   } while (0)
 
 // Each returns hipSuccess or the first launch error.

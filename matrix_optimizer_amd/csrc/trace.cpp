@@ -1,6 +1,7 @@
 // Launch tracing: when enabled, every kernel launch of muon_step and the stage
-// calls is bracketed by two HIP events on the launch stream, so a caller can
-// read per-kernel durations without an external profiler.
+// calls carries two HIP events that the runtime records at the kernel's start
+// and end (hipExtLaunchKernel), so a caller can read per-kernel durations
+// without an external profiler.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -26,21 +27,16 @@ size_t g_next = 0;
 
 namespace muon {
 
-void trace_begin(const char* name, hipStream_t s) {
-  if (!g_on) return;
+bool trace_take(const char* name, hipEvent_t* start, hipEvent_t* stop) {
+  if (!g_on) return false;
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_on || g_next + 2 > g_pool.size()) return;
+  if (!g_on || g_next + 2 > g_pool.size()) return false;
   Rec r{name, g_pool[g_next], g_pool[g_next + 1]};
   g_next += 2;
-  (void)hipEventRecord(r.start, s);
   g_recs.push_back(r);
-}
-
-void trace_end(hipStream_t s) {
-  if (!g_on) return;
-  std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_on || g_recs.empty()) return;
-  (void)hipEventRecord(g_recs.back().stop, s);
+  *start = r.start;
+  *stop = r.stop;
+  return true;
 }
 
 }  // namespace muon
