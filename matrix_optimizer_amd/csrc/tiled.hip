@@ -534,10 +534,12 @@ tl_gemm(GemmArgs g) {
   // direct loads of k-slice k0 of the tile whose operands start at pbase
   // (its first row) and qbase (first row, or first column when QN) into
   // stage st
-  [[maybe_unused]] auto dma_slice = [&](int st, const OP* pbase, const OP* qbase, int64_t k0) {
+  // (qskip: P's rows only; Q's would repeat them)
+  [[maybe_unused]] auto dma_slice = [&](int st, const OP* pbase, const OP* qbase, int64_t k0, bool qskip) {
     constexpr int HALF = C::LPW / 2;
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
+      if (i >= HALF && qskip) break;
       const int ins = w + i * C::WAVES;
       const int64_t rows = (int64_t)(i % HALF) * C::WAVES * C::RPI;
       const OP* src;
@@ -641,6 +643,14 @@ tl_gemm(GemmArgs g) {
     // The last slice of a tile loads the next tile's first slice instead, so
     // a tile starts without waiting for the previous epilogue's stores.
     // K is a multiple of 2 BK: slice kt uses stage kt & 1.
+    // The Gram and poly products multiply a matrix by its own transpose: on
+    // a diagonal tile the Q stage would repeat the P stage, so only P's rows
+    // are loaded and Q's fragments are read from them (dq; ndq for the next
+    // tile, whose first slice the last slice loads).
+    const bool same_pq = (EPI == EPI_GRAM || EPI == EPI_POLY) && C::BM == C::BN && g.P == g.Q &&
+                         g.ldp == g.ldq && g.strideP == g.strideQ;
+    const bool dq = same_pq && ti == tj;
+    bool ndq = false;
     const OP* pb = reinterpret_cast<const OP*>(g.P) + mat * g.strideP + i0 * g.ldp;
     const OP* qb = reinterpret_cast<const OP*>(g.Q) + mat * g.strideQ + (QN ? j0 : j0 * g.ldq);
     const OP* npb = pb;
@@ -648,19 +658,21 @@ tl_gemm(GemmArgs g) {
     if (lin + gridDim.x < total) {
       int64_t nmat, nti, ntj;
       tile_coords<C, EPI>(g, lin + gridDim.x, xcd_map, nmat, nti, ntj);
+      ndq = same_pq && nti == ntj;
       npb = reinterpret_cast<const OP*>(g.P) + nmat * g.strideP + nti * C::BM * g.ldp;
       nqb = reinterpret_cast<const OP*>(g.Q) + nmat * g.strideQ + (QN ? ntj * C::BN : ntj * C::BN * g.ldq);
     }
     npb = uniform_ptr(npb);
     nqb = uniform_ptr(nqb);
     if (!stage0_ready) {
-      dma_slice(0, pb, qb, 0);
+      dma_slice(0, pb, qb, 0, dq);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       lds_barrier();
     }
     bf16x8 fa[2][C::IB], fb[2][C::JB];
     const OP* Pw = lds + (wm * C::WTM + (lane & 31)) * C::LD;
-    const OP* Qw = lds + (C::BM + wn * C::WTN + (lane & 31)) * C::LD;
+    const int qrow0 = dq ? 0 : C::BM;   // first stage row of the Q operand
+    const OP* Qw = lds + (qrow0 + wn * C::WTN + (lane & 31)) * C::LD;
     auto read_frags = [&](int buf, int st, int kk) {
       const int slot = (2 * kk + (lane >> 5)) ^ lds_swz(lane & 31);
 #pragma unroll
@@ -697,7 +709,7 @@ tl_gemm(GemmArgs g) {
     read_frags(0, 0, 0);
     auto slice = [&](int st, int64_t kt) {
       const bool last = kt + 1 == KT;
-      dma_slice(st ^ 1, last ? npb : pb, last ? nqb : qb, last ? 0 : (kt + 1) * C::BK);
+      dma_slice(st ^ 1, last ? npb : pb, last ? nqb : qb, last ? 0 : (kt + 1) * C::BK, last ? ndq : dq);
       read_frags(1, st, 1);
       mfmas(0);
       sched_mfma_block<C::IB * C::JB, C::LPW, C::IB + C::JB>();
@@ -713,7 +725,7 @@ tl_gemm(GemmArgs g) {
       mfmas(1);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (QN) add_ax(lds + st * C::STAGE + C::BM * C::LD, kt);
-      else add_ax(lds + st * C::STAGE + (C::BM + wn * C::WTN + (lane & 31)) * C::LD, kt);
+      else add_ax(lds + st * C::STAGE + (qrow0 + wn * C::WTN + (lane & 31)) * C::LD, kt);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this wave's loads of the next slice
       lds_barrier();                               // everyone's; stage st is free again
       if (!last) read_frags(0, st ^ 1, 0);
