@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 4
+#define MUON_ABI_VERSION 5
 
 typedef enum {
   MUON_OK = 0,
@@ -169,6 +169,30 @@ typedef struct {
   float* const* ns_out;       /* optional device array [count]: fp32 matrices receiving O; NULL to skip */
 } muon_batch_ptrs;
 
+/* A batch whose matrices are row-level views of the caller's parameters and
+ * gradients.  HyperParallel-FSDP §6.6 keeps the storage of a parameter apart
+ * from the matrices Muon sees: one physical parameter may hold several
+ * logical matrices (the heads of a fused QKV projection, the gate and up
+ * matrices of an MoE FC1 weight), reached through a zero-copy view with a
+ * reversible split / concatenate / interleave, and the logical updates are
+ * written back into the physical parameter.  Here each logical matrix is
+ * [M,N] in W's orientation and stored row r of matrix i (N contiguous
+ * elements) sits at rows[i*M + r], so any split, concatenation or interleave
+ * of whole rows, or a column range of each physical row, is a table of row
+ * addresses; the update lands in place, which is the restore.  The tables
+ * are read by the kernels, never by the host: every row address must be
+ * 16-byte aligned, rows must not overlap one another, the other buffers or
+ * the workspace, and the caller keeps the tables valid until the launches
+ * have run.  Momentum and ns_out are the optimizer's own contiguous buffers. */
+typedef struct {
+  void* const* param_rows;        /* device array [count*M]: rows of param_dtype, updated in place */
+  muon_dtype param_dtype;
+  const void* const* grad_rows;   /* device array [count*M]: rows of grad_dtype */
+  muon_dtype grad_dtype;
+  float* momentum;                /* [count,M,N] fp32, contiguous, updated in place */
+  float* ns_out;                  /* optional [count,M,N] fp32, contiguous: receives O; NULL to skip */
+} muon_batch_rows;
+
 int32_t muon_abi_version(void);
 const char* muon_status_str(muon_status s);
 
@@ -203,6 +227,13 @@ muon_status muon_step(const muon_plan* plan, int32_t batch, const muon_batch_buf
  * aligned and must not overlap one another or the workspace; the addresses
  * they hold are the caller's responsibility (see muon_batch_ptrs). */
 muon_status muon_step_ptrs(const muon_plan* plan, int32_t batch, const muon_batch_ptrs* bufs,
+                           const muon_hparams* hp, void* workspace, size_t workspace_bytes, void* stream);
+
+/* muon_step on row-level views (muon_batch_rows); the same kernels, results
+ * bitwise equal to muon_step on the same rows packed.  The row tables must be
+ * non-NULL, 16-byte aligned and must not overlap one another, the momentum,
+ * ns_out or the workspace. */
+muon_status muon_step_rows(const muon_plan* plan, int32_t batch, const muon_batch_rows* bufs,
                            const muon_hparams* hp, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Several batches of one step on several streams.

@@ -29,7 +29,7 @@ EXPORTED = ["muon_abi_version", "muon_status_str", "muon_plan_create", "muon_pla
             "muon_plan_num_batches", "muon_plan_batch_info", "muon_plan_segments",
             "muon_workspace_bytes", "muon_step", "muon_stage_momentum", "muon_stage_ns",
             "muon_stage_update", "muon_trace_start", "muon_trace_stop", "muon_plan_lanes",
-            "muon_step_batches"]
+            "muon_step_batches", "muon_step_rows"]
 
 
 class muon_shape(C.Structure):
@@ -66,6 +66,11 @@ class muon_batch_buffers(C.Structure):
 class muon_batch_ptrs(C.Structure):
     _fields_ = [("params", C.c_void_p), ("param_dtype", C.c_int32), ("grads", C.c_void_p),
                 ("grad_dtype", C.c_int32), ("momenta", C.c_void_p), ("ns_out", C.c_void_p)]
+
+
+class muon_batch_rows(C.Structure):
+    _fields_ = [("param_rows", C.c_void_p), ("param_dtype", C.c_int32), ("grad_rows", C.c_void_p),
+                ("grad_dtype", C.c_int32), ("momentum", C.c_void_p), ("ns_out", C.c_void_p)]
 
 
 class MuonError(RuntimeError):
@@ -108,6 +113,9 @@ def lib():
                             C.c_void_p, C.c_size_t, C.c_void_p]
     L.muon_step_ptrs.restype = C.c_int32
     L.muon_step_ptrs.argtypes = [C.c_void_p, C.c_int32, C.POINTER(muon_batch_ptrs), C.POINTER(muon_hparams),
+                                 C.c_void_p, C.c_size_t, C.c_void_p]
+    L.muon_step_rows.restype = C.c_int32
+    L.muon_step_rows.argtypes = [C.c_void_p, C.c_int32, C.POINTER(muon_batch_rows), C.POINTER(muon_hparams),
                                  C.c_void_p, C.c_size_t, C.c_void_p]
     L.muon_plan_lanes.restype = C.c_int32
     L.muon_plan_lanes.argtypes = [C.c_void_p, C.c_int32, C.POINTER(C.c_int32), C.POINTER(muon_hparams), C.c_int32,
@@ -349,6 +357,54 @@ def muon_step_ptrs(plan: Plan, batch: int, params, grads, momenta, hp: HParams, 
     st = lib().muon_step_ptrs(plan.handle, batch, C.byref(bufs), C.byref(hpc), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "muon_step_ptrs")
+
+
+def row_addresses(t):
+    """Start address of every row of t (an int64 CPU tensor, leading indices in
+    row-major order).  t may be any strided view whose last dimension is
+    contiguous: a slice of rows, a range of columns, every k-th row, or one
+    part of an interleaved layout such as W.view(heads, 3, d, H)[:, 0]."""
+    import torch
+    if t.dim() < 2 or (t.stride(-1) != 1 and t.shape[-1] > 1):
+        raise ValueError("row_addresses: rows must be contiguous (stride 1 along the last dimension)")
+    lead = tuple(t.shape[:-1])
+    addr = torch.full(lead, t.data_ptr(), dtype=torch.int64)
+    for d, (size, stride) in enumerate(zip(lead, t.stride()[:-1])):
+        shape = [1] * len(lead)
+        shape[d] = size
+        addr = addr + (torch.arange(size, dtype=torch.int64) * (stride * t.element_size())).view(shape)
+    return addr.reshape(-1)
+
+
+def row_table(views, device="cuda"):
+    """Device row table for muon_step_rows: the rows of each logical matrix
+    view in `views`, matrix after matrix (batch order).  Each view's rows,
+    flattened over its leading dimensions, are the M stored rows of one
+    [M, N] matrix."""
+    import torch
+    return torch.cat([row_addresses(v) for v in views]).to(device)
+
+
+def muon_step_rows(plan: Plan, batch: int, param_rows, grad_rows, momentum, hp: HParams, workspace,
+                   param_dtype, grad_dtype, ns_out=None, stream=None) -> None:
+    """muon_step on row-level views (muon_step_rows): param_rows / grad_rows are
+    row tables (row_table) of the logical matrices, param_dtype / grad_dtype
+    ("bf16" or "f32") the type of the rows; momentum (and ns_out) contiguous
+    [count, M, N] fp32.  The tables must stay alive until the step has run."""
+    dt = {"bf16": MUON_BF16, "f32": MUON_F32}
+    if param_dtype not in dt or grad_dtype not in dt:
+        raise ValueError("param_dtype and grad_dtype must be 'bf16' or 'f32'")
+    if stream is not None:
+        import torch
+        ext = torch.cuda.ExternalStream(int(stream))
+        param_rows.record_stream(ext)
+        grad_rows.record_stream(ext)
+    hpc, keep = hp.to_c()
+    bufs = muon_batch_rows(_ptr(param_rows), dt[param_dtype], _ptr(grad_rows), dt[grad_dtype], _ptr(momentum),
+                           _ptr(ns_out))
+    st = lib().muon_step_rows(plan.handle, batch, C.byref(bufs), C.byref(hpc), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "muon_step_rows")
 
 
 def plan_lanes(plan: Plan, batches, hp: HParams, nstreams: int):

@@ -458,6 +458,36 @@ muon_status muon_step_ptrs(const muon_plan* plan, int32_t batch, const muon_batc
   return hip_status(dispatch(a, L));
 }
 
+muon_status muon_step_rows(const muon_plan* plan, int32_t batch, const muon_batch_rows* bufs, const muon_hparams* hp,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  const muon_plan::Batch* b = get_batch(plan, batch);
+  if (!b || !bufs) return MUON_ERR_INVALID_ARG;
+  muon_status st = check_hparams(hp, true, true, true);
+  if (st != MUON_OK) return st;
+  if (!valid_dtype(bufs->param_dtype) || !valid_dtype(bufs->grad_dtype)) return MUON_ERR_INVALID_ARG;
+  if (!bufs->param_rows || !bufs->grad_rows || !bufs->momentum) return MUON_ERR_INVALID_ARG;
+  const WsLayout L = workspace_layout(shape_of(*b), hp->precision, b->path);
+  if (workspace_bytes < L.total) return MUON_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return MUON_ERR_INVALID_ARG;
+  const size_t elems = size_t(b->count) * b->M * b->N;
+  const size_t tab_bytes = size_t(b->count) * b->M * sizeof(void*);
+  std::vector<Region> rs = {region(bufs->param_rows, tab_bytes), region(bufs->grad_rows, tab_bytes),
+                            region(bufs->momentum, elems * 4), region(workspace, L.total)};
+  if (bufs->ns_out) rs.push_back(region(bufs->ns_out, elems * 4));
+  if (!regions_ok(rs)) return MUON_ERR_INVALID_ARG;
+
+  StepArgs a;
+  fill_common(a, *b, hp, stream);
+  a.phase = PH_FULL;
+  a.param = nullptr; a.param_dtype = bufs->param_dtype == MUON_BF16 ? DT_BF16 : DT_F32;
+  a.grad = nullptr; a.grad_dtype = bufs->grad_dtype == MUON_BF16 ? DT_BF16 : DT_F32;
+  a.mom = bufs->momentum; a.ns_out = bufs->ns_out;
+  a.tabs.param_rows = reinterpret_cast<const void* const*>(bufs->param_rows);
+  a.tabs.grad_rows = bufs->grad_rows;
+  a.ws = static_cast<char*>(workspace);
+  return hip_status(dispatch(a, L));
+}
+
 muon_status muon_plan_lanes(const muon_plan* plan, int32_t n, const int32_t* batches, const muon_hparams* hp,
                             int32_t nstreams, int32_t* lane_of, size_t* lane_workspace_bytes) {
   muon_status st = check_batch_list(plan, n, batches, nstreams);

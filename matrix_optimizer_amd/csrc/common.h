@@ -94,6 +94,13 @@ __device__ __forceinline__ T* batch_view(T* contig, const void* const* tab, int6
   return reinterpret_cast<T*>(reinterpret_cast<uintptr_t>(tab[b]) - (uintptr_t)(b * mn) * sizeof(T));
 }
 
+// Start of stored row r of matrix b in a row table (R stored rows per
+// matrix); b is uniform, r need not be.
+template <typename T>
+__device__ __forceinline__ T* row_of(const void* const* rows, int64_t b, int64_t R, int64_t r) {
+  return reinterpret_cast<T*>(const_cast<void*>(rows[b * R + r]));
+}
+
 // Decoupled decay plus the orthogonal update on one element, fp32.
 __device__ __forceinline__ float apply_update(float w, float o, float lr, float wd, float s) {
   return w - lr * (wd * w + s * o);

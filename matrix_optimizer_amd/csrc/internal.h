@@ -81,12 +81,16 @@ WsLayout workspace_layout(const BatchShape& b, int prec, int path);
 
 // Per-matrix addresses of a batch's caller buffers (zero-copy batching):
 // device arrays of one pointer per matrix, or null where the buffer is one
-// contiguous [count, M, N] region.
+// contiguous [count, M, N] region.  param_rows / grad_rows: one pointer per
+// stored row instead ([count * M], row r of matrix b at b M + r, N elements
+// each), for matrices that are row-level views of fused parameters.
 struct MatTabs {
   const void* const* param;
   const void* const* grad;
   const void* const* mom;
   const void* const* ns;
+  const void* const* param_rows;
+  const void* const* grad_rows;
 };
 
 struct StepArgs {

@@ -599,7 +599,7 @@ sk_gram_ns(const float* __restrict__ gp, const float* __restrict__ sp, float eps
 // vec: stored rows are X rows and n % 8 == 0 (16-byte vectors along rows).
 // XG: U goes out as MFMA-ready tiles (Gram path), else row-major [m, ldx].
 // ---------------------------------------------------------------------------
-template <int MODE, typename GT, bool XG>
+template <int MODE, typename GT, bool XG, bool ROWS>
 __global__ void __launch_bounds__(SK_THREADS)
 sk_first(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const float* __restrict__ u_in,
          typename SkCfg<MODE>::XS* __restrict__ xws, float* __restrict__ gp_out, float* __restrict__ sp,
@@ -656,7 +656,8 @@ sk_first(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const f
         const int64_t j = j0 + jl;
         if (j >= n) return;   // n % 8 == 0: the 8 columns are all in range or all out
         const int64_t si = mat + (int64_t)r * n + j;
-        gr.load(grad + si);
+        if constexpr (ROWS) gr.load(row_of<const GT>(tabs.grad_rows, b, m, r) + j);
+        else gr.load(grad + si);
         m0 = *reinterpret_cast<const f32x4*>(mom + si);
         m1 = *reinterpret_cast<const f32x4*>(mom + si + 4);
       };
@@ -719,7 +720,12 @@ sk_first(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const f
       if (j < n) {
         const int64_t si = mat + stored_index(transposed, r, j, m, n);
         if (mode == 0) {
-          const float g = ld_as_f32(grad, si);
+          float g;
+          if constexpr (ROWS)
+            g = ld_as_f32(row_of<const GT>(tabs.grad_rows, b, transposed ? n : m, transposed ? j : r),
+                          transposed ? r : j);
+          else
+            g = ld_as_f32(grad, si);
           const float mn = mu * mom[si] + g;
           mom[si] = mn;
           u = nesterov ? g + mu * mn : mn;
@@ -743,7 +749,7 @@ sk_first(int mode, const GT* __restrict__ grad, float* __restrict__ mom, const f
 // One Newton-Schulz step on a chunk: X' = B' X.  LAST: apply the update (or
 // write O) instead of storing X' and its Gram partial.
 // ---------------------------------------------------------------------------
-template <int MODE, typename PT, bool LAST>
+template <int MODE, typename PT, bool LAST, bool ROWS>
 __global__ void __launch_bounds__(SK_THREADS)
 sk_iter(typename SkCfg<MODE>::XS* __restrict__ xws, const BFrag* __restrict__ bfrag, float* __restrict__ gp_out,
         int m, int64_t n, int64_t ldx, int S, int T, int transposed, int vec,
@@ -765,6 +771,12 @@ sk_iter(typename SkCfg<MODE>::XS* __restrict__ xws, const BFrag* __restrict__ bf
     param = batch_view(param, tabs.param, b, (int64_t)m * n);
     ns_out = batch_view(ns_out, tabs.ns, b, (int64_t)m * n);
   }
+  const bool has_w = ROWS || param != nullptr;
+  // W's stored element (row sr, column sc), rows of ncols elements
+  [[maybe_unused]] auto w_at = [&](int64_t sr, int64_t sc, int64_t ncols) -> PT* {
+    if constexpr (ROWS) return row_of<PT>(tabs.param_rows, b, transposed ? n : m, sr) + sc;
+    else return param + mat + sr * ncols + sc;
+  };
   constexpr int PR8 = C::L / 8;                      // 8-column items per row
   constexpr int NI = SK_MP * PR8 / SK_THREADS;       // items per thread (upper bound)
 
@@ -773,12 +785,12 @@ sk_iter(typename SkCfg<MODE>::XS* __restrict__ xws, const BFrag* __restrict__ bf
   // last step, bf16 W: start reading W now, it is needed only at the end
   uint4 wpre[LAST && sizeof(PT) == 2 ? NI : 1];
   if constexpr (LAST && sizeof(PT) == 2) {
-    if (vec && param) {
+    if (vec && has_w) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int v = t + SK_THREADS * i;
         const int r = v / PR8, jl = (v % PR8) * 8;
-        if (r < m && j0 + jl < n) wpre[i] = *reinterpret_cast<const uint4*>(param + mat + (int64_t)r * n + j0 + jl);
+        if (r < m && j0 + jl < n) wpre[i] = *reinterpret_cast<const uint4*>(w_at(r, j0 + jl, n));
       }
     }
   }
@@ -810,7 +822,8 @@ sk_iter(typename SkCfg<MODE>::XS* __restrict__ xws, const BFrag* __restrict__ bf
           *reinterpret_cast<f32x4*>(ns_out + si) = f32x4{o[0], o[1], o[2], o[3]};
           *reinterpret_cast<f32x4*>(ns_out + si + 4) = f32x4{o[4], o[5], o[6], o[7]};
         }
-        if (param) {
+        if (has_w) {
+          PT* wp = w_at(r, j, n);
           if constexpr (sizeof(PT) == 2) {
             const uint4 wv = wpre[i];
             uint32_t w4[4] = {wv.x, wv.y, wv.z, wv.w};
@@ -822,17 +835,17 @@ sk_iter(typename SkCfg<MODE>::XS* __restrict__ xws, const BFrag* __restrict__ bf
               const uint32_t n1 = f2bf(apply_update(w1, o[2 * q + 1], lr, wd, s_scale));
               w4[q] = n0 | (n1 << 16);
             }
-            *reinterpret_cast<uint4*>(param + si) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+            *reinterpret_cast<uint4*>(wp) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
           } else {
-            f32x4 w0 = *reinterpret_cast<const f32x4*>(param + si);
-            f32x4 w1 = *reinterpret_cast<const f32x4*>(param + si + 4);
+            f32x4 w0 = *reinterpret_cast<const f32x4*>(wp);
+            f32x4 w1 = *reinterpret_cast<const f32x4*>(wp + 4);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               w0[q] = apply_update(w0[q], o[q], lr, wd, s_scale);
               w1[q] = apply_update(w1[q], o[q + 4], lr, wd, s_scale);
             }
-            *reinterpret_cast<f32x4*>(param + si) = w0;
-            *reinterpret_cast<f32x4*>(param + si + 4) = w1;
+            *reinterpret_cast<f32x4*>(wp) = w0;
+            *reinterpret_cast<f32x4*>(wp + 4) = w1;
           }
         }
       }
@@ -848,7 +861,10 @@ sk_iter(typename SkCfg<MODE>::XS* __restrict__ xws, const BFrag* __restrict__ bf
         else o = lx[r * C::LDX + jl];
         const int64_t si = mat + stored_index(transposed, r, j, m, n);
         if (ns_out) ns_out[si] = o;
-        if (param) st_from_f32(param, si, apply_update(ld_as_f32(param, si), o, lr, wd, s_scale));
+        if (has_w) {
+          PT* wp = transposed ? w_at(j, r, m) : w_at(r, j, n);
+          st_from_f32(wp, 0, apply_update(ld_as_f32(wp, 0), o, lr, wd, s_scale));
+        }
       }
     }
   }
@@ -967,7 +983,7 @@ __device__ __forceinline__ f32x16 apply_block(const uint32_t (*xr)[MODE == 0 ? 4
   return acc;
 }
 
-template <int MODE, typename PT, bool TRANS>
+template <int MODE, typename PT, bool TRANS, bool ROWS>
 __global__ void __launch_bounds__(SK_THREADS)
 sk_apply(const typename SkCfg<MODE>::XS* __restrict__ xg, const BFrag* __restrict__ qfrag, int m, int64_t n,
          int64_t NB, int G, int64_t upm, int64_t units, int vec, PT* __restrict__ param, float* __restrict__ ns_out,
@@ -987,6 +1003,13 @@ sk_apply(const typename SkCfg<MODE>::XS* __restrict__ xg, const BFrag* __restric
   const int64_t mat = b * (int64_t)m * n;
   param = batch_view(param, tabs.param, b, (int64_t)m * n);
   ns_out = batch_view(ns_out, tabs.ns, b, (int64_t)m * n);
+  const bool has_w = ROWS || param != nullptr;
+  // W's stored element (row sr, column sc): stored rows are U rows (n long),
+  // or U columns (m long) when W is tall
+  auto w_at = [&](int64_t sr, int64_t sc) -> PT* {
+    if constexpr (ROWS) return row_of<PT>(tabs.param_rows, b, TRANS ? n : m, sr) + sc;
+    else return param + mat + sr * (TRANS ? (int64_t)m : n) + sc;
+  };
 
   // U operands of both blocks: bf16 modes K block kb = rows of group 2 kb + h,
   // fp32 mode rows 16 h .. 16 h + 15 (groups 2 h, 2 h + 1)
@@ -1023,11 +1046,11 @@ sk_apply(const typename SkCfg<MODE>::XS* __restrict__ xg, const BFrag* __restric
     const int rr = lane >> 3, cc = (lane & 7) * 8;
     const int64_t col0 = 32 * jb0 + cc;
     typename OV::V wv[4];
-    if (param && vec) {
+    if (has_w && vec) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 8 * i + rr;
-        if (i < G && row < m && col0 < n) wv[i] = OV::load(param + mat + (int64_t)row * n + col0);
+        if (i < G && row < m && col0 < n) wv[i] = OV::load(w_at(row, col0));
       }
     }
     const BFrag fr = qfrag[b * WAVE + lane];
@@ -1057,10 +1080,10 @@ sk_apply(const typename SkCfg<MODE>::XS* __restrict__ xg, const BFrag* __restric
         if (col0 >= n) continue;
         const int64_t idx = mat + (int64_t)row * n + col0;
         if (ns_out) Oct<float>::put(ns_out + idx, ov);
-        if (param) {
+        if (has_w) {
 #pragma unroll
           for (int q = 0; q < 8; ++q) nw[q] = apply_update(OV::get(wv[i], q), ov[q], lr, wd, s_scale);
-          OV::put(param + idx, nw);
+          OV::put(w_at(row, col0), nw);
         }
       } else {
 #pragma unroll
@@ -1068,7 +1091,10 @@ sk_apply(const typename SkCfg<MODE>::XS* __restrict__ xg, const BFrag* __restric
           if (col0 + q >= n) break;
           const int64_t idx = mat + (int64_t)row * n + col0 + q;
           if (ns_out) ns_out[idx] = ov[q];
-          if (param) st_from_f32(param, idx, apply_update(ld_as_f32(param, idx), ov[q], lr, wd, s_scale));
+          if (has_w) {
+            PT* wp = w_at(row, col0 + q);
+            st_from_f32(wp, 0, apply_update(ld_as_f32(wp, 0), ov[q], lr, wd, s_scale));
+          }
         }
       }
     }
@@ -1077,14 +1103,14 @@ sk_apply(const typename SkCfg<MODE>::XS* __restrict__ xg, const BFrag* __restric
     // W at the accumulator positions: quad qd of block jj holds rows
     // 8 qd + 4 h + 0..3 of column 32 jb + c
     typename QV::V wq[2][4];
-    if (param && vec) {
+    if (has_w && vec) {
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
           const int64_t col = 32 * (jb0 + jj) + c;
           const int d = 8 * qd + 4 * h;
-          if (col < n && d < m) wq[jj][qd] = *reinterpret_cast<const typename QV::V*>(param + mat + col * m + d);
+          if (col < n && d < m) wq[jj][qd] = *reinterpret_cast<const typename QV::V*>(w_at(col, d));
         }
     }
     const BFrag fr = qfrag[b * WAVE + lane];
@@ -1104,10 +1130,10 @@ sk_apply(const typename SkCfg<MODE>::XS* __restrict__ xg, const BFrag* __restric
           if (d >= m) continue;
           const int64_t idx = mat + col * m + d;
           if (ns_out) *reinterpret_cast<f32x4*>(ns_out + idx) = f32x4{ov[0], ov[1], ov[2], ov[3]};
-          if (param) {
+          if (has_w) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) nw[i] = apply_update(QV::get(wq[jj][qd], i), ov[i], lr, wd, s_scale);
-            *reinterpret_cast<typename QV::V*>(param + idx) = QV::make(nw);
+            *reinterpret_cast<typename QV::V*>(w_at(col, d)) = QV::make(nw);
           }
         } else {
 #pragma unroll
@@ -1115,7 +1141,10 @@ sk_apply(const typename SkCfg<MODE>::XS* __restrict__ xg, const BFrag* __restric
             if (d + i >= m) break;
             const int64_t idx = mat + col * m + d + i;
             if (ns_out) ns_out[idx] = ov[i];
-            if (param) st_from_f32(param, idx, apply_update(ld_as_f32(param, idx), ov[i], lr, wd, s_scale));
+            if (has_w) {
+              PT* wp = w_at(col, d + i);
+              st_from_f32(wp, 0, apply_update(ld_as_f32(wp, 0), ov[i], lr, wd, s_scale));
+            }
           }
         }
       }
@@ -1134,14 +1163,21 @@ hipError_t launch_first(const StepArgs& a, const WsLayout& L, int mode, int vec)
   const size_t tile = (size_t)(8 * G) * SkCfg<MODE>::LDX * sizeof(XS);
   const size_t red = (size_t)SK_WAVES * SK_MP * (SK_MP + 1) * 4;
   const size_t shm = tile > red ? tile : red;
-  if (L.path == PATH_SKINNY_GRAM)
-    MUON_LAUNCH_SHM(name, (sk_first<MODE, GT, true>), grid, block, shm, a.stream, mode, (const GT*)a.grad, a.mom,
-                    a.u_in, (XS*)(a.ws + L.x), (float*)(a.ws + L.gp0), (float*)(a.ws + L.sp), (int)sh.m, sh.n, L.ldx,
-                    (int)L.S, (int)L.T, (int)sh.transposed, vec, a.mu, a.nesterov, NB, G, a.tabs);
-  else
-    MUON_LAUNCH_SHM(name, (sk_first<MODE, GT, false>), grid, block, shm, a.stream, mode, (const GT*)a.grad, a.mom,
-                    a.u_in, (XS*)(a.ws + L.x), (float*)(a.ws + L.gp0), (float*)(a.ws + L.sp), (int)sh.m, sh.n, L.ldx,
-                    (int)L.S, (int)L.T, (int)sh.transposed, vec, a.mu, a.nesterov, NB, G, a.tabs);
+  // XG: U as MFMA tiles (Gram path); ROWS: the gradient comes through a row table
+  auto go = [&](auto xg, auto rows) {
+    MUON_LAUNCH_SHM(name, (sk_first<MODE, GT, decltype(xg)::value, decltype(rows)::value>), grid, block, shm,
+                    a.stream, mode, (const GT*)a.grad, a.mom, a.u_in, (XS*)(a.ws + L.x), (float*)(a.ws + L.gp0),
+                    (float*)(a.ws + L.sp), (int)sh.m, sh.n, L.ldx, (int)L.S, (int)L.T, (int)sh.transposed, vec, a.mu,
+                    a.nesterov, NB, G, a.tabs);
+  };
+  const bool rows = a.tabs.grad_rows != nullptr;
+  if (L.path == PATH_SKINNY_GRAM) {
+    if (rows) go(std::true_type{}, std::true_type{});
+    else go(std::true_type{}, std::false_type{});
+  } else {
+    if (rows) go(std::false_type{}, std::true_type{});
+    else go(std::false_type{}, std::false_type{});
+  }
   return hipGetLastError();
 }
 
@@ -1162,11 +1198,15 @@ hipError_t launch_iters(const StepArgs& a, const WsLayout& L, int vec) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (k < a.steps - 1)
-      MUON_LAUNCH("sk_ns_step", (sk_iter<MODE, PT, false>), grid, block, a.stream, (XS*)(a.ws + L.x),
+      MUON_LAUNCH("sk_ns_step", (sk_iter<MODE, PT, false, false>), grid, block, a.stream, (XS*)(a.ws + L.x),
+                  (const BFrag*)bfrag, gp[(k + 1) & 1], (int)sh.m, sh.n, L.ldx, (int)L.S, (int)L.T,
+                  (int)sh.transposed, vec, param, a.ns_out, a.lr, a.wd, a.s, a.lrwd, a.tabs);
+    else if (a.tabs.param_rows)
+      MUON_LAUNCH("sk_apply_update", (sk_iter<MODE, PT, true, true>), grid, block, a.stream, (XS*)(a.ws + L.x),
                   (const BFrag*)bfrag, gp[(k + 1) & 1], (int)sh.m, sh.n, L.ldx, (int)L.S, (int)L.T,
                   (int)sh.transposed, vec, param, a.ns_out, a.lr, a.wd, a.s, a.lrwd, a.tabs);
     else
-      MUON_LAUNCH("sk_apply_update", (sk_iter<MODE, PT, true>), grid, block, a.stream, (XS*)(a.ws + L.x),
+      MUON_LAUNCH("sk_apply_update", (sk_iter<MODE, PT, true, false>), grid, block, a.stream, (XS*)(a.ws + L.x),
                   (const BFrag*)bfrag, gp[(k + 1) & 1], (int)sh.m, sh.n, L.ldx, (int)L.S, (int)L.T,
                   (int)sh.transposed, vec, param, a.ns_out, a.lr, a.wd, a.s, a.lrwd, a.tabs);
     e = hipGetLastError();
@@ -1194,18 +1234,23 @@ hipError_t launch_gram(const StepArgs& a, const WsLayout& L, int vec) {
   const int64_t upm = (NB + 1) / 2;                    // 64-column units per matrix
   const int64_t units = sh.count * upm;
   const dim3 grid((unsigned)((units + SK_WAVES - 1) / SK_WAVES));
-  const char* name = (param || a.tabs.param) ? "sk_apply_update" : "sk_apply";
+  const char* name = (param || a.tabs.param || a.tabs.param_rows) ? "sk_apply_update" : "sk_apply";
+  // ROWS: W comes through a row table
+  auto go = [&](auto trans, auto rows) {
+    constexpr bool TR = decltype(trans)::value;
+    const int vec = TR ? (sh.m % 4 == 0 ? 1 : 0) : (sh.n % 8 == 0 ? 1 : 0);
+    const size_t shm = TR ? 0 : (size_t)SK_WAVES * (8 * G) * AP_LD * 4;
+    MUON_LAUNCH_SHM(name, (sk_apply<MODE, PT, TR, decltype(rows)::value>), grid, dim3(SK_THREADS), shm, a.stream,
+                    (const XS*)(a.ws + L.x), (const BFrag*)bfrag, (int)sh.m, sh.n, NB, G, upm, units, vec, param,
+                    a.ns_out, a.lr, a.wd, a.s, a.lrwd, a.tabs);
+  };
+  const bool rows = a.tabs.param_rows != nullptr;
   if (!sh.transposed) {
-    const int vec = sh.n % 8 == 0 ? 1 : 0;
-    const size_t shm = (size_t)SK_WAVES * (8 * G) * AP_LD * 4;
-    MUON_LAUNCH_SHM(name, (sk_apply<MODE, PT, false>), grid, dim3(SK_THREADS), shm, a.stream, (const XS*)(a.ws + L.x),
-                (const BFrag*)bfrag, (int)sh.m, sh.n, NB, G, upm, units, vec, param, a.ns_out, a.lr, a.wd, a.s, a.lrwd,
-                a.tabs);
+    if (rows) go(std::false_type{}, std::true_type{});
+    else go(std::false_type{}, std::false_type{});
   } else {
-    const int vec = sh.m % 4 == 0 ? 1 : 0;
-    MUON_LAUNCH(name, (sk_apply<MODE, PT, true>), grid, dim3(SK_THREADS), a.stream, (const XS*)(a.ws + L.x),
-                (const BFrag*)bfrag, (int)sh.m, sh.n, NB, G, upm, units, vec, param, a.ns_out, a.lr, a.wd, a.s, a.lrwd,
-                a.tabs);
+    if (rows) go(std::true_type{}, std::true_type{});
+    else go(std::true_type{}, std::false_type{});
   }
   return hipGetLastError();
 }

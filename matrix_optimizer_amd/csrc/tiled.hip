@@ -99,7 +99,7 @@ __device__ __forceinline__ void store8(bf16_t* p, const float* f) {
 // 16 x 256 regions instead of 64 x 64: the same 4096 elements (and partial
 // count), but 512-byte runs of each gradient row for the HBM pages.
 // ---------------------------------------------------------------------------
-template <typename GT, typename XO>
+template <typename GT, typename XO, bool ROWS>
 __global__ void __launch_bounds__(256)
 tl_first(int mode, int vec, const GT* __restrict__ grad, float* __restrict__ mom, const float* __restrict__ u_in,
          float* __restrict__ ssp, XO* __restrict__ X, XO* __restrict__ XT, float* __restrict__ X32,
@@ -132,7 +132,10 @@ tl_first(int mode, int vec, const GT* __restrict__ grad, float* __restrict__ mom
       ok[h] = i < m && j < n;   // whole runs: the stored row length is a multiple of 8
       si[h] = sbase + (transposed ? j * m + i : i * n + j);
       if (ok[h]) {
-        gr[h].load(grad + si[h]);
+        if constexpr (ROWS)
+          gr[h].load(row_of<const GT>(tabs.grad_rows, b, transposed ? n : m, transposed ? j : i) + (transposed ? i : j));
+        else
+          gr[h].load(grad + si[h]);
         mr[h].load(mom + si[h]);
       }
     }
@@ -177,7 +180,12 @@ tl_first(int mode, int vec, const GT* __restrict__ grad, float* __restrict__ mom
         if (mode == 1) {
           u = u_in[si];
         } else {
-          const float g = ld_as_f32(grad, si);
+          float g;
+          if constexpr (ROWS)
+            g = ld_as_f32(row_of<const GT>(tabs.grad_rows, b, transposed ? n : m, transposed ? j : i),
+                          transposed ? i : j);
+          else
+            g = ld_as_f32(grad, si);
           const float mn = mu * mom[si] + g;
           mom[si] = mn;
           u = nesterov ? g + mu * mn : mn;
@@ -484,7 +492,8 @@ __device__ __forceinline__ void sched_mfma_block() {
   }
 }
 
-template <class C, int EPI, typename PT>
+// ROWS (last step only): W comes through a row table
+template <class C, int EPI, typename PT, bool ROWS = false>
 __global__ void __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD)
 tl_gemm(GemmArgs g) {
   typedef typename C::Op OP;
@@ -901,6 +910,13 @@ tl_gemm(GemmArgs g) {
       if (W) W += mat * g.m * g.n;
       if (O) O += mat * g.m * g.n;
       const uint32_t m = (uint32_t)g.m, n = (uint32_t)g.n;
+      // W's stored element (row sr, column sc), rows of ncols elements: from
+      // the row table when W is given row by row
+      const bool has_w = ROWS || W != nullptr;
+      auto w_at = [&](uint32_t sr, uint32_t sc, uint32_t ncols) -> PT* {
+        if constexpr (ROWS) return row_of<PT>(g.tabs.param_rows, mat, EPI == EPI_LAST_T ? g.n : g.m, sr) + sc;
+        else return W + sr * ncols + sc;
+      };
       if constexpr (EPI == EPI_LAST) {
         // W row-major: the lane takes 8 consecutive columns of rows rr, rr + 8,
         // rr + 16, rr + 24 of the staged block, so W, the fp32 master and O move
@@ -916,7 +932,7 @@ tl_gemm(GemmArgs g) {
         Raw8<PT> wr[2];
         auto load_group = [&](int p, int buf) __attribute__((always_inline)) {
           const uint32_t i = ib0 + rr + 8 * p;
-          if (W && vec && i < m && j < n) wr[buf].load(W + i * n + j);
+          if (has_w && vec && i < m && j < n) wr[buf].load(w_at(i, j, n));
         };
         load_group(0, 0);
 #pragma unroll
@@ -943,19 +959,22 @@ tl_gemm(GemmArgs g) {
           if (vec) {
             if (j >= n) continue;
             if (O) store8(O + i * n + j, ov);
-            if (W) {
+            if (has_w) {
               float wv[8], nw[8];
               wr[p & 1].to_f32(wv);
 #pragma unroll
               for (int q = 0; q < 8; ++q) nw[q] = apply_update(wv[q], ov[q], ulr, uwd, g.s);
-              store8(W + i * n + j, nw);
+              store8(w_at(i, j, n), nw);
             }
           } else {
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
               if (j + q >= n) break;
               if (O) O[i * n + j + q] = ov[q];
-              if (W) st_from_f32(W, i * n + j + q, apply_update(ld_as_f32(W, i * n + j + q), ov[q], ulr, uwd, g.s));
+              if (has_w) {
+                PT* wp = w_at(i, j + q, n);
+                st_from_f32(wp, 0, apply_update(ld_as_f32(wp, 0), ov[q], ulr, uwd, g.s));
+              }
             }
           }
         }
@@ -981,12 +1000,15 @@ tl_gemm(GemmArgs g) {
             // W is the transpose: this lane's 32 elements are contiguous and 16-byte aligned
             const uint32_t base = jj * m + ib0;
             if (O) store_run32(O + base, o);
-            if (W) update_run32(W + base, o, ulr, uwd, g.s);
+            if (has_w) update_run32(w_at(jj, ib0, m), o, ulr, uwd, g.s);
           } else {
             for (uint32_t q = 0; q < 32 && ib0 + q < m; ++q) {
               const uint32_t si = jj * m + ib0 + q;
               if (O) O[si] = o[q];
-              if (W) st_from_f32(W, si, apply_update(ld_as_f32(W, si), o[q], ulr, uwd, g.s));
+              if (has_w) {
+                PT* wp = w_at(jj, ib0 + q, m);
+                st_from_f32(wp, 0, apply_update(ld_as_f32(wp, 0), o[q], ulr, uwd, g.s));
+              }
             }
           }
         }
@@ -1013,7 +1035,7 @@ tl_update(PT* __restrict__ W, const float* __restrict__ O, int64_t total, float 
 // Persistent grid of tl_gemm<C, EPI, PT>: one wave of resident workgroups
 // (a multiple of 8, so each stays on one XCD), or fewer if there are fewer
 // tiles.
-template <class C, int EPI, typename PT>
+template <class C, int EPI, typename PT, bool ROWS = false>
 unsigned gemm_grid(int64_t tiles) {
   static int per_dev[64] = {0};   // resident workgroups of this kernel per device
   int dev = 0;
@@ -1021,7 +1043,7 @@ unsigned gemm_grid(int64_t tiles) {
   if (per_dev[dev] == 0) {
     int cus = 0, blocks = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, tl_gemm<C, EPI, PT>, C::THREADS, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, tl_gemm<C, EPI, PT, ROWS>, C::THREADS, 0) != hipSuccess ||
         blocks <= 0)
       blocks = 1;
     per_dev[dev] = cus * blocks;
@@ -1093,9 +1115,16 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
     g.ns_out = a.ns_out; g.lr = a.lr; g.wd = a.wd; g.s = a.s; g.lrwd = a.lrwd;
     g.tabs = a.phase == PH_FULL ? a.tabs : MatTabs{};
     g.m = sh.m; g.n = sh.n; g.transposed = sh.transposed;
-    if (g.last && !sh.transposed)
+    const bool rows = g.tabs.param_rows != nullptr;   // W through a row table
+    if (g.last && !sh.transposed && rows)
+      MUON_LAUNCH("tl_apply_update", (tl_gemm<C, EPI_LAST, PT, true>),
+                  dim3(gemm_grid<C, EPI_LAST, PT, true>(g.tiles_total)), dim3(C::THREADS), a.stream, g);
+    else if (g.last && !sh.transposed)
       MUON_LAUNCH("tl_apply_update", (tl_gemm<C, EPI_LAST, PT>), dim3(gemm_grid<C, EPI_LAST, PT>(g.tiles_total)),
                   dim3(C::THREADS), a.stream, g);
+    else if (g.last && rows)
+      MUON_LAUNCH("tl_apply_update", (tl_gemm<C, EPI_LAST_T, PT, true>),
+                  dim3(gemm_grid<C, EPI_LAST_T, PT, true>(g.tiles_total)), dim3(C::THREADS), a.stream, g);
     else if (g.last)
       MUON_LAUNCH("tl_apply_update", (tl_gemm<C, EPI_LAST_T, PT>),
                   dim3(gemm_grid<C, EPI_LAST_T, PT>(g.tiles_total)), dim3(C::THREADS), a.stream, g);
@@ -1141,9 +1170,15 @@ hipError_t tiled_impl(const StepArgs& a, const WsLayout& L) {
 
   // vector form: 16-byte runs of a stored row (n elements, m when stored transposed)
   const int vec = mode == 0 && !XT[0] && (sh.transposed ? sh.m : sh.n) % 8 == 0;
-  MUON_LAUNCH("tl_momentum_layout", (tl_first<GT, OP>), dim3((unsigned)(sh.count * L.nparts)), dim3(256), a.stream,
-              mode, vec, (const GT*)a.grad, a.mom, a.u_in, ssp, X, XT[0], X32, sh.m, sh.n, mp, np, (int)sh.transposed,
-              a.mu, a.nesterov, a.phase == PH_FULL ? a.tabs : MatTabs{});
+  const MatTabs ftabs = a.phase == PH_FULL ? a.tabs : MatTabs{};
+  if (ftabs.grad_rows)   // the gradient through a row table
+    MUON_LAUNCH("tl_momentum_layout", (tl_first<GT, OP, true>), dim3((unsigned)(sh.count * L.nparts)), dim3(256),
+                a.stream, mode, vec, (const GT*)a.grad, a.mom, a.u_in, ssp, X, XT[0], X32, sh.m, sh.n, mp, np,
+                (int)sh.transposed, a.mu, a.nesterov, ftabs);
+  else
+    MUON_LAUNCH("tl_momentum_layout", (tl_first<GT, OP, false>), dim3((unsigned)(sh.count * L.nparts)), dim3(256),
+                a.stream, mode, vec, (const GT*)a.grad, a.mom, a.u_in, ssp, X, XT[0], X32, sh.m, sh.n, mp, np,
+                (int)sh.transposed, a.mu, a.nesterov, ftabs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   MUON_LAUNCH("tl_norm_finalize", tl_norm_finalize, dim3((unsigned)sh.count), dim3(256), a.stream, ssp, L.nparts,

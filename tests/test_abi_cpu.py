@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.EXPORTED)
-    assert B.muon_abi_version() == 4
+    assert B.muon_abi_version() == 5
 
 
 def _cmp_plans(shapes, cap=0, order=0):
@@ -371,3 +371,33 @@ def test_step_batches_rejects_bad_args():
     assert L.muon_step_batches(p.handle, 2, arr, fb, C.byref(hpc), (C.c_void_p * 9)(), (C.c_size_t * 9)(),
                                (C.c_void_p * 9)(), 9) == B.MUON_ERR_INVALID_ARG
     assert all(f.untouched() for f in fbs)
+
+
+def test_step_rows_rejects_bad_args(plan_fb):
+    """muon_step_rows: the row tables, momentum and workspace are checked like
+    buffers (non-null, 16-byte aligned, disjoint); the rows they point at are
+    device data the host never reads."""
+    p, fb = plan_fb
+    L = B.lib()
+    need = p.workspace_bytes(0, "bf16")
+    hpc, keep = B.HParams().to_c()
+
+    def call(prow=None, grow=None, mom=None, out=None, ws=None, wsb=need, pdt=B.MUON_BF16, batch=0):
+        bufs = B.muon_batch_rows(prow if prow is not None else fb.ptr("param"), pdt,
+                                 grow if grow is not None else fb.ptr("grad"), B.MUON_BF16,
+                                 mom if mom is not None else fb.ptr("mom"), out)
+        return L.muon_step_rows(p.handle, batch, C.byref(bufs), C.byref(hpc),
+                                ws if ws is not None else fb.ptr("ws"), wsb, None)
+
+    assert call(wsb=need - 1) == B.MUON_ERR_WORKSPACE_TOO_SMALL
+    assert call(prow=0) == B.MUON_ERR_INVALID_ARG
+    assert call(grow=0) == B.MUON_ERR_INVALID_ARG
+    assert call(mom=0) == B.MUON_ERR_INVALID_ARG
+    assert call(grow=fb.ptr("grad", 8)) == B.MUON_ERR_INVALID_ARG      # table not 16-byte aligned
+    assert call(grow=fb.ptr("param")) == B.MUON_ERR_INVALID_ARG        # same table twice
+    assert call(mom=fb.ptr("ws")) == B.MUON_ERR_INVALID_ARG            # momentum inside the workspace
+    assert call(out=fb.ptr("mom")) == B.MUON_ERR_INVALID_ARG           # O over the momentum
+    assert call(pdt=5) == B.MUON_ERR_INVALID_ARG
+    assert call(batch=9) == B.MUON_ERR_INVALID_ARG
+    assert L.muon_step_rows(p.handle, 0, None, C.byref(hpc), fb.ptr("ws"), need, None) == 1
+    assert fb.untouched()

@@ -1,0 +1,99 @@
+"""muon_step_rows: logical matrices that are row-level views of fused
+physical parameters (the model-adapter views of HyperParallel-FSDP §6.6)
+give bitwise the parameters, momentum and O of muon_step on the same
+matrices packed, and leave every physical element outside them untouched.
+
+Layouts: a fused QKV weight with heads interleaved, a column split with gaps,
+an MoE FC1 weight with gate and up rows interleaved (tall matrices), and row
+and column splits of skinny matrices; bf16 and fp32 parameters, all
+precisions, both skinny Newton-Schulz forms.
+"""
+import pytest
+
+from matrix_optimizer_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+
+
+def _qkv_interleaved(t):
+    """[3H, H] with rows [head][q|k|v][d]: heads 4, d 64 -> three [256, 256]."""
+    v = t.view(4, 3, 64, t.shape[-1])
+    return [v[:, k] for k in range(3)]
+
+
+def _column_split_gaps(t):
+    """[200, 616]: columns 0..199, 208..407, 416..615 -> three [200, 200]."""
+    return [t[:, 208 * k:208 * k + 200] for k in range(3)]
+
+
+def _gate_up_interleaved(t):
+    """[2 experts, 2 x 300, 72], gate and up rows alternating -> four [300, 72]."""
+    return [t[e, k::2] for e in range(2) for k in range(2)]
+
+
+def _skinny_rows(t):
+    """[72, 1000] -> three [24, 1000] row blocks."""
+    return [t[24 * k:24 * k + 24] for k in range(3)]
+
+
+def _skinny_columns_tall(t):
+    """[1000, 72] -> three [1000, 24] column ranges (tall: stored rows are 24 long)."""
+    return [t[:, 24 * k:24 * k + 24] for k in range(3)]
+
+
+CASES = [
+    ("qkv_interleaved", (768, 256), _qkv_interleaved, (256, 256), (0,)),
+    ("column_split_gaps", (200, 616), _column_split_gaps, (200, 200), (0,)),
+    ("gate_up_interleaved", (2, 600, 72), _gate_up_interleaved, (300, 72), (0,)),
+    ("skinny_rows", (72, 1000), _skinny_rows, (24, 1000), (0, 2)),
+    ("skinny_columns_tall", (1000, 72), _skinny_columns_tall, (1000, 24), (0, 2)),
+]
+
+
+@pytest.mark.parametrize("prec", ["bf16", "bf16_x32", "f32"])
+@pytest.mark.parametrize("pdtype", ["bf16", "f32"])
+@pytest.mark.parametrize("name,phys,split,mshape,kernels", CASES, ids=[c[0] for c in CASES])
+def test_step_rows_matches_packed(name, phys, split, mshape, kernels, pdtype, prec):
+    import torch
+    dt = torch.bfloat16 if pdtype == "bf16" else torch.float32
+    gen = torch.Generator(device="cuda").manual_seed(17)
+    for kernel in kernels:
+        Wp = torch.randn(phys, device="cuda", generator=gen).mul_(0.02).to(dt)
+        Gp = torch.randn(phys, device="cuda", generator=gen).to(dt)
+        W0 = Wp.clone()
+        views_w, views_g = split(Wp), split(Gp)
+        count = len(views_w)
+        M, N = mshape
+        assert all(tuple(v.reshape(-1, v.shape[-1]).shape) == (M, N) for v in views_w)
+        plan = B.Plan([mshape] * count, skinny_kernel=kernel)
+        assert len(plan.batches) == 1 and plan.batches[0].count == count
+        hp = B.HParams(precision=prec)
+        P = torch.stack([v.reshape(M, N) for v in views_w])   # packed copies
+        G = torch.stack([v.reshape(M, N) for v in views_g])
+        Mo = torch.randn(count, M, N, device="cuda", generator=gen)
+        Mo2 = Mo.clone()
+        O, O2 = torch.zeros_like(Mo), torch.zeros_like(Mo)
+        ws = torch.zeros(plan.workspace_bytes(0, prec), dtype=torch.uint8, device="cuda")
+        ws2 = torch.zeros_like(ws)
+        B.muon_step(plan, 0, P, G, Mo, hp, ws, ns_out=O)
+        tw, tg = B.row_table(views_w), B.row_table(views_g)
+        B.muon_step_rows(plan, 0, tw, tg, Mo2, hp, ws2, pdtype, pdtype, ns_out=O2)
+        torch.cuda.synchronize()
+        for i, v in enumerate(views_w):
+            assert torch.equal(v.reshape(M, N), P[i]), (name, kernel, i, "param")
+        assert torch.equal(Mo2, Mo) and torch.equal(O2, O), (name, kernel)
+        # physical elements outside every logical matrix are untouched
+        mask = torch.ones(phys, dtype=torch.bool, device="cuda")
+        for v in split(mask):
+            v.fill_(False)
+        assert torch.equal(Wp[mask], W0[mask]), (name, kernel, "outside")
+        # and the gradient is only read
+        assert torch.equal(torch.stack([v.reshape(M, N) for v in views_g]), G)
