@@ -135,3 +135,41 @@ def test_prepared_step_matches_calls(streams):
     for b in idx:
         for k in range(4):
             assert torch.equal(mine[b][k], ref[b][k]), (streams, b, k)
+
+
+def test_moe_workload_two_streams_bitwise():
+    """The MoE expert workload at full size (the 36 + 28 [2048, 7168] expert
+    batches and the [32, 24, 10240] experts) on two streams, as the benchmark
+    runs it: bitwise the parameters and momentum of muon_step on each batch
+    in turn (whose results the full-size parity tests check against the
+    oracle)."""
+    import torch
+    from matrix_optimizer_amd import workloads as WL
+    from tests import harness as H
+    wl = WL.WORKLOADS["moe_experts"]
+    plan = B.Plan([p.shape for p in wl.params])
+    assert [(b.count, b.M, b.N) for b in plan.batches] == [(36, 2048, 7168), (28, 2048, 7168), (32, 24, 10240)]
+    hp = H.c_hparams(wl.hp)
+    gen = torch.Generator(device="cuda").manual_seed(29)
+    ref = []
+    for b in plan.batches:
+        shp = (b.count, b.M, b.N)
+        ref.append((torch.randn(shp, device="cuda", generator=gen).mul_(0.02).to(torch.bfloat16),
+                    torch.randn(shp, device="cuda", generator=gen).mul_(1e-3).to(torch.bfloat16),
+                    torch.randn(shp, device="cuda", generator=gen).mul_(1e-3)))
+    mine = [tuple(t.clone() for t in x) for x in ref]
+    ws = torch.empty(max(plan.workspace_bytes(b.index, hp.precision) for b in plan.batches), dtype=torch.uint8,
+                     device="cuda")
+    for b in plan.batches:
+        P, G, M = ref[b.index]
+        B.muon_step(plan, b.index, P, G, M, hp, ws)
+    idx = [b.index for b in plan.batches]
+    lane_of, need = B.plan_lanes(plan, idx, hp, 2)
+    assert lane_of == [0, 1, 1]
+    wss = [torch.empty(n, dtype=torch.uint8, device="cuda") for n in need]
+    side = torch.cuda.Stream()
+    B.muon_step_batches(plan, idx, mine, hp, wss, [None, side.cuda_stream])
+    torch.cuda.synchronize()
+    for b in plan.batches:
+        assert torch.equal(mine[b.index][0], ref[b.index][0]), (b.index, "param")
+        assert torch.equal(mine[b.index][2], ref[b.index][2]), (b.index, "momentum")
