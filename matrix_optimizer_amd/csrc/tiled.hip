@@ -311,6 +311,34 @@ __device__ __forceinline__ void tri_tile(int64_t t, int64_t& ti, int64_t& tj) {
   tj = t - R * r * (r + 1) / 2;
 }
 
+// Lower-triangle tiles (BM = BN) in groups of GM tile rows, column by
+// column, so the 32 tiles an XCD runs at once share few operand bands in its
+// L2 (about 13 row / column bands instead of about 22 in row order): the
+// tiles before group s are those of its first r0 = GM s rows, then come the
+// group's full columns (GM tiles each), then its diagonal block column by
+// column.  tm: tile rows of the matrix.
+__device__ __forceinline__ void tri_tile_grouped(int64_t tt, int64_t tm, int64_t& ti, int64_t& tj) {
+  constexpr int64_t GM = 4;
+  int64_t r, c0;
+  tri_tile<1>(tt, r, c0);
+  const int64_t r0 = (r / GM) * GM;
+  const int64_t gme = tm - r0 < GM ? tm - r0 : GM;
+  int64_t o = tt - r0 * (r0 + 1) / 2;
+  if (o < gme * r0) {
+    ti = r0 + o % gme;
+    tj = o / gme;
+    return;
+  }
+  o -= gme * r0;
+  int64_t c = 0;
+  while (o >= gme - c) {   // at most GM - 1 rounds
+    o -= gme - c;
+    ++c;
+  }
+  ti = r0 + c + o;
+  tj = r0 + c;
+}
+
 // 32 consecutive elements starting at a 16-byte aligned address, as 16-byte stores.
 __device__ __forceinline__ void store_run32(float* p, const float* o) {
 #pragma unroll
@@ -399,7 +427,8 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& g, int64_t lin, bool
     ti = first + tin % rows;
     tj = tin / rows;
   } else {
-    tri_tile<C::BM / C::BN>(tt, ti, tj);
+    if constexpr (C::BM == C::BN) tri_tile_grouped(tt, g.tiles_n, ti, tj);
+    else tri_tile<C::BM / C::BN>(tt, ti, tj);
   }
 }
 
