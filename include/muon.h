@@ -21,10 +21,12 @@
  * independent matrices (HyperParallel-FSDP §6.3).  muon_plan_create does that
  * bucketing on the host; muon_step runs one batch on the caller's stream.
  *
- * Memory and ownership.  Every device pointer is owned by the caller.  Per
- * batch, param, grad, momentum and ns_out are contiguous row-major
- * [count, M, N] regions (a parameter's matrices sit at the segment offsets
- * that muon_plan_segments reports).  The library never allocates, frees or
+ * Memory and ownership.  Every device pointer is owned by the caller.  For
+ * muon_step, per batch, param, grad, momentum and ns_out are contiguous
+ * row-major [count, M, N] regions (a parameter's matrices sit at the segment
+ * offsets that muon_plan_segments reports); muon_step_ptrs takes one address
+ * per matrix instead, and muon_step_rows one address per stored row of W and
+ * G.  The library never allocates, frees or
  * synchronises device memory or streams; its state is the host-side plan, plus
  * a few HIP events per device that muon_step_batches creates on first use
  * (fork and join markers, no device memory) and keeps until the process ends.
