@@ -3,7 +3,8 @@ physical parameters (the model-adapter views of HyperParallel-FSDP §6.6)
 give bitwise the parameters, momentum and O of muon_step on the same
 matrices packed, and leave every physical element outside them untouched.
 
-Layouts: a fused QKV weight with heads interleaved, a column split with gaps,
+Layouts: a fused QKV weight with heads interleaved, column splits with gaps
+(square, and tall on 256 x 256 tiles),
 an MoE FC1 weight with gate and up rows interleaved (tall matrices), and row
 and column splits of skinny matrices; bf16 and fp32 parameters, all
 precisions, both skinny Newton-Schulz forms.
@@ -49,8 +50,15 @@ def _skinny_columns_tall(t):
     return [t[:, 24 * k:24 * k + 24] for k in range(3)]
 
 
+def _tall_column_split(t):
+    """[768, 528]: columns 0..255 and 272..527 -> two tall [768, 256] (256 x 256
+    tiles, W stored as the transpose of X)."""
+    return [t[:, 0:256], t[:, 272:528]]
+
+
 CASES = [
     ("qkv_interleaved", (768, 256), _qkv_interleaved, (256, 256), (0,)),
+    ("tall_column_split", (768, 528), _tall_column_split, (768, 256), (0,)),
     ("column_split_gaps", (200, 616), _column_split_gaps, (200, 200), (0,)),
     ("gate_up_interleaved", (2, 600, 72), _gate_up_interleaved, (300, 72), (0,)),
     ("skinny_rows", (72, 1000), _skinny_rows, (24, 1000), (0, 2)),
@@ -97,3 +105,25 @@ def test_step_rows_matches_packed(name, phys, split, mshape, kernels, pdtype, pr
         assert torch.equal(Wp[mask], W0[mask]), (name, kernel, "outside")
         # and the gradient is only read
         assert torch.equal(torch.stack([v.reshape(M, N) for v in views_g]), G)
+
+
+def test_step_rows_without_ns_out():
+    """The update alone (no O written) through row tables, against muon_step."""
+    import torch
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    Wp = torch.randn(768, 256, device="cuda", generator=gen).mul_(0.02).to(torch.bfloat16)
+    Gp = torch.randn(768, 256, device="cuda", generator=gen).to(torch.bfloat16)
+    vw, vg = _qkv_interleaved(Wp), _qkv_interleaved(Gp)
+    plan = B.Plan([(256, 256)] * 3)
+    hp = B.HParams()
+    P = torch.stack([v.reshape(256, 256) for v in vw])
+    G = torch.stack([v.reshape(256, 256) for v in vg])
+    Mo = torch.zeros(3, 256, 256, device="cuda")
+    Mo2 = Mo.clone()
+    ws = torch.zeros(plan.workspace_bytes(0), dtype=torch.uint8, device="cuda")
+    B.muon_step(plan, 0, P, G, Mo, hp, ws)
+    B.muon_step_rows(plan, 0, B.row_table(vw), B.row_table(vg), Mo2, hp, torch.zeros_like(ws), "bf16", "bf16")
+    torch.cuda.synchronize()
+    for i, v in enumerate(vw):
+        assert torch.equal(v.reshape(256, 256), P[i]), i
+    assert torch.equal(Mo2, Mo)
