@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 5
+#define MUON_ABI_VERSION 6
 
 typedef enum {
   MUON_OK = 0,
@@ -285,6 +285,39 @@ muon_status muon_stage_ns(const muon_plan* plan, int32_t batch, const float* u_i
                           const muon_hparams* hp, void* workspace, size_t workspace_bytes, void* stream);
 muon_status muon_stage_update(const muon_plan* plan, int32_t batch, void* param, muon_dtype param_dtype,
                               const float* o_in, const muon_hparams* hp, void* stream);
+
+/* Per-step Newton-Schulz coefficients, a pure host computation (no device
+ * work, callable without a GPU).  The DMuon-2 page (App. C.3) steps with a
+ * per-step schedule from the Polar Express method (Amsel et al., 2025) and the
+ * HyperParallel-FSDP evaluation with an "asym5" set; neither prints values.
+ * This call builds one by that method's greedy construction: step k uses the
+ * odd quintic a x + b x^3 + c x^5 closest to 1 in the uniform norm on the
+ * interval [l_k, u_k] that holds the singular values before the step, and
+ * [l_{k+1}, u_{k+1}] is that polynomial's range over [l_k, u_k] (an odd
+ * polynomial of X acts on each singular value).  [l_0, u_0] = [lower, 1]:
+ * Frobenius normalisation leaves no singular value above 1, and `lower` is
+ * the caller's bound on the smallest one.
+ *  steps    K, 1..64.
+ *  lower    in [1e-12, 1).
+ *  safety   in [1, 2]; step k uses p_k(x / safety), so values up to safety*u_k
+ *           (rounding overshoot) stay where p_k is designed.  1 = none.
+ *  cushion  in [0, 1); step k is designed on [max(l_k, cushion*u_k, 1e-4*u_k),
+ *           u_k], which keeps the first steps' coefficients small when `lower`
+ *           is tiny (the bounds still cover [l_k, u_k]).  0 = only the fixed
+ *           1e-4 floor, below which the levelled minimum of p_k would be
+ *           within the coefficients' float rounding of zero.
+ *  coeffs   out, host, 3*K floats (a_k, b_k, c_k), the layout muon_hparams
+ *           takes with num_coeff_sets = ns_steps = K.
+ *  bounds   out, host, optional (NULL): 2*K doubles, [l_{k+1}, u_{k+1}] after
+ *           step k, computed for the float coefficients written.  In exact
+ *           arithmetic every singular value of X_{k+1} lies in it.
+ * With bf16 operands, a large first step (a = 8.47 from lower = 1e-3)
+ * amplifies operand rounding on nearly square tiled matrices; safety 1.01 and
+ * cushion 0.02 keep O within the usual bf16 error there.
+ * Returns INVALID_ARG for an argument out of range (nothing written) and
+ * INTERNAL if the construction fails to level (not seen in the ranges above). */
+muon_status muon_ns_schedule(int32_t steps, double lower, double safety, double cushion, float* coeffs,
+                             double* bounds);
 
 /* Launch tracing, for measurement.  muon_trace_start(n) makes the next (at
  * most n) kernel launches of the step and stage calls carry a start and a

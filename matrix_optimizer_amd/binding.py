@@ -29,7 +29,7 @@ EXPORTED = ["muon_abi_version", "muon_status_str", "muon_plan_create", "muon_pla
             "muon_plan_num_batches", "muon_plan_batch_info", "muon_plan_segments",
             "muon_workspace_bytes", "muon_step", "muon_stage_momentum", "muon_stage_ns",
             "muon_stage_update", "muon_trace_start", "muon_trace_stop", "muon_plan_lanes",
-            "muon_step_batches", "muon_step_rows"]
+            "muon_step_batches", "muon_step_rows", "muon_ns_schedule"]
 
 
 class muon_shape(C.Structure):
@@ -133,6 +133,9 @@ def lib():
     L.muon_stage_update.restype = C.c_int32
     L.muon_stage_update.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p,
                                     C.POINTER(muon_hparams), C.c_void_p]
+    L.muon_ns_schedule.restype = C.c_int32
+    L.muon_ns_schedule.argtypes = [C.c_int32, C.c_double, C.c_double, C.c_double, C.POINTER(C.c_float),
+                                   C.POINTER(C.c_double)]
     L.muon_trace_start.restype = C.c_int32
     L.muon_trace_start.argtypes = [C.c_int32]
     L.muon_trace_stop.restype = C.c_int32
@@ -155,6 +158,18 @@ def _check(status: int, where: str):
 
 def muon_abi_version() -> int:
     return lib().muon_abi_version()
+
+
+def ns_schedule(steps: int, lower: float = 1e-3, safety: float = 1.0, cushion: float = 0.0):
+    """Per-step Newton-Schulz coefficients (muon_ns_schedule): returns (coeffs,
+    bounds), coeffs a tuple of 3*steps floats for HParams(ns_steps=steps,
+    coeffs=coeffs), bounds a list of (lo, hi) singular-value intervals after
+    each step."""
+    co = (C.c_float * (3 * steps))()
+    bo = (C.c_double * (2 * steps))()
+    _check(lib().muon_ns_schedule(int(steps), float(lower), float(safety), float(cushion), co, bo),
+           "muon_ns_schedule")
+    return tuple(float(v) for v in co), [(bo[2 * k], bo[2 * k + 1]) for k in range(steps)]
 
 
 @dataclass

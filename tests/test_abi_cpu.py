@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.EXPORTED)
-    assert B.muon_abi_version() == 5
+    assert B.muon_abi_version() == 6
 
 
 def _cmp_plans(shapes, cap=0, order=0):

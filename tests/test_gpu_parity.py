@@ -129,7 +129,7 @@ def test_small_shapes(name, kernel, dtype, prec):
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("shapes", [[(24, 500)], [(160, 200)]], ids=["skinny", "tiled"])
 @pytest.mark.parametrize("variant", ["one_step", "schedule", "c_zero", "no_nesterov", "no_scale", "eps_zero",
-                                     "seven_steps"])
+                                     "seven_steps", "minimax_schedule"])
 def test_hparam_variants(shapes, variant):
     wl = WL.small_workload("v", shapes, momentum_recipe="normal", wid=300)
     over = {
@@ -142,8 +142,13 @@ def test_hparam_variants(shapes, variant):
         "no_scale": dict(scale="none"),
         "eps_zero": dict(eps=0.0),
         "seven_steps": dict(ns_steps=7),
+        # five greedy minimax steps from a 1e-3 singular-value bound, with
+        # the safety factor 1.01 and cushion 0.02 that bf16 operands need
+        # (first step a = 7.63, b = -21.5, c = 15.5; without them, a = 8.47
+        # amplifies operand rounding past the bf16 bound on 160 x 200)
+        "minimax_schedule": dict(ns_steps=5, coeffs=B.ns_schedule(5, 1e-3, 1.01, 0.02)[0]),
     }[variant]
-    for prec in ("bf16", "f32"):
+    for prec in ("bf16", "bf16_x32", "f32"):
         for kernel in (1, 2):
             check_batch(wl, H.c_hparams(wl.hp, precision=prec, **over), WL.BF16, skinny_kernel=kernel)
 
