@@ -70,6 +70,8 @@ def kernel_model(name, count, M, N, prec, pdt, gdt, with_ns_out=False, ns_steps=
             return "hbm", part + count * S * 4 + count * 4096, "B"
         if name == "sk_apply_update":
             return "hbm", E * (xs + 2 * ps + (4 if with_ns_out else 0)), "B"
+        if name == "sk_ns_apply_update":   # the partials once per matrix, then as sk_apply_update
+            return "hbm", part + count * S * 4 + E * (xs + 2 * ps + (4 if with_ns_out else 0)), "B"
     else:
         if name == "tl_momentum_layout":
             # G read, M read and written, X written (bf16 operands unless f32),

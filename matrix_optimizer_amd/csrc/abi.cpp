@@ -62,14 +62,14 @@ WsLayout workspace_layout(const BatchShape& b, int prec, int path) {
     off = align256(off + bytes);
     return at;
   };
-  if (path == PATH_SKINNY_GRAM || path == PATH_SKINNY_STEPWISE) {
+  if (path == PATH_SKINNY_GRAM || path == PATH_SKINNY_FUSED || path == PATH_SKINNY_STEPWISE) {
     L.skinny = true;
     const int64_t Lc = skinny_chunk(prec);
     L.ldx = round_up(b.n, Lc);
     L.S = L.ldx / Lc;
     L.T = b.m * (b.m + 1) / 2;
     const size_t xs = prec == PREC_BF16 ? 2 : 4;
-    if (path == PATH_SKINNY_GRAM)   // U as 32-column x 8-row MFMA tiles
+    if (path != PATH_SKINNY_STEPWISE)   // U as 32-column x 8-row MFMA tiles
       L.x = take(size_t(b.count) * size_t((b.n + 31) / 32) * size_t((b.m + 7) / 8) * 256 * xs);
     else                            // X row-major, row stride ldx
       L.x = take(size_t(b.count) * b.m * L.ldx * xs);
@@ -188,6 +188,7 @@ muon_status hip_status(hipError_t e) { return e == hipSuccess ? MUON_OK : MUON_E
 hipError_t dispatch(const StepArgs& a, const WsLayout& L) {
   switch (L.path) {
     case PATH_SKINNY_GRAM:
+    case PATH_SKINNY_FUSED:
     case PATH_SKINNY_STEPWISE: return run_skinny(a, L);
     default: return run_tiled(a, L);
   }
@@ -291,7 +292,7 @@ muon_status muon_plan_create(const muon_shape* shapes, int32_t n, const muon_pla
   int32_t order = 0, skinny_kernel = 0;
   if (opt) {
     if (opt->max_batch_elems < 0 || (opt->order != 0 && opt->order != 1)) return MUON_ERR_INVALID_ARG;
-    if (opt->skinny_kernel < 0 || opt->skinny_kernel > 2) return MUON_ERR_INVALID_ARG;
+    if (opt->skinny_kernel < 0 || opt->skinny_kernel > 3) return MUON_ERR_INVALID_ARG;
     if (opt->max_batch_elems > 0) cap = opt->max_batch_elems;
     order = opt->order;
     skinny_kernel = opt->skinny_kernel;
@@ -340,7 +341,8 @@ muon_status muon_plan_create(const muon_shape* shapes, int32_t n, const muon_pla
         const int64_t m = std::min(M, N), n = std::max(M, N);
         if (m > kSkinnyMaxRows) b.path = PATH_TILED;
         else if (skinny_kernel == 2) b.path = PATH_SKINNY_STEPWISE;
-        else b.path = PATH_SKINNY_GRAM;
+        else if (skinny_kernel == 1) b.path = PATH_SKINNY_GRAM;
+        else b.path = PATH_SKINNY_FUSED;
         for (size_t k = start; k < end; ++k) {
           const int32_t pi = mats[k].first;
           const int64_t mi = mats[k].second;
@@ -378,7 +380,7 @@ muon_status muon_plan_batch_info(const muon_plan* plan, int32_t batch, muon_batc
   if (!b || !out) return MUON_ERR_INVALID_ARG;
   out->M = b->M; out->N = b->N; out->count = b->count; out->transposed = b->transposed ? 1 : 0;
   out->num_segments = (int32_t)b->segs.size();
-  out->path = b->path;
+  out->path = b->path == PATH_SKINNY_FUSED ? PATH_SKINNY_GRAM : b->path;
   out->reserved = 0;
   return MUON_OK;
 }

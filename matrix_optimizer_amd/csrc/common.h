@@ -102,8 +102,10 @@ __device__ __forceinline__ T* row_of(const void* const* rows, int64_t b, int64_t
 }
 
 // Decoupled decay plus the orthogonal update on one element, fp32.
+// W - lr (wd W + s O), its two fused multiply-adds spelled out so that every
+// kernel rounds it the same way whatever the compiler would contract.
 __device__ __forceinline__ float apply_update(float w, float o, float lr, float wd, float s) {
-  return w - lr * (wd * w + s * o);
+  return __builtin_fmaf(-lr, __builtin_fmaf(s, o, wd * w), w);
 }
 
 }  // namespace muon

@@ -52,7 +52,10 @@ struct BatchShape {
 // Kernel family of a batch: tiled products (short side > 32), or the skinny
 // chunk kernels with Newton-Schulz in Gram space (3 launches) or step by step
 // (2K + 1 launches).
-enum Path { PATH_TILED = 0, PATH_SKINNY_GRAM = 1, PATH_SKINNY_STEPWISE = 2 };
+// PATH_SKINNY_FUSED: Gram space with the Newton-Schulz and the apply in one
+// launch where the stored rows are U rows (the workspace of PATH_SKINNY_GRAM;
+// reported to callers as path 1).
+enum Path { PATH_TILED = 0, PATH_SKINNY_GRAM = 1, PATH_SKINNY_STEPWISE = 2, PATH_SKINNY_FUSED = 3 };
 
 // Device workspace carve-up of one batch (offsets in bytes from the base).
 struct WsLayout {

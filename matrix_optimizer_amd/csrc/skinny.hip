@@ -304,7 +304,7 @@ __device__ void apply_bx(unsigned char* lds_raw, const BFrag& fr) {
 // K slot (kb, lane/32) is column 16 (lane/32) + kb instead of 2 kb + lane/32,
 // so that a lane's 16 slots are 16 consecutive rows of X.
 template <int MODE, bool HALVES = false>
-__device__ void write_frag(const float (*Q)[SK_MP + 1], BFrag* __restrict__ out, int lane) {
+__device__ __forceinline__ BFrag make_frag(const float (*Q)[SK_MP + 1], int lane) {
   const int row = lane & 31;
   BFrag f;
   if constexpr (MODE == 2) {
@@ -339,7 +339,11 @@ __device__ void write_frag(const float (*Q)[SK_MP + 1], BFrag* __restrict__ out,
     f.q[2] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     f.q[3] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
   }
-  out[lane] = f;
+  return f;
+}
+template <int MODE, bool HALVES = false>
+__device__ void write_frag(const float (*Q)[SK_MP + 1], BFrag* __restrict__ out, int lane) {
+  out[lane] = make_frag<MODE, HALVES>(Q, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -472,52 +476,66 @@ template <typename R, int KM>
 __device__ R* gram_steps(R* A, R* Bm, R* P0, R* P1, R* Tm, int steps, const Coeffs& cf) {
   const int lane = threadIdx.x & (WAVE - 1);
   const int w = threadIdx.x / WAVE, bi = w >> 1, bj = w & 1;
+  const bool active = w < 4;   // waves beyond the fourth only take the barriers
   R* P = P0;
   R* Pn = P1;
   for (int k = 0; k < steps; ++k) {
     const R ca = cf.c[3 * k], cb = cf.c[3 * k + 1], cc = cf.c[3 * k + 2];
-    const typename Mf<R>::V a2 = mul_blk<R, KM>(A, A, bi, bj, lane);
+    if (active) {
+      const typename Mf<R>::V a2 = mul_blk<R, KM>(A, A, bi, bj, lane);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * bi + Mf<R>::row(r, lane), j = 16 * bj + (lane & 15);
-      Bm[i * GSD + j] = (i == j ? ca : R(0)) + cb * A[i * GSD + j] + cc * a2[r];
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * bi + Mf<R>::row(r, lane), j = 16 * bj + (lane & 15);
+        Bm[i * GSD + j] = (i == j ? ca : R(0)) + cb * A[i * GSD + j] + cc * a2[r];
+      }
     }
     __syncthreads();
     const bool more = k + 1 < steps;
-    put_blk<R>(Pn, mul_blk<R, KM>(Bm, P, bi, bj, lane), bi, bj, lane);                // B_k P
-    if (more) put_blk<R>(Tm, mul_blk<R, KM>(A, Bm, bi, bj, lane), bi, bj, lane);      // A_k B_k
+    if (active) {
+      put_blk<R>(Pn, mul_blk<R, KM>(Bm, P, bi, bj, lane), bi, bj, lane);                // B_k P
+      if (more) put_blk<R>(Tm, mul_blk<R, KM>(A, Bm, bi, bj, lane), bi, bj, lane);      // A_k B_k
+    }
     __syncthreads();
     R* t = P; P = Pn; Pn = t;
     if (more) {
-      put_blk<R>(A, mul_blk<R, KM>(Tm, Bm, bi, bj, lane), bi, bj, lane);   // A_{k+1} = B_k A_k B_k
+      if (active) put_blk<R>(A, mul_blk<R, KM>(Tm, Bm, bi, bj, lane), bi, bj, lane);   // A_{k+1} = B_k A_k B_k
       __syncthreads();
     }
   }
   return P;
 }
 
+// LDS of gram_q: A | B | P0 | P1 | Tm, the partials stage aliasing B, P0,
+// P1 and Tm (and beyond).
 template <int MODE>
-__global__ void __launch_bounds__(SK_THREADS)
-sk_gram_ns(const float* __restrict__ gp, const float* __restrict__ sp, float eps, int m, int S, int T, int steps,
-           Coeffs cf, BFrag* __restrict__ bfrag) {
+struct GramLds {
   typedef typename std::conditional<MODE == 2, double, float>::type R;
-  constexpr int MATB = GS_MAT * (int)sizeof(R);
-  constexpr int RAW = 5 * MATB > MATB + 4 * GS_STAGE ? 5 * MATB : MATB + 4 * GS_STAGE;
-  // A | B | P0 | P1 | Tm; the partials stage aliases B, P0, P1 and Tm (and beyond)
-  __shared__ __attribute__((aligned(16))) unsigned char raw[RAW];
-  __shared__ float Qf[SK_MP][SK_MP + 1];
-  __shared__ double inv_s;
+  static constexpr int MATB = GS_MAT * (int)sizeof(R);
+  static constexpr int RAW = 5 * MATB > MATB + 4 * GS_STAGE ? 5 * MATB : MATB + 4 * GS_STAGE;
+};
+
+// Q = B_{K-1} ... B_0 / (||U||_F + eps) of matrix b into Qf (zero outside
+// m x m) by a workgroup of NT threads: all of them load the partials, the
+// first SK_THREADS do the rest, every thread takes the barriers.  raw is
+// GramLds<MODE>::RAW bytes of LDS, free again when this returns (it ends with
+// a barrier).
+template <int MODE, int NT = SK_THREADS>
+__device__ void gram_q(const float* __restrict__ gp, const float* __restrict__ sp, float eps, int m, int S, int T,
+                       int steps, const Coeffs& cf, int64_t b, unsigned char* raw, float (*Qf)[SK_MP + 1],
+                       double* inv_s) {
+  typedef typename GramLds<MODE>::R R;
   R* A = reinterpret_cast<R*>(raw);
   R* Bm = A + GS_MAT;
   R* P = A + 2 * GS_MAT;
   R* P1 = A + 3 * GS_MAT;
   R* Tm = A + 4 * GS_MAT;
-  float* stage = reinterpret_cast<float*>(raw + MATB);
+  float* stage = reinterpret_cast<float*>(raw + GramLds<MODE>::MATB);
 
-  const int64_t b = blockIdx.x;
   const int t = threadIdx.x;
   const int lane = t & (WAVE - 1);
-  for (int e = t; e < GS_MAT; e += SK_THREADS) A[e] = R(0);
+  const bool worker = t < SK_THREADS;
+  if (worker)
+    for (int e = t; e < GS_MAT; e += SK_THREADS) A[e] = R(0);
 
   // A_0 entries: thread t owns packed entries t, t + 256, t + 512 and adds the
   // chunk partials in chunk order (fp64); the partials pass through LDS in
@@ -525,7 +543,8 @@ sk_gram_ns(const float* __restrict__ gp, const float* __restrict__ sp, float eps
   double acc[3] = {0., 0., 0.};
   const float* g = gp + b * (int64_t)S * T;
   const int qb = GS_STAGE / T;
-  constexpr int PER = GS_STAGE / SK_THREADS;
+  static_assert(GS_STAGE % NT == 0 && NT % SK_THREADS == 0, "whole rounds of loads");
+  constexpr int PER = GS_STAGE / NT;
   for (int q0 = 0; q0 < S; q0 += qb) {
     const int nq = S - q0 < qb ? S - q0 : qb;
     const int tot = nq * T;
@@ -533,7 +552,7 @@ sk_gram_ns(const float* __restrict__ gp, const float* __restrict__ sp, float eps
     float v[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int f = t + SK_THREADS * i;
+      const int f = t + NT * i;
       v[i] = f < tot ? src[f] : 0.f;
     }
     if (q0 == 0 && t < WAVE) {
@@ -544,27 +563,27 @@ sk_gram_ns(const float* __restrict__ gp, const float* __restrict__ sp, float eps
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) sv += __shfl_xor(sv, o, WAVE);
       const double den = sqrt(sv) + (double)eps;
-      if (lane == 0) inv_s = den > 0. ? 1. / den : 0.;
+      if (lane == 0) *inv_s = den > 0. ? 1. / den : 0.;
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int f = t + SK_THREADS * i;
+      const int f = t + NT * i;
       if (f < tot) stage[f] = v[i];
     }
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
       const int e = t + SK_THREADS * u;
-      if (e < T)
+      if (worker && e < T)
         for (int q = 0; q < nq; ++q) acc[u] += (double)stage[q * T + e];
     }
     __syncthreads();
   }
-  const double inv = inv_s;
+  const double inv = *inv_s;
 #pragma unroll
   for (int u = 0; u < 3; ++u) {
     const int e = t + SK_THREADS * u;
-    if (e < T) {
+    if (worker && e < T) {
       int r, s;
       tri_rc(e, r, s);
       const R v = (R)(acc[u] * inv * inv);
@@ -572,7 +591,8 @@ sk_gram_ns(const float* __restrict__ gp, const float* __restrict__ sp, float eps
       A[s * GSD + r] = v;
     }
   }
-  for (int e = t; e < GS_MAT; e += SK_THREADS) P[e] = (e / GSD == e % GSD) ? R(1) : R(0);
+  if (worker)
+    for (int e = t; e < GS_MAT; e += SK_THREADS) P[e] = (e / GSD == e % GSD) ? R(1) : R(0);
   __syncthreads();
 
   switch ((m + 7) >> 3) {
@@ -583,12 +603,24 @@ sk_gram_ns(const float* __restrict__ gp, const float* __restrict__ sp, float eps
   }
 
   // Q = P / (||U||_F + eps): the result applies to the stored, unnormalised U
-  for (int e = t; e < SK_MP * SK_MP; e += SK_THREADS) {
-    const int i = e / SK_MP, j = e % SK_MP;
-    Qf[i][j] = (i < m && j < m) ? (float)(inv * (double)P[i * GSD + j]) : 0.f;
-  }
+  if (worker)
+    for (int e = t; e < SK_MP * SK_MP; e += SK_THREADS) {
+      const int i = e / SK_MP, j = e % SK_MP;
+      Qf[i][j] = (i < m && j < m) ? (float)(inv * (double)P[i * GSD + j]) : 0.f;
+    }
   __syncthreads();
-  if (t < WAVE) write_frag<MODE, true>(Qf, bfrag + b * WAVE, lane);
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(SK_THREADS)
+sk_gram_ns(const float* __restrict__ gp, const float* __restrict__ sp, float eps, int m, int S, int T, int steps,
+           Coeffs cf, BFrag* __restrict__ bfrag) {
+  __shared__ __attribute__((aligned(16))) unsigned char raw[GramLds<MODE>::RAW];
+  __shared__ float Qf[SK_MP][SK_MP + 1];
+  __shared__ double inv_s;
+  const int64_t b = blockIdx.x;
+  gram_q<MODE>(gp, sp, eps, m, S, T, steps, cf, b, raw, Qf, &inv_s);
+  if (threadIdx.x < WAVE) write_frag<MODE, true>(Qf, bfrag + b * WAVE, threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -1152,6 +1184,149 @@ sk_apply(const typename SkCfg<MODE>::XS* __restrict__ xg, const BFrag* __restric
   }
 }
 
+// ---------------------------------------------------------------------------
+// Gram-space Newton-Schulz and the apply in one launch, for matrices whose
+// stored rows are U rows.  R workgroups of FW_WAVES waves per matrix, one per
+// CU: the first four waves of each form Q from the chunk partials exactly as
+// sk_gram_ns does (the R copies are bitwise equal; one workgroup per CU keeps
+// their dependent MFMA chains from sharing a SIMD with another copy's), then
+// every wave applies it to its share of the matrix's 64-column units exactly
+// as sk_apply does: wave w of workgroup r takes units r * FW_WAVES + w +
+// i * R * FW_WAVES, so the R workgroups sweep the matrix front to back
+// together.  (Loading each wave's first unit before Q was formed, to overlap
+// the Newton-Schulz latency, made the launch slower: those loads delay the
+// partials Q needs first.)  The O buffers alias gram_q's
+// LDS, which is free once Q is in Qf.  All waves take part in gram_q's
+// barriers; after it there are none.
+constexpr int FW_WAVES = 16;
+constexpr int FW_THREADS = FW_WAVES * WAVE;
+// ---------------------------------------------------------------------------
+template <int MODE, typename PT, bool ROWS>
+__global__ void __launch_bounds__(FW_THREADS)
+sk_ns_apply(const float* __restrict__ gp, const float* __restrict__ sp, float eps, int S, int T, int steps, Coeffs cf,
+            const typename SkCfg<MODE>::XS* __restrict__ xg, int m, int64_t n, int64_t NB, int G, int64_t upm, int R,
+            int vec, PT* __restrict__ param, float* __restrict__ ns_out, float lr, float wd, float s_scale,
+            const float* __restrict__ lrwd, MatTabs tabs) {
+  typedef typename SkCfg<MODE>::XS XS;
+  typedef Oct<PT> OV;
+  constexpr int XW = MODE == 0 ? 4 : 8;     // 32-bit words of U per lane per K block
+  constexpr int OBUF = FW_WAVES * SK_MP * AP_LD * 4;
+  constexpr int RAW = GramLds<MODE>::RAW > OBUF ? GramLds<MODE>::RAW : OBUF;
+  __shared__ __attribute__((aligned(16))) unsigned char raw[RAW];
+  __shared__ float Qf[SK_MP][SK_MP + 1];
+  __shared__ double inv_s;
+
+  update_scalars(lrwd, lr, wd);
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+  const int h = lane >> 5, c = lane & 31;
+  const int64_t b = blockIdx.x / R;
+  const int64_t r = blockIdx.x % R;
+  const int64_t stride = (int64_t)R * FW_WAVES;
+  const int64_t mat = b * (int64_t)m * n;
+  param = batch_view(param, tabs.param, b, (int64_t)m * n);
+  ns_out = batch_view(ns_out, tabs.ns, b, (int64_t)m * n);
+  const bool has_w = ROWS || param != nullptr;
+  auto w_at = [&](int64_t sr, int64_t sc) -> PT* {
+    if constexpr (ROWS) return row_of<PT>(tabs.param_rows, b, m, sr) + sc;
+    else return param + mat + sr * n + sc;
+  };
+  // W rows 8 i + lane / 8, columns 64 u + 8 (lane % 8) .. + 7 of unit u
+  const int rr = lane >> 3, cc = (lane & 7) * 8;
+
+  // U operands of both 32-column blocks of unit u (bf16 modes: K block kb =
+  // rows of group 2 kb + h; fp32 mode: rows 16 h .. 16 h + 15), and W
+  auto load_unit = [&](int64_t u, uint32_t (&xd)[2][2][XW], typename OV::V (&wdst)[4])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int64_t jb = 2 * u + jj;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int g = MODE == 2 ? 2 * h + kb : 2 * kb + h;
+        if (jb < NB && g < G) {
+          const XS* src = xg + xg_tile(b, jb, g, NB, G) + c * 8;
+          const u32x4 v0 = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) xd[jj][kb][q] = v0[q];
+          if constexpr (XW == 8) {
+            const u32x4 v1 = *reinterpret_cast<const u32x4*>(src + 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) xd[jj][kb][4 + q] = v1[q];
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < XW; ++q) xd[jj][kb][q] = 0u;
+        }
+      }
+    }
+    const int64_t col0 = 64 * u + cc;
+    if (has_w && vec) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 8 * i + rr;
+        if (i < G && row < m && col0 < n) wdst[i] = OV::load(w_at(row, col0));
+      }
+    }
+  };
+
+  gram_q<MODE, FW_THREADS>(gp, sp, eps, m, S, T, steps, cf, b, raw, Qf, &inv_s);
+  const BFrag fr = make_frag<MODE, true>(Qf, lane);
+
+  const int mr = 8 * G;
+  float* o = reinterpret_cast<float*>(raw) + w * mr * AP_LD;
+  uint32_t xr[2][2][XW];
+  typename OV::V wv[4];
+  for (int64_t u = r * FW_WAVES + w; u < upm; u += stride) {
+    load_unit(u, xr, wv);
+    wave_sync();   // this wave's reads of the previous unit's O are done
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const f32x16 acc = apply_block<MODE, false>(xr[jj], fr);
+      // lane holds O row c, columns 32 jj + 8 qd + 4 h + 0..3
+      if (c < mr) {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          *reinterpret_cast<f32x4*>(o + c * AP_LD + 32 * jj + 8 * qd + 4 * h) =
+              f32x4{acc[4 * qd], acc[4 * qd + 1], acc[4 * qd + 2], acc[4 * qd + 3]};
+      }
+    }
+    wave_sync();
+    const int64_t col0 = 64 * u + cc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 8 * i + rr;
+      if (i >= G || row >= m) continue;
+      float ov[8], nw[8];
+      const f32x4 o0 = *reinterpret_cast<const f32x4*>(o + row * AP_LD + cc);
+      const f32x4 o1 = *reinterpret_cast<const f32x4*>(o + row * AP_LD + cc + 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { ov[q] = o0[q]; ov[q + 4] = o1[q]; }
+      if (vec) {
+        if (col0 >= n) continue;
+        const int64_t idx = mat + (int64_t)row * n + col0;
+        if (ns_out) Oct<float>::put(ns_out + idx, ov);
+        if (has_w) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) nw[q] = apply_update(OV::get(wv[i], q), ov[q], lr, wd, s_scale);
+          OV::put(w_at(row, col0), nw);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if (col0 + q >= n) break;
+          const int64_t idx = mat + (int64_t)row * n + col0 + q;
+          if (ns_out) ns_out[idx] = ov[q];
+          if (has_w) {
+            PT* wp = w_at(row, col0 + q);
+            st_from_f32(wp, 0, apply_update(ld_as_f32(wp, 0), ov[q], lr, wd, s_scale));
+          }
+        }
+      }
+    }
+  }
+}
+
 template <int MODE, typename GT>
 hipError_t launch_first(const StepArgs& a, const WsLayout& L, int mode, int vec) {
   typedef typename SkCfg<MODE>::XS XS;
@@ -1171,7 +1346,7 @@ hipError_t launch_first(const StepArgs& a, const WsLayout& L, int mode, int vec)
                     a.nesterov, NB, G, a.tabs);
   };
   const bool rows = a.tabs.grad_rows != nullptr;
-  if (L.path == PATH_SKINNY_GRAM) {
+  if (L.path == PATH_SKINNY_GRAM || L.path == PATH_SKINNY_FUSED) {
     if (rows) go(std::true_type{}, std::true_type{});
     else go(std::true_type{}, std::false_type{});
   } else {
@@ -1215,6 +1390,50 @@ hipError_t launch_iters(const StepArgs& a, const WsLayout& L, int vec) {
   return hipSuccess;
 }
 
+// Workgroups per matrix of sk_ns_apply: as many as fill one round of resident
+// workgroups (one per CU), but no more than give every wave a unit.
+template <int MODE, typename PT, bool ROWS>
+int64_t fused_groups(int64_t count, int64_t upm) {
+  static int per_dev[64] = {0};   // resident workgroups of this kernel per device
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (per_dev[dev] == 0) {
+    int cus = 0, blocks = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, sk_ns_apply<MODE, PT, ROWS>, FW_THREADS, 0) !=
+            hipSuccess || blocks <= 0)
+      blocks = 1;
+    per_dev[dev] = cus * blocks;
+  }
+  int64_t R = per_dev[dev] / count;
+  const int64_t most = (upm + FW_WAVES - 1) / FW_WAVES;
+  if (R > most) R = most;
+  return R < 1 ? 1 : R;
+}
+
+template <int MODE, typename PT>
+hipError_t launch_fused(const StepArgs& a, const WsLayout& L, const Coeffs& cf) {
+  typedef typename SkCfg<MODE>::XS XS;
+  const BatchShape& sh = a.shape;
+  PT* param = a.phase == PH_FULL ? (PT*)a.param : nullptr;
+  const int64_t NB = (sh.n + 31) / 32;
+  const int G = (int)((sh.m + 7) / 8);
+  const int64_t upm = (NB + 1) / 2;                    // 64-column units per matrix
+  const int vec = sh.n % 8 == 0 ? 1 : 0;
+  const char* name = (param || a.tabs.param || a.tabs.param_rows) ? "sk_ns_apply_update" : "sk_ns_apply";
+  auto go = [&](auto rows) {
+    constexpr bool RW = decltype(rows)::value;
+    const int64_t R = fused_groups<MODE, PT, RW>(sh.count, upm);
+    if (sh.count * R > 0x7fffffffll) return hipErrorInvalidValue;
+    MUON_LAUNCH(name, (sk_ns_apply<MODE, PT, RW>), dim3((unsigned)(sh.count * R)), dim3(FW_THREADS), a.stream,
+                (const float*)(a.ws + L.gp0), (const float*)(a.ws + L.sp), a.eps, (int)L.S, (int)L.T, a.steps, cf,
+                (const XS*)(a.ws + L.x), (int)sh.m, sh.n, NB, G, upm, (int)R, vec, param, a.ns_out, a.lr, a.wd,
+                a.s, a.lrwd, a.tabs);
+    return hipGetLastError();
+  };
+  return a.tabs.param_rows ? go(std::true_type{}) : go(std::false_type{});
+}
+
 template <int MODE, typename PT>
 hipError_t launch_gram(const StepArgs& a, const WsLayout& L, int vec) {
   typedef typename SkCfg<MODE>::XS XS;
@@ -1222,6 +1441,8 @@ hipError_t launch_gram(const StepArgs& a, const WsLayout& L, int vec) {
   if (a.steps < 0 || a.steps > 64 || (int)a.coeffs.size() < 3 * a.steps) return hipErrorInvalidValue;
   Coeffs cf = {};
   for (int i = 0; i < 3 * a.steps; ++i) cf.c[i] = a.coeffs[i];
+  if constexpr (MODE == 0)   // bf16 precision: the other modes' operands need more registers than 16 waves have
+    if (L.path == PATH_SKINNY_FUSED && !sh.transposed) return launch_fused<MODE, PT>(a, L, cf);
   BFrag* bfrag = (BFrag*)(a.ws + L.bfrag);
   MUON_LAUNCH("sk_gram_ns", (sk_gram_ns<MODE>), dim3((unsigned)sh.count), dim3(SK_THREADS), a.stream,
               (const float*)(a.ws + L.gp0), (const float*)(a.ws + L.sp), a.eps, (int)sh.m, (int)L.S, (int)L.T,
@@ -1267,7 +1488,7 @@ hipError_t run_mode(const StepArgs& a, const WsLayout& L) {
                                          : launch_first<MODE, float>(a, L, mode, vec);
   if (e != hipSuccess) return e;
   const bool pbf = (a.phase == PH_FULL && a.param_dtype == DT_BF16);
-  if (L.path == PATH_SKINNY_GRAM)
+  if (L.path == PATH_SKINNY_GRAM || L.path == PATH_SKINNY_FUSED)
     return pbf ? launch_gram<MODE, bf16_t>(a, L, vec) : launch_gram<MODE, float>(a, L, vec);
   return pbf ? launch_iters<MODE, bf16_t>(a, L, vec) : launch_iters<MODE, float>(a, L, vec);
 }

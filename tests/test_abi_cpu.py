@@ -85,7 +85,8 @@ def test_plan_errors():
     assert _plan_status([]) == B.MUON_ERR_INVALID_ARG
     assert _plan_status([(2, 2)], cap=-1) == B.MUON_ERR_INVALID_ARG
     assert _plan_status([(2, 2)], order=2) == B.MUON_ERR_INVALID_ARG
-    assert _plan_status([(2, 2)], skinny_kernel=3) == B.MUON_ERR_INVALID_ARG
+    assert _plan_status([(2, 2)], skinny_kernel=4) == B.MUON_ERR_INVALID_ARG
+    assert _plan_status([(2, 2)], skinny_kernel=3) == B.MUON_OK
     assert _plan_status([(2, 2)], skinny_kernel=-1) == B.MUON_ERR_INVALID_ARG
     assert _plan_status([(1 << 20, 1 << 20)]) == B.MUON_ERR_UNSUPPORTED   # above 2^31 elements
     assert _plan_status([(1 << 40, 1 << 40)]) == B.MUON_ERR_INVALID_ARG   # int64 overflow

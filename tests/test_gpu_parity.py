@@ -111,8 +111,9 @@ def _skinny(name):
     return all(min(WL.ParamSpec("x", tuple(s)).matrix_shape) <= 32 for s in SHAPE_SETS[name])
 
 
-# skinny shapes run through both Newton-Schulz forms: 1 = Gram space, 2 = step by step
-SHAPE_CASES = [(n, k) for n in sorted(SHAPE_SETS) for k in ((1, 2) if _skinny(n) else (0,))]
+# skinny shapes run through every Newton-Schulz form: 0 = Gram space, one launch for the
+# iteration and the apply (bf16 precision), 1 = Gram space in three launches, 2 = step by step
+SHAPE_CASES = [(n, k) for n in sorted(SHAPE_SETS) for k in ((0, 1, 2) if _skinny(n) else (0,))]
 
 
 @pytest.mark.parametrize("prec", PRECS)
@@ -149,7 +150,7 @@ def test_hparam_variants(shapes, variant):
         "minimax_schedule": dict(ns_steps=5, coeffs=B.ns_schedule(5, 1e-3, 1.01, 0.02)[0]),
     }[variant]
     for prec in ("bf16", "bf16_x32", "f32"):
-        for kernel in (1, 2):
+        for kernel in (0, 1, 2):
             check_batch(wl, H.c_hparams(wl.hp, precision=prec, **over), WL.BF16, skinny_kernel=kernel)
 
 
@@ -183,8 +184,9 @@ def test_zero_gradient_and_zero_lr(shapes, kernel):
 # --------------------------------------------------------------------------
 # determinism, batch independence, transpose symmetry
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("shapes,kernel", [([(24, 3000)] * 3, 1), ([(24, 3000)] * 3, 2), ([(300, 500)] * 3, 0)],
-                         ids=["skinny-gram", "skinny-stepwise", "tiled"])
+@pytest.mark.parametrize("shapes,kernel", [([(24, 3000)] * 3, 0), ([(24, 3000)] * 3, 1), ([(24, 3000)] * 3, 2),
+                                           ([(300, 500)] * 3, 0)],
+                         ids=["skinny-fused", "skinny-gram", "skinny-stepwise", "tiled"])
 @pytest.mark.parametrize("prec", PRECS)
 def test_deterministic_and_batch_independent(shapes, kernel, prec):
     wl = WL.small_workload("d", shapes, momentum_recipe="normal", wid=302)
@@ -262,7 +264,7 @@ def test_stage_entry_points(shapes, kernel):
 # --------------------------------------------------------------------------
 # the workloads at full size
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("kernel", [0, 2], ids=["gram", "stepwise"])
+@pytest.mark.parametrize("kernel", [0, 1, 2], ids=["gram-fused", "gram", "stepwise"])
 def test_fused_74x24x10240_full(kernel):
     wl = WL.WORKLOADS["fused_74x24x10240"]
     errs = check_batch(wl, H.c_hparams(wl.hp), WL.BF16, skinny_kernel=kernel)
