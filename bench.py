@@ -91,6 +91,19 @@ def kernel_model(name, count, M, N, prec, pdt, gdt, with_ns_out=False, ns_steps=
     return None
 
 
+def kernel_form(b, skinny_kernel: int, prec: str) -> str:
+    """Which kernels a batch runs: tiled products, Gram space in two launches
+    (the iteration and the apply in one, for bf16 precision where W's stored
+    rows are its long side, unless plan option 1 asks for three), Gram space
+    in three launches, or step by step."""
+    if b.path == 0:
+        return "tiled"
+    if b.path == 2:
+        return "skinny_stepwise"
+    two = skinny_kernel in (0, 3) and prec == "bf16" and b.M <= b.N
+    return "skinny_gram_2launch" if two else "skinny_gram_3launch"
+
+
 def executed_flops(plan, K: int) -> float:
     """Flops the kernels as built perform in one step (padding excluded):
     tiled products m(m+1)n (one triangle of the Gram), m^2(m+1) (one triangle of
@@ -450,7 +463,7 @@ def main():
     cfg = {"workload": wl.name, "matrices": int(sum(b.count for b in plan.batches)), "launch": args.launch,
            "streams": nstreams, "lanes": lane_of,
            "batches": [[b.count, b.M, b.N] for b in plan.batches],
-           "kernels": [["tiled", "skinny_gram", "skinny_stepwise"][b.path] for b in plan.batches],
+           "kernels": [kernel_form(b, args.skinny_kernel, prec) for b in plan.batches],
            "param_dtype": dtype,
            "precision": prec, "ns_steps": hp.ns_steps, "coeffs": list(hp.coeffs),
            "inputs": ("seeded synthetic, drawn on the GPU (torch generators)" if args.device_inputs else
