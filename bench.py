@@ -2,21 +2,34 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--precision P]
 
-A step is one full muon_step over every batch of the workload (momentum,
+A step is one full Muon step over every batch of the workload (momentum,
 normalisation, transpose-first, K Newton-Schulz steps, decay and update), with
-all inputs resident in device memory; several batches are spread over
---streams streams (muon_step_batches).  Prints ONE JSON line with:
+all inputs resident in device memory; the batches are spread over --streams
+streams (muon_step_batches).  The default workload is the largest one that
+fits one GPU: 16 bf16 matrices of 8192 x 28672 plus 16 of 28672 x 8192, in 16
+batches of two, with an fp32 master copy of X (bf16_x32).
+
+Protocol (the DMuon-2 paper's timing, App. D.3): W untimed repetitions, then
+K timed ones; before each, W and M are restored from device copies (outside
+the timed events), so every repetition runs the same step on the same
+values; each repetition is timed between HIP events on the caller's stream
+and ms_per_step is their median.  The first timed repetition's W' and M' are
+checked against the float64 oracle: at the sampled positions the oracle's
+values were stored for (tests/golden/), or against the oracle run of the
+cpu_baseline leg on the same matrices.  Prints ONE JSON line with:
 
 * value: Newton-Schulz TFLOP/s, counting 4 m^2 n + 2 m^3 flops per
   Newton-Schulz step per matrix (m <= n), divided by the full step time;
-* ms_per_step: batched step latency;
-* roofline: the dominant kernel (largest share of traced time), its
-  algorithmic bytes (or flops) per launch over its average launch time,
-  measured with HIP events recorded by the library on the launch stream
-  (with batches on several streams a launch's time includes what it shares
-  with the other lanes' kernels);
+  detail.executed_tflops counts the flops the kernels perform (symmetric
+  products on one triangle);
+* ms_per_step: batched step latency (median over the timed repetitions);
+* roofline: the dominant kernel (largest share of traced time) of a pass on
+  one stream, its algorithmic bytes (or flops) per launch over its average
+  launch time, from HIP events the library records at the kernel's start and
+  end;
 * cpu_baseline: the float64 CPU oracle timed on a bounded sample of the same
-  workload on this host.
+  workload on this host (for the 8192 x 28672 matrices one Newton-Schulz
+  iteration of one matrix, extrapolated).
 """
 from __future__ import annotations
 
@@ -196,7 +209,6 @@ def measured_traffic(workload: str, kernel: str, prec: str):
 def make_device_batches(wl, plan, dtype, reuse_shapes: bool):
     """Per-batch device buffers from the seeded generator.  With reuse_shapes,
     batches of identical [count, M, N] get copies of the first one's data."""
-    import torch
     from tests import harness as H
     cache = {}
     out = []
@@ -219,7 +231,9 @@ def make_device_batches(wl, plan, dtype, reuse_shapes: bool):
 def make_device_batches_gpu(wl, plan, dtype, seed=0):
     """Per-batch device buffers drawn on the GPU with seeded torch generators,
     following the workload's recipes (for large workloads, where drawing on
-    the host would take minutes).  Not the generator the parity tests use."""
+    the host would take minutes).  Not the generator the parity tests use:
+    the matrices the bench checks are redrawn with it afterwards
+    (put_host_matrices)."""
     import torch
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     out = []
@@ -248,67 +262,209 @@ def make_device_batches_gpu(wl, plan, dtype, seed=0):
     return out
 
 
-def cpu_baseline(wl, plan, dtype, hp, budget_s=12.0, max_matrices=None):
-    """Time the float64 oracle on this host on a bounded sample of the workload."""
-    from oracle import muon_oracle as ORC
+def locate(plan, pi: int, mi: int):
+    """(batch, position in the batch) of matrix mi of parameter pi."""
+    for b in plan.batches:
+        for (p, first, num, off) in b.segments:
+            if p == pi and first <= mi < first + num:
+                return b, off // (b.M * b.N) + mi - first
+    raise KeyError((pi, mi))
+
+
+def put_host_matrices(wl, plan, bufs, ids, dtype):
+    """Overwrite matrices `ids` [(param, matrix)] of device-drawn buffers with
+    the seeded host generator's values (the parity tests' inputs), drawn in
+    threads.  Returns {(param, matrix): stored host arrays}."""
+    from concurrent.futures import ThreadPoolExecutor
     from tests import harness as H
+    jobs = [(pi, mi, kind) for (pi, mi) in ids for kind in ("param", "grad", "momentum")]
+    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        mats = list(ex.map(lambda j: wl.matrix(*j), jobs))
+    host = {}
+    for (pi, mi, kind), arr in zip(jobs, mats):
+        host.setdefault((pi, mi), {})[kind] = arr
+        b, q = locate(plan, pi, mi)
+        bufs[b.index][kind][q].copy_(H.to_device(arr, "f32" if kind == "momentum" else dtype))
+    return host
+
+
+def blas_info():
+    """(threads, description) of the BLAS library NumPy calls."""
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
     except Exception:
-        cores = os.cpu_count() or 1
-    kw = None
-    flops = 0.0
-    t0 = time.perf_counter()
-    done = 0
-    reps = 0
-    samples = []
-    for b in plan.batches:
-        ids = H.matrix_ids(b)
-        take = ids if max_matrices is None else ids[:max_matrices]
-        for (pi, mi) in take:
-            samples.append((b, pi, mi))
-    # decode the sample once, then run the oracle until the budget is used
+        info = []
+    if not info:
+        return os.cpu_count() or 1, "unknown"
+    i = info[0]
+    return int(i.get("num_threads", 1)), f"{i.get('internal_api')} {i.get('version')} ({i.get('architecture')})"
+
+
+def cpu_baseline(wl, plan, hp, samples, budget_s=12.0):
+    """Time the float64 oracle on this host on a bounded sample of the workload.
+
+    samples: [(param, matrix)].  Each sampled matrix runs the oracle's full
+    step, or, where a full step would take minutes (the 8192 x 28672
+    matrices), its momentum and one Newton-Schulz iteration, whose rate then
+    stands for the whole step's (labelled extrapolated).  Repeats until the
+    budget is spent.  Returns (record, refs): refs maps each matrix that ran
+    the full step to the oracle's W', M' and O (first repetition), for checking
+    the GPU's timed result."""
+    from oracle import muon_oracle as ORC
+    from tests import harness as H
+    threads, blas = blas_info()
     data = []
-    for (b, pi, mi) in samples:
+    for (pi, mi) in samples:
         W = H.decode(wl.matrix(pi, mi, "param"))
         G = H.decode(wl.matrix(pi, mi, "grad"))
         Mo = wl.matrix(pi, mi, "momentum").astype(np.float64)
-        data.append((b, W, G, Mo))
-        if max_matrices is not None and len(data) >= max_matrices:
-            break
-    # a full step on one very large matrix can take minutes here: then time the
-    # oracle's momentum + one Newton-Schulz step of it instead (same arithmetic)
-    b0 = data[0][0]
-    m0, n0 = min(b0.M, b0.N), max(b0.M, b0.N)
+        data.append(((pi, mi), wl.params[pi].matrix_shape, W, G, Mo))
+    (M0, N0) = data[0][1]
+    m0, n0 = min(M0, N0), max(M0, N0)
     est = hp.ns_steps * (4.0 * m0 * m0 * n0 + 2.0 * m0 ** 3) / 0.3e12
     steps = hp.ns_steps if est <= 2.5 * budget_s else 1
+    refs = {}
+    flops = 0.0
+    done = reps = 0
     t0 = time.perf_counter()
     while True:
-        for (b, W, G, Mo) in data:
-            kw = H.oracle_kwargs(hp, b.M, b.N)
+        for (key, (M, N), W, G, Mo) in data:
+            kw = H.oracle_kwargs(hp, M, N)
             kw["ns_steps"] = steps
             if steps != hp.ns_steps:
                 kw["coeffs"] = kw["coeffs"][:3]
-            ORC.muon_step_matrix(W, G, Mo, **kw)
-            m, n = min(b.M, b.N), max(b.M, b.N)
+            r = ORC.muon_step_matrix(W, G, Mo, **kw)
+            if reps == 0 and steps == hp.ns_steps:
+                refs[key] = {"W": r["W"], "M": r["M"], "O": r["O"]}
+            m, n = min(M, N), max(M, N)
             flops += steps * (4.0 * m * m * n + 2.0 * m ** 3)
             done += 1
         reps += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{len(data)} matrices of the workload x {reps} repetitions ({done} oracle steps of "
-                      f"{steps} Newton-Schulz iterations, {el:.1f} s, float64 NumPy)"}
+    what = (f"{len(data)} matrices of the workload x {reps} repetitions ({done} oracle steps of {steps} "
+            f"Newton-Schulz iterations, {el:.1f} s, float64 NumPy)")
+    rec = {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": what, "blas": blas, "host_cpus": os.cpu_count(),
+           "extrapolated": steps != hp.ns_steps}
+    if steps != hp.ns_steps:
+        rec["sample"] = ("extrapolated: " + what + f"; the rate of momentum plus one of the {hp.ns_steps} "
+                         "iterations on that matrix stands for the whole step")
+        rec["full_step_s_extrapolated"] = wl.nominal_ns_flops() / (flops / el) if flops else None
+    return rec, refs
+
+
+GOLDEN = {"large_8192x28672": os.path.join(ROOT, "tests", "golden", "large_8192x28672_samples.npz")}
+
+
+def check_plan(wl, plan):
+    """Matrices whose timed results are checked, and their reference:
+    ("golden", npz) -- oracle values stored at sampled positions -- or
+    ("oracle", None) -- the cpu_baseline leg's oracle results on the same
+    matrices (all matrices of skinny batches, the first matrix of each
+    distinct tiled batch shape)."""
+    if wl.name in GOLDEN and os.path.exists(GOLDEN[wl.name]):
+        gold = np.load(GOLDEN[wl.name])
+        meta = json.loads(str(gold["meta"]))
+        return [(pi, meta["matrix"]) for pi in meta["params"]], ("golden", gold)
+    ids, seen = [], set()
+    for b in plan.batches:
+        mats = [(pi, first + q) for (pi, first, num, off) in b.segments for q in range(num)]
+        if min(b.M, b.N) <= SKINNY_MAX_ROWS:
+            ids += mats
+        elif (b.M, b.N) not in seen:
+            ids.append(mats[0])
+        seen.add((b.M, b.N))
+    return ids, ("oracle", None)
+
+
+def snapshot(plan, bufs, ids, ref, o_bufs=None):
+    """Device copies of W' and M' (and O, from o_bufs {batch: [count, M, N]})
+    of the checked matrices, at the golden positions or whole, taken on the
+    current stream right after a step."""
+    import torch
+    snap = {}
+    for (pi, mi) in ids:
+        b, q = locate(plan, pi, mi)
+        ts = [bufs[b.index]["param"][q], bufs[b.index]["momentum"][q]]
+        if o_bufs is not None:
+            ts.append(o_bufs[b.index][q])
+        if ref[0] == "golden":
+            gold = ref[1]
+            idx = torch.from_numpy(gold[f"p{pi}_rows"] * b.N + gold[f"p{pi}_cols"]).to("cuda")
+            snap[(pi, mi)] = tuple(t.reshape(-1).index_select(0, idx) for t in ts)
+        else:
+            snap[(pi, mi)] = tuple(t.clone() for t in ts)
+    return snap
+
+
+def check_result(wl, plan, hp, snap, snap_o, host, ref, refs):
+    """The timed step's result against the oracle.
+
+    snap: W' and M' of the first timed repetition; snap_o: W', M' and O of
+    the same batches stepped once more (untimed, from the same restored
+    inputs) with O written out.  Checks: that repetition's W' and M' are
+    bitwise those of the timed one (the step is deterministic, so O is the
+    timed step's O); O within the relative Frobenius bound (3e-2 bf16 modes,
+    1e-5 fp32); M' elementwise within 1e-6 (|mu M| + |G|); W' - W within the
+    O bound plus the bf16 rounding of the stored W'."""
+    from tests import harness as H
+    out = {"reference": ref[0], "matrices": 0, "max_O_error": 0.0, "max_dW_error": 0.0,
+           "bound": H.o_tolerance(hp.precision), "bitwise_as_timed": True, "momentum_ok": True, "ok": True}
+    for (pi, mi), (Wd, Md) in snap.items():
+        Wo, Mo_, Od = snap_o[(pi, mi)]
+        arr = host[(pi, mi)]
+        if ref[0] == "golden":
+            gold = ref[1]
+            rows, cols = gold[f"p{pi}_rows"], gold[f"p{pi}_cols"]
+            W0 = H.decode(arr["param"][rows, cols])
+            G = H.decode(arr["grad"][rows, cols])
+            M0 = arr["momentum"][rows, cols].astype(np.float64)
+            Wref, Oref = gold[f"p{pi}_W"], gold[f"p{pi}_O"]
+        else:
+            if (pi, mi) not in refs:
+                continue
+            W0, G = H.decode(arr["param"]), H.decode(arr["grad"])
+            M0 = arr["momentum"].astype(np.float64)
+            Wref, Oref = refs[(pi, mi)]["W"], refs[(pi, mi)]["O"]
+        Wg, Mg, Og = H.to_host(Wd), H.to_host(Md), H.to_host(Od)
+        if not (np.array_equal(Wg, H.to_host(Wo)) and np.array_equal(Mg, H.to_host(Mo_))):
+            out["bitwise_as_timed"] = False
+        try:
+            H.check_momentum(Mg, M0, G, H.f32(hp.momentum))
+        except AssertionError:
+            out["momentum_ok"] = False
+        eo = H.rel_fro(Og.astype(np.float64), Oref)
+        dW_ref = Wref - W0
+        half_ulp = 0.0
+        if Wg.dtype == np.uint16:
+            half_ulp = np.linalg.norm(2.0 ** (np.floor(np.log2(np.maximum(np.abs(Wref), 1e-38))) - 8))
+        nref = np.linalg.norm(dW_ref)
+        e = H.rel_fro(H.decode(Wg) - W0, dW_ref)
+        slack = half_ulp / nref if nref > 0 else 0.0
+        out["max_O_error"] = max(out["max_O_error"], eo)
+        out["max_dW_error"] = max(out["max_dW_error"], e)
+        out["matrices"] += 1
+        if not (np.all(np.isfinite(Og)) and eo <= out["bound"] and e <= out["bound"] + slack + 1e-6):
+            out["ok"] = False
+    out["ok"] = bool(out["ok"] and out["momentum_ok"] and out["bitwise_as_timed"] and out["matrices"] > 0)
+    if ref[0] == "golden":
+        out["positions_per_matrix"] = int(len(ref[1][f"p{next(iter(snap))[0]}_rows"]))
+    return out
+
+
+def progress(msg: str) -> None:
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="fused_74x24x10240")
+    ap.add_argument("--steps", type=int, default=30, help="timed repetitions of the step")
+    ap.add_argument("--warmup", type=int, default=20, help="untimed repetitions before them")
+    ap.add_argument("--workload", default="large_8192x28672")
     ap.add_argument("--precision", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -318,13 +474,18 @@ def main():
                     help="timed steps as eager muon_step calls (default) or replays of one captured HIP graph")
     ap.add_argument("--skinny-kernel", type=int, default=0,
                     help="short sides <= 32: 0 or 1 Newton-Schulz in Gram space, 2 step by step")
-    ap.add_argument("--device-inputs", action="store_true",
-                    help="draw the inputs on the GPU with seeded torch generators (large workloads)")
+    ap.add_argument("--inputs", choices=["auto", "host", "device"], default="auto",
+                    help="host: every matrix from the seeded host generator; device: drawn on the GPU with "
+                         "seeded torch generators, the checked matrices from the host generator; auto: device "
+                         "above 2^28 elements")
+    ap.add_argument("--device-inputs", action="store_true", help="same as --inputs device")
     ap.add_argument("--streams", type=int, default=2,
                     help="spread the batches of a step over this many streams (muon_step_batches; at most the "
                          "number of batches; 1 = the batches in plan order on one stream)")
+    ap.add_argument("--trace-steps", type=int, default=0,
+                    help="steps of the one-stream traced pass (0: enough for about 2 s, at most --steps)")
     ap.add_argument("--reuse-shapes", action="store_true",
-                    help="batches of identical shape share generated input values (copied per batch)")
+                    help="host inputs: batches of identical shape share generated values (copied per batch)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -342,11 +503,27 @@ def main():
     hp = H.c_hparams(wl.hp, precision=prec)
     torch.cuda.set_device(0)
     plan = B.Plan([p.shape for p in wl.params], skinny_kernel=args.skinny_kernel)
-    if args.device_inputs:
+    inputs = "device" if args.device_inputs else args.inputs
+    if inputs == "auto":
+        inputs = "device" if wl.num_elements() > (1 << 28) else "host"
+    check_ids, ref = check_plan(wl, plan)
+    if inputs == "device":
         bufs = make_device_batches_gpu(wl, plan, dtype)
+        host = put_host_matrices(wl, plan, bufs, check_ids, dtype)
     else:
         bufs = make_device_batches(wl, plan, dtype, args.reuse_shapes)
+        host = {(pi, mi): {k: wl.matrix(pi, mi, k) for k in ("param", "grad", "momentum")} for (pi, mi) in check_ids}
+    torch.cuda.synchronize()
+    progress(f"inputs ready ({inputs}; {len(plan.batches)} batches, {len(check_ids)} checked matrices)")
+    # pristine copies: every repetition starts from the same W and M
+    pristine = [{"param": d["param"].clone(), "momentum": d["momentum"].clone()} for d in bufs]
     stream = torch.cuda.current_stream()
+
+    def restore():
+        for d, p in zip(bufs, pristine):
+            d["param"].copy_(p["param"])
+            d["momentum"].copy_(p["momentum"])
+
     # lr and decay from device scalars, so a captured step needs no recapture
     lr_wd = torch.tensor([hp.lr, hp.weight_decay], dtype=torch.float32, device="cuda")
     hp_run = dataclasses.replace(hp, lr_wd=lr_wd)
@@ -357,18 +534,8 @@ def main():
     side = [torch.cuda.Stream() for _ in range(nstreams - 1)]
     step_bufs = [(bufs[i]["param"], bufs[i]["grad"], bufs[i]["momentum"]) for i in bidx]
 
-    def step():
-        # the caller's part on the current stream (the capture stream while a
-        # graph is recorded), the other lanes on side streams
-        if nstreams == 1:
-            for b in plan.batches:
-                d = bufs[b.index]
-                B.muon_step(plan, b.index, d["param"], d["grad"], d["momentum"], hp_run, wss[0])
-        else:
-            B.muon_step_batches(plan, bidx, step_bufs, hp_run, wss, [None] + [s.cuda_stream for s in side])
-
-    # eager timing: the same calls with their arguments marshalled once, so the
-    # host enqueues a step well inside the GPU's time for it
+    # the step as deployed: every batch, its arguments marshalled once
+    # (muon_step per batch on one stream, or muon_step_batches over lanes)
     if nstreams == 1:
         prepared = [B.PreparedStep(plan, b.index, step_bufs[i], hp_run, wss[0], stream.cuda_stream)
                     for i, b in enumerate(plan.batches)]
@@ -380,49 +547,91 @@ def main():
         for call in prepared:
             call()
 
-    for _ in range(args.warmup):
-        step_prepared()
-    torch.cuda.synchronize()
     run = step_prepared
     if args.launch == "graph":
         graph = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(graph, stream=side):
-                step()
-        stream.wait_stream(side)
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                if nstreams == 1:
+                    for b in plan.batches:
+                        d = bufs[b.index]
+                        B.muon_step(plan, b.index, d["param"], d["grad"], d["momentum"], hp_run, wss[0])
+                else:
+                    B.muon_step_batches(plan, bidx, step_bufs, hp_run, wss, [None] + [s.cuda_stream for s in side])
+        stream.wait_stream(cap)
         run = graph.replay
-        run()   # one untimed replay
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    for _ in range(args.warmup):
+        restore()
+        run()
+    torch.cuda.synchronize()
+    progress(f"{args.warmup} warm-up repetitions done")
+
+    # timed repetitions: W and M restored before each (outside the events),
+    # the step between two events on the caller's stream (which the other
+    # lanes join); the first repetition's W' and M' are kept for the check
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    snap = None
     torch.cuda.synchronize()
     gc.disable()   # no collector pause inside the timed region
-    e0.record(stream)
-    for _ in range(args.steps):
+    w0 = time.perf_counter()
+    for r in range(args.steps):
+        restore()
+        ev[r][0].record(stream)
         run()
-    e1.record(stream)
+        ev[r][1].record(stream)
+        if r == 0:
+            snap = snapshot(plan, bufs, check_ids, ref)
     torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
     gc.enable()
-    ms = e0.elapsed_time(e1) / args.steps
+    per_rep = [a.elapsed_time(b) for a, b in ev]
+    ms = float(np.median(per_rep))
+    del ev
+    progress(f"{args.steps} timed repetitions: median {ms:.4f} ms")
 
-    # per-kernel times: a second pass of the same K steps with library launch tracing
-    launches = 0
-    for b in plan.batches:
-        launches += 64
-    B.muon_trace_start(args.steps * launches + 16)
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(args.steps):
-        step_prepared()
-    t1.record(stream)
+    # the checked batches once more, untimed, from the same restored inputs,
+    # with O written out (the deployed step writes none)
+    restore()
+    o_bufs = {}
+    for (pi, mi) in check_ids:
+        b, q = locate(plan, pi, mi)
+        if b.index in o_bufs:
+            continue
+        o_bufs[b.index] = torch.empty((b.count, b.M, b.N), dtype=torch.float32, device="cuda")
+        d = bufs[b.index]
+        ws = wss[lane_of[bidx.index(b.index)]] if nstreams > 1 else wss[0]
+        B.muon_step(plan, b.index, d["param"], d["grad"], d["momentum"], hp_run, ws, ns_out=o_bufs[b.index])
+    snap_o = snapshot(plan, bufs, check_ids, ref, o_bufs)
     torch.cuda.synchronize()
-    traced_ms = t0.elapsed_time(t1) / args.steps
+    del o_bufs
+
+    # per-kernel times: a pass on one stream (plan order) with library launch
+    # tracing, so each launch's time is its own and not shared with a lane
+    one = [B.PreparedStep(plan, b.index, step_bufs[i], hp_run, wss[lane_of[i]] if nstreams > 1 else wss[0],
+                          stream.cuda_stream) for i, b in enumerate(plan.batches)]
+    tsteps = args.trace_steps or max(1, min(args.steps, int(math.ceil(2000.0 / max(ms, 1e-3)))))
+    B.muon_trace_start(tsteps * 64 * len(plan.batches) + 16)
+    tr = []
+    for _ in range(tsteps):
+        restore()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for call in one:
+            call()
+        t1.record(stream)
+        tr.append((t0, t1))
+    torch.cuda.synchronize()
+    traced_ms = float(np.median([a.elapsed_time(b) for a, b in tr]))
     recs = B.muon_trace_stop()
+    progress(f"one-stream traced pass: {tsteps} steps, {traced_ms:.4f} ms per step")
     per = {}
     for name, t in recs:
         per.setdefault(name, []).append(t)
-    kernels = {k: {"launches_per_step": len(v) / args.steps, "avg_ms": float(np.mean(v)),
-                   "total_ms_per_step": float(np.sum(v)) / args.steps} for k, v in per.items()}
+    kernels = {k: {"launches_per_step": len(v) / tsteps, "avg_ms": float(np.mean(v)),
+                   "total_ms_per_step": float(np.sum(v)) / tsteps} for k, v in per.items()}
     dom = max(kernels, key=lambda k: kernels[k]["total_ms_per_step"])
     # algorithmic quantity of one launch of the dominant kernel, averaged over the
     # batches it runs on (its launches per batch per step follow from the path)
@@ -455,10 +664,12 @@ def main():
     roof["avg_launch_ms"] = kernels[dom]["avg_ms"]
     roof["algorithmic_per_launch"] = qty_per_launch
     roof["algorithmic_unit"] = "bytes" if unit == "B" else "flops"
+    roof["timing"] = "library HIP events at the kernel's start and end, one-stream traced pass"
 
     flops = wl.nominal_ns_flops()
     if hp.ns_steps != wl.hp.ns_steps:
         flops = flops / wl.hp.ns_steps * hp.ns_steps
+    exe = executed_flops(plan, hp.ns_steps)
     value = flops / (ms / 1e3) / 1e12
     cfg = {"workload": wl.name, "matrices": int(sum(b.count for b in plan.batches)), "launch": args.launch,
            "streams": nstreams, "lanes": lane_of,
@@ -466,15 +677,24 @@ def main():
            "kernels": [kernel_form(b, args.skinny_kernel, prec) for b in plan.batches],
            "param_dtype": dtype,
            "precision": prec, "ns_steps": hp.ns_steps, "coeffs": list(hp.coeffs),
-           "inputs": ("seeded synthetic, drawn on the GPU (torch generators)" if args.device_inputs else
-                      "seeded synthetic" + (", same-shape batches share values" if args.reuse_shapes else ""))}
+           "inputs": ("seeded synthetic: drawn on the GPU with seeded torch generators, the checked matrices "
+                      "from the seeded host generator" if inputs == "device" else
+                      "seeded synthetic (host generator)" + (", same-shape batches share values"
+                                                             if args.reuse_shapes else ""))}
     out = {"metric": "Muon-step NS TFLOP/s (bf16 MFMA)", "value": value, "unit": "TFLOP/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if prec != "f32" else "f32",
            "data": "synthetic", "config": cfg, "roofline": roof,
-           "detail": {"ns_frac_of_bf16_peak": value / BF16_PEAK_TFLOPS, "traced_ms_per_step": traced_ms,
-                      "executed_tflop_per_step": executed_flops(plan, hp.ns_steps) / 1e12,
+           "detail": {"timing": "median of the timed repetitions, each between HIP events on the caller's "
+                                "stream, W and M restored from device copies before each",
+                      "ms_per_rep": {"median": ms, "mean": float(np.mean(per_rep)), "min": float(np.min(per_rep)),
+                                     "max": float(np.max(per_rep))},
+                      "wall_s_timed_region": wall,
+                      "ns_frac_of_bf16_peak": value / BF16_PEAK_TFLOPS,
+                      "executed_tflop_per_step": exe / 1e12, "executed_tflops": exe / (ms / 1e3) / 1e12,
+                      "executed_frac_of_bf16_peak": exe / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
                       "nominal_tflop_per_step": flops / 1e12,
+                      "traced_ms_per_step_one_stream": traced_ms, "traced_steps": tsteps,
                       "kernels": kernels, "device": device_info()}}
 
     # plain device copy of known size (512 MiB read + 512 MiB written): the
@@ -497,6 +717,16 @@ def main():
         roof["frac_of_measured_copy"] = roof["achieved"] / copy_gbps
 
     if ms < 20.0:
+        # back to back: the same step repeated without restores (the
+        # accumulated state does not change the work)
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_bb = max(args.steps, 50)
+        a0.record(stream)
+        for _ in range(n_bb):
+            run()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        out["detail"]["back_to_back_ms_per_step"] = a0.elapsed_time(a1) / n_bb
         # cold steps: reading 1 GiB between steps evicts the 256 MB Infinity
         # Cache with clean lines, so each timed step starts from HBM (the warm
         # value above may be served partly from that cache) and pays for no
@@ -504,21 +734,34 @@ def main():
         cold = []
         flush = torch.cat([src.view(torch.int32), dst.view(torch.int32)])
         for _ in range(min(args.steps, 10)):
+            restore()
             flush.sum()
             a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a0.record(stream)
-            step_prepared()
+            run()
             a1.record(stream)
             torch.cuda.synchronize()
             cold.append(a0.elapsed_time(a1))
         out["detail"]["cold_ms_per_step"] = float(np.median(cold))
         out["detail"]["cold_tflops"] = flops / (np.median(cold) / 1e3) / 1e12
+        del flush
     del src, dst
-    flush = None
+    refs = {}
+    progress("GPU work done")
     if not args.no_cpu_baseline:
-        maxm = None if min(wl.params[0].matrix_shape) <= SKINNY_MAX_ROWS else 1
-        out["cpu_baseline"] = cpu_baseline(wl, plan, dtype, hp, args.cpu_budget, maxm)
+        # with stored oracle values the sample needs no reference: one matrix
+        sample = check_ids[:1] if ref[0] == "golden" else check_ids
+        out["cpu_baseline"], refs = cpu_baseline(wl, plan, hp, sample, args.cpu_budget)
+    if ref[0] == "golden" or refs:
+        out["detail"]["check"] = check_result(wl, plan, hp, snap, snap_o, host, ref, refs)
+    else:
+        out["detail"]["check"] = {"reference": None, "ok": None,
+                                  "note": "no oracle reference without the cpu_baseline leg"}
     print(json.dumps(out), flush=True)
+    if out["detail"]["check"]["ok"] is False:
+        print("bench: the timed step's result is outside the oracle bound: " + json.dumps(out["detail"]["check"]),
+              file=sys.stderr)
+        sys.exit(3)
 
 
 if __name__ == "__main__":
