@@ -533,17 +533,18 @@ class BatchedMuon:
         muon_step_batches(self.plan, [b.index for b in self.plan.batches], bufs, self.hp, self.workspaces,
                           [stream] + [s.cuda_stream for s in self.side_streams])
 
-    def capture_graph(self):
+    def capture_graph(self, ns_outs=None):
         """Record one step (every batch) into a HIP graph (torch.cuda.CUDAGraph)
-        and return it; graph.replay() then runs a step on the same buffers.
-        With hp.lr_wd set, the learning rate and decay written into that
-        device tensor before a replay are the ones the replay uses."""
+        and return it; graph.replay() then runs a step on the same buffers
+        (and writes O into ns_outs, one [count, M, N] fp32 tensor per batch,
+        if given).  With hp.lr_wd set, the learning rate and decay written
+        into that device tensor before a replay are the ones the replay uses."""
         import torch
         graph = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             with torch.cuda.graph(graph, stream=side):
-                self.step()
+                self.step(ns_outs)
         torch.cuda.current_stream().wait_stream(side)
         return graph

@@ -1,15 +1,20 @@
-"""muon_step_batches: the batches of a plan spread over several streams give
-bitwise the parameters, momentum and O of muon_step run on each batch in turn.
+"""muon_step_batches: the batches of a plan spread over several streams.
 
 The plan mixes tiled batches (128 x 128 and 256 x 256 tiles, a transposed
 one), skinny batches in both orientations and an expert tensor, with a batch
 cap that splits one shape into two batches, so lanes hold batches of every
-path.  Lanes run concurrently on separate workspaces; every kernel's
+path.  Inputs come from the seeded generator (workloads.py).  The
+multi-stream step is checked against the float64 oracle (tests/parity.py
+bars: O, M', W' per matrix) and bitwise against muon_step run on each batch
+in turn: lanes run concurrently on separate workspaces, and every kernel's
 reductions have a fixed order, so overlap changes no bit.
 """
 import pytest
 
 from matrix_optimizer_amd import binding as B
+from matrix_optimizer_amd import workloads as WL
+from tests import harness as H
+from tests import parity as P
 
 pytestmark = pytest.mark.gpu
 
@@ -39,20 +44,35 @@ def _filled(plan, dtype, seed):
     return out
 
 
+def _seeded(plan, wl):
+    """Per-batch (param, grad, momentum, O) device buffers holding the seeded
+    generator's values, and the stored host arrays they came from."""
+    import torch
+    dev, host = [], []
+    for b in plan.batches:
+        arr = H.batch_arrays(wl, b)
+        host.append(arr)
+        dev.append((H.to_device(arr["param"], WL.BF16), H.to_device(arr["grad"], WL.BF16),
+                    H.to_device(arr["momentum"], WL.F32),
+                    torch.zeros((b.count, b.M, b.N), dtype=torch.float32, device="cuda")))
+    return dev, host
+
+
 @pytest.mark.parametrize("prec", ["bf16", "bf16_x32", "f32"])
 @pytest.mark.parametrize("streams", [2, 3])
-def test_step_batches_matches_sequential(streams, prec):
+def test_step_batches_matches_oracle_and_sequential(streams, prec):
     import torch
     plan = B.Plan(SHAPES, max_batch_elems=CAP)
     assert len(plan.batches) >= 6 and {b.path for b in plan.batches} >= {0, 1}
     hp = B.HParams(precision=prec)
-    ref = _filled(plan, torch.bfloat16, 21)
+    wl = WL.small_workload("batches", SHAPES, momentum_recipe="normal", wid=510)
+    ref, host = _seeded(plan, wl)
     mine = [tuple(t.clone() for t in bufs) for bufs in ref]
     ws = torch.zeros(max(plan.workspace_bytes(b.index, prec) for b in plan.batches), dtype=torch.uint8,
                      device="cuda")
     for b in plan.batches:
-        P, G, M, O = ref[b.index]
-        B.muon_step(plan, b.index, P, G, M, hp, ws, ns_out=O)
+        Pb, G, M, O = ref[b.index]
+        B.muon_step(plan, b.index, Pb, G, M, hp, ws, ns_out=O)
 
     idx = [b.index for b in plan.batches]
     lane_of, need = B.plan_lanes(plan, idx, hp, streams)
@@ -64,6 +84,11 @@ def test_step_batches_matches_sequential(streams, prec):
     for b in plan.batches:
         for k, name in enumerate(["param", "grad", "momentum", "O"]):
             assert torch.equal(mine[b.index][k], ref[b.index][k]), (streams, prec, b.index, name)
+        Wp, Mp, O = (H.to_host(mine[b.index][k]) for k in (0, 2, 3))
+        arr = host[b.index]
+        for q in range(b.count):
+            P.check_matrix(arr["param"][q], arr["grad"][q], arr["momentum"][q], Wp[q], Mp[q], O[q], hp,
+                           f"streams {streams} {prec} batch {b.index} ({b.M}x{b.N}) matrix {q}")
 
 
 def test_step_batches_orders_after_and_before_caller_stream():

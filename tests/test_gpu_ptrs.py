@@ -1,6 +1,8 @@
 """muon_step_ptrs: a batch whose matrices sit at independent addresses (one
-pointer per matrix, no packing) gives bitwise the same parameters, momentum
-and O as muon_step on the same values packed into [count, M, N] buffers.
+pointer per matrix, no packing).  Inputs come from the seeded generator
+(workloads.py); the result is checked against the float64 oracle
+(tests/parity.py bars: O, M', W' per matrix) and bitwise against muon_step
+on the same values packed into [count, M, N] buffers.
 
 The per-matrix tensors are carved out of one allocation in reverse order with
 gaps, so their addresses are neither contiguous nor increasing.  Skinny (both
@@ -10,6 +12,9 @@ batches, expert tensors, bf16 and fp32 parameters, and all precisions.
 import pytest
 
 from matrix_optimizer_amd import binding as B
+from matrix_optimizer_amd import workloads as WL
+from tests import harness as H
+from tests import parity as P
 
 pytestmark = pytest.mark.gpu
 
@@ -43,33 +48,36 @@ def _scattered(count, M, N, dtype, gap=64):
 @pytest.mark.parametrize("prec", ["bf16", "bf16_x32", "f32"])
 @pytest.mark.parametrize("pdtype", ["bf16", "f32"])
 @pytest.mark.parametrize("name,shapes,kernel", CASES, ids=[c[0] for c in CASES])
-def test_step_ptrs_matches_packed(name, shapes, kernel, pdtype, prec):
+def test_step_ptrs_matches_oracle_and_packed(name, shapes, kernel, pdtype, prec):
     import torch
     dt = torch.bfloat16 if pdtype == "bf16" else torch.float32
+    wdt = WL.BF16 if pdtype == "bf16" else WL.F32
     plan = B.Plan(shapes, skinny_kernel=kernel)
     hp = B.HParams(precision=prec)
-    gen = torch.Generator(device="cuda").manual_seed(11)
+    wl = WL.small_workload(name, shapes, dtype=wdt, momentum_recipe="normal",
+                           wid=520 + [c[0] for c in CASES].index(name))
     for bi, b in enumerate(plan.batches):
         cnt, M, N = b.count, b.M, b.N
-        P = torch.randn(cnt, M, N, device="cuda", generator=gen).mul_(0.02).to(dt)
-        G = torch.randn(cnt, M, N, device="cuda", generator=gen).to(dt)
-        Mo = torch.randn(cnt, M, N, device="cuda", generator=gen)
+        arr = H.batch_arrays(wl, b)
+        Pk, G, Mo = H.to_device(arr["param"], wdt), H.to_device(arr["grad"], wdt), H.to_device(arr["momentum"], WL.F32)
         O = torch.zeros(cnt, M, N, device="cuda")
         ws = torch.zeros(plan.workspace_bytes(bi, prec), dtype=torch.uint8, device="cuda")
 
         ps, gs, ms, os_ = (_scattered(cnt, M, N, dt), _scattered(cnt, M, N, dt),
                            _scattered(cnt, M, N, torch.float32), _scattered(cnt, M, N, torch.float32))
         for i in range(cnt):
-            ps[i].copy_(P[i]); gs[i].copy_(G[i]); ms[i].copy_(Mo[i]); os_[i].zero_()
+            ps[i].copy_(Pk[i]); gs[i].copy_(G[i]); ms[i].copy_(Mo[i]); os_[i].zero_()
         ws2 = torch.zeros_like(ws)
 
-        B.muon_step(plan, bi, P, G, Mo, hp, ws, ns_out=O)
+        B.muon_step(plan, bi, Pk, G, Mo, hp, ws, ns_out=O)
         B.muon_step_ptrs(plan, bi, ps, gs, ms, hp, ws2, ns_out=os_)
         torch.cuda.synchronize()
         for i in range(cnt):
-            assert torch.equal(ps[i], P[i]), (name, bi, i, "param")
+            assert torch.equal(ps[i], Pk[i]), (name, bi, i, "param")
             assert torch.equal(ms[i], Mo[i]), (name, bi, i, "momentum")
             assert torch.equal(os_[i], O[i]), (name, bi, i, "O")
+            P.check_matrix(arr["param"][i], arr["grad"][i], arr["momentum"][i], H.to_host(ps[i]),
+                           H.to_host(ms[i]), H.to_host(os_[i]), hp, f"{name} {pdtype} {prec} batch {bi} matrix {i}")
 
 
 def test_step_ptrs_tables_reused_across_steps():

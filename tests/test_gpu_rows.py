@@ -1,7 +1,11 @@
 """muon_step_rows: logical matrices that are row-level views of fused
-physical parameters (the model-adapter views of HyperParallel-FSDP §6.6)
-give bitwise the parameters, momentum and O of muon_step on the same
-matrices packed, and leave every physical element outside them untouched.
+physical parameters (the model-adapter views of HyperParallel-FSDP §6.6).
+
+The physical parameters and gradients, and the logical matrices' momentum,
+come from the seeded generator (workloads.py).  The logical matrices' W', M'
+and O are checked against the float64 oracle (tests/parity.py bars) and
+bitwise against muon_step on the same matrices packed, and every physical
+element outside them must be untouched.
 
 Layouts: a fused QKV weight with heads interleaved, column splits with gaps
 (square, and tall on 256 x 256 tiles),
@@ -12,6 +16,9 @@ precisions, both skinny Newton-Schulz forms.
 import pytest
 
 from matrix_optimizer_amd import binding as B
+from matrix_optimizer_amd import workloads as WL
+from tests import harness as H
+from tests import parity as P
 
 pytestmark = pytest.mark.gpu
 
@@ -69,13 +76,17 @@ CASES = [
 @pytest.mark.parametrize("prec", ["bf16", "bf16_x32", "f32"])
 @pytest.mark.parametrize("pdtype", ["bf16", "f32"])
 @pytest.mark.parametrize("name,phys,split,mshape,kernels", CASES, ids=[c[0] for c in CASES])
-def test_step_rows_matches_packed(name, phys, split, mshape, kernels, pdtype, prec):
+def test_step_rows_matches_oracle_and_packed(name, phys, split, mshape, kernels, pdtype, prec):
+    import numpy as np
     import torch
     dt = torch.bfloat16 if pdtype == "bf16" else torch.float32
-    gen = torch.Generator(device="cuda").manual_seed(17)
+    wdt = WL.BF16 if pdtype == "bf16" else WL.F32
+    case = [c[0] for c in CASES].index(name)
     for kernel in kernels:
-        Wp = torch.randn(phys, device="cuda", generator=gen).mul_(0.02).to(dt)
-        Gp = torch.randn(phys, device="cuda", generator=gen).to(dt)
+        wl = WL.small_workload(name, [phys], dtype=wdt, wid=530 + 10 * case + kernel)
+        Wp = H.to_device(wl.tensor(0, "param"), wdt)
+        Gp = H.to_device(wl.tensor(0, "grad"), wdt)
+        assert Wp.dtype == dt and tuple(Wp.shape) == tuple(phys)
         W0 = Wp.clone()
         views_w, views_g = split(Wp), split(Gp)
         count = len(views_w)
@@ -84,20 +95,30 @@ def test_step_rows_matches_packed(name, phys, split, mshape, kernels, pdtype, pr
         plan = B.Plan([mshape] * count, skinny_kernel=kernel)
         assert len(plan.batches) == 1 and plan.batches[0].count == count
         hp = B.HParams(precision=prec)
-        P = torch.stack([v.reshape(M, N) for v in views_w])   # packed copies
+        Pk = torch.stack([v.reshape(M, N) for v in views_w])   # packed copies
         G = torch.stack([v.reshape(M, N) for v in views_g])
-        Mo = torch.randn(count, M, N, device="cuda", generator=gen)
+        wlm = WL.small_workload(name + "_momentum", [mshape] * count, momentum_recipe="normal",
+                                wid=531 + 10 * case + kernel)
+        M0 = np.stack([wlm.matrix(i, 0, "momentum") for i in range(count)])
+        Mo = H.to_device(M0, WL.F32)
+        W0s, G0s = H.to_host(Pk), H.to_host(G)
         Mo2 = Mo.clone()
         O, O2 = torch.zeros_like(Mo), torch.zeros_like(Mo)
         ws = torch.zeros(plan.workspace_bytes(0, prec), dtype=torch.uint8, device="cuda")
         ws2 = torch.zeros_like(ws)
-        B.muon_step(plan, 0, P, G, Mo, hp, ws, ns_out=O)
+        B.muon_step(plan, 0, Pk, G, Mo, hp, ws, ns_out=O)
         tw, tg = B.row_table(views_w), B.row_table(views_g)
         B.muon_step_rows(plan, 0, tw, tg, Mo2, hp, ws2, pdtype, pdtype, ns_out=O2)
         torch.cuda.synchronize()
         for i, v in enumerate(views_w):
-            assert torch.equal(v.reshape(M, N), P[i]), (name, kernel, i, "param")
+            assert torch.equal(v.reshape(M, N), Pk[i]), (name, kernel, i, "param")
         assert torch.equal(Mo2, Mo) and torch.equal(O2, O), (name, kernel)
+        # the logical matrices as updated in place in the physical parameter
+        Wl = H.to_host(torch.stack([v.reshape(M, N) for v in views_w]))
+        Ml, Ol = H.to_host(Mo2), H.to_host(O2)
+        for i in range(count):
+            P.check_matrix(W0s[i], G0s[i], M0[i], Wl[i], Ml[i], Ol[i], hp,
+                           f"{name} {pdtype} {prec} kernel {kernel} matrix {i}")
         # physical elements outside every logical matrix are untouched
         mask = torch.ones(phys, dtype=torch.bool, device="cuda")
         for v in split(mask):
