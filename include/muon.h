@@ -29,7 +29,9 @@
  * G.  The library never allocates, frees or
  * synchronises device memory or streams; its state is the host-side plan, plus
  * a few HIP events per device that muon_step_batches creates on first use
- * (fork and join markers, no device memory) and keeps until the process ends.
+ * (fork and join markers, no device memory) and keeps until the process ends,
+ * and the static device array of muon_step_noalloc (part of the loaded code,
+ * one copy per device).
  * All kernels are enqueued on `stream` (a hipStream_t; NULL = the null stream)
  * and the call returns without waiting for them.
  *
@@ -52,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 6
+#define MUON_ABI_VERSION 7
 
 typedef enum {
   MUON_OK = 0,
@@ -240,6 +242,24 @@ muon_status muon_step_ptrs(const muon_plan* plan, int32_t batch, const muon_batc
  * ns_out or the workspace. */
 muon_status muon_step_rows(const muon_plan* plan, int32_t batch, const muon_batch_rows* bufs,
                            const muon_hparams* hp, void* workspace, size_t workspace_bytes, void* stream);
+
+/* muon_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same step, with the workspace taken from a static device array of
+ * MUON_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs
+ * on until the process ends.  Nothing is allocated or freed, and no library
+ * routine that allocates is called.  A batch whose workspace
+ * (muon_workspace_bytes) exceeds that size returns
+ * MUON_ERR_WORKSPACE_TOO_SMALL before anything touches the device; other
+ * arguments are checked as by muon_step.  The first call on a device (with
+ * that device current) looks up the array's device address.  Every call on a
+ * device shares that device's array: calls that overlap on one device (other
+ * streams, other threads) race and give undefined results; calls ordered on
+ * one stream are fine, and nothing carries over from one call to the next.
+ * Results are bitwise those of muon_step. */
+#define MUON_NOALLOC_SCRATCH_BYTES (64u << 20)
+muon_status muon_step_noalloc(const muon_plan* plan, int32_t batch, const muon_batch_buffers* bufs,
+                              const muon_hparams* hp, void* stream);
 
 /* Several batches of one step on several streams.
  *

@@ -29,7 +29,10 @@ EXPORTED = ["muon_abi_version", "muon_status_str", "muon_plan_create", "muon_pla
             "muon_plan_num_batches", "muon_plan_batch_info", "muon_plan_segments",
             "muon_workspace_bytes", "muon_step", "muon_stage_momentum", "muon_stage_ns",
             "muon_stage_update", "muon_trace_start", "muon_trace_stop", "muon_plan_lanes",
-            "muon_step_batches", "muon_step_rows", "muon_ns_schedule"]
+            "muon_step_batches", "muon_step_rows", "muon_ns_schedule", "muon_step_noalloc"]
+
+# size of the static device workspace of muon_step_noalloc (MUON_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class muon_shape(C.Structure):
@@ -111,6 +114,9 @@ def lib():
     L.muon_step.restype = C.c_int32
     L.muon_step.argtypes = [C.c_void_p, C.c_int32, C.POINTER(muon_batch_buffers), C.POINTER(muon_hparams),
                             C.c_void_p, C.c_size_t, C.c_void_p]
+    L.muon_step_noalloc.restype = C.c_int32
+    L.muon_step_noalloc.argtypes = [C.c_void_p, C.c_int32, C.POINTER(muon_batch_buffers), C.POINTER(muon_hparams),
+                                    C.c_void_p]
     L.muon_step_ptrs.restype = C.c_int32
     L.muon_step_ptrs.argtypes = [C.c_void_p, C.c_int32, C.POINTER(muon_batch_ptrs), C.POINTER(muon_hparams),
                                  C.c_void_p, C.c_size_t, C.c_void_p]
@@ -283,6 +289,19 @@ def muon_step(plan: Plan, batch: int, param, grad, momentum, hp: HParams, worksp
     st = lib().muon_step(plan.handle, batch, C.byref(bufs), C.byref(hpc), _ptr(workspace),
                          workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "muon_step")
+
+
+def muon_step_noalloc(plan: Plan, batch: int, param, grad, momentum, hp: HParams, ns_out=None,
+                      stream=None) -> None:
+    """muon_step with the library's static device workspace (muon_step_noalloc):
+    no workspace argument, nothing allocated.  Raises MuonError (workspace too
+    small) for a batch needing more than NOALLOC_SCRATCH_BYTES.  Calls that
+    overlap on one device share that workspace and race."""
+    hpc, keep = hp.to_c()
+    bufs = muon_batch_buffers(_ptr(param), _dtype_code(param), _ptr(grad), _dtype_code(grad),
+                              _ptr(momentum), _ptr(ns_out))
+    _check(lib().muon_step_noalloc(plan.handle, batch, C.byref(bufs), C.byref(hpc), _stream(stream)),
+           "muon_step_noalloc")
 
 
 class PreparedStep:

@@ -15,7 +15,7 @@ BUILD = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libmuon.so")
 
-SOURCES = ["abi.cpp", "trace.cpp", "schedule.cpp", "skinny.hip", "tiled.hip"]
+SOURCES = ["abi.cpp", "trace.cpp", "schedule.cpp", "skinny.hip", "tiled.hip", "noalloc.hip"]
 ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.EXPORTED)
-    assert B.muon_abi_version() == 6
+    assert B.muon_abi_version() == 7
 
 
 def _cmp_plans(shapes, cap=0, order=0):
@@ -401,4 +401,27 @@ def test_step_rows_rejects_bad_args(plan_fb):
     assert call(pdt=5) == B.MUON_ERR_INVALID_ARG
     assert call(batch=9) == B.MUON_ERR_INVALID_ARG
     assert L.muon_step_rows(p.handle, 0, None, C.byref(hpc), fb.ptr("ws"), need, None) == 1
+    assert fb.untouched()
+
+
+# ---------------------------------------------------------------------------
+# muon_step_noalloc: refusals that happen before the device is touched
+# ---------------------------------------------------------------------------
+def test_step_noalloc_refuses_before_touching_anything():
+    if _gpu_visible():
+        pytest.skip("fake-pointer validation tests run only where no GPU is visible")
+    big = B.Plan([(4096, 4096)])   # workspace far above the static array
+    assert big.workspace_bytes(0, "bf16") > B.NOALLOC_SCRATCH_BYTES
+    fb = FakeBuffers(B.Plan([(24, 100)]))
+    hpc, keep = B.HParams().to_c()
+    bufs = B.muon_batch_buffers(fb.ptr("param"), 1, fb.ptr("grad"), 1, fb.ptr("mom"), None)
+    L = B.lib()
+    assert L.muon_step_noalloc(big.handle, 0, C.byref(bufs), C.byref(hpc), None) == B.MUON_ERR_WORKSPACE_TOO_SMALL
+    small = B.Plan([(24, 100)])
+    assert L.muon_step_noalloc(small.handle, 1, C.byref(bufs), C.byref(hpc), None) == B.MUON_ERR_INVALID_ARG
+    assert L.muon_step_noalloc(None, 0, C.byref(bufs), C.byref(hpc), None) == B.MUON_ERR_INVALID_ARG
+    assert L.muon_step_noalloc(small.handle, 0, None, C.byref(hpc), None) == B.MUON_ERR_INVALID_ARG
+    assert L.muon_step_noalloc(small.handle, 0, C.byref(bufs), None, None) == B.MUON_ERR_INVALID_ARG
+    hpc.precision = 9
+    assert L.muon_step_noalloc(small.handle, 0, C.byref(bufs), C.byref(hpc), None) == B.MUON_ERR_INVALID_ARG
     assert fb.untouched()
