@@ -210,21 +210,44 @@ const char* muon_status_str(muon_status s);
 muon_status muon_plan_create(const muon_shape* shapes, int32_t n, const muon_plan_options* opt,
                              muon_plan** out);
 void muon_plan_destroy(muon_plan* plan);
+/* The plan's batches: one per chunk of a core-shape group (HyperParallel-FSDP
+ * §6.6, Figure 10(a): the [A,B], [A,1,B] and [N,A,B] parameters of one (A,B)
+ * group are merged into one batched tensor; the memory-safe cap splits a
+ * group into chunks).  muon_plan_batch_info: the batch's stored matrix shape,
+ * its matrix count, the transpose-first flag (rows > cols, §6.6) and its
+ * kernel family; INVALID_ARG for a bad index or a null out.
+ * muon_plan_segments: the runs of consecutive matrices of one parameter that
+ * make up the batch, in the order the matrices sit in the batch buffers
+ * (parameter i's matrices at elem_offset), copied into out[0 .. capacity-1];
+ * INVALID_ARG for a bad index, a null out or a negative capacity.
+ * muon_plan_num_batches returns -1 for a null plan. */
 int32_t muon_plan_num_batches(const muon_plan* plan);
 muon_status muon_plan_batch_info(const muon_plan* plan, int32_t batch, muon_batch_info* out);
-/* Copies up to `capacity` segments of a batch into out. */
 muon_status muon_plan_segments(const muon_plan* plan, int32_t batch, muon_segment* out, int32_t capacity);
 
 /* Device workspace (bytes, a multiple of 256) that muon_step / muon_stage_ns
- * need for this batch at this precision.  Pure host computation. */
+ * need for this batch at this precision: the batched iterate X (and its fp32
+ * master with MUON_PREC_BF16_X32), the Gram matrix A, the polynomial B and the
+ * norm partials, sized once per batch as HyperParallel-FSDP §6.6 sizes the
+ * workspace of one batched invocation (memory-safe batching keeps it bounded
+ * by the 2^29-element cap).  Pure host computation; INVALID_ARG for a bad
+ * index, precision or a null out. */
 muon_status muon_workspace_bytes(const muon_plan* plan, int32_t batch, muon_precision precision,
                                  size_t* out);
 
-/* One full Muon step on one batch: momentum, normalisation, transpose-first,
- * K Newton-Schulz steps, decay and update.  workspace: device memory of at
- * least muon_workspace_bytes, 256-byte aligned, owned by the caller and not
- * shared with a concurrent call.  Buffers must not overlap one another or the
- * workspace; device pointers must be 16-byte aligned. */
+/* One full Muon step on one batch, the owner-side step of the pages: the
+ * momentum recurrence and Nesterov direction (DMuon-2 §2.1), normalisation
+ * and K quintic Newton-Schulz steps (HyperParallel-FSDP §2.3, Eq. (1)) run
+ * batched over the merged [count, M, N] tensor with transpose-first
+ * (HyperParallel-FSDP §6.6; each matrix keeps its own norm, §6.3), then
+ * decoupled decay and the scaled update (HyperParallel-FSDP §6.3 / §6.4 step
+ * 4, §2.3).  workspace: device memory of at least muon_workspace_bytes,
+ * 256-byte aligned, owned by the caller and not shared with a concurrent call.
+ * Buffers must not overlap one another or the workspace; device pointers must
+ * be 16-byte aligned.  Errors: INVALID_ARG (null or misaligned pointer, bad
+ * index or dtype, overlap, an hparam out of range), WORKSPACE_TOO_SMALL
+ * (nothing launched in either case); HIP if a launch is refused (kernels
+ * already enqueued for the batch may have run). */
 muon_status muon_step(const muon_plan* plan, int32_t batch, const muon_batch_buffers* bufs,
                       const muon_hparams* hp, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -287,7 +310,9 @@ muon_status muon_step_noalloc(const muon_plan* plan, int32_t batch, const muon_b
  * muon_step on each batch.  Batch indices must be distinct; every buffer and
  * every used lane's workspace (workspaces[l] may be NULL for a lane with no
  * batch) must be disjoint from all others, since lanes run concurrently.
- * A HIP error part-way returns MUON_ERR_HIP with some batches enqueued.
+ * A HIP error part-way returns MUON_ERR_HIP with some batches enqueued; every
+ * lane that was forked is still joined into streams[0] first, so work enqueued
+ * there afterwards follows what was enqueued, and a capture still ends cleanly.
  * Capturable into a HIP graph on streams[0] (the fork and join are event
  * records and waits). */
 #define MUON_MAX_STREAMS 8
@@ -299,9 +324,16 @@ muon_status muon_step_batches(const muon_plan* plan, int32_t n, const int32_t* b
 
 /* Stage entry points, same validation.  They run the stages of muon_step one
  * at a time so each can be checked on its own.
- *  momentum: M' = mu M + G (in place) and u_out = U (fp32 [count,M,N]).
- *  ns:       o_out = O from u_in (both fp32 [count,M,N], W's orientation).
- *  update:   W' = W - lr (wd W + s O) from o_in (fp32 [count,M,N]). */
+ *  momentum: M' = mu M + G (in place) and u_out = U (fp32 [count,M,N]): the
+ *            momentum recurrence and its Nesterov direction, DMuon-2 §2.1.
+ *  ns:       o_out = O from u_in (both fp32 [count,M,N], W's orientation):
+ *            normalisation, transpose-first and the K quintic steps,
+ *            HyperParallel-FSDP §2.3, Eq. (1) and §6.6.
+ *  update:   W' = W - lr (wd W + s O) from o_in (fp32 [count,M,N]): decoupled
+ *            decay and the RMS-scaled update, HyperParallel-FSDP §6.3 / §6.4
+ *            step 4 and §2.3.
+ * Buffers are device memory owned by the caller, contiguous and 16-byte
+ * aligned, and must not overlap; errors as for muon_step. */
 muon_status muon_stage_momentum(const muon_plan* plan, int32_t batch, const void* grad, muon_dtype grad_dtype,
                                 float* momentum, float* u_out, const muon_hparams* hp, void* stream);
 muon_status muon_stage_ns(const muon_plan* plan, int32_t batch, const float* u_in, float* o_out,
@@ -341,6 +373,14 @@ muon_status muon_stage_update(const muon_plan* plan, int32_t batch, void* param,
  * INTERNAL if the construction fails to level (not seen in the ranges above). */
 muon_status muon_ns_schedule(int32_t steps, double lower, double safety, double cushion, float* coeffs,
                              double* bounds);
+
+/* Failure injection, for tests of the error paths: the (n + 1)-th batch
+ * dispatch from now on (by any step call, on any thread) returns MUON_ERR_HIP
+ * without launching anything, as a refused launch would, and the injection
+ * is then off; n < 0 turns it off.  It lets a test drive a multi-stream step
+ * into its part-way failure (muon_step_batches joins every forked lane before
+ * returning) without a real launch failure. */
+void muon_debug_fail_dispatch(int32_t n);
 
 /* Launch tracing, for measurement.  muon_trace_start(n) makes the next (at
  * most n) kernel launches of the step and stage calls carry a start and a

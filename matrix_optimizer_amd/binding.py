@@ -29,7 +29,8 @@ EXPORTED = ["muon_abi_version", "muon_status_str", "muon_plan_create", "muon_pla
             "muon_plan_num_batches", "muon_plan_batch_info", "muon_plan_segments",
             "muon_workspace_bytes", "muon_step", "muon_stage_momentum", "muon_stage_ns",
             "muon_stage_update", "muon_trace_start", "muon_trace_stop", "muon_plan_lanes",
-            "muon_step_batches", "muon_step_rows", "muon_ns_schedule", "muon_step_noalloc"]
+            "muon_step_batches", "muon_step_rows", "muon_ns_schedule", "muon_step_noalloc",
+            "muon_debug_fail_dispatch"]
 
 # size of the static device workspace of muon_step_noalloc (MUON_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -142,6 +143,8 @@ def lib():
     L.muon_ns_schedule.restype = C.c_int32
     L.muon_ns_schedule.argtypes = [C.c_int32, C.c_double, C.c_double, C.c_double, C.POINTER(C.c_float),
                                    C.POINTER(C.c_double)]
+    L.muon_debug_fail_dispatch.restype = None
+    L.muon_debug_fail_dispatch.argtypes = [C.c_int32]
     L.muon_trace_start.restype = C.c_int32
     L.muon_trace_start.argtypes = [C.c_int32]
     L.muon_trace_stop.restype = C.c_int32
@@ -347,11 +350,22 @@ class PreparedStep:
             raise MuonError(st, self._where)
 
 
+def _check_aligned(addrs, what: str) -> None:
+    """The kernels move 16-byte runs: every address must be 16-byte aligned."""
+    bad = [a for a in addrs if a % 16]
+    if bad:
+        raise ValueError(f"{what}: {len(bad)} address(es) not 16-byte aligned (first {bad[0]:#x}); "
+                         "the kernels issue 16-byte loads and stores there")
+
+
 def pointer_table(tensors, device="cuda"):
     """Device array (int64 tensor) of the data pointers of `tensors`, one per
-    matrix, for muon_step_ptrs.  Keep it alive until the step has run."""
+    matrix, for muon_step_ptrs.  Every pointer must be 16-byte aligned
+    (ValueError otherwise).  Keep it alive until the step has run."""
     import torch
-    return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
+    ptrs = [t.data_ptr() for t in tensors]
+    _check_aligned(ptrs, "pointer_table")
+    return torch.tensor(ptrs, dtype=torch.int64, device=device)
 
 
 def muon_step_ptrs(plan: Plan, batch: int, params, grads, momenta, hp: HParams, workspace,
@@ -397,7 +411,10 @@ def row_addresses(t):
     """Start address of every row of t (an int64 CPU tensor, leading indices in
     row-major order).  t may be any strided view whose last dimension is
     contiguous: a slice of rows, a range of columns, every k-th row, or one
-    part of an interleaved layout such as W.view(heads, 3, d, H)[:, 0]."""
+    part of an interleaved layout such as W.view(heads, 3, d, H)[:, 0].  Every
+    row must start at a 16-byte aligned address (for a column range of bf16
+    rows: a first column that is a multiple of 8, and a row stride that keeps
+    it so); ValueError otherwise."""
     import torch
     if t.dim() < 2 or (t.stride(-1) != 1 and t.shape[-1] > 1):
         raise ValueError("row_addresses: rows must be contiguous (stride 1 along the last dimension)")
@@ -407,7 +424,10 @@ def row_addresses(t):
         shape = [1] * len(lead)
         shape[d] = size
         addr = addr + (torch.arange(size, dtype=torch.int64) * (stride * t.element_size())).view(shape)
-    return addr.reshape(-1)
+    addr = addr.reshape(-1)
+    if bool((addr % 16 != 0).any()):
+        _check_aligned(addr.tolist(), "row_addresses")
+    return addr
 
 
 def row_table(views, device="cuda"):
@@ -491,6 +511,13 @@ def muon_stage_update(plan: Plan, batch: int, param, o_in, hp: HParams, stream=N
     hpc, keep = hp.to_c()
     _check(lib().muon_stage_update(plan.handle, batch, _ptr(param), _dtype_code(param), _ptr(o_in),
                                    C.byref(hpc), _stream(stream)), "muon_stage_update")
+
+
+def muon_debug_fail_dispatch(n: int) -> None:
+    """Failure injection for tests of the error paths: the (n + 1)-th batch
+    dispatch from now returns MUON_ERR_HIP without launching anything (then
+    the injection is off); n < 0 turns it off."""
+    lib().muon_debug_fail_dispatch(int(n))
 
 
 def muon_trace_start(max_launches: int) -> None:

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <map>
@@ -185,7 +186,17 @@ const muon_plan::Batch* get_batch(const muon_plan* plan, int32_t batch) {
 
 muon_status hip_status(hipError_t e) { return e == hipSuccess ? MUON_OK : MUON_ERR_HIP; }
 
+// Failure injection (muon_debug_fail_dispatch): dispatches left before one
+// fails without launching; -1 = off.
+std::atomic<int> g_fail_after{-1};
+
 hipError_t dispatch(const StepArgs& a, const WsLayout& L) {
+  for (int n = g_fail_after.load(std::memory_order_relaxed); n >= 0;) {
+    if (g_fail_after.compare_exchange_weak(n, n - 1, std::memory_order_relaxed)) {
+      if (n == 0) return hipErrorInvalidValue;
+      break;
+    }
+  }
   switch (L.path) {
     case PATH_SKINNY_GRAM:
     case PATH_SKINNY_FUSED:
@@ -573,17 +584,35 @@ muon_status muon_step_batches(const muon_plan* plan, int32_t n, const int32_t* b
     if ((e = device_events(dev, size_t(nstreams), ev)) != hipSuccess) return MUON_ERR_HIP;
     const hipStream_t s0 = reinterpret_cast<hipStream_t>(streams[0]);
     if ((e = hipEventRecord((*ev)[0], s0)) != hipSuccess) return MUON_ERR_HIP;
-    for (int32_t l = 1; l < nstreams; ++l)
-      if (need[l] > 0 && (e = hipStreamWaitEvent(reinterpret_cast<hipStream_t>(streams[l]), (*ev)[0], 0)) != hipSuccess)
-        return MUON_ERR_HIP;
-    for (int32_t l = 0; l < nstreams; ++l)
-      if ((l == 0 || need[l] > 0) && (e = run_lane(l)) != hipSuccess) return MUON_ERR_HIP;
+    // Every lane that waited on the fork is joined back into streams[0], also
+    // when a launch fails part-way: eagerly, later work on the caller's stream
+    // stays ordered after what the lanes did enqueue, and under graph capture
+    // no side stream is left unjoined.
+    std::vector<char> forked(size_t(nstreams), 0);
+    auto join = [&]() -> hipError_t {
+      hipError_t first = hipSuccess;
+      for (int32_t l = 1; l < nstreams; ++l) {
+        if (!forked[l]) continue;
+        hipError_t r = hipEventRecord((*ev)[l], reinterpret_cast<hipStream_t>(streams[l]));
+        if (r == hipSuccess) r = hipStreamWaitEvent(s0, (*ev)[l], 0);
+        if (r != hipSuccess && first == hipSuccess) first = r;
+      }
+      return first;
+    };
     for (int32_t l = 1; l < nstreams; ++l) {
       if (need[l] == 0) continue;
-      if ((e = hipEventRecord((*ev)[l], reinterpret_cast<hipStream_t>(streams[l]))) != hipSuccess) return MUON_ERR_HIP;
-      if ((e = hipStreamWaitEvent(s0, (*ev)[l], 0)) != hipSuccess) return MUON_ERR_HIP;
+      if ((e = hipStreamWaitEvent(reinterpret_cast<hipStream_t>(streams[l]), (*ev)[0], 0)) != hipSuccess) {
+        (void)join();
+        return MUON_ERR_HIP;
+      }
+      forked[l] = 1;
     }
-    return MUON_OK;
+    for (int32_t l = 0; l < nstreams; ++l)
+      if ((l == 0 || need[l] > 0) && (e = run_lane(l)) != hipSuccess) {
+        (void)join();
+        return MUON_ERR_HIP;
+      }
+    return join() == hipSuccess ? MUON_OK : MUON_ERR_HIP;
   } catch (const std::bad_alloc&) {
     return MUON_ERR_NO_MEMORY;
   }
@@ -643,5 +672,7 @@ muon_status muon_stage_update(const muon_plan* plan, int32_t batch, void* param,
   a.o_in = o_in;
   return hip_status(run_update_only(a));
 }
+
+void muon_debug_fail_dispatch(int32_t n) { g_fail_after.store(n < 0 ? -1 : n, std::memory_order_relaxed); }
 
 }  // extern "C"

@@ -6,9 +6,26 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <vector>
 
 namespace muon {
+
+// Per-device value that every caller computes the same way (resident
+// workgroups of a kernel): read and published atomically, so concurrent first
+// calls on a device race benignly (each stores the same value).
+constexpr int kMaxDevices = 64;
+template <class F>
+int per_device_cached(std::atomic<int> (&cache)[kMaxDevices], F compute) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  int v = cache[dev].load(std::memory_order_acquire);
+  if (v == 0) {
+    v = compute(dev);
+    cache[dev].store(v, std::memory_order_release);
+  }
+  return v;
+}
 
 enum Dtype { DT_F32 = 0, DT_BF16 = 1 };
 enum Prec { PREC_BF16 = 0, PREC_BF16_X32 = 1, PREC_F32 = 2 };

@@ -1394,18 +1394,16 @@ hipError_t launch_iters(const StepArgs& a, const WsLayout& L, int vec) {
 // workgroups (one per CU), but no more than give every wave a unit.
 template <int MODE, typename PT, bool ROWS>
 int64_t fused_groups(int64_t count, int64_t upm) {
-  static int per_dev[64] = {0};   // resident workgroups of this kernel per device
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (per_dev[dev] == 0) {
+  static std::atomic<int> per_dev[kMaxDevices];   // resident workgroups of this kernel per device
+  const int slots = per_device_cached(per_dev, [](int dev) {
     int cus = 0, blocks = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, sk_ns_apply<MODE, PT, ROWS>, FW_THREADS, 0) !=
             hipSuccess || blocks <= 0)
       blocks = 1;
-    per_dev[dev] = cus * blocks;
-  }
-  int64_t R = per_dev[dev] / count;
+    return cus * blocks;
+  });
+  int64_t R = slots / count;
   const int64_t most = (upm + FW_WAVES - 1) / FW_WAVES;
   if (R > most) R = most;
   return R < 1 ? 1 : R;

@@ -20,6 +20,8 @@
 //
 // Operands are bf16 on v_mfma_f32_32x32x16_bf16 with fp32 accumulation, or
 // fp32 on v_mfma_f32_32x32x2f32 for the check path.
+#include <cmath>
+
 #include "common.h"
 #include "internal.h"
 
@@ -1066,18 +1068,15 @@ tl_update(PT* __restrict__ W, const float* __restrict__ O, int64_t total, float 
 // tiles.
 template <class C, int EPI, typename PT, bool ROWS = false>
 unsigned gemm_grid(int64_t tiles) {
-  static int per_dev[64] = {0};   // resident workgroups of this kernel per device
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (per_dev[dev] == 0) {
+  static std::atomic<int> per_dev[kMaxDevices];   // resident workgroups of this kernel per device
+  const int64_t slots = per_device_cached(per_dev, [](int dev) {
     int cus = 0, blocks = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, tl_gemm<C, EPI, PT, ROWS>, C::THREADS, 0) != hipSuccess ||
         blocks <= 0)
       blocks = 1;
-    per_dev[dev] = cus * blocks;
-  }
-  const int64_t slots = per_dev[dev];
+    return cus * blocks;
+  });
   return (unsigned)(tiles < slots ? tiles : slots);
 }
 
@@ -1100,8 +1099,10 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
     const float ca = a.coeffs[3 * k], cb = a.coeffs[3 * k + 1], cc = a.coeffs[3 * k + 2];
     // bf16 products without the fp32 master: the poly takes b A from its bf16
     // A operand tiles in LDS (as the products' A is bf16 anyway), so the Gram
-    // writes no fp32 copy of A
-    const bool a_in_lds = sizeof(OP) == 2 && X32 == nullptr && cc != 0.f;
+    // writes no fp32 copy of A.  It accumulates A A + (b / c) A and scales by
+    // c, so c must not be tiny next to b (|b / c| <= 1e6 keeps the sum far
+    // from overflow, |A| being about 1); otherwise b A comes from fp32 A.
+    const bool a_in_lds = sizeof(OP) == 2 && X32 == nullptr && cc != 0.f && std::fabs(cc) >= 1e-6f * std::fabs(cb);
     OP* Xk = C::DIRECT ? Xb[k & 1] : X;
     GemmArgs g = {};
     // Gram: A = X X^T

@@ -4,6 +4,7 @@
 // without an external profiler.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -18,7 +19,7 @@ struct Rec {
 };
 
 std::mutex g_mu;
-bool g_on = false;
+std::atomic<bool> g_on{false};   // read without the lock on every launch
 std::vector<hipEvent_t> g_pool;
 std::vector<Rec> g_recs;
 size_t g_next = 0;
@@ -28,9 +29,9 @@ size_t g_next = 0;
 namespace muon {
 
 bool trace_take(const char* name, hipEvent_t* start, hipEvent_t* stop) {
-  if (!g_on) return false;
+  if (!g_on.load(std::memory_order_acquire)) return false;
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_on || g_next + 2 > g_pool.size()) return false;
+  if (!g_on.load(std::memory_order_relaxed) || g_next + 2 > g_pool.size()) return false;
   Rec r{name, g_pool[g_next], g_pool[g_next + 1]};
   g_next += 2;
   g_recs.push_back(r);
@@ -54,14 +55,14 @@ muon_status muon_trace_start(int32_t max_launches) {
   g_recs.clear();
   g_recs.reserve(max_launches);
   g_next = 0;
-  g_on = true;
+  g_on.store(true, std::memory_order_release);
   return MUON_OK;
 }
 
 int32_t muon_trace_stop(float* ms, const char** names, int32_t capacity) {
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_on) return -1;
-  g_on = false;
+  if (!g_on.load(std::memory_order_relaxed)) return -1;
+  g_on.store(false, std::memory_order_release);
   int32_t n = 0;
   for (const Rec& r : g_recs) {
     if (n < capacity) {

@@ -425,3 +425,27 @@ def test_step_noalloc_refuses_before_touching_anything():
     hpc.precision = 9
     assert L.muon_step_noalloc(small.handle, 0, C.byref(bufs), C.byref(hpc), None) == B.MUON_ERR_INVALID_ARG
     assert fb.untouched()
+
+
+# ---------------------------------------------------------------------------
+# host-built address tables refuse addresses the kernels cannot take
+# ---------------------------------------------------------------------------
+def test_row_and_pointer_tables_refuse_misaligned_addresses():
+    import torch
+    base = torch.zeros(64, 64, dtype=torch.bfloat16)
+    assert base.data_ptr() % 16 == 0
+    # a column range starting at column 3 of bf16 rows: rows start 6 bytes in
+    with pytest.raises(ValueError, match="16-byte"):
+        B.row_addresses(base[:, 3:27])
+    # starting at column 8 (16 bytes) with a 128-byte row stride is fine
+    addr = B.row_addresses(base[:, 8:32])
+    assert bool((addr % 16 == 0).all()) and addr.numel() == 64
+    # an odd row stride misaligns every other row
+    odd = torch.zeros(64 * 33, dtype=torch.bfloat16)[: 64 * 33].view(64, 33)
+    with pytest.raises(ValueError, match="16-byte"):
+        B.row_addresses(odd[:, 0:24])
+    flat = torch.zeros(4096, dtype=torch.float32)
+    mats = [flat[i * 256:(i + 1) * 256].view(16, 16) for i in range(3)]
+    assert B.pointer_table(mats, device="cpu").numel() == 3
+    with pytest.raises(ValueError, match="16-byte"):
+        B.pointer_table([flat[1:257].view(16, 16)], device="cpu")

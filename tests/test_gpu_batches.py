@@ -198,3 +198,68 @@ def test_moe_workload_two_streams_bitwise():
     for b in plan.batches:
         assert torch.equal(mine[b.index][0], ref[b.index][0]), (b.index, "param")
         assert torch.equal(mine[b.index][2], ref[b.index][2]), (b.index, "momentum")
+
+
+def test_step_batches_failure_part_way_joins_lanes():
+    """A launch that fails part-way through a two-stream step (forced from the
+    host with muon_debug_fail_dispatch: lane 1's second batch is refused)
+    returns MUON_ERR_HIP after joining every forked lane into the caller's
+    stream: work enqueued there afterwards sees lane 1's first batch
+    complete, and the same failure under graph capture still lets the
+    capture end cleanly."""
+    import torch
+    plan = B.Plan(SHAPES, max_batch_elems=CAP)
+    hp = B.HParams()
+    idx = [b.index for b in plan.batches]
+    lane_of, need = B.plan_lanes(plan, idx, hp, 2)
+    lane1 = [i for i in range(len(idx)) if lane_of[i] == 1]
+    lane0 = [i for i in range(len(idx)) if lane_of[i] == 0]
+    assert len(lane1) >= 2
+    wss = [torch.zeros(n, dtype=torch.uint8, device="cuda") for n in need]
+    side = torch.cuda.Stream()
+    ref = _filled(plan, torch.bfloat16, 31)
+    mine = [tuple(t.clone() for t in bufs) for bufs in ref]
+    ws = torch.zeros(max(need), dtype=torch.uint8, device="cuda")
+    for b in plan.batches:   # the per-batch results
+        Pb, G, M, O = ref[b.index]
+        B.muon_step(plan, b.index, Pb, G, M, hp, ws, ns_out=O)
+    torch.cuda.synchronize()
+    try:
+        # lane 0's batches dispatch first, then lane 1's: fail lane 1's second
+        B.muon_debug_fail_dispatch(len(lane0) + 1)
+        with pytest.raises(B.MuonError) as ei:
+            B.muon_step_batches(plan, idx, mine, hp, wss, [None, side.cuda_stream])
+        assert ei.value.status == B.MUON_ERR_HIP
+        # read back on the caller's stream, without synchronising first: every
+        # lane-0 batch and exactly one lane-1 batch (its first) are complete
+        got = [tuple(t.clone() for t in mine[i]) for i in range(len(idx))]
+        torch.cuda.current_stream().synchronize()
+        done = [all(torch.equal(got[i][k], ref[i][k]) for k in (0, 2, 3)) for i in range(len(idx))]
+        assert all(done[i] for i in lane0)
+        assert sum(done[i] for i in lane1) == 1
+        # the same failure while capturing: the capture must still end cleanly
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        B.muon_debug_fail_dispatch(len(lane0) + 1)
+        with pytest.raises(B.MuonError):
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(graph, stream=cap):
+                    B.muon_step_batches(plan, idx, mine, hp, wss, [None, side.cuda_stream])
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        del graph
+    finally:
+        B.muon_debug_fail_dispatch(-1)
+    # the library and the streams still work: a full step matches the per-batch calls
+    ref2 = _filled(plan, torch.bfloat16, 32)
+    mine2 = [tuple(t.clone() for t in bufs) for bufs in ref2]
+    for b in plan.batches:
+        Pb, G, M, O = ref2[b.index]
+        B.muon_step(plan, b.index, Pb, G, M, hp, ws, ns_out=O)
+    B.muon_step_batches(plan, idx, mine2, hp, wss, [None, side.cuda_stream])
+    torch.cuda.synchronize()
+    for b in plan.batches:
+        for k in range(4):
+            assert torch.equal(mine2[b.index][k], ref2[b.index][k]), (b.index, k)

@@ -104,7 +104,7 @@ def test_small_shapes(name, kernel, dtype, prec):
 # hyperparameter variants
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("shapes", [[(24, 500)], [(160, 200)]], ids=["skinny", "tiled"])
-@pytest.mark.parametrize("variant", ["one_step", "schedule", "c_zero", "no_nesterov", "no_scale", "eps_zero",
+@pytest.mark.parametrize("variant", ["one_step", "schedule", "c_zero", "c_tiny", "no_nesterov", "no_scale", "eps_zero",
                                      "seven_steps", "minimax_schedule"])
 def test_hparam_variants(shapes, variant):
     wl = WL.small_workload("v", shapes, momentum_recipe="normal", wid=300)
@@ -114,6 +114,9 @@ def test_hparam_variants(shapes, variant):
         # a cubic step (c = 0) between quintic ones: the tiled bf16 poly then
         # takes b A from the fp32 copy of A instead of its operand tiles
         "c_zero": dict(ns_steps=3, coeffs=(3.4445, -4.7750, 2.0315, 1.5, -0.5, 0.0, 3.4445, -4.7750, 2.0315)),
+        # a nonzero but subnormal c: b / c would overflow, so the same fp32-A
+        # fallback must take it
+        "c_tiny": dict(ns_steps=3, coeffs=(3.4445, -4.7750, 2.0315, 1.5, -0.5, 1e-39, 3.4445, -4.7750, 2.0315)),
         "no_nesterov": dict(nesterov=False),
         "no_scale": dict(scale="none"),
         "eps_zero": dict(eps=0.0),
