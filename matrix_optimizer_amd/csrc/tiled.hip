@@ -1097,12 +1097,15 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
   const int64_t tri = (C::BM / C::BN) * tm * (tm + 1) / 2;   // triangle tiles
   for (int k = 0; k < a.steps; ++k) {
     const float ca = a.coeffs[3 * k], cb = a.coeffs[3 * k + 1], cc = a.coeffs[3 * k + 2];
-    // bf16 products without the fp32 master: the poly takes b A from its bf16
-    // A operand tiles in LDS (as the products' A is bf16 anyway), so the Gram
-    // writes no fp32 copy of A.  It accumulates A A + (b / c) A and scales by
-    // c, so c must not be tiny next to b (|b / c| <= 1e6 keeps the sum far
-    // from overflow, |A| being about 1); otherwise b A comes from fp32 A.
-    const bool a_in_lds = sizeof(OP) == 2 && X32 == nullptr && cc != 0.f && std::fabs(cc) >= 1e-6f * std::fabs(cb);
+    // bf16 products (with or without the fp32 master of X): the poly takes
+    // b A from its bf16 A operand tiles in LDS, so B = b A + c A A is one
+    // polynomial of the same bf16 A (b A from an fp32 copy makes B a
+    // polynomial of two slightly different matrices, which costs accuracy),
+    // and the Gram writes no fp32 copy of A.  It accumulates A A + (b / c) A
+    // and scales by c, so c must not be tiny next to b (|b / c| <= 1e6 keeps
+    // the sum far from overflow, |A| being about 1); otherwise b A comes from
+    // fp32 A.
+    const bool a_in_lds = sizeof(OP) == 2 && cc != 0.f && std::fabs(cc) >= 1e-6f * std::fabs(cb);
     OP* Xk = C::DIRECT ? Xb[k & 1] : X;
     GemmArgs g = {};
     // Gram: A = X X^T
