@@ -106,15 +106,13 @@ def kernel_model(name, count, M, N, prec, pdt, gdt, with_ns_out=False, ns_steps=
 
 def kernel_form(b, skinny_kernel: int, prec: str) -> str:
     """Which kernels a batch runs: tiled products, Gram space in two launches
-    (the iteration and the apply in one, for bf16 precision where W's stored
-    rows are its long side, unless plan option 1 asks for three), Gram space
-    in three launches, or step by step."""
+    (the iteration and the apply in one, unless plan option 1 asks for
+    three), Gram space in three launches, or step by step."""
     if b.path == 0:
         return "tiled"
     if b.path == 2:
         return "skinny_stepwise"
-    two = skinny_kernel in (0, 3) and prec == "bf16" and b.M <= b.N
-    return "skinny_gram_2launch" if two else "skinny_gram_3launch"
+    return "skinny_gram_2launch" if skinny_kernel in (0, 3) else "skinny_gram_3launch"
 
 
 def executed_flops(plan, K: int) -> float:
@@ -609,14 +607,16 @@ def main():
     del o_bufs
 
     # per-kernel times: a pass on one stream (plan order) with library launch
-    # tracing, so each launch's time is its own and not shared with a lane
+    # tracing, so each launch's time is its own and not shared with a lane;
+    # the steps run back to back on the evolving values (no restore: its
+    # copies would leave dirty lines whose write-back competes with the
+    # kernels, and the kernels' time does not depend on the values)
     one = [B.PreparedStep(plan, b.index, step_bufs[i], hp_run, wss[lane_of[i]] if nstreams > 1 else wss[0],
                           stream.cuda_stream) for i, b in enumerate(plan.batches)]
     tsteps = args.trace_steps or max(1, min(args.steps, int(math.ceil(2000.0 / max(ms, 1e-3)))))
     B.muon_trace_start(tsteps * 64 * len(plan.batches) + 16)
     tr = []
     for _ in range(tsteps):
-        restore()
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record(stream)
         for call in one:
@@ -733,17 +733,28 @@ def main():
         # write-back of someone else's data
         cold = []
         flush = torch.cat([src.view(torch.int32), dst.view(torch.int32)])
-        for _ in range(min(args.steps, 10)):
+        ncold = min(args.steps, 10)
+        # the cold steps carry launch tracing too: per-kernel times from HBM
+        B.muon_trace_start(ncold * 64 * len(plan.batches) + 16)
+        for _ in range(ncold):
             restore()
             flush.sum()
             a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a0.record(stream)
-            run()
+            step_prepared()
             a1.record(stream)
             torch.cuda.synchronize()
             cold.append(a0.elapsed_time(a1))
+        cper = {}
+        for name, t in B.muon_trace_stop():
+            cper.setdefault(name, []).append(t)
         out["detail"]["cold_ms_per_step"] = float(np.median(cold))
         out["detail"]["cold_tflops"] = flops / (np.median(cold) / 1e3) / 1e12
+        out["detail"]["cold_kernels"] = {k: {"launches_per_step": len(v) / ncold, "median_ms": float(np.median(v))}
+                                         for k, v in cper.items()}
+        if roof["bound"] == "hbm" and dom in cper:
+            roof["cold_achieved"] = qty_per_launch / (float(np.median(cper[dom])) / 1e3) / 1e9
+            roof["cold_frac"] = roof["cold_achieved"] / HBM_PEAK_GBPS
         del flush
     del src, dst
     refs = {}

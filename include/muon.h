@@ -99,8 +99,7 @@ typedef struct {
                                Newton-Schulz in Gram space (the iteration runs on the m x m
                                Gram matrix and multiplies back into X once, DMuon-2 Appendix
                                C.3) with 0 or 3: the Gram iteration and the apply in one launch
-                               (2 launches in all) for bf16 precision where W's stored rows are
-                               its long side, else as 1; 1: 3 launches; 2 step by step,
+                               (2 launches in all); 1: 3 launches; 2 step by step,
                                X <- B' X each step (2K+1 launches).  All Gram-space forms give
                                bitwise the same results and report path 1. */
 } muon_plan_options;

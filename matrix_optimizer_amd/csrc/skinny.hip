@@ -1185,32 +1185,33 @@ sk_apply(const typename SkCfg<MODE>::XS* __restrict__ xg, const BFrag* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Gram-space Newton-Schulz and the apply in one launch, for matrices whose
-// stored rows are U rows.  R workgroups of FW_WAVES waves per matrix, one per
-// CU: the first four waves of each form Q from the chunk partials exactly as
-// sk_gram_ns does (the R copies are bitwise equal; one workgroup per CU keeps
-// their dependent MFMA chains from sharing a SIMD with another copy's), then
-// every wave applies it to its share of the matrix's 64-column units exactly
-// as sk_apply does: wave w of workgroup r takes units r * FW_WAVES + w +
-// i * R * FW_WAVES, so the R workgroups sweep the matrix front to back
-// together.  (Loading each wave's first unit before Q was formed, to overlap
-// the Newton-Schulz latency, made the launch slower: those loads delay the
-// partials Q needs first.)  The O buffers alias gram_q's
-// LDS, which is free once Q is in Qf.  All waves take part in gram_q's
-// barriers; after it there are none.
-constexpr int FW_WAVES = 16;
-constexpr int FW_THREADS = FW_WAVES * WAVE;
+// Gram-space Newton-Schulz and the apply in one launch.  R workgroups of NW
+// waves per matrix, one per CU: the first four waves of each form Q from the
+// chunk partials exactly as sk_gram_ns does (the R copies are bitwise equal;
+// one workgroup per CU keeps their dependent MFMA chains from sharing a SIMD
+// with another copy's), then every wave applies it to its share of the
+// matrix's 64-column units exactly as sk_apply does, in both orientations of
+// W: wave w of workgroup r takes units r * NW + w + i * R * NW, so the R
+// workgroups sweep the matrix front to back together.  (Loading each wave's
+// first unit before Q was formed, to overlap the Newton-Schulz latency, made
+// the launch slower: those loads delay the partials Q needs first.)  For a
+// row-major W the O buffers alias gram_q's LDS, which is free once Q is in Qf.
+// All waves take part in gram_q's barriers; after it there are none.
+//   NW = 16: bf16 operands (the 16-wave register budget, 128 per lane, holds
+//            them), batches too large for R >= 8 workgroups per matrix;
+//   NW = 8:  fp32 operands (bf16_x32 and the check path need the 256-register
+//            budget of two waves per SIMD), and small batches, whose R already
+//            fills the CUs: fewer waves per workgroup wait at fewer barriers.
 // ---------------------------------------------------------------------------
-template <int MODE, typename PT, bool ROWS>
-__global__ void __launch_bounds__(FW_THREADS)
+template <int MODE, typename PT, bool ROWS, int NW, bool TRANS>
+__global__ void __launch_bounds__(NW * WAVE)
 sk_ns_apply(const float* __restrict__ gp, const float* __restrict__ sp, float eps, int S, int T, int steps, Coeffs cf,
             const typename SkCfg<MODE>::XS* __restrict__ xg, int m, int64_t n, int64_t NB, int G, int64_t upm, int R,
             int vec, PT* __restrict__ param, float* __restrict__ ns_out, float lr, float wd, float s_scale,
             const float* __restrict__ lrwd, MatTabs tabs) {
   typedef typename SkCfg<MODE>::XS XS;
-  typedef Oct<PT> OV;
   constexpr int XW = MODE == 0 ? 4 : 8;     // 32-bit words of U per lane per K block
-  constexpr int OBUF = FW_WAVES * SK_MP * AP_LD * 4;
+  constexpr int OBUF = TRANS ? 0 : NW * SK_MP * AP_LD * 4;
   constexpr int RAW = GramLds<MODE>::RAW > OBUF ? GramLds<MODE>::RAW : OBUF;
   __shared__ __attribute__((aligned(16))) unsigned char raw[RAW];
   __shared__ float Qf[SK_MP][SK_MP + 1];
@@ -1222,22 +1223,21 @@ sk_ns_apply(const float* __restrict__ gp, const float* __restrict__ sp, float ep
   const int h = lane >> 5, c = lane & 31;
   const int64_t b = blockIdx.x / R;
   const int64_t r = blockIdx.x % R;
-  const int64_t stride = (int64_t)R * FW_WAVES;
+  const int64_t stride = (int64_t)R * NW;
   const int64_t mat = b * (int64_t)m * n;
   param = batch_view(param, tabs.param, b, (int64_t)m * n);
   ns_out = batch_view(ns_out, tabs.ns, b, (int64_t)m * n);
   const bool has_w = ROWS || param != nullptr;
+  // W's stored element (row sr, column sc): stored rows are U rows (n long),
+  // or U columns (m long) when W is tall
   auto w_at = [&](int64_t sr, int64_t sc) -> PT* {
-    if constexpr (ROWS) return row_of<PT>(tabs.param_rows, b, m, sr) + sc;
-    else return param + mat + sr * n + sc;
+    if constexpr (ROWS) return row_of<PT>(tabs.param_rows, b, TRANS ? n : m, sr) + sc;
+    else return param + mat + sr * (TRANS ? (int64_t)m : n) + sc;
   };
-  // W rows 8 i + lane / 8, columns 64 u + 8 (lane % 8) .. + 7 of unit u
-  const int rr = lane >> 3, cc = (lane & 7) * 8;
 
   // U operands of both 32-column blocks of unit u (bf16 modes: K block kb =
-  // rows of group 2 kb + h; fp32 mode: rows 16 h .. 16 h + 15), and W
-  auto load_unit = [&](int64_t u, uint32_t (&xd)[2][2][XW], typename OV::V (&wdst)[4])
-      __attribute__((always_inline)) {
+  // rows of group 2 kb + h; fp32 mode: rows 16 h .. 16 h + 15)
+  auto load_u = [&](int64_t u, uint32_t (&xd)[2][2][XW]) __attribute__((always_inline)) {
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       const int64_t jb = 2 * u + jj;
@@ -1260,66 +1260,124 @@ sk_ns_apply(const float* __restrict__ gp, const float* __restrict__ sp, float ep
         }
       }
     }
-    const int64_t col0 = 64 * u + cc;
-    if (has_w && vec) {
+  };
+
+  gram_q<MODE, NW * WAVE>(gp, sp, eps, m, S, T, steps, cf, b, raw, Qf, &inv_s);
+  const BFrag fr = make_frag<MODE, true>(Qf, lane);
+
+  uint32_t xr[2][2][XW];
+  if constexpr (!TRANS) {
+    typedef Oct<PT> OV;
+    // W rows 8 i + lane / 8, columns 64 u + 8 (lane % 8) .. + 7 of unit u
+    const int rr = lane >> 3, cc = (lane & 7) * 8;
+    const int mr = 8 * G;
+    float* o = reinterpret_cast<float*>(raw) + w * mr * AP_LD;
+    typename OV::V wv[4];
+    for (int64_t u = r * NW + w; u < upm; u += stride) {
+      load_u(u, xr);
+      const int64_t col0 = 64 * u + cc;
+      if (has_w && vec) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 8 * i + rr;
+          if (i < G && row < m && col0 < n) wv[i] = OV::load(w_at(row, col0));
+        }
+      }
+      wave_sync();   // this wave's reads of the previous unit's O are done
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const f32x16 acc = apply_block<MODE, false>(xr[jj], fr);
+        // lane holds O row c, columns 32 jj + 8 qd + 4 h + 0..3
+        if (c < mr) {
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            *reinterpret_cast<f32x4*>(o + c * AP_LD + 32 * jj + 8 * qd + 4 * h) =
+                f32x4{acc[4 * qd], acc[4 * qd + 1], acc[4 * qd + 2], acc[4 * qd + 3]};
+        }
+      }
+      wave_sync();
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 8 * i + rr;
-        if (i < G && row < m && col0 < n) wdst[i] = OV::load(w_at(row, col0));
-      }
-    }
-  };
-
-  gram_q<MODE, FW_THREADS>(gp, sp, eps, m, S, T, steps, cf, b, raw, Qf, &inv_s);
-  const BFrag fr = make_frag<MODE, true>(Qf, lane);
-
-  const int mr = 8 * G;
-  float* o = reinterpret_cast<float*>(raw) + w * mr * AP_LD;
-  uint32_t xr[2][2][XW];
-  typename OV::V wv[4];
-  for (int64_t u = r * FW_WAVES + w; u < upm; u += stride) {
-    load_unit(u, xr, wv);
-    wave_sync();   // this wave's reads of the previous unit's O are done
+        if (i >= G || row >= m) continue;
+        float ov[8], nw[8];
+        const f32x4 o0 = *reinterpret_cast<const f32x4*>(o + row * AP_LD + cc);
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(o + row * AP_LD + cc + 4);
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const f32x16 acc = apply_block<MODE, false>(xr[jj], fr);
-      // lane holds O row c, columns 32 jj + 8 qd + 4 h + 0..3
-      if (c < mr) {
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-          *reinterpret_cast<f32x4*>(o + c * AP_LD + 32 * jj + 8 * qd + 4 * h) =
-              f32x4{acc[4 * qd], acc[4 * qd + 1], acc[4 * qd + 2], acc[4 * qd + 3]};
-      }
-    }
-    wave_sync();
-    const int64_t col0 = 64 * u + cc;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 8 * i + rr;
-      if (i >= G || row >= m) continue;
-      float ov[8], nw[8];
-      const f32x4 o0 = *reinterpret_cast<const f32x4*>(o + row * AP_LD + cc);
-      const f32x4 o1 = *reinterpret_cast<const f32x4*>(o + row * AP_LD + cc + 4);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) { ov[q] = o0[q]; ov[q + 4] = o1[q]; }
-      if (vec) {
-        if (col0 >= n) continue;
-        const int64_t idx = mat + (int64_t)row * n + col0;
-        if (ns_out) Oct<float>::put(ns_out + idx, ov);
-        if (has_w) {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) nw[q] = apply_update(OV::get(wv[i], q), ov[q], lr, wd, s_scale);
-          OV::put(w_at(row, col0), nw);
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          if (col0 + q >= n) break;
-          const int64_t idx = mat + (int64_t)row * n + col0 + q;
-          if (ns_out) ns_out[idx] = ov[q];
+        for (int q = 0; q < 4; ++q) { ov[q] = o0[q]; ov[q + 4] = o1[q]; }
+        if (vec) {
+          if (col0 >= n) continue;
+          const int64_t idx = mat + (int64_t)row * n + col0;
+          if (ns_out) Oct<float>::put(ns_out + idx, ov);
           if (has_w) {
-            PT* wp = w_at(row, col0 + q);
-            st_from_f32(wp, 0, apply_update(ld_as_f32(wp, 0), ov[q], lr, wd, s_scale));
+#pragma unroll
+            for (int q = 0; q < 8; ++q) nw[q] = apply_update(OV::get(wv[i], q), ov[q], lr, wd, s_scale);
+            OV::put(w_at(row, col0), nw);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            if (col0 + q >= n) break;
+            const int64_t idx = mat + (int64_t)row * n + col0 + q;
+            if (ns_out) ns_out[idx] = ov[q];
+            if (has_w) {
+              PT* wp = w_at(row, col0 + q);
+              st_from_f32(wp, 0, apply_update(ld_as_f32(wp, 0), ov[q], lr, wd, s_scale));
+            }
+          }
+        }
+      }
+    }
+  } else {
+    // stored-transposed W: O = Q U straight from the accumulators; quad qd of
+    // block jj holds rows 8 qd + 4 h + 0..3 of column 32 jb + c (as sk_apply)
+    typedef Quad<PT> QV;
+    typename QV::V wq[2][4];
+    for (int64_t u = r * NW + w; u < upm; u += stride) {
+      const int64_t jb0 = 2 * u;
+      load_u(u, xr);
+      if (has_w && vec) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const int64_t col = 32 * (jb0 + jj) + c;
+            const int d = 8 * qd + 4 * h;
+            if (col < n && d < m) wq[jj][qd] = *reinterpret_cast<const typename QV::V*>(w_at(col, d));
+          }
+      }
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int64_t col = 32 * (jb0 + jj) + c;
+        if (jb0 + jj >= NB) break;
+        const f32x16 acc = apply_block<MODE, true>(xr[jj], fr);
+        if (col >= n) continue;
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int d = 8 * qd + 4 * h;
+          float ov[4], nw[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ov[i] = acc[4 * qd + i];
+          if (vec) {
+            if (d >= m) continue;
+            const int64_t idx = mat + col * m + d;
+            if (ns_out) *reinterpret_cast<f32x4*>(ns_out + idx) = f32x4{ov[0], ov[1], ov[2], ov[3]};
+            if (has_w) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) nw[i] = apply_update(QV::get(wq[jj][qd], i), ov[i], lr, wd, s_scale);
+              *reinterpret_cast<typename QV::V*>(w_at(col, d)) = QV::make(nw);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (d + i >= m) break;
+              const int64_t idx = mat + col * m + d + i;
+              if (ns_out) ns_out[idx] = ov[i];
+              if (has_w) {
+                PT* wp = w_at(col, d + i);
+                st_from_f32(wp, 0, apply_update(ld_as_f32(wp, 0), ov[i], lr, wd, s_scale));
+              }
+            }
           }
         }
       }
@@ -1390,24 +1448,27 @@ hipError_t launch_iters(const StepArgs& a, const WsLayout& L, int vec) {
   return hipSuccess;
 }
 
-// Workgroups per matrix of sk_ns_apply: as many as fill one round of resident
-// workgroups (one per CU), but no more than give every wave a unit.
-template <int MODE, typename PT, bool ROWS>
+// Workgroups per matrix of sk_ns_apply: one per CU over the whole batch (a
+// second resident workgroup would run its copy of the Gram iteration on the
+// same SIMDs), but no more than give every wave a unit.
+template <int MODE, typename PT, bool ROWS, int NW, bool TRANS>
 int64_t fused_groups(int64_t count, int64_t upm) {
-  static std::atomic<int> per_dev[kMaxDevices];   // resident workgroups of this kernel per device
+  static std::atomic<int> per_dev[kMaxDevices];   // CUs of the device
   const int slots = per_device_cached(per_dev, [](int dev) {
-    int cus = 0, blocks = 0;
+    int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, sk_ns_apply<MODE, PT, ROWS>, FW_THREADS, 0) !=
-            hipSuccess || blocks <= 0)
-      blocks = 1;
-    return cus * blocks;
+    return cus;
   });
   int64_t R = slots / count;
-  const int64_t most = (upm + FW_WAVES - 1) / FW_WAVES;
+  const int64_t most = (upm + NW - 1) / NW;
   if (R > most) R = most;
   return R < 1 ? 1 : R;
 }
+
+// Waves per workgroup of sk_ns_apply: 8 for fp32 operands, and for batches of
+// at most 32 matrices (R >= 8 workgroups per matrix fill the CUs);
+// 16 otherwise.
+inline int fused_waves(int mode, int64_t count) { return (mode != 0 || count <= 32) ? 8 : 16; }
 
 template <int MODE, typename PT>
 hipError_t launch_fused(const StepArgs& a, const WsLayout& L, const Coeffs& cf) {
@@ -1417,19 +1478,30 @@ hipError_t launch_fused(const StepArgs& a, const WsLayout& L, const Coeffs& cf) 
   const int64_t NB = (sh.n + 31) / 32;
   const int G = (int)((sh.m + 7) / 8);
   const int64_t upm = (NB + 1) / 2;                    // 64-column units per matrix
-  const int vec = sh.n % 8 == 0 ? 1 : 0;
   const char* name = (param || a.tabs.param || a.tabs.param_rows) ? "sk_ns_apply_update" : "sk_ns_apply";
-  auto go = [&](auto rows) {
+  // ROWS: W through a row table; NW waves per workgroup; TRANS: W stored as U^T
+  auto go = [&](auto rows, auto nw, auto trans) {
     constexpr bool RW = decltype(rows)::value;
-    const int64_t R = fused_groups<MODE, PT, RW>(sh.count, upm);
+    constexpr int NW = decltype(nw)::value;
+    constexpr bool TR = decltype(trans)::value;
+    const int vec = TR ? (sh.m % 4 == 0 ? 1 : 0) : (sh.n % 8 == 0 ? 1 : 0);
+    const int64_t R = fused_groups<MODE, PT, RW, NW, TR>(sh.count, upm);
     if (sh.count * R > 0x7fffffffll) return hipErrorInvalidValue;
-    MUON_LAUNCH(name, (sk_ns_apply<MODE, PT, RW>), dim3((unsigned)(sh.count * R)), dim3(FW_THREADS), a.stream,
+    MUON_LAUNCH(name, (sk_ns_apply<MODE, PT, RW, NW, TR>), dim3((unsigned)(sh.count * R)), dim3(NW * WAVE), a.stream,
                 (const float*)(a.ws + L.gp0), (const float*)(a.ws + L.sp), a.eps, (int)L.S, (int)L.T, a.steps, cf,
                 (const XS*)(a.ws + L.x), (int)sh.m, sh.n, NB, G, upm, (int)R, vec, param, a.ns_out, a.lr, a.wd,
                 a.s, a.lrwd, a.tabs);
     return hipGetLastError();
   };
-  return a.tabs.param_rows ? go(std::true_type{}) : go(std::false_type{});
+  auto by_trans = [&](auto rows, auto nw) {
+    return sh.transposed ? go(rows, nw, std::true_type{}) : go(rows, nw, std::false_type{});
+  };
+  auto by_waves = [&](auto rows) {
+    if constexpr (MODE == 0)
+      if (fused_waves(MODE, sh.count) == 16) return by_trans(rows, std::integral_constant<int, 16>{});
+    return by_trans(rows, std::integral_constant<int, 8>{});
+  };
+  return a.tabs.param_rows ? by_waves(std::true_type{}) : by_waves(std::false_type{});
 }
 
 template <int MODE, typename PT>
@@ -1439,8 +1511,7 @@ hipError_t launch_gram(const StepArgs& a, const WsLayout& L, int vec) {
   if (a.steps < 0 || a.steps > 64 || (int)a.coeffs.size() < 3 * a.steps) return hipErrorInvalidValue;
   Coeffs cf = {};
   for (int i = 0; i < 3 * a.steps; ++i) cf.c[i] = a.coeffs[i];
-  if constexpr (MODE == 0)   // bf16 precision: the other modes' operands need more registers than 16 waves have
-    if (L.path == PATH_SKINNY_FUSED && !sh.transposed) return launch_fused<MODE, PT>(a, L, cf);
+  if (L.path == PATH_SKINNY_FUSED) return launch_fused<MODE, PT>(a, L, cf);
   BFrag* bfrag = (BFrag*)(a.ws + L.bfrag);
   MUON_LAUNCH("sk_gram_ns", (sk_gram_ns<MODE>), dim3((unsigned)sh.count), dim3(SK_THREADS), a.stream,
               (const float*)(a.ws + L.gp0), (const float*)(a.ws + L.sp), a.eps, (int)sh.m, (int)L.S, (int)L.T,

@@ -1,16 +1,18 @@
-"""The fused Gram-space form (plan option skinny_kernel = 3: the
-Newton-Schulz on the Gram matrix and the apply in one launch, for matrices
-whose stored rows are U rows) gives bitwise the parameters, momentum and O of
-the three-launch form (skinny_kernel = 1), which the parity tests check
-against the oracle.  Both form Q and apply it with the same arithmetic; only
-the launch structure differs.
+"""The fused Gram-space form (plan option skinny_kernel = 3, the default's
+form: the Newton-Schulz on the Gram matrix and the apply in one launch) gives
+bitwise the parameters, momentum and O of the three-launch form
+(skinny_kernel = 1), which the parity tests check against the oracle.  Both
+form Q and apply it with the same arithmetic; only the launch structure
+differs.
 
 Cases: wide shapes with full and ragged 64-column units, an odd unit count,
 rows that are not a multiple of 8 (no 16-byte vectors), a single unit, 1 and
 32 rows, expert tensors, batches large enough that each matrix gets one
-workgroup, tall shapes (which keep the three launches), all three
-precisions, bf16 and fp32 parameters; the update without O, O without the
-update (the stage call), pointer tables and row tables.
+workgroup (16-wave workgroups) and small ones (8-wave), tall shapes (W stored
+as the transpose of U: short sides that are and are not a multiple of 4, 32
+rows, many matrices), all three precisions (8-wave workgroups for the fp32
+operands), bf16 and fp32 parameters; the update without O, O without the
+update (the stage call), pointer tables and row tables of both orientations.
 """
 import numpy as np
 import pytest
@@ -30,6 +32,9 @@ CASES = [
     ("experts", [(3, 17, 2000)]),
     ("many", [(8, 256)] * 600),
     ("tall", [(700, 20)] * 2),
+    ("tall_not_vec", [(500, 7)] * 3),
+    ("tall_rows32", [(2048, 32)] * 2),
+    ("tall_many", [(300, 8)] * 300),
 ]
 
 
@@ -103,12 +108,13 @@ def _scattered(count, M, N, dtype, gap=64):
     return [base[(count - 1 - i) * per + gap:(count - 1 - i) * per + gap + M * N].view(M, N) for i in range(count)]
 
 
-@pytest.mark.parametrize("prec", ["bf16", "f32"])
-def test_fused_pointer_and_row_tables(prec):
+@pytest.mark.parametrize("prec", ["bf16", "bf16_x32", "f32"])
+@pytest.mark.parametrize("shape", [(24, 3000), (3000, 24)], ids=["wide", "tall"])
+def test_fused_pointer_and_row_tables(prec, shape):
     """Pointer tables and row tables (rows in reverse order, gaps between
     them) through the fused launch equal the packed three-launch step."""
     import torch
-    shapes = [(24, 3000)] * 3
+    shapes = [shape] * 3
     hp = B.HParams(precision=prec)
     p1 = B.Plan(shapes, skinny_kernel=1)
     p3 = B.Plan(shapes, skinny_kernel=3)
