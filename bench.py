@@ -731,20 +731,27 @@ def main():
         # Cache with clean lines, so each timed step starts from HBM (the warm
         # value above may be served partly from that cache) and pays for no
         # write-back of someone else's data
-        cold = []
         flush = torch.cat([src.view(torch.int32), dst.view(torch.int32)])
         ncold = min(args.steps, 10)
-        # the cold steps carry launch tracing too: per-kernel times from HBM
+
+        def cold_steps():
+            times = []
+            for _ in range(ncold):
+                restore()
+                flush.sum()
+                a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a0.record(stream)
+                step_prepared()
+                a1.record(stream)
+                torch.cuda.synchronize()
+                times.append(a0.elapsed_time(a1))
+            return times
+
+        cold = cold_steps()
+        # the same again with launch tracing (its events lengthen the step,
+        # so the step time above is taken without): per-kernel times from HBM
         B.muon_trace_start(ncold * 64 * len(plan.batches) + 16)
-        for _ in range(ncold):
-            restore()
-            flush.sum()
-            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a0.record(stream)
-            step_prepared()
-            a1.record(stream)
-            torch.cuda.synchronize()
-            cold.append(a0.elapsed_time(a1))
+        cold_steps()
         cper = {}
         for name, t in B.muon_trace_stop():
             cper.setdefault(name, []).append(t)
