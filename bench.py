@@ -477,6 +477,8 @@ def main():
                          "seeded torch generators, the checked matrices from the host generator; auto: device "
                          "above 2^28 elements")
     ap.add_argument("--device-inputs", action="store_true", help="same as --inputs device")
+    ap.add_argument("--max-batch-elems", type=int, default=0,
+                    help="plan cap on elements per batch (0: the library default, 2^29)")
     ap.add_argument("--streams", type=int, default=2,
                     help="spread the batches of a step over this many streams (muon_step_batches; at most the "
                          "number of batches; 1 = the batches in plan order on one stream)")
@@ -500,7 +502,8 @@ def main():
     dtype = wl.params[0].dtype
     hp = H.c_hparams(wl.hp, precision=prec)
     torch.cuda.set_device(0)
-    plan = B.Plan([p.shape for p in wl.params], skinny_kernel=args.skinny_kernel)
+    plan = B.Plan([p.shape for p in wl.params], max_batch_elems=args.max_batch_elems,
+                  skinny_kernel=args.skinny_kernel)
     inputs = "device" if args.device_inputs else args.inputs
     if inputs == "auto":
         inputs = "device" if wl.num_elements() > (1 << 28) else "host"
@@ -672,7 +675,7 @@ def main():
     exe = executed_flops(plan, hp.ns_steps)
     value = flops / (ms / 1e3) / 1e12
     cfg = {"workload": wl.name, "matrices": int(sum(b.count for b in plan.batches)), "launch": args.launch,
-           "streams": nstreams, "lanes": lane_of,
+           "streams": nstreams, "lanes": lane_of, "max_batch_elems": args.max_batch_elems or (1 << 29),
            "batches": [[b.count, b.M, b.N] for b in plan.batches],
            "kernels": [kernel_form(b, args.skinny_kernel, prec) for b in plan.batches],
            "param_dtype": dtype,

@@ -345,8 +345,13 @@ muon_status muon_plan_create(const muon_shape* shapes, int32_t n, const muon_pla
       const int64_t M = bk.first.first, N = bk.first.second, per = M * N;
       const int64_t max_count = std::max<int64_t>(1, cap / per);
       const auto& mats = bk.second;
-      for (size_t start = 0; start < mats.size(); start += (size_t)max_count) {
-        const size_t end = std::min(mats.size(), start + (size_t)max_count);
+      // as few chunks as the cap allows, their sizes within one of each other (larger first)
+      const int64_t total = (int64_t)mats.size();
+      const int64_t chunks = (total + max_count - 1) / max_count;
+      const int64_t base = total / chunks, extra = total % chunks;
+      size_t start = 0;
+      for (int64_t c = 0; c < chunks; ++c) {
+        const size_t end = start + (size_t)(base + (c < extra ? 1 : 0));
         muon_plan::Batch b;
         b.M = M; b.N = N; b.count = (int64_t)(end - start); b.transposed = M > N;
         const int64_t m = std::min(M, N), n = std::max(M, N);
@@ -368,6 +373,7 @@ muon_status muon_plan_create(const muon_shape* shapes, int32_t n, const muon_pla
           }
         }
         p->batches.push_back(std::move(b));
+        start = end;
       }
     }
     if (order == 0)

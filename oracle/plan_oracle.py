@@ -14,8 +14,11 @@ item 3:
   parameter, in input order.
 * A batch holds at most ``cap`` elements (the "memory-safe batching" cap of
   §6.6, read as 2^29 elements; one GPU, so the shard-group scaling is 1).  A
-  bucket is cut greedily into chunks of floor(cap / (A*B)) matrices (at least
-  one, so a single matrix above the cap still runs whole).
+  chunk holds at most floor(cap / (A*B)) matrices (at least one, so a single
+  matrix above the cap still runs whole).  The section fixes only the cap, so
+  a bucket is cut into as few chunks as that allows, of sizes that differ by
+  at most one, the larger ones first (64 matrices at 36 per chunk: 32 + 32,
+  not 36 + 28).
 * Batches run in descending size (Figure 10(b), Algorithm 2); equal sizes keep
   their creation order.
 * A batch whose matrices have more rows than columns is marked transposed
@@ -74,8 +77,11 @@ def plan(shapes: Sequence[Sequence[int]], cap: int = DEFAULT_CAP, order: int = 0
     for (M, N), mats in buckets.items():
         per = M * N
         max_count = max(1, cap // per)
-        for start in range(0, len(mats), max_count):
-            chunk = mats[start:start + max_count]
+        n_chunks = -(-len(mats) // max_count)
+        sizes = [len(mats) // n_chunks + (1 if c < len(mats) % n_chunks else 0) for c in range(n_chunks)]
+        starts = [sum(sizes[:c]) for c in range(n_chunks)]
+        for start, size in zip(starts, sizes):
+            chunk = mats[start:start + size]
             segs: List[Segment] = []
             for k, (pi, mi) in enumerate(chunk):
                 if segs and segs[-1].param_index == pi and segs[-1].first_matrix + segs[-1].num_matrices == mi:

@@ -285,9 +285,9 @@ def test_status_strings():
 def test_plan_lanes():
     """muon_plan_lanes: the longest batch first, each onto the least-loaded
     lane; a lane's workspace is the largest of its batches'."""
-    p = B.Plan([(2048, 7168)] * 64 + [(24, 10240)] * 32)
+    p = B.Plan([(2048, 7168)] * 36 + [(2048, 4096)] * 20 + [(24, 10240)] * 32)
     idx = [b.index for b in p.batches]
-    assert [(b.count, b.M, b.N) for b in p.batches] == [(36, 2048, 7168), (28, 2048, 7168), (32, 24, 10240)]
+    assert [(b.count, b.M, b.N) for b in p.batches] == [(36, 2048, 7168), (20, 2048, 4096), (32, 24, 10240)]
     hp = B.HParams()
     ws = [p.workspace_bytes(i, "bf16") for i in idx]
     lanes, need = B.plan_lanes(p, idx, hp, 1)

@@ -36,11 +36,13 @@ def test_descending_and_stable_ties():
     assert [b[:3] for b in summary(PO.plan(shapes, order=1))] == [(2, 3, 2), (5, 2, 1), (3, 2, 3)]
 
 
-def test_cap_split_greedy():
-    # cap 50 elements, matrices of 12 -> 4 per chunk; 10 matrices -> 4 + 4 + 2
+def test_cap_split_balanced():
+    # cap 50 elements, matrices of 12 -> at most 4 per chunk; 10 matrices need 3 chunks -> 4 + 3 + 3
     got = summary(PO.plan([(10, 3, 4)], cap=50))
     assert [(b[2], b[4]) for b in got] == [
-        (4, [(0, 0, 4, 0)]), (4, [(0, 4, 4, 0)]), (2, [(0, 8, 2, 0)])]
+        (4, [(0, 0, 4, 0)]), (3, [(0, 4, 3, 0)]), (3, [(0, 7, 3, 0)])]
+    # 8 matrices -> 4 + 4 (no smaller chunk when the count divides)
+    assert [b[2] for b in summary(PO.plan([(8, 3, 4)], cap=50))] == [4, 4]
     # one matrix above the cap still runs whole
     assert summary(PO.plan([(8, 8)], cap=10)) == [(8, 8, 1, False, [(0, 0, 1, 0)])]
 
@@ -57,16 +59,18 @@ def test_decoder_workload_plan():
     for _ in range(32):
         shapes += [(4096, 4096)] * 4 + [(11008, 4096)] * 2 + [(4096, 11008)]
     b = PO.plan(shapes)
-    # 2^29 // 4096^2 = 32; 2^29 // (11008*4096) = 11
+    # 2^29 // 4096^2 = 32; 2^29 // (11008*4096) = 11, so 64 matrices -> 6 chunks (11,11,11,11,10,10)
+    # and 32 -> 3 chunks (11,11,10); larger batches first, ties in creation order
     counts = [(x.M, x.N, x.count) for x in b]
-    assert counts == ([(4096, 4096, 32)] * 4 + [(11008, 4096, 11)] * 5 + [(4096, 11008, 11)] * 2
-                      + [(4096, 11008, 10)] + [(11008, 4096, 9)])
+    assert counts == ([(4096, 4096, 32)] * 4 + [(11008, 4096, 11)] * 4 + [(4096, 11008, 11)] * 2
+                      + [(11008, 4096, 10)] * 2 + [(4096, 11008, 10)])
     assert sum(x.count for x in b if x.M == 11008) == 64
 
 
 def test_moe_and_large_plans():
     b = PO.plan([(32, 24, 10240), (64, 2048, 7168)])
-    assert [(x.M, x.N, x.count) for x in b] == [(2048, 7168, 36), (2048, 7168, 28), (24, 10240, 32)]
+    # 2^29 // (2048*7168) = 36, so 64 experts take 2 chunks of 32
+    assert [(x.M, x.N, x.count) for x in b] == [(2048, 7168, 32), (2048, 7168, 32), (24, 10240, 32)]
     shapes = [(8192, 28672)] * 16 + [(28672, 8192)] * 16
     b = PO.plan(shapes)
     assert len(b) == 16 and all(x.count == 2 for x in b)
