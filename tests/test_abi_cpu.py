@@ -89,6 +89,14 @@ def test_plan_errors():
     assert _plan_status([(2, 2)], skinny_kernel=3) == B.MUON_OK
     assert _plan_status([(2, 2)], skinny_kernel=-1) == B.MUON_ERR_INVALID_ARG
     assert _plan_status([(1 << 20, 1 << 20)]) == B.MUON_ERR_UNSUPPORTED   # above 2^31 elements
+    # the limit is on the matrix padded to 256 x 256 tiles: exactly 2^31 padded elements pass, in
+    # either orientation and as an expert tensor, one more column (padded to 256 more) does not
+    assert _plan_status([(32768, 65536)]) == B.MUON_OK
+    assert _plan_status([(65536, 32768)]) == B.MUON_OK
+    assert _plan_status([(3, 32768, 65536)]) == B.MUON_OK
+    assert _plan_status([(32768, 65537)]) == B.MUON_ERR_UNSUPPORTED
+    assert _plan_status([(32513, 65536)]) == B.MUON_OK             # rows pad up to 32768
+    assert _plan_status([(32769, 65536)]) == B.MUON_ERR_UNSUPPORTED
     assert _plan_status([(1 << 40, 1 << 40)]) == B.MUON_ERR_INVALID_ARG   # int64 overflow
     assert _plan_status([(1 << 62, 4, 1 << 30)]) == B.MUON_ERR_INVALID_ARG
 
