@@ -50,8 +50,20 @@ __global__ void __launch_bounds__(256)
 tl_norm_finalize(const float* __restrict__ ssp, int64_t nparts, float eps, float* __restrict__ inv) {
   __shared__ float wsum[4];
   const int64_t b = blockIdx.x;
+  const float* p = ssp + b * nparts;
   float v = 0.f;
-  for (int64_t q = threadIdx.x; q < nparts; q += 256) v += ssp[b * nparts + q];
+  // thread t adds partials t, t + 256, t + 512, ... in that order; 16 loads
+  // in flight at a time (one workgroup per matrix, so the loads' latency, not
+  // bandwidth, sets the time)
+  int64_t q = threadIdx.x;
+  for (; q + 15 * 256 < nparts; q += 16 * 256) {
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = p[q + i * 256];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v += x[i];
+  }
+  for (; q < nparts; q += 256) v += p[q];
   v = wave_sum(v);
   if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = v;
   __syncthreads();
