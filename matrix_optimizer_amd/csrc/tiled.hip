@@ -968,21 +968,20 @@ tl_gemm(GemmArgs g) {
         const int rr = lane >> 3, cc = (lane & 7) * 8;
         const uint32_t j = (uint32_t)(j0 + wn * C::WTN + jp * 64 + cc);
         const bool vec = (n % 8) == 0;   // aligned runs of 8 inside the matrix
-        // The read of W for row group p + 1 is issued before the stores of
-        // row group p (the stores could alias the reads, so the compiler would
+        // The reads of W for all four row groups are issued before any store
+        // of the round (the stores could alias the reads, so the compiler would
         // otherwise wait out one memory latency per row group); W stays in its
-        // stored form until used (4 registers for bf16).
-        Raw8<PT> wr[2];
-        auto load_group = [&](int p, int buf) __attribute__((always_inline)) {
+        // stored form until used (4 registers per group for bf16).
+        Raw8<PT> wr[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
           const uint32_t i = ib0 + rr + 8 * p;
-          if (has_w && vec && i < m && j < n) wr[buf].load(w_at(i, j, n));
-        };
-        load_group(0, 0);
+          if (has_w && vec && i < m && j < n) wr[p].load(w_at(i, j, n));
+        }
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           float xv[8];
           if (X32) load8(X32 + (ib0 + rr + 8 * p) * ldx + j, xv);   // padded rows and columns: always readable
-          if (p + 1 < 4) load_group(p + 1, (p + 1) & 1);
           float ov[8];
           const f32x4 a = *reinterpret_cast<const f32x4*>(stg + (rr + 8 * p) * SLD + cc);
           const f32x4 b = *reinterpret_cast<const f32x4*>(stg + (rr + 8 * p) * SLD + cc + 4);
@@ -1004,7 +1003,7 @@ tl_gemm(GemmArgs g) {
             if (O) store8(O + i * n + j, ov);
             if (has_w) {
               float wv[8], nw[8];
-              wr[p & 1].to_f32(wv);
+              wr[p].to_f32(wv);
 #pragma unroll
               for (int q = 0; q < 8; ++q) nw[q] = apply_update(wv[q], ov[q], ulr, uwd, g.s);
               store8(w_at(i, j, n), nw);
