@@ -100,6 +100,7 @@ WsLayout workspace_layout(const BatchShape& b, int prec, int path) {
     L.pb = take(ae * op);
     L.ssp = take(size_t(b.count) * L.nparts * 4);
     L.inv = take(size_t(b.count) * 4);
+    if (L.big_tiles) L.sched = take(size_t(kSchedSlots) * kSchedPerLaunch * 4);
   }
   L.total = off;
   return L;

@@ -46,10 +46,14 @@ tl_momentum(const GT* __restrict__ grad, float* __restrict__ mom, float* __restr
 }
 
 // inv[b] = 1 / (sqrt(sum of partials) + eps), or 0 if that denominator is 0.
+// Block 0 also zeroes the nsched tile counters of the step's products.
 __global__ void __launch_bounds__(256)
-tl_norm_finalize(const float* __restrict__ ssp, int64_t nparts, float eps, float* __restrict__ inv) {
+tl_norm_finalize(const float* __restrict__ ssp, int64_t nparts, float eps, float* __restrict__ inv,
+                 unsigned* __restrict__ sched, int nsched) {
   __shared__ float wsum[4];
   const int64_t b = blockIdx.x;
+  if (sched && b == 0)
+    for (int i = threadIdx.x; i < nsched; i += 256) sched[i] = 0u;
   const float* p = ssp + b * nparts;
   float v = 0.f;
   // thread t adds partials t, t + 256, t + 512, ... in that order; 16 loads
@@ -265,6 +269,7 @@ struct GemmArgs {
   const float* lrwd;   // optional device {lr, wd}
   MatTabs tabs;        // per-matrix W / O addresses (zero-copy batching), or null
   int64_t m, n; int transposed;
+  unsigned* sched;     // dynamic tile order: this launch's 8 counters (zero at launch), or null
 };
 
 // Tile configuration of the NT product kernel: BM x BN output tile per
@@ -423,10 +428,7 @@ __device__ __forceinline__ void stage_store(const StageRegs<C>& sr, typename C::
 // tiles stay on one XCD; each XCD gets a contiguous range of tiles so the
 // operand panels its concurrent tiles share meet in its L2.
 template <class C, int EPI>
-__device__ __forceinline__ void tile_coords(const GemmArgs& g, int64_t lin, bool xcd_map, int64_t& mat, int64_t& ti,
-                                            int64_t& tj) {
-  const int64_t total = g.tiles_total;
-  const int64_t bid = xcd_map ? (lin & 7) * (total >> 3) + (lin >> 3) : lin;
+__device__ __forceinline__ void tile_coords(const GemmArgs& g, int64_t bid, int64_t& mat, int64_t& ti, int64_t& tj) {
   mat = bid / g.tiles_per_mat;
   const int64_t tt = bid % g.tiles_per_mat;
   if (EPI >= EPI_APPLY) {
@@ -557,10 +559,36 @@ tl_gemm(GemmArgs g) {
   const int lane = t & 63;
   const int w = t >> 6;
   const int wm = w / C::WAVES_N, wn = w % C::WAVES_N;
-  // Persistent: workgroup b takes tiles b, b + gridDim, ...  A tile's
-  // epilogue stores drain while the next tile's main loop runs.
+  // Persistent: each workgroup runs tiles until none are left; a tile's
+  // epilogue stores drain while the next tile's main loop runs.  Tiles are
+  // numbered so that XCD x (workgroups b with b % 8 == x, dealt round-robin)
+  // has the contiguous range x total/8 .. and its concurrent tiles share
+  // operand panels in its L2 (tile_coords' order).
+  //  - static: workgroup b takes launch-linear tiles b, b + gridDim, ...
+  //  - dynamic (direct-load tiles given counters): workgroup b takes the next
+  //    untaken tile of its XCD's range, then of the other ranges.  A workgroup
+  //    that starts late (its CU still busy with another stream's kernel)
+  //    takes fewer tiles instead of finishing last.  Thread 0 takes the next
+  //    tile while the current one starts; the other threads read it from LDS
+  //    after the tile's first k-slice barrier.  Each tile is computed exactly
+  //    as in the static order.
   const int64_t total = g.tiles_total;
   const bool xcd_map = (total & 7) == 0 && (gridDim.x & 7) == 0;
+  const bool dyn = C::DIRECT && g.sched != nullptr && xcd_map;
+  __shared__ int64_t next_slot[2];
+  auto static_tile = [&](int64_t l) -> int64_t {
+    return l < total ? (xcd_map ? (l & 7) * (total >> 3) + (l >> 3) : l) : -1;
+  };
+  auto take_tile = [&]() -> int64_t {   // thread 0 only
+    const int64_t per = total >> 3;
+    const int x = blockIdx.x & 7;
+    for (int r = 0; r < 8; ++r) {
+      const int xr = (x + r) & 7;
+      const unsigned i = __hip_atomic_fetch_add(g.sched + xr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((int64_t)i < per) return xr * per + (int64_t)i;
+    }
+    return -1;
+  };
 
   // direct loads: instruction i of this wave fills rows (w + i WAVES) RPI ..
   // + RPI - 1 of the stage (P's rows first, then Q's); the lane's byte offset
@@ -613,9 +641,22 @@ tl_gemm(GemmArgs g) {
   };
   bool stage0_ready = false;   // direct loads: stage 0 already holds this tile's first k-slice
 
-  for (int64_t lin = blockIdx.x; lin < total; lin += gridDim.x) {
+  int64_t bid;
+  if (dyn) {
+    if (t == 0) next_slot[0] = take_tile();
+    __syncthreads();
+    bid = next_slot[0];
+  } else {
+    bid = static_tile(blockIdx.x);
+  }
+  int64_t lin = blockIdx.x;
+  int par = 0;   // next_slot[par ^ 1] receives the tile after this one
+  while (bid >= 0) {
   int64_t mat, ti, tj;
-  tile_coords<C, EPI>(g, lin, xcd_map, mat, ti, tj);
+  tile_coords<C, EPI>(g, bid, mat, ti, tj);
+  int64_t nbid = dyn ? -1 : static_tile(lin + gridDim.x);
+  [[maybe_unused]] int64_t taken = -1;
+  if (dyn && t == 0) taken = take_tile();
   mat = uniform64(mat); ti = uniform64(ti); tj = uniform64(tj);
   const int64_t i0 = ti * C::BM, j0 = tj * C::BN;
 
@@ -707,15 +748,20 @@ tl_gemm(GemmArgs g) {
     const OP* qb = reinterpret_cast<const OP*>(g.Q) + mat * g.strideQ + (QN ? j0 : j0 * g.ldq);
     const OP* npb = pb;
     const OP* nqb = qb;
-    if (lin + gridDim.x < total) {
-      int64_t nmat, nti, ntj;
-      tile_coords<C, EPI>(g, lin + gridDim.x, xcd_map, nmat, nti, ntj);
-      ndq = same_pq && nti == ntj;
-      npb = reinterpret_cast<const OP*>(g.P) + nmat * g.strideP + nti * C::BM * g.ldp;
-      nqb = reinterpret_cast<const OP*>(g.Q) + nmat * g.strideQ + (QN ? ntj * C::BN : ntj * C::BN * g.ldq);
-    }
-    npb = uniform_ptr(npb);
-    nqb = uniform_ptr(nqb);
+    // operands of the next tile, whose first slice the last slice loads
+    auto set_next = [&](int64_t nb) {
+      nbid = nb;
+      if (nb >= 0) {
+        int64_t nmat, nti, ntj;
+        tile_coords<C, EPI>(g, nb, nmat, nti, ntj);
+        ndq = same_pq && nti == ntj;
+        npb = reinterpret_cast<const OP*>(g.P) + nmat * g.strideP + nti * C::BM * g.ldp;
+        nqb = reinterpret_cast<const OP*>(g.Q) + nmat * g.strideQ + (QN ? ntj * C::BN : ntj * C::BN * g.ldq);
+      }
+      npb = uniform_ptr(npb);
+      nqb = uniform_ptr(nqb);
+    };
+    if (!dyn) set_next(nbid);
     if (!stage0_ready) {
       dma_slice(0, pb, qb, 0, dq);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -779,14 +825,16 @@ tl_gemm(GemmArgs g) {
       if constexpr (QN) add_ax(lds + st * C::STAGE + C::BM * C::LD, kt);
       else add_ax(lds + st * C::STAGE + (qrow0 + wn * C::WTN + (lane & 31)) * C::LD, kt);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this wave's loads of the next slice
+      if (dyn && kt == 0 && t == 0) next_slot[par ^ 1] = taken;
       lds_barrier();                               // everyone's; stage st is free again
       if (!last) read_frags(0, st ^ 1, 0);
     };
     for (int64_t kt = 0; kt < KT; kt += 2) {
       slice(0, kt);
+      if (dyn && kt == 0) set_next(next_slot[par ^ 1]);
       slice(1, kt + 1);
     }
-    stage0_ready = lin + gridDim.x < total;
+    stage0_ready = nbid >= 0;
   } else {
   const int r0 = t / C::VPR, cv = (t % C::VPR) * C::EPV;
   const OP* Pp = reinterpret_cast<const OP*>(g.P) + mat * g.strideP + (i0 + r0) * g.ldp + cv;
@@ -1061,6 +1109,9 @@ tl_gemm(GemmArgs g) {
   // loads land there (no wait for this tile's stores)
   if constexpr (C::DIRECT) lds_barrier();
   else __syncthreads();
+  lin += gridDim.x;
+  par ^= 1;
+  bid = nbid;
   }  // tiles
 }
 
@@ -1099,7 +1150,7 @@ unsigned gemm_grid(int64_t tiles) {
 template <class C, typename PT>
 hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C::Op* X, typename C::Op* X1,
                             typename C::Op* XT[2], float* X32, float* A32, bf16_t* A16, typename C::Op* PB,
-                            int64_t mp, int64_t np, const float* inv) {
+                            int64_t mp, int64_t np, const float* inv, unsigned* sched) {
   typedef typename C::Op OP;
   hipError_t e;
   if (C::DIRECT ? X1 == nullptr : (XT[0] == nullptr || XT[1] == nullptr)) return hipErrorInvalidValue;
@@ -1124,6 +1175,7 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
     g.tiles_n = tm; g.tiles_per_mat = tri; g.tiles_total = sh.count * tri;
     g.inv0 = k == 0 ? inv : nullptr;
     g.A32 = a_in_lds ? nullptr : A32; g.A16 = A16; g.lda = mp; g.strideA = mp * mp;
+    g.sched = sched ? sched + (3 * k) * kSchedPerLaunch : nullptr;
     MUON_LAUNCH("tl_gram", (tl_gemm<C, EPI_GRAM, PT>), dim3(gemm_grid<C, EPI_GRAM, PT>(g.tiles_total)),
                 dim3(C::THREADS), a.stream, g);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1134,6 +1186,7 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
     g.tiles_n = tm; g.tiles_per_mat = tri; g.tiles_total = sh.count * tri;
     g.A32 = a_in_lds ? nullptr : A32; g.PB = PB; g.lda = mp; g.strideA = mp * mp; g.cb = cb; g.cc = cc;
     g.ca = a_in_lds ? cb / cc : 0.f;   // the factor add_ax applies
+    g.sched = sched ? sched + (3 * k + 1) * kSchedPerLaunch : nullptr;
     MUON_LAUNCH("tl_poly", (tl_gemm<C, EPI_POLY, PT>), dim3(gemm_grid<C, EPI_POLY, PT>(g.tiles_total)),
                 dim3(C::THREADS), a.stream, g);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1159,6 +1212,7 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
     g.ns_out = a.ns_out; g.lr = a.lr; g.wd = a.wd; g.s = a.s; g.lrwd = a.lrwd;
     g.tabs = a.phase == PH_FULL ? a.tabs : MatTabs{};
     g.m = sh.m; g.n = sh.n; g.transposed = sh.transposed;
+    g.sched = sched ? sched + (3 * k + 2) * kSchedPerLaunch : nullptr;
     const bool rows = g.tabs.param_rows != nullptr;   // W through a row table
     if (g.last && !sh.transposed && rows)
       MUON_LAUNCH("tl_apply_update", (tl_gemm<C, EPI_LAST, PT, true>),
@@ -1182,17 +1236,18 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
 
 template <typename OP, typename PT>
 hipError_t run_products(const StepArgs& a, const BatchShape& sh, OP* X, OP* X1, OP* XT[2], float* X32, float* A32,
-                        bf16_t* A16, OP* PB, int64_t mp, int64_t np, bool big_tiles, const float* inv) {
+                        bf16_t* A16, OP* PB, int64_t mp, int64_t np, bool big_tiles, const float* inv,
+                        unsigned* sched) {
   if constexpr (sizeof(OP) == 4) {
     if (big_tiles) return hipErrorInvalidValue;
-    return run_products_cfg<CfgF32, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, inv);
+    return run_products_cfg<CfgF32, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, inv, nullptr);
   } else {
     // the tile choice is the workspace's (use_big_tiles)
     if (big_tiles) {
       if (mp % CfgBig::BM != 0 || np % CfgBig::BN != 0) return hipErrorInvalidValue;
-      return run_products_cfg<CfgBig, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, inv);
+      return run_products_cfg<CfgBig, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, inv, sched);
     }
-    return run_products_cfg<CfgSmall, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, inv);
+    return run_products_cfg<CfgSmall, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, inv, nullptr);
   }
 }
 
@@ -1225,10 +1280,11 @@ hipError_t tiled_impl(const StepArgs& a, const WsLayout& L) {
                 (int)sh.transposed, a.mu, a.nesterov, ftabs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  unsigned* sched = L.big_tiles ? (unsigned*)(a.ws + L.sched) : nullptr;
   MUON_LAUNCH("tl_norm_finalize", tl_norm_finalize, dim3((unsigned)sh.count), dim3(256), a.stream, ssp, L.nparts,
-              a.eps, inv);
+              a.eps, inv, sched, kSchedSlots * kSchedPerLaunch);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return run_products<OP, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, L.big_tiles, inv);
+  return run_products<OP, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, L.big_tiles, inv, sched);
 }
 
 template <typename OP>
