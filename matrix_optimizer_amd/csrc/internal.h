@@ -88,13 +88,14 @@ struct WsLayout {
   int64_t mp = 0, np = 0, nparts = 0;
   bool big_tiles = false;
   size_t x1 = 0, xt0 = 0, xt1 = 0, x32 = 0, a32 = 0, a16 = 0, pb = 0, ssp = 0, inv = 0;
-  // tile counters of the 256 x 256 products: kSchedSlots launches of a step
-  // (3 per Newton-Schulz step), 8 per launch (one per XCD tile range)
+  // tile counters of the 256 x 256 Gram and poly products: kSchedSlots
+  // launches of a step (2 per Newton-Schulz step), 8 per launch (one per XCD
+  // tile range)
   size_t sched = 0;
 };
 
 constexpr int kSchedPerLaunch = 8;
-constexpr int kSchedSlots = 3 * 64;   // ns_steps <= 64
+constexpr int kSchedSlots = 2 * 64;   // ns_steps <= 64
 
 // The tiled products use 256 x 256 tiles (direct loads, row-major X operand
 // of the apply) when both padded sides are multiples of 256 and the operands

@@ -565,29 +565,52 @@ tl_gemm(GemmArgs g) {
   // has the contiguous range x total/8 .. and its concurrent tiles share
   // operand panels in its L2 (tile_coords' order).
   //  - static: workgroup b takes launch-linear tiles b, b + gridDim, ...
-  //  - dynamic (direct-load tiles given counters): workgroup b takes the next
+  //  - dynamic (Gram and poly on direct-load tiles, given counters: their
+  //    triangles leave partial last rounds, and diagonal tiles, which load
+  //    half the operands, run faster): workgroup b takes the next
   //    untaken tile of its XCD's range, then of the other ranges.  A workgroup
   //    that starts late (its CU still busy with another stream's kernel)
-  //    takes fewer tiles instead of finishing last.  Thread 0 takes the next
+  //    takes fewer tiles instead of finishing last.  Wave 0 takes the next
   //    tile while the current one starts; the other threads read it from LDS
-  //    after the tile's first k-slice barrier.  Each tile is computed exactly
-  //    as in the static order.
+  //    after a k-slice barrier before the last slice.  Each tile is computed
+  //    exactly as in the static order.
   const int64_t total = g.tiles_total;
   const bool xcd_map = (total & 7) == 0 && (gridDim.x & 7) == 0;
-  const bool dyn = C::DIRECT && g.sched != nullptr && xcd_map;
+  const bool dyn = C::DIRECT && EPI < EPI_APPLY && g.sched != nullptr && xcd_map;
   __shared__ int64_t next_slot[2];
   auto static_tile = [&](int64_t l) -> int64_t {
     return l < total ? (xcd_map ? (l & 7) * (total >> 3) + (l >> 3) : l) : -1;
   };
-  auto take_tile = [&]() -> int64_t {   // thread 0 only
-    const int64_t per = total >> 3;
-    const int x = blockIdx.x & 7;
-    for (int r = 0; r < 8; ++r) {
-      const int xr = (x + r) & 7;
-      const unsigned i = __hip_atomic_fetch_add(g.sched + xr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if ((int64_t)i < per) return xr * per + (int64_t)i;
+  // Taking a tile: lane 0 of wave 0 adds 1 to its XCD's counter (own_try,
+  // issued at the start of a tile, its result first used later); wave 0 then
+  // resolves it (take_resolve): the tile own_try names, or, once its own
+  // range is empty, another range's.  For that, lanes 0..7 read all counters
+  // at once and lane 0 tries the first range with tiles left; a failed try
+  // leaves that counter past its range, so at most 8 tries fail.  -1: every
+  // range is exhausted.
+  const int64_t per_range = total >> 3;
+  const int home = blockIdx.x & 7;
+  auto own_try = [&]() -> unsigned {
+    return __hip_atomic_fetch_add(g.sched + home, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto take_resolve = [&](unsigned first) -> int64_t {
+    const int64_t per = per_range;
+    const int x = home;
+    int64_t got = (lane == 0 && (int64_t)first < per) ? x * per + (int64_t)first : -1;
+    got = __shfl(got, 0, 64);
+    while (got < 0) {
+      unsigned c = (unsigned)per;
+      if (lane < 8) c = __hip_atomic_load(g.sched + ((x + lane) & 7), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned long long open = __ballot(lane < 8 && (int64_t)c < per);
+      if (open == 0ull) break;
+      const int xr = (x + __ffsll(open) - 1) & 7;
+      if (lane == 0) {
+        const unsigned i = __hip_atomic_fetch_add(g.sched + xr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((int64_t)i < per) got = xr * per + (int64_t)i;
+      }
+      got = __shfl(got, 0, 64);
     }
-    return -1;
+    return got;
   };
 
   // direct loads: instruction i of this wave fills rows (w + i WAVES) RPI ..
@@ -643,7 +666,10 @@ tl_gemm(GemmArgs g) {
 
   int64_t bid;
   if (dyn) {
-    if (t == 0) next_slot[0] = take_tile();
+    if (w == 0) {
+      const int64_t first = take_resolve(lane == 0 ? own_try() : 0u);
+      if (lane == 0) next_slot[0] = first;
+    }
     __syncthreads();
     bid = next_slot[0];
   } else {
@@ -655,8 +681,8 @@ tl_gemm(GemmArgs g) {
   int64_t mat, ti, tj;
   tile_coords<C, EPI>(g, bid, mat, ti, tj);
   int64_t nbid = dyn ? -1 : static_tile(lin + gridDim.x);
-  [[maybe_unused]] int64_t taken = -1;
-  if (dyn && t == 0) taken = take_tile();
+  [[maybe_unused]] unsigned tried = 0u;
+  if (dyn && w == 0 && lane == 0) tried = own_try();
   mat = uniform64(mat); ti = uniform64(ti); tj = uniform64(tj);
   const int64_t i0 = ti * C::BM, j0 = tj * C::BN;
 
@@ -805,6 +831,9 @@ tl_gemm(GemmArgs g) {
           acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][ib], fb[buf][jb], acc[ib][jb], 0, 0, 0);
     };
     read_frags(0, 0, 0);
+    // slice whose barrier publishes the next tile (dynamic order): late
+    // enough that thread 0's atomic has returned, before the last slice
+    const int64_t kpub = KT >= 8 ? 4 : 0;
     auto slice = [&](int st, int64_t kt) {
       const bool last = kt + 1 == KT;
       dma_slice(st ^ 1, last ? npb : pb, last ? nqb : qb, last ? 0 : (kt + 1) * C::BK, last ? ndq : dq);
@@ -825,13 +854,16 @@ tl_gemm(GemmArgs g) {
       if constexpr (QN) add_ax(lds + st * C::STAGE + C::BM * C::LD, kt);
       else add_ax(lds + st * C::STAGE + (qrow0 + wn * C::WTN + (lane & 31)) * C::LD, kt);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this wave's loads of the next slice
-      if (dyn && kt == 0 && t == 0) next_slot[par ^ 1] = taken;
+      if (dyn && kt == kpub && w == 0) {
+        const int64_t nb = take_resolve(tried);
+        if (lane == 0) next_slot[par ^ 1] = nb;
+      }
       lds_barrier();                               // everyone's; stage st is free again
       if (!last) read_frags(0, st ^ 1, 0);
     };
     for (int64_t kt = 0; kt < KT; kt += 2) {
       slice(0, kt);
-      if (dyn && kt == 0) set_next(next_slot[par ^ 1]);
+      if (dyn && kt == kpub) set_next(next_slot[par ^ 1]);
       slice(1, kt + 1);
     }
     stage0_ready = nbid >= 0;
@@ -1175,7 +1207,7 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
     g.tiles_n = tm; g.tiles_per_mat = tri; g.tiles_total = sh.count * tri;
     g.inv0 = k == 0 ? inv : nullptr;
     g.A32 = a_in_lds ? nullptr : A32; g.A16 = A16; g.lda = mp; g.strideA = mp * mp;
-    g.sched = sched ? sched + (3 * k) * kSchedPerLaunch : nullptr;
+    g.sched = sched ? sched + (2 * k) * kSchedPerLaunch : nullptr;
     MUON_LAUNCH("tl_gram", (tl_gemm<C, EPI_GRAM, PT>), dim3(gemm_grid<C, EPI_GRAM, PT>(g.tiles_total)),
                 dim3(C::THREADS), a.stream, g);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1186,7 +1218,7 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
     g.tiles_n = tm; g.tiles_per_mat = tri; g.tiles_total = sh.count * tri;
     g.A32 = a_in_lds ? nullptr : A32; g.PB = PB; g.lda = mp; g.strideA = mp * mp; g.cb = cb; g.cc = cc;
     g.ca = a_in_lds ? cb / cc : 0.f;   // the factor add_ax applies
-    g.sched = sched ? sched + (3 * k + 1) * kSchedPerLaunch : nullptr;
+    g.sched = sched ? sched + (2 * k + 1) * kSchedPerLaunch : nullptr;
     MUON_LAUNCH("tl_poly", (tl_gemm<C, EPI_POLY, PT>), dim3(gemm_grid<C, EPI_POLY, PT>(g.tiles_total)),
                 dim3(C::THREADS), a.stream, g);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1212,7 +1244,6 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
     g.ns_out = a.ns_out; g.lr = a.lr; g.wd = a.wd; g.s = a.s; g.lrwd = a.lrwd;
     g.tabs = a.phase == PH_FULL ? a.tabs : MatTabs{};
     g.m = sh.m; g.n = sh.n; g.transposed = sh.transposed;
-    g.sched = sched ? sched + (3 * k + 2) * kSchedPerLaunch : nullptr;
     const bool rows = g.tabs.param_rows != nullptr;   // W through a row table
     if (g.last && !sh.transposed && rows)
       MUON_LAUNCH("tl_apply_update", (tl_gemm<C, EPI_LAST, PT, true>),
