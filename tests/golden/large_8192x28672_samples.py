@@ -1,6 +1,9 @@
 """Writes large_8192x28672_samples.npz: oracle values at sampled positions of
 the first matrix of each orientation of the 16 x 8192x28672 + 16 x
-28672x8192 workload (rank-64 plus noise gradients, zero momentum).
+28672x8192 workload (rank-64 plus noise gradients, zero momentum), and, with
+the argument "extra", large_8192x28672_extra_samples.npz for the second
+matrix of each orientation (the other matrix of the same plan batches; the
+GPU test checks both files, the benchmark only the first).
 
 The float64 oracle needs about 44 TFLOP per matrix here, too slow for a test
 run, so its output is stored at 4096 seeded positions per matrix: O (the
@@ -8,7 +11,7 @@ orthogonalised direction) and W' (the updated parameter).  The GPU test runs
 the same seeded inputs through the library and compares those positions.
 
 Calls only the oracle and the seeded input generator:
-    python tests/golden/large_8192x28672_samples.py
+    python tests/golden/large_8192x28672_samples.py [extra]
 """
 import json
 import os
@@ -22,16 +25,20 @@ sys.path.insert(0, ROOT)
 from matrix_optimizer_amd import workloads as WL  # noqa: E402
 from oracle import muon_oracle as ORC  # noqa: E402
 
-OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "large_8192x28672_samples.npz")
+HERE = os.path.dirname(os.path.abspath(__file__))
 SAMPLES = 4096
-PARAMS = (0, 16)   # first [8192, 28672] parameter and first [28672, 8192] parameter; matrix 0 of each
+# (parameters, output): the first [8192, 28672] and [28672, 8192] parameters, or the second ones (extra);
+# each parameter is one matrix (matrix 0)
+SETS = {"main": ((0, 16), os.path.join(HERE, "large_8192x28672_samples.npz")),
+        "extra": ((1, 17), os.path.join(HERE, "large_8192x28672_extra_samples.npz"))}
 
 
 def f32(x):
     return float(np.float32(x))
 
 
-def main():
+def main(which="main"):
+    PARAMS, OUT = SETS[which]
     wl = WL.WORKLOADS["large_8192x28672"]
     hp = wl.hp
     # the fp32 values the kernels receive
@@ -60,4 +67,4 @@ def main():
 
 
 if __name__ == "__main__":
-    main()
+    main(sys.argv[1] if len(sys.argv) > 1 else "main")

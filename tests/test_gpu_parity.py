@@ -336,37 +336,50 @@ def test_decoder_full_size_sampled():
 
 def test_large_8192x28672_golden_samples():
     """The first batch of each orientation of the 8192x28672 workload at full
-    size (two matrices each, the bf16 + fp32-master placement); matrix 0 of
-    each is compared at 4096 positions with oracle values stored by
-    tests/golden/large_8192x28672_samples.py (O and W'), and its M' in
-    full against the momentum update."""
+    size (two matrices each, the bf16 + fp32-master placement); both matrices
+    of each are compared at 4096 positions with oracle values stored by
+    tests/golden/large_8192x28672_samples.py (O and W'; the main file holds
+    matrix 0 of each batch, the extra file matrix 1), and their M' in full
+    against the momentum update."""
     import json
     import os
-    gold = np.load(os.path.join(os.path.dirname(__file__), "golden", "large_8192x28672_samples.npz"))
-    meta = json.loads(str(gold["meta"]))
+    here = os.path.join(os.path.dirname(__file__), "golden")
+    golds = [np.load(os.path.join(here, f)) for f in ("large_8192x28672_samples.npz",
+                                                      "large_8192x28672_extra_samples.npz")]
+    per_param = {}
+    for gold in golds:
+        meta = json.loads(str(gold["meta"]))
+        for pi in meta["params"]:
+            per_param[pi] = (gold, meta)
     wl = WL.WORKLOADS[meta["workload"]]
     h = H.c_hparams(wl.hp)
-    assert meta["hparams"] == {k: (list(v) if isinstance(v, tuple) else v)
-                               for k, v in H.oracle_kwargs(h, 8192, 28672).items()}
     plan = B.Plan([p.shape for p in wl.params])
-    for pi in meta["params"]:
+    by_batch = {}
+    for pi, (gold, meta) in per_param.items():
+        assert meta["hparams"] == {k: (list(v) if isinstance(v, tuple) else v)
+                                   for k, v in H.oracle_kwargs(h, 8192, 28672).items()}
         binfo = next(b for b in plan.batches if any(s[0] == pi and s[1] == 0 for s in b.segments))
-        q = next(s[3] // (binfo.M * binfo.N) for s in binfo.segments if s[0] == pi and s[1] == 0)
+        by_batch.setdefault(binfo.index, (binfo, []))[1].append(pi)
+    assert len(by_batch) == 2 and all(len(v[1]) == 2 for v in by_batch.values())
+    for binfo, params in by_batch.values():
         arrays = H.batch_arrays(wl, binfo)
         Wp, Mp, O = H.run_gpu_step(plan, binfo, arrays, WL.BF16, h)
-        # M' over the whole matrix (the oracle's momentum update is elementwise)
-        H.check_momentum(Mp[q], arrays["momentum"][q].astype(np.float64), H.decode(arrays["grad"][q]),
-                         H.f32(h.momentum))
-        rows, cols = gold[f"p{pi}_rows"], gold[f"p{pi}_cols"]
-        o = O[q][rows, cols].astype(np.float64)
-        e = H.rel_fro(o, gold[f"p{pi}_O"])
-        print(f"large param {pi} ({binfo.M}x{binfo.N}, batch of {binfo.count}): sampled O error {e:.3g}")
-        assert np.all(np.isfinite(O[q]))
-        assert e <= H.o_tolerance(h.precision)
-        W0 = H.decode(arrays["param"][q][rows, cols])
-        dW = H.decode(Wp[q][rows, cols]) - W0
-        dW_ref = gold[f"p{pi}_W"] - W0
-        half_ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(gold[f"p{pi}_W"]), 1e-38))) - 8)
-        slack = np.linalg.norm(half_ulp) / np.linalg.norm(dW_ref)
-        assert H.rel_fro(dW, dW_ref) <= H.o_tolerance(h.precision) + slack + 1e-6
+        for pi in params:
+            gold, meta = per_param[pi]
+            q = next(s[3] // (binfo.M * binfo.N) for s in binfo.segments if s[0] == pi and s[1] == 0)
+            # M' over the whole matrix (the oracle's momentum update is elementwise)
+            H.check_momentum(Mp[q], arrays["momentum"][q].astype(np.float64), H.decode(arrays["grad"][q]),
+                             H.f32(h.momentum))
+            rows, cols = gold[f"p{pi}_rows"], gold[f"p{pi}_cols"]
+            o = O[q][rows, cols].astype(np.float64)
+            e = H.rel_fro(o, gold[f"p{pi}_O"])
+            print(f"large param {pi} ({binfo.M}x{binfo.N}, batch of {binfo.count}): sampled O error {e:.3g}")
+            assert np.all(np.isfinite(O[q]))
+            assert e <= H.o_tolerance(h.precision)
+            W0 = H.decode(arrays["param"][q][rows, cols])
+            dW = H.decode(Wp[q][rows, cols]) - W0
+            dW_ref = gold[f"p{pi}_W"] - W0
+            half_ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(gold[f"p{pi}_W"]), 1e-38))) - 8)
+            slack = np.linalg.norm(half_ulp) / np.linalg.norm(dW_ref)
+            assert H.rel_fro(dW, dW_ref) <= H.o_tolerance(h.precision) + slack + 1e-6
         del arrays, Wp, Mp, O
