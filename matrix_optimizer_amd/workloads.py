@@ -221,6 +221,12 @@ WORKLOADS: Dict[str, Workload] = {
         "moe_experts", 2,
         [ParamSpec("experts_a", (32, 24, 10240)), ParamSpec("experts_b", (64, 2048, 7168))],
         "row_scaled", "zeros", HParams(precision="bf16"), grad_scale=1e-3),
+    # the skinny expert tensor of moe_experts alone (same seeds, so the same
+    # matrices): a small HBM-bound batch of its own
+    "moe_experts_24x10240": Workload(
+        "moe_experts_24x10240", 2,
+        [ParamSpec("experts_a", (32, 24, 10240))],
+        "row_scaled", "zeros", HParams(precision="bf16"), grad_scale=1e-3),
     # every Muon matrix of a 32-layer dense decoder (hidden 4096, MLP 11008)
     "decoder32_h4096_f11008": Workload(
         "decoder32_h4096_f11008", 3, _decoder32(),
