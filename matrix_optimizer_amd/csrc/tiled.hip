@@ -839,9 +839,12 @@ tl_gemm(GemmArgs g) {
     // enough that thread 0's atomic has returned, before the last slice
     const int64_t kpub = KT >= 8 ? 4 : 0;
     // The next slice's loads are split between the first two MFMA steps:
-    // P's rows among the first step's MFMAs, Q's before the second's.  All
-    // of them in the first step queue behind each other in the load path
-    // and arrive later (every product 2.5-4% slower).
+    // P's rows as one burst at the head of the first step, Q's at the head
+    // of the second (the loads are inline asm, which the scheduling hints
+    // leave in place).  All of them at the head of the first step queue
+    // behind each other in the load path and arrive later (every product
+    // 2.5-4% slower); one instruction at a time between the MFMAs, or the
+    // step's fragment reads issued before its burst, is slower still.
     auto slice = [&](int st, int64_t kt) {
       const bool last = kt + 1 == KT;
       const OP* lp = last ? npb : pb;
