@@ -640,22 +640,36 @@ def main():
     kernels = {k: {"launches_per_step": len(v) / tsteps, "avg_ms": float(np.mean(v)),
                    "total_ms_per_step": float(np.sum(v)) / tsteps} for k, v in per.items()}
     dom = max(kernels, key=lambda k: kernels[k]["total_ms_per_step"])
-    # algorithmic quantity of one launch of the dominant kernel, averaged over the
-    # batches it runs on (its launches per batch per step follow from the path)
-    qty = 0.0
-    nlaunch = 0
-    bound, unit = "hbm", "B"
-    for b in plan.batches:
-        res = kernel_model(dom, b.count, b.M, b.N, prec, dtype, dtype, ns_steps=hp.ns_steps)
-        if res is None:
+
+    def per_launch(kname):
+        """(bound, algorithmic quantity of one launch, unit) of a traced kernel,
+        averaged over the batches it runs on (its launches per batch per step
+        follow from the path), or None without a model."""
+        qty, nl, bd, u = 0.0, 0, None, None
+        for b in plan.batches:
+            res = kernel_model(kname, b.count, b.M, b.N, prec, dtype, dtype, ns_steps=hp.ns_steps)
+            if res is None:
+                continue
+            bd, q, u = res
+            per_batch = {"sk_ns_step": hp.ns_steps - 1, "sk_bprime": hp.ns_steps, "tl_gram": hp.ns_steps,
+                         "tl_poly": hp.ns_steps, "tl_apply": hp.ns_steps - 1}.get(kname, 1)
+            qty += q * per_batch
+            nl += per_batch
+        return None if bd is None else (bd, qty / max(nl, 1), u)
+
+    # every traced kernel against its own roofline (the dominant one is `roofline`)
+    for k, rec in kernels.items():
+        r = per_launch(k)
+        if r is None:
             continue
-        bd, q, u = res
-        per_batch = {"sk_ns_step": hp.ns_steps - 1, "sk_bprime": hp.ns_steps, "tl_gram": hp.ns_steps,
-                     "tl_poly": hp.ns_steps, "tl_apply": hp.ns_steps - 1}.get(dom, 1)
-        qty += q * per_batch
-        nlaunch += per_batch
-        bound, unit = bd, u
-    qty_per_launch = qty / max(nlaunch, 1)
+        bd, q, u = r
+        s_ = rec["avg_ms"] / 1e3
+        if bd == "hbm":
+            rec.update({"bound": "hbm", "achieved": q / s_ / 1e9, "unit": "GB/s", "frac": q / s_ / 1e9 / HBM_PEAK_GBPS})
+        else:
+            pk = FP32_PEAK_TFLOPS if prec == "f32" else BF16_PEAK_TFLOPS
+            rec.update({"bound": "mfma", "achieved": q / s_ / 1e12, "unit": "TFLOP/s", "frac": q / s_ / 1e12 / pk})
+    bound, qty_per_launch, unit = per_launch(dom) or ("hbm", 0.0, "B")
     avg_s = kernels[dom]["avg_ms"] / 1e3
     if bound == "hbm":
         achieved = qty_per_launch / avg_s / 1e9
