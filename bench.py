@@ -92,12 +92,17 @@ def kernel_model(name, count, M, N, prec, pdt, gdt, with_ns_out=False, ns_steps=
             ops = 4 if prec == "f32" else 2
             mp, np_ = -(-m // 128) * 128, -(-n // 128) * 128
             big = prec != "f32" and mp % 256 == 0 and np_ % 256 == 0
-            return "hbm", E * (gs + 8) + E * (ops * (1 if big else 2) + (4 if prec == "bf16_x32" else 0)), "B"
+            return "hbm", E * (gs + 8) + E * (ops * (1 if big else 2) + (4 if prec in ("bf16_x32", "bf16_x32c") else 0)), "B"
+        if name == "tl_residual":   # the padded fp32 master read, its bf16 residue written
+            if prec != "bf16_x32c" or m < 128:
+                return None
+            mp, np_ = -(-m // 128) * 128, -(-n // 128) * 128
+            return "hbm", count * mp * np_ * (4 + 2), "B"
         if name == "tl_gram":
             return "mfma", count * m * (m + 1) * n, "flop"
         if name == "tl_poly":
             return "mfma", count * m * m * (m + 1), "flop"
-        if name in ("tl_apply", "tl_apply_update"):
+        if name in ("tl_apply", "tl_apply_update", "tl_apply_comp"):
             return "mfma", count * 2 * m * m * n, "flop"
         if name == "tl_norm_finalize":
             return "hbm", count * 4 * 1024, "B"
@@ -115,17 +120,18 @@ def kernel_form(b, skinny_kernel: int, prec: str) -> str:
     return "skinny_gram_2launch" if skinny_kernel in (0, 3) else "skinny_gram_3launch"
 
 
-def executed_flops(plan, K: int) -> float:
+def executed_flops(plan, K: int, prec: str = "bf16") -> float:
     """Flops the kernels as built perform in one step (padding excluded):
     tiled products m(m+1)n (one triangle of the Gram), m^2(m+1) (one triangle of
-    A^2) and 2m^2 n (apply) per step; the Gram-space skinny path one Gram m^2 n,
-    four m x m products per step and one apply 2m^2 n; the step-by-step skinny
-    path a Gram and an apply per step."""
+    A^2) and 2m^2 n (apply, twice in the compensated mode) per step; the
+    Gram-space skinny path one Gram m^2 n, four m x m products per step and one
+    apply 2m^2 n; the step-by-step skinny path a Gram and an apply per step."""
     tot = 0.0
     for b in plan.batches:
         m, n = min(b.M, b.N), max(b.M, b.N)
         if b.path == 0:
-            tot += b.count * K * (m * (m + 1) * n + m * m * (m + 1) + 2.0 * m * m * n)
+            napply = 2 if prec == "bf16_x32c" and m >= 128 else 1
+            tot += b.count * K * (m * (m + 1) * n + m * m * (m + 1) + napply * 2.0 * m * m * n)
         elif b.path == 1:
             tot += b.count * (m * m * n + K * 4 * 2.0 * m ** 3 + 2.0 * m * m * n)
         else:
@@ -651,8 +657,10 @@ def main():
             if res is None:
                 continue
             bd, q, u = res
+            comp = prec == "bf16_x32c" and min(b.M, b.N) >= 128   # the compensated mode's second apply
             per_batch = {"sk_ns_step": hp.ns_steps - 1, "sk_bprime": hp.ns_steps, "tl_gram": hp.ns_steps,
-                         "tl_poly": hp.ns_steps, "tl_apply": hp.ns_steps - 1}.get(kname, 1)
+                         "tl_poly": hp.ns_steps, "tl_apply": hp.ns_steps - (0 if comp else 1),
+                         "tl_apply_comp": hp.ns_steps - 1 if comp else 0}.get(kname, 1)
             qty += q * per_batch
             nl += per_batch
         return None if bd is None else (bd, qty / max(nl, 1), u)
@@ -690,7 +698,7 @@ def main():
     flops = wl.nominal_ns_flops()
     if hp.ns_steps != wl.hp.ns_steps:
         flops = flops / wl.hp.ns_steps * hp.ns_steps
-    exe = executed_flops(plan, hp.ns_steps)
+    exe = executed_flops(plan, hp.ns_steps, prec)
     value = flops / (ms / 1e3) / 1e12
     cfg = {"workload": wl.name, "matrices": int(sum(b.count for b in plan.batches)), "launch": args.launch,
            "streams": nstreams, "lanes": lane_of, "max_batch_elems": args.max_batch_elems or (1 << 29),

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 7
+#define MUON_ABI_VERSION 8
 
 typedef enum {
   MUON_OK = 0,
@@ -74,13 +74,30 @@ typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
  *                     operands; for ill-conditioned inputs.
  *  MUON_PREC_F32      every product and every stored intermediate in fp32
  *                     (the check path).
+ *  MUON_PREC_BF16_X32C (ABI version 8) the fp32 master of MUON_PREC_BF16_X32,
+ *                     and each step also applies B to the part of X that
+ *                     bf16 cannot hold: X' = a X + B bf16(X) + B bf16(X - bf16(X)),
+ *                     a second bf16 product the size of the apply.  With
+ *                     only the master, that residue enters each step with
+ *                     the weight a instead of the polynomial's own slope, so
+ *                     on well-conditioned inputs the master mode's error is
+ *                     1.1-1.7 times plain bf16's; with the second product it
+ *                     is 0.86-0.99 times plain bf16's there, and on
+ *                     ill-conditioned inputs it keeps the small singular
+ *                     directions as the master mode does.  The apply's
+ *                     flops double: the 8192 x 28672 step takes about 1.65
+ *                     times as long as with MUON_PREC_BF16_X32.  The
+ *                     workspace holds two more bf16 copies of X.  Batches
+ *                     with a short side of at most 32 run it as
+ *                     MUON_PREC_BF16_X32 (their Gram-space products are
+ *                     fp32 already), those from 33 to 127 as MUON_PREC_F32.
  * Matrices whose short side is at most 32 form the Gram matrix of the stored X
  * with fp32 accumulation, run the polynomial on it in fp32 (fp64 on the check
  * path) and apply it with about 16-bit (bf16 hi + lo) or fp32 operands in
  * every mode (the small products are cheap); those
  * with a short side from 33 to 127 run every product on fp32 operands in every
  * mode, because bf16 rounding of A and B costs too much accuracy there. */
-typedef enum { MUON_PREC_BF16 = 0, MUON_PREC_BF16_X32 = 1, MUON_PREC_F32 = 2 } muon_precision;
+typedef enum { MUON_PREC_BF16 = 0, MUON_PREC_BF16_X32 = 1, MUON_PREC_F32 = 2, MUON_PREC_BF16_X32C = 3 } muon_precision;
 
 /* MUON_SCALE_RMS: s = 0.2 sqrt(max(M, N)); MUON_SCALE_NONE: s = 1. */
 typedef enum { MUON_SCALE_NONE = 0, MUON_SCALE_RMS = 1 } muon_scale;

@@ -19,10 +19,11 @@ _lib = None
 MUON_OK, MUON_ERR_INVALID_ARG, MUON_ERR_UNSUPPORTED, MUON_ERR_WORKSPACE_TOO_SMALL, \
     MUON_ERR_NO_MEMORY, MUON_ERR_HIP, MUON_ERR_INTERNAL = range(7)
 MUON_F32, MUON_BF16 = 0, 1
-MUON_PREC_BF16, MUON_PREC_BF16_X32, MUON_PREC_F32 = 0, 1, 2
+MUON_PREC_BF16, MUON_PREC_BF16_X32, MUON_PREC_F32, MUON_PREC_BF16_X32C = 0, 1, 2, 3
 MUON_SCALE_NONE, MUON_SCALE_RMS = 0, 1
 
-PRECISIONS = {"bf16": MUON_PREC_BF16, "bf16_x32": MUON_PREC_BF16_X32, "f32": MUON_PREC_F32}
+PRECISIONS = {"bf16": MUON_PREC_BF16, "bf16_x32": MUON_PREC_BF16_X32, "f32": MUON_PREC_F32,
+              "bf16_x32c": MUON_PREC_BF16_X32C}
 SCALES = {"none": MUON_SCALE_NONE, "rms": MUON_SCALE_RMS}
 
 EXPORTED = ["muon_abi_version", "muon_status_str", "muon_plan_create", "muon_plan_destroy", "muon_step_ptrs",

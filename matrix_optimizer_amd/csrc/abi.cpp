@@ -94,7 +94,13 @@ WsLayout workspace_layout(const BatchShape& b, int prec, int path) {
       L.xt0 = take(xe * op);
       L.xt1 = take(xe * op);
     }
-    if (prec == PREC_BF16_X32) L.x32 = take(xe * 4);
+    if (has_master(prec)) L.x32 = take(xe * 4);
+    // the bf16 residues X - bf16(X) of the compensated mode, ping-pong (as
+    // X when the apply reads X row-major, else as X^T)
+    if (prec == PREC_BF16_X32C) {
+      L.r0 = take(xe * 2);
+      L.r1 = take(xe * 2);
+    }
     L.a32 = take(ae * 4);
     if (prec != PREC_F32) L.a16 = take(ae * 2);
     L.pb = take(ae * op);
@@ -125,7 +131,8 @@ muon_status check_hparams(const muon_hparams* hp, bool need_ns, bool need_update
     for (int i = 0; i < 3 * hp->num_coeff_sets; ++i)
       if (!finite(hp->coeffs[i])) return MUON_ERR_INVALID_ARG;
     if (!finite(hp->eps) || hp->eps < 0.f) return MUON_ERR_INVALID_ARG;
-    if (hp->precision != MUON_PREC_BF16 && hp->precision != MUON_PREC_BF16_X32 && hp->precision != MUON_PREC_F32)
+    if (hp->precision != MUON_PREC_BF16 && hp->precision != MUON_PREC_BF16_X32 && hp->precision != MUON_PREC_F32 &&
+        hp->precision != MUON_PREC_BF16_X32C)
       return MUON_ERR_INVALID_ARG;
   }
   if (need_update) {
@@ -414,7 +421,8 @@ muon_status muon_plan_segments(const muon_plan* plan, int32_t batch, muon_segmen
 muon_status muon_workspace_bytes(const muon_plan* plan, int32_t batch, muon_precision precision, size_t* out) {
   const muon_plan::Batch* b = get_batch(plan, batch);
   if (!b || !out) return MUON_ERR_INVALID_ARG;
-  if (precision != MUON_PREC_BF16 && precision != MUON_PREC_BF16_X32 && precision != MUON_PREC_F32)
+  if (precision != MUON_PREC_BF16 && precision != MUON_PREC_BF16_X32 && precision != MUON_PREC_F32 &&
+      precision != MUON_PREC_BF16_X32C)
     return MUON_ERR_INVALID_ARG;
   *out = workspace_layout(shape_of(*b), precision, b->path).total;
   return MUON_OK;

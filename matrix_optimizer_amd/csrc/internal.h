@@ -28,7 +28,9 @@ int per_device_cached(std::atomic<int> (&cache)[kMaxDevices], F compute) {
 }
 
 enum Dtype { DT_F32 = 0, DT_BF16 = 1 };
-enum Prec { PREC_BF16 = 0, PREC_BF16_X32 = 1, PREC_F32 = 2 };
+enum Prec { PREC_BF16 = 0, PREC_BF16_X32 = 1, PREC_F32 = 2, PREC_BF16_X32C = 3 };
+// Precisions that keep an fp32 master of X on the tiled path.
+inline bool has_master(int prec) { return prec == PREC_BF16_X32 || prec == PREC_BF16_X32C; }
 
 // Which part of the step a call runs.
 enum Phase { PH_FULL = 0, PH_MOMENTUM = 1, PH_NS = 2, PH_UPDATE = 3 };
@@ -55,7 +57,11 @@ constexpr int64_t kTiledBf16MinRows = 128;
 
 // Precision the kernels actually run for a matrix with short side m.
 inline int effective_prec(int64_t m, int prec) {
-  return (m > kSkinnyMaxRows && m < kTiledBf16MinRows) ? PREC_F32 : prec;
+  if (m > kSkinnyMaxRows && m < kTiledBf16MinRows) return PREC_F32;
+  // the skinny path's Gram-space products are fp32 already: the second
+  // (compensating) product is a tiled-path placement
+  if (m <= kSkinnyMaxRows && prec == PREC_BF16_X32C) return PREC_BF16_X32;
+  return prec;
 }
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -88,6 +94,7 @@ struct WsLayout {
   int64_t mp = 0, np = 0, nparts = 0;
   bool big_tiles = false;
   size_t x1 = 0, xt0 = 0, xt1 = 0, x32 = 0, a32 = 0, a16 = 0, pb = 0, ssp = 0, inv = 0;
+  size_t r0 = 0, r1 = 0;   // compensated mode: bf16 residues of X (X's layout, or X^T's)
   // tile counters of the 256 x 256 Gram and poly products: kSchedSlots
   // launches of a step (2 per Newton-Schulz step), 8 per launch (one per XCD
   // tile range)

@@ -246,6 +246,26 @@ tl_first(int mode, int vec, const GT* __restrict__ grad, float* __restrict__ mom
 }
 
 // ---------------------------------------------------------------------------
+// The part of the first step's fp32 master that bf16 cannot hold, rounded to
+// bf16: R = bf16(X32 - bf16(X32)) (compensated mode), stored as X (rt = 0) or
+// as X^T (rt = 1), padding included (zero).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+tl_residual(const float* __restrict__ X32, bf16_t* __restrict__ R, int64_t count, int64_t mp, int64_t np, int rt) {
+  const int64_t per = mp * np, total = count * per;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const float v = X32[e];
+    const bf16_t r = f2bf(v - bf2f(f2bf(v)));
+    if (rt) {
+      const int64_t b = e / per, i = (e % per) / np, j = e % np;
+      R[b * per + j * mp + i] = r;
+    } else {
+      R[e] = r;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // NT product on MFMA with three epilogues.
 // ---------------------------------------------------------------------------
 // EPI_APPLY writes X' (both layouts); EPI_LAST / EPI_LAST_T are the last
@@ -264,6 +284,7 @@ struct GemmArgs {
   float ca, cb, cc;
   // EPI_APPLY
   void* X; float* X32; void* XT; int64_t ldx, ldxt, strideX;
+  void* R;             // compensated mode (RES): bf16(X' - bf16(X')) out, in the layout the next apply reads
   int last;
   void* param; int param_bf16; float* ns_out; float lr, wd, s;
   const float* lrwd;   // optional device {lr, wd}
@@ -539,8 +560,10 @@ __device__ __forceinline__ void sched_mfma_block() {
   }
 }
 
-// ROWS (last step only): W comes through a row table
-template <class C, int EPI, typename PT, bool ROWS = false>
+// ROWS (last step only): W comes through a row table.  RES (apply with the
+// fp32 master): also write the bf16 residue of X' for the next step's
+// compensating product.
+template <class C, int EPI, typename PT, bool ROWS = false, bool RES = false>
 __global__ void __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD)
 tl_gemm(GemmArgs g) {
   typedef typename C::Op OP;
@@ -1036,9 +1059,23 @@ tl_gemm(GemmArgs g) {
         }
 #pragma unroll
         for (int q = 0; q < 8; ++q) st_from_f32(X, (ib0 + 8 * hh + q) * ldx + jj, o[8 * hh + q]);
+        if constexpr (RES && QN) {
+          bf16_t* R = reinterpret_cast<bf16_t*>(g.R) + mat * g.strideX;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float v = o[8 * hh + q];
+            R[(ib0 + 8 * hh + q) * ldx + jj] = f2bf(v - bf2f(f2bf(v)));
+          }
+        }
       }
       if constexpr (!QN)   // the next apply reads X^T
         store_run32(reinterpret_cast<OP*>(g.XT) + mat * g.strideX + jj * (uint32_t)g.ldxt + ib0, o);
+      if constexpr (RES && !QN) {
+        float r[32];
+#pragma unroll
+        for (int q = 0; q < 32; ++q) r[q] = o[q] - bf2f(f2bf(o[q]));
+        store_run32(reinterpret_cast<bf16_t*>(g.R) + mat * g.strideX + jj * (uint32_t)g.ldxt + ib0, r);
+      }
     } else {
       float ulr = g.lr, uwd = g.wd;
       update_scalars(g.lrwd, ulr, uwd);
@@ -1176,13 +1213,13 @@ tl_update(PT* __restrict__ W, const float* __restrict__ O, int64_t total, float 
 // Persistent grid of tl_gemm<C, EPI, PT>: one wave of resident workgroups
 // (a multiple of 8, so each stays on one XCD), or fewer if there are fewer
 // tiles.
-template <class C, int EPI, typename PT, bool ROWS = false>
+template <class C, int EPI, typename PT, bool ROWS = false, bool RES = false>
 unsigned gemm_grid(int64_t tiles) {
   static std::atomic<int> per_dev[kMaxDevices];   // resident workgroups of this kernel per device
   const int64_t slots = per_device_cached(per_dev, [](int dev) {
     int cus = 0, blocks = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, tl_gemm<C, EPI, PT, ROWS>, C::THREADS, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, tl_gemm<C, EPI, PT, ROWS, RES>, C::THREADS, 0) != hipSuccess ||
         blocks <= 0)
       blocks = 1;
     return cus * blocks;
@@ -1195,10 +1232,13 @@ unsigned gemm_grid(int64_t tiles) {
 // row-major buffer, the apply reads X row-major and writes the next X to
 // the other buffer.  Otherwise XT holds X^T (ping-pong) and X is updated in
 // place.
+// R (compensated mode, else null): the bf16 residues X - bf16(X) of the
+// step's input (R[k & 1], in the layout the apply reads X) and of its output
+// (R[(k + 1) & 1]).
 template <class C, typename PT>
 hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C::Op* X, typename C::Op* X1,
                             typename C::Op* XT[2], float* X32, float* A32, bf16_t* A16, typename C::Op* PB,
-                            int64_t mp, int64_t np, const float* inv, unsigned* sched) {
+                            int64_t mp, int64_t np, const float* inv, unsigned* sched, bf16_t* const* R) {
   typedef typename C::Op OP;
   hipError_t e;
   if (C::DIRECT ? X1 == nullptr : (XT[0] == nullptr || XT[1] == nullptr)) return hipErrorInvalidValue;
@@ -1261,6 +1301,29 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
     g.tabs = a.phase == PH_FULL ? a.tabs : MatTabs{};
     g.m = sh.m; g.n = sh.n; g.transposed = sh.transposed;
     const bool rows = g.tabs.param_rows != nullptr;   // W through a row table
+    if constexpr (sizeof(OP) == 2) {
+      if (R) {
+        // compensated mode, two products: X' = a X + B bf16(X) into the
+        // master (first step: unscaled, no update), then
+        // X' += B bf16(X - bf16(X)) from the residue, which applies the first
+        // step's 1 / (||U|| + eps) to the sum, writes the next residue or, in
+        // the last step, updates W
+        GemmArgs g1 = g;
+        g1.inv0 = nullptr; g1.last = 0; g1.param = nullptr; g1.ns_out = nullptr; g1.tabs = MatTabs{};
+        MUON_LAUNCH("tl_apply", (tl_gemm<C, EPI_APPLY, PT>), dim3(gemm_grid<C, EPI_APPLY, PT>(g1.tiles_total)),
+                    dim3(C::THREADS), a.stream, g1);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        g.Q = R[k & 1];   // same layout and strides as the X operand above
+        g.ca = 1.f;
+        if (!g.last) {
+          g.R = R[(k + 1) & 1];
+          MUON_LAUNCH("tl_apply_comp", (tl_gemm<C, EPI_APPLY, PT, false, true>),
+                      dim3(gemm_grid<C, EPI_APPLY, PT, false, true>(g.tiles_total)), dim3(C::THREADS), a.stream, g);
+          if ((e = hipGetLastError()) != hipSuccess) return e;
+          continue;
+        }
+      }
+    }
     if (g.last && !sh.transposed && rows)
       MUON_LAUNCH("tl_apply_update", (tl_gemm<C, EPI_LAST, PT, true>),
                   dim3(gemm_grid<C, EPI_LAST, PT, true>(g.tiles_total)), dim3(C::THREADS), a.stream, g);
@@ -1284,17 +1347,17 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
 template <typename OP, typename PT>
 hipError_t run_products(const StepArgs& a, const BatchShape& sh, OP* X, OP* X1, OP* XT[2], float* X32, float* A32,
                         bf16_t* A16, OP* PB, int64_t mp, int64_t np, bool big_tiles, const float* inv,
-                        unsigned* sched) {
+                        unsigned* sched, bf16_t* const* R) {
   if constexpr (sizeof(OP) == 4) {
-    if (big_tiles) return hipErrorInvalidValue;
-    return run_products_cfg<CfgF32, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, inv, nullptr);
+    if (big_tiles || R) return hipErrorInvalidValue;
+    return run_products_cfg<CfgF32, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, inv, nullptr, nullptr);
   } else {
     // the tile choice is the workspace's (use_big_tiles)
     if (big_tiles) {
       if (mp % CfgBig::BM != 0 || np % CfgBig::BN != 0) return hipErrorInvalidValue;
-      return run_products_cfg<CfgBig, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, inv, sched);
+      return run_products_cfg<CfgBig, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, inv, sched, R);
     }
-    return run_products_cfg<CfgSmall, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, inv, nullptr);
+    return run_products_cfg<CfgSmall, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, inv, nullptr, R);
   }
 }
 
@@ -1307,7 +1370,9 @@ hipError_t tiled_impl(const StepArgs& a, const WsLayout& L) {
   OP* X = (OP*)(a.ws + L.x);
   OP* X1 = L.big_tiles ? (OP*)(a.ws + L.x1) : nullptr;
   OP* XT[2] = {L.big_tiles ? nullptr : (OP*)(a.ws + L.xt0), L.big_tiles ? nullptr : (OP*)(a.ws + L.xt1)};
-  float* X32 = a.prec == PREC_BF16_X32 ? (float*)(a.ws + L.x32) : nullptr;
+  float* X32 = has_master(a.prec) ? (float*)(a.ws + L.x32) : nullptr;
+  bf16_t* Rbuf[2] = {(bf16_t*)(a.ws + L.r0), (bf16_t*)(a.ws + L.r1)};
+  bf16_t* const* R = a.prec == PREC_BF16_X32C ? Rbuf : nullptr;
   float* A32 = (float*)(a.ws + L.a32);
   bf16_t* A16 = a.prec == PREC_F32 ? nullptr : (bf16_t*)(a.ws + L.a16);
   OP* PB = (OP*)(a.ws + L.pb);
@@ -1331,7 +1396,15 @@ hipError_t tiled_impl(const StepArgs& a, const WsLayout& L) {
   MUON_LAUNCH("tl_norm_finalize", tl_norm_finalize, dim3((unsigned)sh.count), dim3(256), a.stream, ssp, L.nparts,
               a.eps, inv, sched, kSchedSlots * kSchedPerLaunch);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return run_products<OP, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, L.big_tiles, inv, sched);
+  if (R) {   // the residue of the first step's input (U), where the first apply reads X
+    const int64_t total = sh.count * mp * np;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    MUON_LAUNCH("tl_residual", tl_residual, dim3((unsigned)blocks), dim3(256), a.stream, X32, R[0], sh.count, mp, np,
+                L.big_tiles ? 0 : 1);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return run_products<OP, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, L.big_tiles, inv, sched, R);
 }
 
 template <typename OP>

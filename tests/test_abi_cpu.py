@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.EXPORTED)
-    assert B.muon_abi_version() == 7
+    assert B.muon_abi_version() == 8
 
 
 def _cmp_plans(shapes, cap=0, order=0):
@@ -128,8 +128,19 @@ def test_workspace_bytes():
             assert w > 0 and w % 256 == 0
     tiled = [b for b in p.batches if b.M == 300][0]   # short side 200: bf16 placements apply
     assert p.workspace_bytes(tiled.index, "bf16_x32") > p.workspace_bytes(tiled.index, "bf16")
+    # the compensated mode adds two bf16 residue buffers of X (2 x 256 x 384
+    # padded) on the tiled path; the skinny path runs it as the master mode,
+    # short sides 33..127 as fp32
+    xe = 2 * 256 * 384
+    assert p.workspace_bytes(tiled.index, "bf16_x32c") == p.workspace_bytes(tiled.index, "bf16_x32") + 2 * xe * 2
+    sk = [b for b in p.batches if b.M == 24][0]
+    assert p.workspace_bytes(sk.index, "bf16_x32c") == p.workspace_bytes(sk.index, "bf16_x32")
+    mid = B.Plan([(100, 700)] * 2)
+    assert mid.workspace_bytes(0, "bf16_x32c") == mid.workspace_bytes(0, "f32")
     with pytest.raises(B.MuonError):
         p.workspace_bytes(99, "bf16")
+    out = C.c_size_t(0)
+    assert B.lib().muon_workspace_bytes(p.handle, 0, 4, C.byref(out)) == B.MUON_ERR_INVALID_ARG
 
 
 # ---------------------------------------------------------------------------
@@ -198,7 +209,7 @@ def test_step_rejects_bad_hparams(plan_fb):
     for h in bad:
         assert _step(p, fb, hp=h) == B.MUON_ERR_INVALID_ARG, h
     hpc, keep = B.HParams().to_c()
-    hpc.precision = 7
+    hpc.precision = 4
     bufs = B.muon_batch_buffers(fb.ptr("param"), 1, fb.ptr("grad"), 1, fb.ptr("mom"), None)
     assert B.lib().muon_step(p.handle, 0, C.byref(bufs), C.byref(hpc), fb.ptr("ws"), 1 << 40, None) == 1
     hpc.precision = 0

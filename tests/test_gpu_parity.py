@@ -41,7 +41,7 @@ def check_batch(wl, h: B.HParams, dtype: str, select=None, plan=None, batches=No
     return errs
 
 
-PRECS = ["bf16", "bf16_x32", "f32"]
+PRECS = ["bf16", "bf16_x32", "bf16_x32c", "f32"]
 
 
 # --------------------------------------------------------------------------
@@ -127,7 +127,7 @@ def test_hparam_variants(shapes, variant):
         # amplifies operand rounding past the bf16 bound on 160 x 200)
         "minimax_schedule": dict(ns_steps=5, coeffs=B.ns_schedule(5, 1e-3, 1.01, 0.02)[0]),
     }[variant]
-    for prec in ("bf16", "bf16_x32", "f32"):
+    for prec in PRECS:
         for kernel in (0, 1, 2):
             check_batch(wl, H.c_hparams(wl.hp, precision=prec, **over), WL.BF16, skinny_kernel=kernel)
 

@@ -1,5 +1,5 @@
-"""The two bf16 placements of the tiled path side by side against the float64
-oracle (tests/parity.py bars):
+"""The three bf16 placements of the tiled path side by side against the
+float64 oracle (tests/parity.py bars):
 
 * MUON_PREC_BF16 keeps X in bf16 between steps;
 * MUON_PREC_BF16_X32 keeps an fp32 master of X and adds a X from it, with the
@@ -11,7 +11,11 @@ oracle (tests/parity.py bars):
   s = 1 the slope of p is about -0.7, not a, so on well-conditioned inputs the
   carried rounding residue adds error instead of being damped: the master
   mode stays within a small factor of plain bf16 there.
-Both use one polynomial of the same bf16 A for B = b A + c A A.
+* MUON_PREC_BF16_X32C adds a second bf16 product, B bf16(X - bf16(X)), so the
+  residue goes through the polynomial as the rest of X does: it keeps the
+  small singular values as the master mode does, and on well-conditioned
+  inputs its error is no larger than plain bf16's.
+All use one polynomial of the same bf16 A for B = b A + c A A.
 """
 import numpy as np
 import pytest
@@ -22,6 +26,8 @@ from tests import harness as H
 from tests import parity as P
 
 pytestmark = pytest.mark.gpu
+
+PRECS = ("bf16", "bf16_x32", "bf16_x32c")
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -35,7 +41,7 @@ def _gpu():
 def _errors(wl, dtype, over=None):
     plan = B.Plan([p.shape for p in wl.params])
     out = {}
-    for prec in ("bf16", "bf16_x32"):
+    for prec in PRECS:
         h = H.c_hparams(wl.hp, precision=prec, **(over or {}))
         errs = []
         for b in plan.batches:
@@ -52,6 +58,9 @@ CASES = {
     "single_128x256": lambda: (WL.WORKLOADS["single_128x256_f32"], WL.F32, None),
     "160x200": lambda: (WL.small_workload("p160", [(160, 200)], momentum_recipe="normal", wid=700), WL.BF16, None),
     "512x768": lambda: (WL.small_workload("p512", [(512, 768)], momentum_recipe="normal", wid=701), WL.BF16, None),
+    "768x512_tall": lambda: (WL.small_workload("p768t", [(768, 512)], momentum_recipe="normal", wid=705), WL.BF16, None),
+    "300x500_128_tiles": lambda: (WL.small_workload("p300", [(300, 500)], momentum_recipe="normal", wid=706), WL.BF16,
+                                  None),
     "1024x1024": lambda: (WL.small_workload("p1024", [(1024, 1024)], momentum_recipe="normal", wid=702), WL.BF16, None),
     "160x200_cushioned_minimax": lambda: (WL.small_workload("p160s", [(160, 200)], momentum_recipe="normal", wid=703),
                                           WL.BF16, dict(ns_steps=5, coeffs=B.ns_schedule(5, 1e-3, 1.01, 0.02)[0])),
@@ -62,9 +71,11 @@ CASES = {
 def test_well_conditioned_both_modes(name):
     wl, dtype, over = CASES[name]()
     e = _errors(wl, dtype, over)
-    print(f"{name}: O error bf16 {e['bf16']:.3g}, bf16_x32 {e['bf16_x32']:.3g}")
-    # both pass the parity bar inside _errors; the master mode stays close to plain bf16
+    print(f"{name}: O error bf16 {e['bf16']:.3g}, bf16_x32 {e['bf16_x32']:.3g}, bf16_x32c {e['bf16_x32c']:.3g}")
+    # all pass the parity bar inside _errors; the master mode stays close to
+    # plain bf16, the compensated one at or below it
     assert e["bf16_x32"] <= 1.6 * e["bf16"] + 1e-3
+    assert e["bf16_x32c"] <= 1.05 * e["bf16"]
 
 
 def test_ill_conditioned_needs_the_master():
@@ -75,7 +86,7 @@ def test_ill_conditioned_needs_the_master():
     b = plan.batches[0]
     arr = H.batch_arrays(wl, b)
     errs = {}
-    for prec in ("bf16", "bf16_x32"):
+    for prec in PRECS:
         h = H.c_hparams(wl.hp, precision=prec)
         Wp, Mp, O = H.run_gpu_step(plan, b, arr, WL.BF16, h)
         from oracle import muon_oracle as ORC
@@ -83,6 +94,8 @@ def test_ill_conditioned_needs_the_master():
         ref = ORC.muon_step_matrix(H.decode(arr["param"][0]), H.decode(arr["grad"][0]),
                                    arr["momentum"][0].astype(np.float64), **kw)
         errs[prec] = H.rel_fro(O[0].astype(np.float64), ref["O"])
-    print(f"rank-64 + noise 1024x3584: O error bf16 {errs['bf16']:.3g}, bf16_x32 {errs['bf16_x32']:.3g}")
-    assert errs["bf16_x32"] <= 1e-2
-    assert errs["bf16"] > 5 * errs["bf16_x32"]
+    print(f"rank-64 + noise 1024x3584: O error bf16 {errs['bf16']:.3g}, bf16_x32 {errs['bf16_x32']:.3g}, "
+          f"bf16_x32c {errs['bf16_x32c']:.3g}")
+    for prec in ("bf16_x32", "bf16_x32c"):
+        assert errs[prec] <= 1e-2
+        assert errs["bf16"] > 5 * errs[prec]

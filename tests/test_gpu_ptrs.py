@@ -45,7 +45,7 @@ def _scattered(count, M, N, dtype, gap=64):
     return [base[(count - 1 - i) * per + gap:(count - 1 - i) * per + gap + M * N].view(M, N) for i in range(count)]
 
 
-@pytest.mark.parametrize("prec", ["bf16", "bf16_x32", "f32"])
+@pytest.mark.parametrize("prec", ["bf16", "bf16_x32", "bf16_x32c", "f32"])
 @pytest.mark.parametrize("pdtype", ["bf16", "f32"])
 @pytest.mark.parametrize("name,shapes,kernel", CASES, ids=[c[0] for c in CASES])
 def test_step_ptrs_matches_oracle_and_packed(name, shapes, kernel, pdtype, prec):

@@ -73,7 +73,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("prec", ["bf16", "bf16_x32", "f32"])
+@pytest.mark.parametrize("prec", ["bf16", "bf16_x32", "bf16_x32c", "f32"])
 @pytest.mark.parametrize("pdtype", ["bf16", "f32"])
 @pytest.mark.parametrize("name,phys,split,mshape,kernels", CASES, ids=[c[0] for c in CASES])
 def test_step_rows_matches_oracle_and_packed(name, phys, split, mshape, kernels, pdtype, prec):
