@@ -7,7 +7,7 @@ normalisation, transpose-first, K Newton-Schulz steps, decay and update), with
 all inputs resident in device memory; the batches are spread over --streams
 streams (muon_step_batches).  The default workload is the largest one that
 fits one GPU: 16 bf16 matrices of 8192 x 28672 plus 16 of 28672 x 8192, in 16
-batches of two, with an fp32 master copy of X (bf16_x32).
+batches of two, with a master copy of X (bf16_x32: bf16 plus a bf16 residue).
 
 Protocol (the DMuon-2 paper's timing, App. D.3): W untimed repetitions, then
 K timed ones; before each, W and M are restored from device copies (outside
@@ -88,22 +88,17 @@ def kernel_model(name, count, M, N, prec, pdt, gdt, with_ns_out=False, ns_steps=
     else:
         if name == "tl_momentum_layout":
             # G read, M read and written, X written (bf16 operands unless f32),
-            # X^T too unless the products use 256 x 256 tiles, the fp32 master
+            # X^T too unless the products use 256 x 256 tiles, the master's bf16 residue
             ops = 4 if prec == "f32" else 2
             mp, np_ = -(-m // 128) * 128, -(-n // 128) * 128
             big = prec != "f32" and mp % 256 == 0 and np_ % 256 == 0
-            return "hbm", E * (gs + 8) + E * (ops * (1 if big else 2) + (4 if prec in ("bf16_x32", "bf16_x32c") else 0)), "B"
-        if name == "tl_residual":   # the padded fp32 master read, its bf16 residue written
-            if prec != "bf16_x32c" or m < 128:
-                return None
-            mp, np_ = -(-m // 128) * 128, -(-n // 128) * 128
-            return "hbm", count * mp * np_ * (4 + 2), "B"
+            return "hbm", E * (gs + 8) + E * (ops * (1 if big else 2) + (2 if prec in ("bf16_x32", "bf16_x32c") else 0)), "B"
         if name == "tl_gram":
             return "mfma", count * m * (m + 1) * n, "flop"
         if name == "tl_poly":
             return "mfma", count * m * m * (m + 1), "flop"
-        if name in ("tl_apply", "tl_apply_update", "tl_apply_comp"):
-            return "mfma", count * 2 * m * m * n, "flop"
+        if name in ("tl_apply", "tl_apply_update"):   # compensated: B X~ and B R in one launch
+            return "mfma", count * 2 * m * m * n * (2 if prec == "bf16_x32c" and m >= 128 else 1), "flop"
         if name == "tl_norm_finalize":
             return "hbm", count * 4 * 1024, "B"
     return None
@@ -657,10 +652,8 @@ def main():
             if res is None:
                 continue
             bd, q, u = res
-            comp = prec == "bf16_x32c" and min(b.M, b.N) >= 128   # the compensated mode's second apply
             per_batch = {"sk_ns_step": hp.ns_steps - 1, "sk_bprime": hp.ns_steps, "tl_gram": hp.ns_steps,
-                         "tl_poly": hp.ns_steps, "tl_apply": hp.ns_steps - (0 if comp else 1),
-                         "tl_apply_comp": hp.ns_steps - 1 if comp else 0}.get(kname, 1)
+                         "tl_poly": hp.ns_steps, "tl_apply": hp.ns_steps - 1}.get(kname, 1)
             qty += q * per_batch
             nl += per_batch
         return None if bd is None else (bd, qty / max(nl, 1), u)

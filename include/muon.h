@@ -70,14 +70,16 @@ typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
 
 /* Where Newton-Schulz keeps X and what the matrix products take as operands.
  *  MUON_PREC_BF16     X stored in bf16; bf16 MFMA operands, fp32 accumulation.
- *  MUON_PREC_BF16_X32 fp32 master copy of X (the a X term in fp32), bf16 MFMA
- *                     operands; for ill-conditioned inputs.
+ *  MUON_PREC_BF16_X32 a master copy of X with a 16-bit significand: bf16(X)
+ *                     plus the bf16 rounding of X - bf16(X), kept beside
+ *                     each other, so the a X term carries what bf16 cannot
+ *                     hold; bf16 MFMA operands; for ill-conditioned inputs.
  *  MUON_PREC_F32      every product and every stored intermediate in fp32
  *                     (the check path).
- *  MUON_PREC_BF16_X32C (ABI version 8) the fp32 master of MUON_PREC_BF16_X32,
- *                     and each step also applies B to the part of X that
- *                     bf16 cannot hold: X' = a X + B bf16(X) + B bf16(X - bf16(X)),
- *                     a second bf16 product the size of the apply.  With
+ *  MUON_PREC_BF16_X32C (ABI version 8) the master of MUON_PREC_BF16_X32, and
+ *                     each step also applies B to the part of X that bf16
+ *                     cannot hold: X' = a X + B bf16(X) + B bf16(X - bf16(X)),
+ *                     the apply running over twice the inner length.  With
  *                     only the master, that residue enters each step with
  *                     the weight a instead of the polynomial's own slope, so
  *                     on well-conditioned inputs the master mode's error is
@@ -85,12 +87,12 @@ typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
  *                     is 0.86-0.99 times plain bf16's there, and on
  *                     ill-conditioned inputs it keeps the small singular
  *                     directions as the master mode does.  The apply's
- *                     flops double: the 8192 x 28672 step takes about 1.65
- *                     times as long as with MUON_PREC_BF16_X32.  The
- *                     workspace holds two more bf16 copies of X.  Batches
- *                     with a short side of at most 32 run it as
- *                     MUON_PREC_BF16_X32 (their Gram-space products are
- *                     fp32 already), those from 33 to 127 as MUON_PREC_F32.
+ *                     flops double: the 8192 x 28672 step takes about 1.55
+ *                     times as long as with MUON_PREC_BF16_X32, with the
+ *                     same workspace.  Batches with a short side of at most
+ *                     32 run it as MUON_PREC_BF16_X32 (their Gram-space
+ *                     products are fp32 already), those from 33 to 127 as
+ *                     MUON_PREC_F32.
  * Matrices whose short side is at most 32 form the Gram matrix of the stored X
  * with fp32 accumulation, run the polynomial on it in fp32 (fp64 on the check
  * path) and apply it with about 16-bit (bf16 hi + lo) or fp32 operands in
@@ -242,8 +244,9 @@ muon_status muon_plan_batch_info(const muon_plan* plan, int32_t batch, muon_batc
 muon_status muon_plan_segments(const muon_plan* plan, int32_t batch, muon_segment* out, int32_t capacity);
 
 /* Device workspace (bytes, a multiple of 256) that muon_step / muon_stage_ns
- * need for this batch at this precision: the batched iterate X (and its fp32
- * master with MUON_PREC_BF16_X32), the Gram matrix A, the polynomial B and the
+ * need for this batch at this precision: the batched iterate X (and the
+ * residues of its master with MUON_PREC_BF16_X32 and _X32C), the Gram matrix
+ * A, the polynomial B and the
  * norm partials, sized once per batch as HyperParallel-FSDP §6.6 sizes the
  * workspace of one batched invocation (memory-safe batching keeps it bounded
  * by the 2^29-element cap).  Pure host computation; INVALID_ARG for a bad

@@ -94,10 +94,9 @@ WsLayout workspace_layout(const BatchShape& b, int prec, int path) {
       L.xt0 = take(xe * op);
       L.xt1 = take(xe * op);
     }
-    if (has_master(prec)) L.x32 = take(xe * 4);
-    // the bf16 residues X - bf16(X) of the compensated mode, ping-pong (as
-    // X when the apply reads X row-major, else as X^T)
-    if (prec == PREC_BF16_X32C) {
+    // the master: the residues bf16(X - bf16(X)) of X, ping-pong (as X when
+    // the apply reads X row-major, else as X^T)
+    if (has_master(prec)) {
       L.r0 = take(xe * 2);
       L.r1 = take(xe * 2);
     }

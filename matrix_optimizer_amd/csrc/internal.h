@@ -29,7 +29,8 @@ int per_device_cached(std::atomic<int> (&cache)[kMaxDevices], F compute) {
 
 enum Dtype { DT_F32 = 0, DT_BF16 = 1 };
 enum Prec { PREC_BF16 = 0, PREC_BF16_X32 = 1, PREC_F32 = 2, PREC_BF16_X32C = 3 };
-// Precisions that keep an fp32 master of X on the tiled path.
+// Precisions that keep a master of X on the tiled path: X = bf16(X) +
+// bf16(X - bf16(X)), the second term (the residue) in its own buffer.
 inline bool has_master(int prec) { return prec == PREC_BF16_X32 || prec == PREC_BF16_X32C; }
 
 // Which part of the step a call runs.
@@ -93,8 +94,8 @@ struct WsLayout {
   // kept in xt0 / xt1 beside x.
   int64_t mp = 0, np = 0, nparts = 0;
   bool big_tiles = false;
-  size_t x1 = 0, xt0 = 0, xt1 = 0, x32 = 0, a32 = 0, a16 = 0, pb = 0, ssp = 0, inv = 0;
-  size_t r0 = 0, r1 = 0;   // compensated mode: bf16 residues of X (X's layout, or X^T's)
+  size_t x1 = 0, xt0 = 0, xt1 = 0, a32 = 0, a16 = 0, pb = 0, ssp = 0, inv = 0;
+  size_t r0 = 0, r1 = 0;   // the master: bf16 residues of X (X's layout, or X^T's)
   // tile counters of the 256 x 256 Gram and poly products: kSchedSlots
   // launches of a step (2 per Newton-Schulz step), 8 per launch (one per XCD
   // tile range)

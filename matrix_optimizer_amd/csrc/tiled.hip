@@ -21,6 +21,7 @@
 // Operands are bf16 on v_mfma_f32_32x32x16_bf16 with fp32 accumulation, or
 // fp32 on v_mfma_f32_32x32x2f32 for the check path.
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -98,12 +99,25 @@ __device__ __forceinline__ void store8(bf16_t* p, const float* f) {
   for (int q = 0; q < 4; ++q) v[q] = (uint32_t)f2bf(f[2 * q]) | ((uint32_t)f2bf(f[2 * q + 1]) << 16);
   *reinterpret_cast<u32x4*>(p) = v;
 }
+// The part of v that bf16 cannot hold: v - bf16(v), exact in fp32 (stored
+// rounded to bf16, it makes bf16(v) + bf16(v - bf16(v)) a 16-bit-mantissa
+// copy of v).
+__device__ __forceinline__ float bf_res(float v) { return v - bf2f(f2bf(v)); }
+__device__ __forceinline__ void store_res8(bf16_t* p, const float* f) {
+  float r[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) r[q] = bf_res(f[q]);
+  store8(p, r);
+}
 
 // ---------------------------------------------------------------------------
 // First pass of the tiled path, one 64x64 tile (Newton-Schulz orientation)
 // per workgroup: momentum and the Nesterov direction U (or a given U), the
-// tile's share of ||U||_F^2, and U, unnormalised, row-major, transposed when
-// the apply products read X^T (XT non-null), and as the fp32 master.  The first Newton-Schulz step applies 1 / (||U||_F + eps): the Gram
+// tile's share of ||U||_F^2, and U, unnormalised, row-major and transposed
+// when the apply products read X^T (XT non-null).  With the master (R
+// non-null) also the part of U that bf16 cannot hold, bf16(U - bf16(U)), in
+// the layout in which the apply reads X: row-major, or transposed when XT is
+// given.  The first Newton-Schulz step applies 1 / (||U||_F + eps): the Gram
 // epilogue scales by its square, the apply epilogue by it.  One pass over G
 // and M instead of two.
 //   mode 0: M' = mu M + G (in place), U = G + mu M' or M'
@@ -120,7 +134,7 @@ __device__ __forceinline__ void store8(bf16_t* p, const float* f) {
 template <typename GT, typename XO, bool ROWS>
 __global__ void __launch_bounds__(256)
 tl_first(int mode, int vec, const GT* __restrict__ grad, float* __restrict__ mom, const float* __restrict__ u_in,
-         float* __restrict__ ssp, XO* __restrict__ X, XO* __restrict__ XT, float* __restrict__ X32,
+         float* __restrict__ ssp, XO* __restrict__ X, XO* __restrict__ XT, bf16_t* __restrict__ R,
          int64_t m, int64_t n, int64_t mp, int64_t np, int transposed, float mu, int nesterov, MatTabs tabs) {
   __shared__ float tile[64][65];
   __shared__ float wsum[4];
@@ -183,7 +197,7 @@ tl_first(int mode, int vec, const GT* __restrict__ grad, float* __restrict__ mom
       } else {
         const int64_t xi = xb + (i0 + sr) * np + j0 + sc;
         store8(X + xi, u);
-        if (X32) store8(X32 + xi, u);
+        if (R) store_res8(R + xi, u);
       }
     }
   } else {
@@ -223,7 +237,7 @@ tl_first(int mode, int vec, const GT* __restrict__ grad, float* __restrict__ mom
       const float v = tile[li][lj];
       const int64_t xi = xb + (i0 + li) * np + j0 + lj;
       st_from_f32(X, xi, v);
-      if (X32) X32[xi] = v;
+      if (R && !XT) st_from_f32(R, xi, bf_res(v));
     }
   } else if (transposed) {
 #pragma unroll
@@ -234,33 +248,15 @@ tl_first(int mode, int vec, const GT* __restrict__ grad, float* __restrict__ mom
       for (int q = 0; q < 8; ++q) u[q] = tile[li][lj + q];
       const int64_t xi = xb + (i0 + li) * np + j0 + lj;
       store8(X + xi, u);
-      if (X32) store8(X32 + xi, u);
+      if (R) store_res8(R + xi, u);
     }
   }
   if (XT) {
     for (int e = threadIdx.x; e < 64 * 64; e += 256) {
       const int lj = e >> 6, li = e & 63;
-      st_from_f32(XT, xb + (j0 + lj) * mp + i0 + li, tile[li][lj]);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// The part of the first step's fp32 master that bf16 cannot hold, rounded to
-// bf16: R = bf16(X32 - bf16(X32)) (compensated mode), stored as X (rt = 0) or
-// as X^T (rt = 1), padding included (zero).
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256)
-tl_residual(const float* __restrict__ X32, bf16_t* __restrict__ R, int64_t count, int64_t mp, int64_t np, int rt) {
-  const int64_t per = mp * np, total = count * per;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-    const float v = X32[e];
-    const bf16_t r = f2bf(v - bf2f(f2bf(v)));
-    if (rt) {
-      const int64_t b = e / per, i = (e % per) / np, j = e % np;
-      R[b * per + j * mp + i] = r;
-    } else {
-      R[e] = r;
+      const int64_t ti = xb + (j0 + lj) * mp + i0 + li;
+      st_from_f32(XT, ti, tile[li][lj]);
+      if (R) st_from_f32(R, ti, bf_res(tile[li][lj]));
     }
   }
 }
@@ -283,8 +279,14 @@ struct GemmArgs {
   float* A32; bf16_t* A16; void* PB; int64_t lda, strideA;
   float ca, cb, cc;
   // EPI_APPLY
-  void* X; float* X32; void* XT; int64_t ldx, ldxt, strideX;
-  void* R;             // compensated mode (RES): bf16(X' - bf16(X')) out, in the layout the next apply reads
+  void* X; void* XT; int64_t ldx, ldxt, strideX;
+  // The master (bf16 modes): X = X~ + R with X~ = bf16(X) the product
+  // operand and R = bf16(X - X~), R in the layout in which the apply reads X
+  // (row-major on direct-load tiles, else as X^T).  Rin: the input's R,
+  // added as a R in the epilogue; Rout: the output's R (null: none).
+  // Compensated: k-slices kswitch .. of the K loop (K = 2 m) multiply B by
+  // the input's R (Q2, Q's layout) instead of X~, and a R comes in with them.
+  const bf16_t* Rin; bf16_t* Rout; const void* Q2; int64_t kswitch;
   int last;
   void* param; int param_bf16; float* ns_out; float lr, wd, s;
   const float* lrwd;   // optional device {lr, wd}
@@ -377,6 +379,21 @@ __device__ __forceinline__ void tri_tile_grouped(int64_t tt, int64_t tm, int64_t
   }
   ti = r0 + c + o;
   tj = r0 + c;
+}
+
+// Element i of a wave-uniform base, addressed by a 32-bit byte offset (the
+// caller guarantees i * sizeof(T) < 2^32): the access takes the base from
+// scalar registers and one offset register, instead of a 64-bit address per
+// access (which, at full register use, serialises a group of loads).
+template <typename T> __device__ __forceinline__ T* at32(T* base, uint32_t i) {
+  typedef typename std::conditional<std::is_const<T>::value, const char, char>::type B;
+  return reinterpret_cast<T*>(reinterpret_cast<B*>(base) + i * (uint32_t)sizeof(T));
+}
+
+// 32 consecutive bf16 elements starting at a 16-byte aligned address, as floats.
+__device__ __forceinline__ void load_run32(const bf16_t* p, float* o) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) load8(p + 8 * q, o + 8 * q);
 }
 
 // 32 consecutive elements starting at a 16-byte aligned address, as 16-byte stores.
@@ -560,10 +577,10 @@ __device__ __forceinline__ void sched_mfma_block() {
   }
 }
 
-// ROWS (last step only): W comes through a row table.  RES (apply with the
-// fp32 master): also write the bf16 residue of X' for the next step's
-// compensating product.
-template <class C, int EPI, typename PT, bool ROWS = false, bool RES = false>
+// ROWS (last step only): W comes through a row table.  COMP (apply
+// products, compensated mode): the second half of K multiplies B by the
+// input's R (k-slices g.kswitch ..).
+template <class C, int EPI, typename PT, bool ROWS = false, bool COMP = false>
 __global__ void __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD)
 tl_gemm(GemmArgs g) {
   typedef typename C::Op OP;
@@ -723,13 +740,14 @@ tl_gemm(GemmArgs g) {
   // a X term of the apply products: the Q stage holds X^T[j][k] = X[k][j]
   // for this k-slice; when the slice covers rows of this wave's output, add
   // a X[i][j] from LDS to the accumulators (no global read in the epilogue).
-  // The fp32 master (X32) is added in the epilogue instead.  The poly
+  // With the master, a R comes in the epilogue, or, compensated, from the
+  // R slices of the second half of K (the caller passes their k).  The poly
   // product reads the same way: its Q stage holds A[j][k] = A[k][j], and
   // without an fp32 A (A32 null) it adds (b / c) A[i][j] here, the epilogue
   // scaling the sum by c.
   auto add_ax = [&](const OP* Qs, int64_t kt) {
     if constexpr (EPI >= EPI_APPLY || EPI == EPI_POLY) {
-      if (EPI == EPI_POLY ? g.A32 == nullptr : g.X32 == nullptr) {
+      if (EPI != EPI_POLY || g.A32 == nullptr) {
         const int64_t krel = kt * C::BK - (i0 + wm * C::WTM);
         if (krel > -C::BK && krel < C::WTM) {
 #pragma unroll
@@ -799,6 +817,12 @@ tl_gemm(GemmArgs g) {
     bool ndq = false;
     const OP* pb = reinterpret_cast<const OP*>(g.P) + mat * g.strideP + i0 * g.ldp;
     const OP* qb = reinterpret_cast<const OP*>(g.Q) + mat * g.strideQ + (QN ? j0 : j0 * g.ldq);
+    // compensated apply: the second half of K reads the input's R, which
+    // has Q's layout, so its slices sit dq2 elements from X~'s (both lie in
+    // the workspace; an offset rather than a second pointer keeps the
+    // compiler from spilling the loop)
+    const int64_t ksw = COMP && EPI >= EPI_APPLY ? g.kswitch : 0;
+    const int64_t dq2 = ksw > 0 ? (reinterpret_cast<const OP*>(g.Q2) - reinterpret_cast<const OP*>(g.Q)) : 0;
     const OP* npb = pb;
     const OP* nqb = qb;
     // operands of the next tile, whose first slice the last slice loads
@@ -870,9 +894,11 @@ tl_gemm(GemmArgs g) {
     // step's fragment reads issued before its burst, is slower still.
     auto slice = [&](int st, int64_t kt) {
       const bool last = kt + 1 == KT;
+      const bool sw = ksw > 0 && kt + 1 >= ksw;   // the next slice is one of R's
       const OP* lp = last ? npb : pb;
-      const OP* lq = last ? nqb : qb;
-      const int64_t lk = last ? 0 : (kt + 1) * C::BK;
+      const int64_t kb = sw ? ksw : 0;
+      const OP* lq = last ? nqb : qb + (sw ? dq2 : 0);
+      const int64_t lk = last ? 0 : (kt + 1 - kb) * C::BK;
       const bool lskip = last ? ndq : dq;
       dma_slice(st ^ 1, lp, lq, lk, lskip, 0, HALF);
       read_frags(1, st, 1);
@@ -890,8 +916,9 @@ tl_gemm(GemmArgs g) {
       __builtin_amdgcn_sched_barrier(0);
       mfmas(1);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (QN) add_ax(lds + st * C::STAGE + C::BM * C::LD, kt);
-      else add_ax(lds + st * C::STAGE + (qrow0 + wn * C::WTN + (lane & 31)) * C::LD, kt);
+      const int64_t ke = ksw > 0 && kt >= ksw ? kt - ksw : kt;   // k-slice within its half
+      if constexpr (QN) add_ax(lds + st * C::STAGE + C::BM * C::LD, ke);
+      else add_ax(lds + st * C::STAGE + (qrow0 + wn * C::WTN + (lane & 31)) * C::LD, ke);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this wave's loads of the next slice
       if (dyn && kt == kpub && w == 0) {
         const int64_t nb = take_resolve(tried);
@@ -911,6 +938,9 @@ tl_gemm(GemmArgs g) {
   const OP* Pp = reinterpret_cast<const OP*>(g.P) + mat * g.strideP + (i0 + r0) * g.ldp + cv;
   const OP* Qp = reinterpret_cast<const OP*>(g.Q) + mat * g.strideQ + (j0 + r0) * g.ldq + cv;
   const int64_t pstep = (int64_t)C::RPP * g.ldp, qstep = (int64_t)C::RPP * g.ldq;
+  // compensated apply: the second half of K reads the input's R instead
+  const int64_t ksw = COMP && EPI >= EPI_APPLY ? g.kswitch : 0;
+  const OP* Qp2 = ksw > 0 ? reinterpret_cast<const OP*>(g.Q2) + mat * g.strideQ + (j0 + r0) * g.ldq + cv : Qp;
 
   StageRegs<C> sr;
   stage_load<C>(sr, Pp, Qp, pstep, qstep, 0);
@@ -918,7 +948,10 @@ tl_gemm(GemmArgs g) {
   __syncthreads();
   for (int64_t kt = 0; kt < KT; ++kt) {
     const int st = (int)(kt & 1);
-    if (kt + 1 < KT) stage_load<C>(sr, Pp, Qp, pstep, qstep, (kt + 1) * C::BK);
+    if (kt + 1 < KT) {
+      const bool sw = ksw > 0 && kt + 1 >= ksw;
+      stage_load<C>(sr, Pp, sw ? Qp2 : Qp, pstep, qstep, (kt + 1 - (sw ? ksw : 0)) * C::BK);
+    }
     const OP* Ps = lds + st * C::STAGE + (wm * C::WTM + (lane & 31)) * C::LD;
     const OP* Qs = lds + st * C::STAGE + (C::BM + wn * C::WTN + (lane & 31)) * C::LD;
     if constexpr (sizeof(OP) == 2) {
@@ -952,7 +985,7 @@ tl_gemm(GemmArgs g) {
             acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[ib], bv[jb], acc[ib][jb], 0, 0, 0);
       }
     }
-    add_ax(Qs, kt);
+    add_ax(Qs, ksw > 0 && kt >= ksw ? kt - ksw : kt);
     if (kt + 1 < KT) stage_store<C>(sr, lds + (st ^ 1) * C::STAGE + r0 * C::LD + cv);
     __syncthreads();
   }
@@ -982,6 +1015,36 @@ tl_gemm(GemmArgs g) {
       for (int r = 0; r < 16; ++r)
         stg[mfma32_row(lane, r) * SLD + jb * 32 + (lane & 31)] = acc[ib][2 * jp + jb][r];
     wave_sync();
+    if constexpr (C::DIRECT && (EPI == EPI_APPLY || EPI == EPI_LAST_T)) {
+      // the master (R row-major): a R joins the staged block, read by rows,
+      // 8 columns per lane, so the four 16-byte loads of a lane are in flight
+      // together (the column layout below would need 32 2-byte loads)
+      if (g.Rin) {
+        const bf16_t* Ri = g.Rin + mat * g.strideX;
+        const int rr = lane >> 3, cc = (lane & 7) * 8;
+        const uint32_t rw = (uint32_t)(i0 + wm * C::WTM + ib * 32 + rr);
+        const uint32_t cw = (uint32_t)(j0 + wn * C::WTN + jp * 64 + cc);
+        u32x4 raw[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          raw[p] = *reinterpret_cast<const u32x4*>(at32(Ri, (rw + 8 * p) * (uint32_t)g.ldx + cw));
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          float* srow = stg + (rr + 8 * p) * SLD + cc;
+          f32x4 lo = *reinterpret_cast<const f32x4*>(srow), hi = *reinterpret_cast<const f32x4*>(srow + 4);
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            lo[2 * e] += g.ca * __uint_as_float(raw[p][e] << 16);
+            lo[2 * e + 1] += g.ca * __uint_as_float(raw[p][e] & 0xffff0000u);
+            hi[2 * e] += g.ca * __uint_as_float(raw[p][e + 2] << 16);
+            hi[2 * e + 1] += g.ca * __uint_as_float(raw[p][e + 2] & 0xffff0000u);
+          }
+          *reinterpret_cast<f32x4*>(srow) = lo;
+          *reinterpret_cast<f32x4*>(srow + 4) = hi;
+        }
+        wave_sync();
+      }
+    }
     float o[32];
     if constexpr (EPI != EPI_LAST) {   // lane l: column l of the block, 32 rows
 #pragma unroll
@@ -1037,50 +1100,52 @@ tl_gemm(GemmArgs g) {
     } else if constexpr (EPI == EPI_APPLY) {
       const uint32_t ldx = (uint32_t)g.ldx;
       OP* X = reinterpret_cast<OP*>(g.X) + mat * g.strideX;
-      float* X32 = g.X32 ? g.X32 + mat * g.strideX : nullptr;
-      // a X is in the accumulators already, except with the fp32 master;
-      // first step: X' = inv (a U + B U).
-      // four quarters of 8 rows: the reads of a quarter are issued together
+      // a X~ is in the accumulators (compensated: a R and B R too); with the
+      // master, a R is added here.  First step: X' = inv (a U + B U).
       const float sc = g.inv0 ? g.inv0[mat] : 1.f;
+      if constexpr (QN) {
+        // R row-major, like X (a R came in with the staged block)
+        bf16_t* Ro = g.Rout ? g.Rout + mat * g.strideX : nullptr;
 #pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        if (X32) {
-          float xv[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) xv[q] = X32[(ib0 + 8 * hh + q) * ldx + jj];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            o[8 * hh + q] = sc * (g.ca * xv[q] + o[8 * hh + q]);
-            X32[(ib0 + 8 * hh + q) * ldx + jj] = o[8 * hh + q];
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) o[8 * hh + q] *= sc;
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) st_from_f32(X, (ib0 + 8 * hh + q) * ldx + jj, o[8 * hh + q]);
-        if constexpr (RES && QN) {
-          bf16_t* R = reinterpret_cast<bf16_t*>(g.R) + mat * g.strideX;
+        for (int hh = 0; hh < 4; ++hh) {
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
-            const float v = o[8 * hh + q];
-            R[(ib0 + 8 * hh + q) * ldx + jj] = f2bf(v - bf2f(f2bf(v)));
+            o[8 * hh + q] *= sc;
+            *at32(X, (ib0 + 8 * hh + q) * ldx + jj) = f2bf(o[8 * hh + q]);
+          }
+          if (Ro) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) *at32(Ro, (ib0 + 8 * hh + q) * ldx + jj) = f2bf(bf_res(o[8 * hh + q]));
           }
         }
-      }
-      if constexpr (!QN)   // the next apply reads X^T
-        store_run32(reinterpret_cast<OP*>(g.XT) + mat * g.strideX + jj * (uint32_t)g.ldxt + ib0, o);
-      if constexpr (RES && !QN) {
-        float r[32];
+      } else {
+        // the next apply reads X^T; R sits as X^T too, so the lane's 32 rows
+        // of it are 32 contiguous elements
+        const uint32_t tofs = jj * (uint32_t)g.ldxt + ib0;
+        if (g.Rin) {
+          float rv[32];
+          load_run32(g.Rin + mat * g.strideX + tofs, rv);
 #pragma unroll
-        for (int q = 0; q < 32; ++q) r[q] = o[q] - bf2f(f2bf(o[q]));
-        store_run32(reinterpret_cast<bf16_t*>(g.R) + mat * g.strideX + jj * (uint32_t)g.ldxt + ib0, r);
+          for (int q = 0; q < 32; ++q) o[q] += g.ca * rv[q];
+        }
+#pragma unroll
+        for (int q = 0; q < 32; ++q) {
+          o[q] *= sc;
+          st_from_f32(X, (ib0 + q) * ldx + jj, o[q]);
+        }
+        store_run32(reinterpret_cast<OP*>(g.XT) + mat * g.strideX + tofs, o);
+        if (g.Rout) {
+          float r[32];
+#pragma unroll
+          for (int q = 0; q < 32; ++q) r[q] = bf_res(o[q]);
+          store_run32(g.Rout + mat * g.strideX + tofs, r);
+        }
       }
     } else {
       float ulr = g.lr, uwd = g.wd;
       update_scalars(g.lrwd, ulr, uwd);
       const uint32_t ldx = (uint32_t)g.ldx;
-      const float* X32 = g.X32 ? g.X32 + mat * g.strideX : nullptr;
+      const bf16_t* Ri = g.Rin ? g.Rin + mat * g.strideX : nullptr;   // the master: a R joins a X~
       PT* W = batch_view(reinterpret_cast<PT*>(g.param), g.tabs.param, mat, g.m * g.n);
       float* O = batch_view(g.ns_out, g.tabs.ns, mat, g.m * g.n);
       if (W) W += mat * g.m * g.n;
@@ -1095,7 +1160,7 @@ tl_gemm(GemmArgs g) {
       };
       if constexpr (EPI == EPI_LAST) {
         // W row-major: the lane takes 8 consecutive columns of rows rr, rr + 8,
-        // rr + 16, rr + 24 of the staged block, so W, the fp32 master and O move
+        // rr + 16, rr + 24 of the staged block, so W, the master's R and O move
         // as 16-byte vectors (8 lanes per 128-byte row segment), and all reads
         // of the round are issued before its stores.
         const int rr = lane >> 3, cc = (lane & 7) * 8;
@@ -1114,14 +1179,21 @@ tl_gemm(GemmArgs g) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           float xv[8];
-          if (X32) load8(X32 + (ib0 + rr + 8 * p) * ldx + j, xv);   // padded rows and columns: always readable
+          if (Ri) {   // padded rows and columns: always readable
+            if constexpr (C::DIRECT) {
+              load8(at32(Ri, (ib0 + rr + 8 * p) * ldx + j), xv);
+            } else {   // R as X^T
+#pragma unroll
+              for (int q = 0; q < 8; ++q) xv[q] = bf2f(Ri[(j + q) * (uint32_t)g.ldxt + ib0 + rr + 8 * p]);
+            }
+          }
           float ov[8];
           const f32x4 a = *reinterpret_cast<const f32x4*>(stg + (rr + 8 * p) * SLD + cc);
           const f32x4 b = *reinterpret_cast<const f32x4*>(stg + (rr + 8 * p) * SLD + cc + 4);
 #pragma unroll
           for (int q = 0; q < 4; ++q) { ov[q] = a[q]; ov[q + 4] = b[q]; }
           const uint32_t i = ib0 + rr + 8 * p;
-          if (X32) {
+          if (Ri) {
 #pragma unroll
             for (int q = 0; q < 8; ++q) ov[q] = g.ca * xv[q] + ov[q];
           }
@@ -1155,15 +1227,12 @@ tl_gemm(GemmArgs g) {
         }
       } else {
         if (jj < n) {
-          if (X32) {
-            // four quarters of 8 rows: the reads of a quarter are issued together
+          if constexpr (!C::DIRECT) {   // (direct loads: a R came in with the staged block)
+            if (Ri) {   // R as X^T: the lane's 32 rows are contiguous
+              float rv[32];
+              load_run32(Ri + jj * (uint32_t)g.ldxt + ib0, rv);
 #pragma unroll
-            for (int hh = 0; hh < 4; ++hh) {
-              float xh[8];
-#pragma unroll
-              for (int q = 0; q < 8; ++q) xh[q] = X32[(ib0 + 8 * hh + q) * ldx + jj];   // padded rows: readable
-#pragma unroll
-              for (int q = 0; q < 8; ++q) o[8 * hh + q] = g.ca * xh[q] + o[8 * hh + q];
+              for (int q = 0; q < 32; ++q) o[q] = g.ca * rv[q] + o[q];
             }
           }
           if (g.inv0) {   // K = 1: X held U unscaled
@@ -1213,13 +1282,13 @@ tl_update(PT* __restrict__ W, const float* __restrict__ O, int64_t total, float 
 // Persistent grid of tl_gemm<C, EPI, PT>: one wave of resident workgroups
 // (a multiple of 8, so each stays on one XCD), or fewer if there are fewer
 // tiles.
-template <class C, int EPI, typename PT, bool ROWS = false, bool RES = false>
+template <class C, int EPI, typename PT, bool ROWS = false, bool COMP = false>
 unsigned gemm_grid(int64_t tiles) {
   static std::atomic<int> per_dev[kMaxDevices];   // resident workgroups of this kernel per device
   const int64_t slots = per_device_cached(per_dev, [](int dev) {
     int cus = 0, blocks = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, tl_gemm<C, EPI, PT, ROWS, RES>, C::THREADS, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, tl_gemm<C, EPI, PT, ROWS, COMP>, C::THREADS, 0) != hipSuccess ||
         blocks <= 0)
       blocks = 1;
     return cus * blocks;
@@ -1232,13 +1301,14 @@ unsigned gemm_grid(int64_t tiles) {
 // row-major buffer, the apply reads X row-major and writes the next X to
 // the other buffer.  Otherwise XT holds X^T (ping-pong) and X is updated in
 // place.
-// R (compensated mode, else null): the bf16 residues X - bf16(X) of the
-// step's input (R[k & 1], in the layout the apply reads X) and of its output
-// (R[(k + 1) & 1]).
+// R (the master, else null): the residues bf16(X - bf16(X)) of step k's
+// input in R[k & 1] and of its output in R[(k + 1) & 1], in the layout in
+// which the apply reads X.  comp: the apply also multiplies B by the input's
+// R (one launch over K = 2 m).
 template <class C, typename PT>
 hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C::Op* X, typename C::Op* X1,
-                            typename C::Op* XT[2], float* X32, float* A32, bf16_t* A16, typename C::Op* PB,
-                            int64_t mp, int64_t np, const float* inv, unsigned* sched, bf16_t* const* R) {
+                            typename C::Op* XT[2], bf16_t* const* R, bool comp, float* A32, bf16_t* A16,
+                            typename C::Op* PB, int64_t mp, int64_t np, const float* inv, unsigned* sched) {
   typedef typename C::Op OP;
   hipError_t e;
   if (C::DIRECT ? X1 == nullptr : (XT[0] == nullptr || XT[1] == nullptr)) return hipErrorInvalidValue;
@@ -1247,7 +1317,7 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
   const int64_t tri = (C::BM / C::BN) * tm * (tm + 1) / 2;   // triangle tiles
   for (int k = 0; k < a.steps; ++k) {
     const float ca = a.coeffs[3 * k], cb = a.coeffs[3 * k + 1], cc = a.coeffs[3 * k + 2];
-    // bf16 products (with or without the fp32 master of X): the poly takes
+    // bf16 products (with or without the master of X): the poly takes
     // b A from its bf16 A operand tiles in LDS, so B = b A + c A A is one
     // polynomial of the same bf16 A (b A from an fp32 copy makes B a
     // polynomial of two slightly different matrices, which costs accuracy),
@@ -1289,7 +1359,15 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
     }
     g.tiles_n = tn; g.tiles_per_mat = tm * tn; g.tiles_total = sh.count * tm * tn;
     g.inv0 = k == 0 ? inv : nullptr;
-    g.ca = ca; g.X32 = X32; g.ldx = np; g.ldxt = mp; g.strideX = mp * np;
+    g.ca = ca; g.ldx = np; g.ldxt = mp; g.strideX = mp * np;
+    if (R) {
+      if (comp) {   // K = 2 m: B X~ over the first half, B R over the second
+        g.Q2 = R[k & 1]; g.kswitch = mp / C::BK; g.K = 2 * mp;
+      } else {
+        g.Rin = R[k & 1];
+      }
+      if (k + 1 < a.steps) g.Rout = R[(k + 1) & 1];
+    }
     if (C::DIRECT) {
       g.X = Xb[(k + 1) & 1]; g.XT = nullptr;
     } else {
@@ -1301,63 +1379,49 @@ hipError_t run_products_cfg(const StepArgs& a, const BatchShape& sh, typename C:
     g.tabs = a.phase == PH_FULL ? a.tabs : MatTabs{};
     g.m = sh.m; g.n = sh.n; g.transposed = sh.transposed;
     const bool rows = g.tabs.param_rows != nullptr;   // W through a row table
+    auto launch = [&](auto comp_tag) {
+      constexpr bool CP = decltype(comp_tag)::value;
+      if (g.last && !sh.transposed && rows)
+        MUON_LAUNCH("tl_apply_update", (tl_gemm<C, EPI_LAST, PT, true, CP>),
+                    dim3(gemm_grid<C, EPI_LAST, PT, true, CP>(g.tiles_total)), dim3(C::THREADS), a.stream, g);
+      else if (g.last && !sh.transposed)
+        MUON_LAUNCH("tl_apply_update", (tl_gemm<C, EPI_LAST, PT, false, CP>),
+                    dim3(gemm_grid<C, EPI_LAST, PT, false, CP>(g.tiles_total)), dim3(C::THREADS), a.stream, g);
+      else if (g.last && rows)
+        MUON_LAUNCH("tl_apply_update", (tl_gemm<C, EPI_LAST_T, PT, true, CP>),
+                    dim3(gemm_grid<C, EPI_LAST_T, PT, true, CP>(g.tiles_total)), dim3(C::THREADS), a.stream, g);
+      else if (g.last)
+        MUON_LAUNCH("tl_apply_update", (tl_gemm<C, EPI_LAST_T, PT, false, CP>),
+                    dim3(gemm_grid<C, EPI_LAST_T, PT, false, CP>(g.tiles_total)), dim3(C::THREADS), a.stream, g);
+      else
+        MUON_LAUNCH("tl_apply", (tl_gemm<C, EPI_APPLY, PT, false, CP>),
+                    dim3(gemm_grid<C, EPI_APPLY, PT, false, CP>(g.tiles_total)), dim3(C::THREADS), a.stream, g);
+    };
     if constexpr (sizeof(OP) == 2) {
-      if (R) {
-        // compensated mode, two products: X' = a X + B bf16(X) into the
-        // master (first step: unscaled, no update), then
-        // X' += B bf16(X - bf16(X)) from the residue, which applies the first
-        // step's 1 / (||U|| + eps) to the sum, writes the next residue or, in
-        // the last step, updates W
-        GemmArgs g1 = g;
-        g1.inv0 = nullptr; g1.last = 0; g1.param = nullptr; g1.ns_out = nullptr; g1.tabs = MatTabs{};
-        MUON_LAUNCH("tl_apply", (tl_gemm<C, EPI_APPLY, PT>), dim3(gemm_grid<C, EPI_APPLY, PT>(g1.tiles_total)),
-                    dim3(C::THREADS), a.stream, g1);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        g.Q = R[k & 1];   // same layout and strides as the X operand above
-        g.ca = 1.f;
-        if (!g.last) {
-          g.R = R[(k + 1) & 1];
-          MUON_LAUNCH("tl_apply_comp", (tl_gemm<C, EPI_APPLY, PT, false, true>),
-                      dim3(gemm_grid<C, EPI_APPLY, PT, false, true>(g.tiles_total)), dim3(C::THREADS), a.stream, g);
-          if ((e = hipGetLastError()) != hipSuccess) return e;
-          continue;
-        }
-      }
+      if (g.kswitch > 0) launch(std::true_type{});
+      else launch(std::false_type{});
+    } else {
+      launch(std::false_type{});
     }
-    if (g.last && !sh.transposed && rows)
-      MUON_LAUNCH("tl_apply_update", (tl_gemm<C, EPI_LAST, PT, true>),
-                  dim3(gemm_grid<C, EPI_LAST, PT, true>(g.tiles_total)), dim3(C::THREADS), a.stream, g);
-    else if (g.last && !sh.transposed)
-      MUON_LAUNCH("tl_apply_update", (tl_gemm<C, EPI_LAST, PT>), dim3(gemm_grid<C, EPI_LAST, PT>(g.tiles_total)),
-                  dim3(C::THREADS), a.stream, g);
-    else if (g.last && rows)
-      MUON_LAUNCH("tl_apply_update", (tl_gemm<C, EPI_LAST_T, PT, true>),
-                  dim3(gemm_grid<C, EPI_LAST_T, PT, true>(g.tiles_total)), dim3(C::THREADS), a.stream, g);
-    else if (g.last)
-      MUON_LAUNCH("tl_apply_update", (tl_gemm<C, EPI_LAST_T, PT>),
-                  dim3(gemm_grid<C, EPI_LAST_T, PT>(g.tiles_total)), dim3(C::THREADS), a.stream, g);
-    else
-      MUON_LAUNCH("tl_apply", (tl_gemm<C, EPI_APPLY, PT>), dim3(gemm_grid<C, EPI_APPLY, PT>(g.tiles_total)),
-                  dim3(C::THREADS), a.stream, g);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
 template <typename OP, typename PT>
-hipError_t run_products(const StepArgs& a, const BatchShape& sh, OP* X, OP* X1, OP* XT[2], float* X32, float* A32,
-                        bf16_t* A16, OP* PB, int64_t mp, int64_t np, bool big_tiles, const float* inv,
-                        unsigned* sched, bf16_t* const* R) {
+hipError_t run_products(const StepArgs& a, const BatchShape& sh, OP* X, OP* X1, OP* XT[2], bf16_t* const* R, bool comp,
+                        float* A32, bf16_t* A16, OP* PB, int64_t mp, int64_t np, bool big_tiles, const float* inv,
+                        unsigned* sched) {
   if constexpr (sizeof(OP) == 4) {
     if (big_tiles || R) return hipErrorInvalidValue;
-    return run_products_cfg<CfgF32, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, inv, nullptr, nullptr);
+    return run_products_cfg<CfgF32, PT>(a, sh, X, X1, XT, nullptr, false, A32, A16, PB, mp, np, inv, nullptr);
   } else {
     // the tile choice is the workspace's (use_big_tiles)
     if (big_tiles) {
       if (mp % CfgBig::BM != 0 || np % CfgBig::BN != 0) return hipErrorInvalidValue;
-      return run_products_cfg<CfgBig, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, inv, sched, R);
+      return run_products_cfg<CfgBig, PT>(a, sh, X, X1, XT, R, comp, A32, A16, PB, mp, np, inv, sched);
     }
-    return run_products_cfg<CfgSmall, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, inv, nullptr, R);
+    return run_products_cfg<CfgSmall, PT>(a, sh, X, X1, XT, R, comp, A32, A16, PB, mp, np, inv, nullptr);
   }
 }
 
@@ -1370,9 +1434,8 @@ hipError_t tiled_impl(const StepArgs& a, const WsLayout& L) {
   OP* X = (OP*)(a.ws + L.x);
   OP* X1 = L.big_tiles ? (OP*)(a.ws + L.x1) : nullptr;
   OP* XT[2] = {L.big_tiles ? nullptr : (OP*)(a.ws + L.xt0), L.big_tiles ? nullptr : (OP*)(a.ws + L.xt1)};
-  float* X32 = has_master(a.prec) ? (float*)(a.ws + L.x32) : nullptr;
   bf16_t* Rbuf[2] = {(bf16_t*)(a.ws + L.r0), (bf16_t*)(a.ws + L.r1)};
-  bf16_t* const* R = a.prec == PREC_BF16_X32C ? Rbuf : nullptr;
+  bf16_t* const* R = has_master(a.prec) ? Rbuf : nullptr;   // the master's residues
   float* A32 = (float*)(a.ws + L.a32);
   bf16_t* A16 = a.prec == PREC_F32 ? nullptr : (bf16_t*)(a.ws + L.a16);
   OP* PB = (OP*)(a.ws + L.pb);
@@ -1382,13 +1445,14 @@ hipError_t tiled_impl(const StepArgs& a, const WsLayout& L) {
   // vector form: 16-byte runs of a stored row (n elements, m when stored transposed)
   const int vec = mode == 0 && !XT[0] && (sh.transposed ? sh.m : sh.n) % 8 == 0;
   const MatTabs ftabs = a.phase == PH_FULL ? a.tabs : MatTabs{};
+  bf16_t* R0 = R ? R[0] : nullptr;   // the first step's input residue
   if (ftabs.grad_rows)   // the gradient through a row table
     MUON_LAUNCH("tl_momentum_layout", (tl_first<GT, OP, true>), dim3((unsigned)(sh.count * L.nparts)), dim3(256),
-                a.stream, mode, vec, (const GT*)a.grad, a.mom, a.u_in, ssp, X, XT[0], X32, sh.m, sh.n, mp, np,
+                a.stream, mode, vec, (const GT*)a.grad, a.mom, a.u_in, ssp, X, XT[0], R0, sh.m, sh.n, mp, np,
                 (int)sh.transposed, a.mu, a.nesterov, ftabs);
   else
     MUON_LAUNCH("tl_momentum_layout", (tl_first<GT, OP, false>), dim3((unsigned)(sh.count * L.nparts)), dim3(256),
-                a.stream, mode, vec, (const GT*)a.grad, a.mom, a.u_in, ssp, X, XT[0], X32, sh.m, sh.n, mp, np,
+                a.stream, mode, vec, (const GT*)a.grad, a.mom, a.u_in, ssp, X, XT[0], R0, sh.m, sh.n, mp, np,
                 (int)sh.transposed, a.mu, a.nesterov, ftabs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1396,15 +1460,8 @@ hipError_t tiled_impl(const StepArgs& a, const WsLayout& L) {
   MUON_LAUNCH("tl_norm_finalize", tl_norm_finalize, dim3((unsigned)sh.count), dim3(256), a.stream, ssp, L.nparts,
               a.eps, inv, sched, kSchedSlots * kSchedPerLaunch);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (R) {   // the residue of the first step's input (U), where the first apply reads X
-    const int64_t total = sh.count * mp * np;
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    MUON_LAUNCH("tl_residual", tl_residual, dim3((unsigned)blocks), dim3(256), a.stream, X32, R[0], sh.count, mp, np,
-                L.big_tiles ? 0 : 1);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  return run_products<OP, PT>(a, sh, X, X1, XT, X32, A32, A16, PB, mp, np, L.big_tiles, inv, sched, R);
+  return run_products<OP, PT>(a, sh, X, X1, XT, R, a.prec == PREC_BF16_X32C, A32, A16, PB, mp, np, L.big_tiles, inv,
+                              sched);
 }
 
 template <typename OP>

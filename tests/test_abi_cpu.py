@@ -128,11 +128,12 @@ def test_workspace_bytes():
             assert w > 0 and w % 256 == 0
     tiled = [b for b in p.batches if b.M == 300][0]   # short side 200: bf16 placements apply
     assert p.workspace_bytes(tiled.index, "bf16_x32") > p.workspace_bytes(tiled.index, "bf16")
-    # the compensated mode adds two bf16 residue buffers of X (2 x 256 x 384
-    # padded) on the tiled path; the skinny path runs it as the master mode,
-    # short sides 33..127 as fp32
+    # the master is two bf16 residue buffers of X (2 x 256 x 384 padded) on
+    # the tiled path; the compensated mode needs nothing more, and the
+    # skinny path runs it as the master mode, short sides 33..127 as fp32
     xe = 2 * 256 * 384
-    assert p.workspace_bytes(tiled.index, "bf16_x32c") == p.workspace_bytes(tiled.index, "bf16_x32") + 2 * xe * 2
+    assert p.workspace_bytes(tiled.index, "bf16_x32") == p.workspace_bytes(tiled.index, "bf16") + 2 * xe * 2
+    assert p.workspace_bytes(tiled.index, "bf16_x32c") == p.workspace_bytes(tiled.index, "bf16_x32")
     sk = [b for b in p.batches if b.M == 24][0]
     assert p.workspace_bytes(sk.index, "bf16_x32c") == p.workspace_bytes(sk.index, "bf16_x32")
     mid = B.Plan([(100, 700)] * 2)

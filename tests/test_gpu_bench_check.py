@@ -1,6 +1,6 @@
 """The 16 x 8192x28672 + 16 x 28672x8192 workload at full size, in the launch
 configuration the benchmark times (all 16 batches through muon_step_batches on
-two streams, bf16 + fp32 master), checked the way the benchmark checks its
+two streams, bf16 + the master of X), checked the way the benchmark checks its
 first timed repetition: the two matrices with stored oracle values
 (tests/golden/large_8192x28672_samples.py) at their 4096 positions (O within
 the 3e-2 bar, W' within it plus the bf16 rounding of the stored W'), M'

@@ -2,8 +2,9 @@
 float64 oracle (tests/parity.py bars):
 
 * MUON_PREC_BF16 keeps X in bf16 between steps;
-* MUON_PREC_BF16_X32 keeps an fp32 master of X and adds a X from it, with the
-  products on the same bf16 operands.  The master carries the part of X that
+* MUON_PREC_BF16_X32 keeps a master of X (bf16(X) plus the bf16 rounding of
+  X - bf16(X)) and adds a X from it, with the products on the same bf16
+  operands.  The master carries the part of X that
   bf16 cannot hold (X - bf16(X)) into the next step with the weight a of the
   a X term.  For small singular values that is the polynomial's own slope
   (p(s) ~ a s), so they survive: on a rank-64-plus-noise matrix bf16 loses
