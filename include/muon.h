@@ -87,7 +87,7 @@ typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
  *                     is 0.86-0.99 times plain bf16's there, and on
  *                     ill-conditioned inputs it keeps the small singular
  *                     directions as the master mode does.  The apply's
- *                     flops double: the 8192 x 28672 step takes about 1.55
+ *                     flops double: the 8192 x 28672 step takes about 1.57
  *                     times as long as with MUON_PREC_BF16_X32, with the
  *                     same workspace.  Batches with a short side of at most
  *                     32 run it as MUON_PREC_BF16_X32 (their Gram-space
