@@ -58,7 +58,7 @@ def _seeded(plan, wl):
     return dev, host
 
 
-@pytest.mark.parametrize("prec", ["bf16", "bf16_x32", "f32"])
+@pytest.mark.parametrize("prec", ["bf16", "bf16_x32", "bf16_x32c", "f32"])
 @pytest.mark.parametrize("streams", [2, 3])
 def test_step_batches_matches_oracle_and_sequential(streams, prec):
     import torch

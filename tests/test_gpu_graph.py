@@ -45,7 +45,7 @@ def _fill(bm, wl, kinds):
 
 
 @pytest.mark.parametrize("streams", [1, 2])
-@pytest.mark.parametrize("prec", ["bf16", "f32"])
+@pytest.mark.parametrize("prec", ["bf16", "bf16_x32c", "f32"])
 def test_graph_replays_match_eager_and_oracle(prec, streams):
     import torch
     wl = WL.small_workload("graph", SHAPES, momentum_recipe="normal", wid=500)

@@ -12,8 +12,9 @@ would fail: a skipped tile leaves NaN or the previous call's values.
 The batch of 10 [2048, 2048] matrices gives 360 Gram and poly tiles and
 640 apply tiles, more than one tile per workgroup, so the 256 x 256
 products' dynamic tile order runs several rounds and takes tiles from other
-XCDs' ranges; the other cases cover 256 x 256 tiles in both orientations and
-precisions, 128 x 128 tiles and the skinny path in both Newton-Schulz forms.
+XCDs' ranges; the other cases cover 256 x 256 tiles in both orientations
+and in every bf16 precision, 128 x 128 tiles and the skinny path in both
+Newton-Schulz forms.
 """
 import pytest
 
@@ -24,6 +25,8 @@ pytestmark = pytest.mark.gpu
 CASES = [
     ("tiled_256_rounds", [(10, 2048, 2048)], 0, "bf16"),
     ("tiled_256_wide_x32", [(512, 1280)] * 3, 0, "bf16_x32"),
+    ("tiled_256_tall_x32c", [(1280, 512)] * 3, 0, "bf16_x32c"),
+    ("tiled_128_x32c", [(300, 700)] * 2, 0, "bf16_x32c"),
     ("tiled_256_tall", [(1280, 512)] * 3, 0, "bf16"),
     ("tiled_128", [(300, 700)] * 2, 0, "bf16"),
     ("skinny_fused", [(24, 3000)] * 5, 0, "bf16"),
