@@ -81,7 +81,7 @@ def test_well_conditioned_both_modes(name):
 
 def test_ill_conditioned_needs_the_master():
     """Rank-64 plus N(0, 0.01) noise (the large workload's recipe at 1024 x 3584):
-    plain bf16 loses the small singular values, the fp32 master keeps them."""
+    plain bf16 loses the small singular values, the master keeps them."""
     wl = WL.small_workload("p_lr", [(1024, 3584)], grad_recipe="low_rank_noise", momentum_recipe="zeros", wid=704)
     plan = B.Plan([p.shape for p in wl.params])
     b = plan.batches[0]
