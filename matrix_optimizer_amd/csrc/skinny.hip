@@ -518,11 +518,16 @@ struct GramLds {
 // m x m) by a workgroup of NT threads: all of them load the partials, the
 // first SK_THREADS do the rest, every thread takes the barriers.  raw is
 // GramLds<MODE>::RAW bytes of LDS, free again when this returns (it ends with
-// a barrier).
-template <int MODE, int NT = SK_THREADS>
+// a barrier).  mid() runs in every thread once the partials are summed (the
+// loads of the workgroup's other work may start there without delaying the
+// partials).
+struct NoMid {
+  __device__ void operator()() const {}
+};
+template <int MODE, int NT = SK_THREADS, typename MID = NoMid>
 __device__ void gram_q(const float* __restrict__ gp, const float* __restrict__ sp, float eps, int m, int S, int T,
                        int steps, const Coeffs& cf, int64_t b, unsigned char* raw, float (*Qf)[SK_MP + 1],
-                       double* inv_s) {
+                       double* inv_s, MID mid = MID{}) {
   typedef typename GramLds<MODE>::R R;
   R* A = reinterpret_cast<R*>(raw);
   R* Bm = A + GS_MAT;
@@ -579,6 +584,7 @@ __device__ void gram_q(const float* __restrict__ gp, const float* __restrict__ s
     }
     __syncthreads();
   }
+  mid();
   const double inv = *inv_s;
 #pragma unroll
   for (int u = 0; u < 3; ++u) {
@@ -949,7 +955,12 @@ template <> struct Oct<bf16_t> {
     for (int q = 0; q < 4; ++q) v[q] = (uint32_t)f2bf(f[2 * q]) | ((uint32_t)f2bf(f[2 * q + 1]) << 16);
     *reinterpret_cast<u32x4*>(p) = v;
   }
-  static __device__ __forceinline__ V load(const bf16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+  // W is device memory: a global load (a pointer from a row table would
+  // otherwise make it a flat load, which also holds the LDS counter that the
+  // next barrier waits on)
+  static __device__ __forceinline__ V load(const bf16_t* p) {
+    return *(const __attribute__((address_space(1))) u32x4*)(p);
+  }
 };
 template <> struct Oct<float> {
   struct V { f32x4 a, b; };
@@ -959,7 +970,8 @@ template <> struct Oct<float> {
     *reinterpret_cast<f32x4*>(p + 4) = f32x4{f[4], f[5], f[6], f[7]};
   }
   static __device__ __forceinline__ V load(const float* p) {
-    return V{*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4)};
+    typedef const __attribute__((address_space(1))) f32x4* G;
+    return V{*(G)(p), *(G)(p + 4)};
   }
 };
 
@@ -1192,9 +1204,10 @@ sk_apply(const typename SkCfg<MODE>::XS* __restrict__ xg, const BFrag* __restric
 // with another copy's), then every wave applies it to its share of the
 // matrix's 64-column units exactly as sk_apply does, in both orientations of
 // W: wave w of workgroup r takes units r * NW + w + i * R * NW, so the R
-// workgroups sweep the matrix front to back together.  (Loading each wave's
-// first unit before Q was formed, to overlap the Newton-Schulz latency, made
-// the launch slower: those loads delay the partials Q needs first.)  For a
+// workgroups sweep the matrix front to back together.  The waves that do not
+// form Q load their first unit (U and a wide W) once the partials are summed,
+// while the iteration runs (loaded before the partials, they delayed the
+// partials Q needs first).  For a
 // row-major W the O buffers alias gram_q's LDS, which is free once Q is in Qf.
 // All waves take part in gram_q's barriers; after it there are none.
 //   NW = 16: bf16 operands (the 16-wave register budget, 128 per lane, holds
@@ -1262,19 +1275,14 @@ sk_ns_apply(const float* __restrict__ gp, const float* __restrict__ sp, float ep
     }
   };
 
-  gram_q<MODE, NW * WAVE>(gp, sp, eps, m, S, T, steps, cf, b, raw, Qf, &inv_s);
-  const BFrag fr = make_frag<MODE, true>(Qf, lane);
-
   uint32_t xr[2][2][XW];
   if constexpr (!TRANS) {
     typedef Oct<PT> OV;
     // W rows 8 i + lane / 8, columns 64 u + 8 (lane % 8) .. + 7 of unit u
     const int rr = lane >> 3, cc = (lane & 7) * 8;
     const int mr = 8 * G;
-    float* o = reinterpret_cast<float*>(raw) + w * mr * AP_LD;
     typename OV::V wv[4];
-    for (int64_t u = r * NW + w; u < upm; u += stride) {
-      load_u(u, xr);
+    auto load_w = [&](int64_t u) __attribute__((always_inline)) {
       const int64_t col0 = 64 * u + cc;
       if (has_w && vec) {
 #pragma unroll
@@ -1283,6 +1291,25 @@ sk_ns_apply(const float* __restrict__ gp, const float* __restrict__ sp, float ep
           if (i < G && row < m && col0 < n) wv[i] = OV::load(w_at(row, col0));
         }
       }
+    };
+    // The waves that do not form Q load their first unit (U and W) while the
+    // first four run the Newton-Schulz iteration, once the partials are in.
+    const int64_t u0 = r * NW + w;
+    const bool pre = w * WAVE >= SK_THREADS && u0 < upm;
+    gram_q<MODE, NW * WAVE>(gp, sp, eps, m, S, T, steps, cf, b, raw, Qf, &inv_s, [&]() {
+      if (pre) {
+        load_u(u0, xr);
+        load_w(u0);
+      }
+    });
+    const BFrag fr = make_frag<MODE, true>(Qf, lane);
+    float* o = reinterpret_cast<float*>(raw) + w * mr * AP_LD;
+    for (int64_t u = u0; u < upm; u += stride) {
+      if (!pre || u != u0) {
+        load_u(u, xr);
+        load_w(u);
+      }
+      const int64_t col0 = 64 * u + cc;
       wave_sync();   // this wave's reads of the previous unit's O are done
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
@@ -1329,6 +1356,8 @@ sk_ns_apply(const float* __restrict__ gp, const float* __restrict__ sp, float ep
       }
     }
   } else {
+    gram_q<MODE, NW * WAVE>(gp, sp, eps, m, S, T, steps, cf, b, raw, Qf, &inv_s);
+    const BFrag fr = make_frag<MODE, true>(Qf, lane);
     // stored-transposed W: O = Q U straight from the accumulators; quad qd of
     // block jj holds rows 8 qd + 4 h + 0..3 of column 32 jb + c (as sk_apply)
     typedef Quad<PT> QV;
