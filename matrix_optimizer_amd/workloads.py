@@ -115,7 +115,7 @@ class HParams:
     ns_steps: int = 5
     coeffs: Tuple[float, ...] = DEFAULT_COEFFS     # 3 (constant) or 3*ns_steps
     scale: str = "rms"                              # "rms" -> 0.2*sqrt(max(M,N)); "none" -> 1
-    precision: str = "bf16"                         # "bf16" | "bf16_x32" | "f32"
+    precision: str = "bf16"                         # "bf16" | "bf16_x32" | "bf16_x32c" | "f32"
 
 
 @dataclass
