@@ -334,13 +334,14 @@ def test_decoder_full_size_sampled():
               f"over {len(sampled)}, whole-matrix O errors {whole}")
 
 
-def test_large_8192x28672_golden_samples():
+@pytest.mark.parametrize("prec", ["bf16_x32", "bf16_x32c"])
+def test_large_8192x28672_golden_samples(prec):
     """The first batch of each orientation of the 8192x28672 workload at full
-    size (two matrices each, the bf16 + fp32-master placement); both matrices
-    of each are compared at 4096 positions with oracle values stored by
-    tests/golden/large_8192x28672_samples.py (O and W'; the main file holds
-    matrix 0 of each batch, the extra file matrix 1), and their M' in full
-    against the momentum update."""
+    size (two matrices each, bf16 products with the master of X, and with the
+    compensating half); both matrices of each are compared at 4096 positions
+    with oracle values stored by tests/golden/large_8192x28672_samples.py (O
+    and W'; the main file holds matrix 0 of each batch, the extra file matrix
+    1), and their M' in full against the momentum update."""
     import json
     import os
     here = os.path.join(os.path.dirname(__file__), "golden")
@@ -352,7 +353,7 @@ def test_large_8192x28672_golden_samples():
         for pi in meta["params"]:
             per_param[pi] = (gold, meta)
     wl = WL.WORKLOADS[meta["workload"]]
-    h = H.c_hparams(wl.hp)
+    h = H.c_hparams(wl.hp, precision=prec)
     plan = B.Plan([p.shape for p in wl.params])
     by_batch = {}
     for pi, (gold, meta) in per_param.items():
