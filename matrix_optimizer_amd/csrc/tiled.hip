@@ -1225,6 +1225,35 @@ tl_gemm(GemmArgs g) {
             }
           }
         }
+      } else if (C::DIRECT && ib0 + 32 <= m && (m % 8) == 0) {
+        // W is the transpose, its row j holding this block's column j: by W
+        // rows, 8 elements per lane, four lanes per 32-element row piece and
+        // 16 rows per round, so each access instruction covers 16 pieces of
+        // 64 bytes (a lane per row would touch 64 rows with 16 bytes each);
+        // the W reads of all four rounds go before their stores
+        const float sc = g.inv0 ? g.inv0[mat] : 1.f;   // K = 1: X held U unscaled
+        const int sub = lane & 3, jr = lane >> 2;
+        const uint32_t jb = (uint32_t)(j0 + wn * C::WTN + jp * 64 + jr);
+        Raw8<PT> wr[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          if (has_w && jb + 16 * p < n) wr[p].load(w_at(jb + 16 * p, ib0 + 8 * sub, m));
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t j = jb + 16 * p;
+          if (j >= n) continue;
+          float ov[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) ov[q] = sc * stg[(8 * sub + q) * SLD + 16 * p + jr];
+          if (O) store8(O + j * m + ib0 + 8 * sub, ov);
+          if (has_w) {
+            float wv[8], nw[8];
+            wr[p].to_f32(wv);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) nw[q] = apply_update(wv[q], ov[q], ulr, uwd, g.s);
+            store8(w_at(j, ib0 + 8 * sub, m), nw);
+          }
+        }
       } else {
         if (jj < n) {
           if constexpr (!C::DIRECT) {   // (direct loads: a R came in with the staged block)
