@@ -1104,19 +1104,22 @@ tl_gemm(GemmArgs g) {
       // master, a R is added here.  First step: X' = inv (a U + B U).
       const float sc = g.inv0 ? g.inv0[mat] : 1.f;
       if constexpr (QN) {
-        // R row-major, like X (a R came in with the staged block)
+        // R row-major, like X (a R came in with the staged block).  By rows
+        // of the staged block, 8 columns per lane: X' and R' leave as one
+        // 16-byte store per 8 rows each (not 32 two-byte stores)
         bf16_t* Ro = g.Rout ? g.Rout + mat * g.strideX : nullptr;
+        const int rr = lane >> 3, cc = (lane & 7) * 8;
+        const uint32_t col = (uint32_t)(j0 + wn * C::WTN + jp * 64 + cc);
 #pragma unroll
-        for (int hh = 0; hh < 4; ++hh) {
+        for (int p = 0; p < 4; ++p) {
+          const float* srow = stg + (rr + 8 * p) * SLD + cc;
+          const f32x4 lo = *reinterpret_cast<const f32x4*>(srow), hi = *reinterpret_cast<const f32x4*>(srow + 4);
+          float v[8];
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            o[8 * hh + q] *= sc;
-            *at32(X, (ib0 + 8 * hh + q) * ldx + jj) = f2bf(o[8 * hh + q]);
-          }
-          if (Ro) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) *at32(Ro, (ib0 + 8 * hh + q) * ldx + jj) = f2bf(bf_res(o[8 * hh + q]));
-          }
+          for (int e = 0; e < 4; ++e) { v[e] = sc * lo[e]; v[e + 4] = sc * hi[e]; }
+          const uint32_t idx = (ib0 + rr + 8 * p) * ldx + col;
+          store8(at32(X, idx), v);
+          if (Ro) store_res8(at32(Ro, idx), v);
         }
       } else {
         // the next apply reads X^T; R sits as X^T too, so the lane's 32 rows
